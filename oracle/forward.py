@@ -1,0 +1,121 @@
+"""Routing and the f64 forward of the 2-bit routed-expert MoE layer (test infrastructure; see
+oracle/__init__). Plain definitions, no blocking or fusion beyond what the definition states;
+numpy's matmul is the only library step.
+
+Definition (reading of the pages; the plain reading is stated where they are silent):
+* weights: W[r, k] = CODEBOOK[code[r, k]] * 2**(scale[r, k // 32] - 127)
+  (README bullet "2-bit expert planes - the sign-bias finding" for the codebook; "The v0.24.0
+  port", section "Our hooks", modelopt.py bullet for UE8M0 block-32 scales).
+* gate_up[e] holds 2I rows: rows 0..I-1 are the gate projection, rows I..2I-1 the up projection
+  (the pages are silent on the order; this is the usual fused w13 layout).
+* per pair (t, j) with expert e = ids[t, j]:  g = G_e x_t,  u = U_e x_t,
+  a = silu(g) * u with silu(z) = z / (1 + exp(-z)),  o = D_e a   (gated MLP; the pages name the
+  SiLU-gated product only through the method statement, not a formula).
+* y[t] = sum over j = 0..top_k-1 in ascending order of w[t, j] * o_(t, j)  ("Deterministic
+  unpermute" bullet: bijective per-pair placement, fixed-order sum). Pairs whose id is outside
+  [0, E) contribute nothing (reading; the pages' miss path zeroes a missing expert's
+  contribution - "The v0.24.0 port", BASE cache bullet).
+* routing: offsets = exclusive scan of per-expert pair counts; perm = the pair indices
+  p = t*top_k + j stably sorted by expert id, invalid ids last ("Deterministic unpermute" bullet:
+  valid sorted ids form a permutation of token*top_k+j).
+"""
+import numpy as np
+
+from .formats import CODEBOOK, unpack_codes
+
+_CODEBOOK = np.array(CODEBOOK, dtype=np.float64)
+
+
+def dequant_rows(packed, scale_bytes):
+    """Packed codes [rows, n/4] + UE8M0 scale bytes [rows, n/32] -> f64 weights [rows, n]."""
+    codes = unpack_codes(packed)
+    vals = _CODEBOOK[codes]
+    sb = np.asarray(scale_bytes).astype(np.int64)
+    if sb.size and (sb.max() > 254 or sb.min() < 0):
+        raise ValueError("UE8M0 scale byte out of range")
+    s = np.ldexp(1.0, sb - 127)
+    return vals * np.repeat(s, 32, axis=-1)
+
+
+def route(topk_ids, E):
+    """Stable expert sort of the pairs p = t*top_k + j.
+
+    Returns (offsets int32 [E+1], perm int32 [T*top_k]). offsets[E] counts the valid pairs;
+    perm[offsets[E]:] lists the invalid pairs (id outside [0, E)) in ascending order.
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    valid = (ids >= 0) & (ids < E)
+    counts = np.bincount(ids[valid], minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    key = np.where(valid, ids, E)
+    perm = np.argsort(key, kind="stable")
+    return offsets.astype(np.int32), perm.astype(np.int32)
+
+
+def silu(z):
+    """z * sigmoid(z) = z / (1 + exp(-z)) in f64."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None):
+    """Per-pair down-projection outputs o[(t, j)] in f64.
+
+    x: [T, K] f64 (the bf16 activations' exact values). Returns an array [len(tokens), top_k, K];
+    rows of invalid pairs are zero. ``tokens`` restricts the computation to a subset of tokens
+    (for spot checks of large workloads); default all tokens.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    T, K = x.shape
+    E, two_i, _ = gu_codes.shape
+    I = two_i // 2
+    top_k = ids.shape[1]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    out = np.zeros((len(tokens), top_k, K), dtype=np.float64)
+    sel = ids[tokens]  # [n_tok, top_k]
+    for e in np.unique(sel):
+        if e < 0 or e >= E:
+            continue
+        rows, js = np.nonzero(sel == e)
+        w_gu = dequant_rows(gu_codes[e], gu_scales[e])  # [2I, K]
+        w_dn = dequant_rows(dn_codes[e], dn_scales[e])  # [K, I]
+        xe = x[tokens[rows]]                              # [n_e, K]
+        g = xe @ w_gu[:I].T                               # [n_e, I]
+        u = xe @ w_gu[I:].T
+        a = silu(g) * u
+        out[rows, js] = a @ w_dn.T                        # [n_e, K]
+    return out
+
+
+def moe_forward(x, topk_ids, topk_w, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None):
+    """y[t] = sum_j (ascending) w[t, j] * o_(t, j); f64 [len(tokens), K]."""
+    o = pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens)
+    w = np.asarray(topk_w, dtype=np.float64)
+    tokens = np.arange(o.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    w = w[tokens]
+    y = np.zeros((o.shape[0], o.shape[2]), dtype=np.float64)
+    for j in range(o.shape[1]):
+        y += w[:, j:j + 1] * o[:, j]
+    return y
+
+
+def moe_forward_act(x, topk_ids, gu_codes, gu_scales, tokens=None):
+    """The gated intermediate a = silu(G x) * (U x) per pair, f64 [len(tokens), top_k, I]
+    (for localising a disagreement; not part of the layer's output)."""
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    E, two_i, _ = gu_codes.shape
+    I = two_i // 2
+    tokens = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    out = np.zeros((len(tokens), ids.shape[1], I), dtype=np.float64)
+    sel = ids[tokens]
+    for e in np.unique(sel):
+        if e < 0 or e >= E:
+            continue
+        rows, js = np.nonzero(sel == e)
+        w_gu = dequant_rows(gu_codes[e], gu_scales[e])
+        xe = x[tokens[rows]]
+        out[rows, js] = silu(xe @ w_gu[:I].T) * (xe @ w_gu[I:].T)
+    return out

@@ -1,0 +1,164 @@
+"""Pins for oracle.forward: routing against a hand-worked fixture and invariants; the forward
+against a library routine in its dense special case (E=1, top-1), hand-derived closed forms and
+exact invariants."""
+import os
+
+import numpy as np
+import torch
+
+from oracle import formats, forward
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_route_example():
+    d = {}
+    with open(os.path.join(GOLDEN, "route_example.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, rest = line.split(None, 1)
+            d[key] = rest
+    ids = np.array([[int(v) for v in tok.split()] for tok in d["ids"].split("|")], dtype=np.int32)
+    return ids, np.array(d["offsets"].split(), dtype=np.int32), np.array(d["perm"].split(), dtype=np.int32)
+
+
+def test_route_hand_example():
+    ids, offsets, perm = _read_route_example()
+    got_o, got_p = forward.route(ids, E=4)
+    assert np.array_equal(got_o, offsets)
+    assert np.array_equal(got_p, perm)
+
+
+def test_route_invariants():
+    rng = np.random.default_rng(3)
+    for T, E, k in [(1, 256, 8), (37, 16, 4), (500, 256, 8), (64, 8, 8)]:
+        ids = rng.integers(-2, E + 2, size=(T, k)).astype(np.int32)
+        offsets, perm = forward.route(ids, E)
+        flat = ids.reshape(-1)
+        assert sorted(perm.tolist()) == list(range(T * k))            # a permutation
+        assert offsets[0] == 0 and np.all(np.diff(offsets) >= 0)
+        valid = (flat >= 0) & (flat < E)
+        assert offsets[E] == valid.sum()
+        for e in range(E):
+            seg = perm[offsets[e]:offsets[e + 1]]
+            assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)  # stable
+        tail = perm[offsets[E]:]
+        assert np.all(~valid[tail]) and np.all(np.diff(tail) > 0)
+
+
+def _dense_weights_independent(packed, scale_bytes):
+    """Dequantize with torch's float8_e8m0fnu for the scale and the printed codebook."""
+    book = {}
+    with open(os.path.join(GOLDEN, "codebook.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                c, v = line.split()
+                book[int(c)] = float(v)
+    p = np.asarray(packed)
+    rows, nb = p.shape
+    vals = np.zeros((rows, nb * 4))
+    for sh in range(4):
+        codes = (p >> (2 * sh)) & 3
+        vals[:, sh::4] = np.vectorize(book.get)(codes)
+    s = torch.from_numpy(np.ascontiguousarray(scale_bytes, dtype=np.uint8)).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    return vals * np.repeat(s, 32, axis=1)
+
+
+def test_single_expert_top1_is_dense_silu_mlp():
+    """E = 1, top-1, weight 1: the layer is the dense gated MLP D (silu(G x) * (U x)), computed
+    here with torch's silu and matmul in float64 on independently dequantized weights."""
+    rng = np.random.default_rng(12)
+    T, K, I = 6, 64, 96
+    planes = workloads.draw_planes(rng, 1, K, I)
+    x = formats.bf16_bits_to_f64(workloads.draw_x(rng, T, K))
+    ids = np.zeros((T, 1), np.int32)
+    w = np.ones((T, 1), np.float32)
+    y = forward.moe_forward(x, ids, w, **planes)
+    wgu = torch.from_numpy(_dense_weights_independent(planes["gu_codes"][0], planes["gu_scales"][0]))
+    wdn = torch.from_numpy(_dense_weights_independent(planes["dn_codes"][0], planes["dn_scales"][0]))
+    xt = torch.from_numpy(x)
+    ref = torch.matmul(torch.nn.functional.silu(torch.matmul(xt, wgu[:I].T)) * torch.matmul(xt, wgu[I:].T), wdn.T)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12 * np.abs(ref.numpy()).max())
+
+
+def test_hand_case_all_plus_one():
+    """T=1, K=I=32, E=1: every code +1 (code 2), every scale byte 127 (2^0), x = 1. Then each gate
+    and up output is 32, a = 32 * sigmoid(32) * 32 for all 32 intermediate units, and every output
+    is 32 * a, scaled by the router weight 0.5."""
+    K = I = 32
+    gu = np.full((1, 2 * I, K // 4), 0xAA, np.uint8)       # 0b10101010 = four codes 2
+    gus = np.full((1, 2 * I, 1), 127, np.uint8)
+    dn = np.full((1, K, I // 4), 0xAA, np.uint8)
+    dns = np.full((1, K, 1), 127, np.uint8)
+    x = np.ones((1, K))
+    y = forward.moe_forward(x, np.zeros((1, 1), np.int32), np.full((1, 1), 0.5, np.float32), gu, gus, dn, dns)
+    a = 32.0 * 32.0 / (1.0 + np.exp(-32.0))
+    np.testing.assert_allclose(y, np.full((1, K), 0.5 * 32.0 * a), rtol=1e-15)
+
+
+def test_gate_and_up_are_not_swapped():
+    """Gate rows (0..I-1) all -1 and up rows (I..2I-1) all +1 with x = 20/32 per element give
+    g = -20, u = +20: a = silu(-20) * 20 ~ -4e-8. Swapping gate and up would give silu(20)*(-20)
+    = -400."""
+    K = I = 32
+    gu = np.concatenate([np.full((1, I, K // 4), 0x55, np.uint8),     # code 1 = -1
+                         np.full((1, I, K // 4), 0xAA, np.uint8)], axis=1)  # code 2 = +1
+    gus = np.full((1, 2 * I, 1), 127, np.uint8)
+    a = forward.moe_forward_act(np.full((1, K), 20.0 / 32.0), np.zeros((1, 1), np.int32), gu, gus)
+    want = -20.0 / (1.0 + np.exp(20.0)) * 20.0
+    np.testing.assert_allclose(a[0, 0], np.full(I, want), rtol=1e-13)
+
+
+def _tiny_inputs(seed=0):
+    d = workloads.tiny(seed)
+    x = formats.bf16_bits_to_f64(d["x"])
+    return d, x
+
+
+def test_linear_in_router_weights_and_invalid_ids_contribute_nothing():
+    d, x = _tiny_inputs()
+    P = dict(gu_codes=d["gu_codes"], gu_scales=d["gu_scales"], dn_codes=d["dn_codes"], dn_scales=d["dn_scales"])
+    w1 = d["topk_w"]
+    w2 = np.random.default_rng(1).uniform(-1, 1, w1.shape).astype(np.float32)
+    y1 = forward.moe_forward(x, d["topk_ids"], w1, **P)
+    y2 = forward.moe_forward(x, d["topk_ids"], w2, **P)
+    y12 = forward.moe_forward(x, d["topk_ids"], w1.astype(np.float64) + w2, **P)
+    np.testing.assert_allclose(y12, y1 + y2, rtol=1e-12, atol=1e-12 * np.abs(y1).max())
+    bad = d["topk_ids"].copy()
+    bad[:, 1] = -1
+    yb = forward.moe_forward(x, bad, w1, **P)
+    only0 = forward.moe_forward(x, d["topk_ids"][:, :1], w1[:, :1], **P)
+    assert np.array_equal(yb, only0)
+
+
+def test_duplicate_ids_sum_their_weights():
+    d, x = _tiny_inputs()
+    P = dict(gu_codes=d["gu_codes"], gu_scales=d["gu_scales"], dn_codes=d["dn_codes"], dn_scales=d["dn_scales"])
+    ids = np.stack([d["topk_ids"][:, 0]] * 2, axis=1)
+    w = np.array([[0.25, 0.5]] * d["T"], np.float32)
+    y = forward.moe_forward(x, ids, w, **P)
+    y1 = forward.moe_forward(x, ids[:, :1], np.full((d["T"], 1), 0.75, np.float32), **P)
+    np.testing.assert_allclose(y, y1, rtol=1e-13, atol=1e-14 * np.abs(y1).max())
+
+
+def test_down_scale_and_sign_invariants_are_exact():
+    """Down scale bytes + 1 double y exactly; down codes c -> 3 - c negate y exactly (f64)."""
+    d, x = _tiny_inputs()
+    P = dict(gu_codes=d["gu_codes"], gu_scales=d["gu_scales"], dn_codes=d["dn_codes"], dn_scales=d["dn_scales"])
+    y = forward.moe_forward(x, d["topk_ids"], d["topk_w"], **P)
+    P2 = dict(P, dn_scales=(d["dn_scales"] + 1).astype(np.uint8))
+    assert np.array_equal(forward.moe_forward(x, d["topk_ids"], d["topk_w"], **P2), 2 * y)
+    P3 = dict(P, dn_codes=(~d["dn_codes"]).astype(np.uint8))    # NOT of every 2-bit field = 3 - c
+    assert np.array_equal(forward.moe_forward(x, d["topk_ids"], d["topk_w"], **P3), -y)
+
+
+def test_token_subset_matches_full():
+    d, x = _tiny_inputs()
+    P = dict(gu_codes=d["gu_codes"], gu_scales=d["gu_scales"], dn_codes=d["dn_codes"], dn_scales=d["dn_scales"])
+    y = forward.moe_forward(x, d["topk_ids"], d["topk_w"], **P)
+    ys = forward.moe_forward(x, d["topk_ids"], d["topk_w"], tokens=[3, 1], **P)
+    # same arithmetic; BLAS may block a smaller batch differently, so allow f64 rounding
+    np.testing.assert_allclose(ys, y[[3, 1]], rtol=1e-12, atol=1e-14 * np.abs(y).max())
