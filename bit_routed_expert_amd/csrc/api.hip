@@ -1,0 +1,233 @@
+// C ABI of libmoew2 (declared in include/moe_w2.h): argument checks, workspace layout and the
+// sequence of kernel launches for each entry point.
+#include <string.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace moew2 {
+
+Workspace workspace_layout(int E, int K, int I, int T, int top_k) {
+  Workspace w;
+  memset(&w, 0, sizeof(w));
+  const int P = T * top_k;
+  w.P = P;
+  w.max_tiles = P > 0 ? P / kGemmBM + (E < P ? E : P) + 1 : 0;
+  size_t o = 0;
+  w.counters = o;  o += align_up(2 * sizeof(long long));
+  w.offsets = o;   o += align_up((size_t)(E + 1) * 4);
+  w.perm = o;      o += align_up((size_t)P * 4);
+  w.active = o;    o += align_up((size_t)E * 4);
+  w.meta = o;      o += align_up(8 * 4);
+  w.tiles = o;     o += align_up((size_t)w.max_tiles * 2 * 4);
+  const size_t rs = route_scratch_bytes(E, P);
+  w.chunk_cnt = o;
+  w.rank = o + (rs - align_up((size_t)P * 4));
+  o += rs;
+  w.act = o;       o += align_up((size_t)P * I * 2);
+  w.pair_out = o;  o += align_up((size_t)P * K * 4);
+  w.total = o;
+  return w;
+}
+
+static bool shape_ok(int E, int K, int I) {
+  return E >= 1 && E <= 1024 && K >= 256 && I >= 256 && K % 256 == 0 && I % 256 == 0;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_W2_OK : MOE_W2_EHIP; }
+
+}  // namespace moew2
+
+using namespace moew2;
+
+extern "C" {
+
+int moe_w2_abi_version(void) { return 1; }
+
+const char* moe_w2_status_string(int status) {
+  switch (status) {
+    case MOE_W2_OK: return "ok";
+    case MOE_W2_EINVAL: return "invalid argument (null pointer, negative size or bad enum value)";
+    case MOE_W2_EUNSUPPORTED: return "unsupported shape";
+    case MOE_W2_ESCALE: return "scale byte out of the representable range";
+    case MOE_W2_ENOMEM: return "device allocation failed";
+    case MOE_W2_EHIP: return "HIP runtime error";
+    case MOE_W2_EWORKSPACE: return "workspace missing or too small";
+    case MOE_W2_ENVFP4: return "NaN e4m3 scale or non-finite scale_2 in NVFP4 input";
+    default: return "unknown status";
+  }
+}
+
+int moe_w2_pack(int E, int K, int I, const uint8_t* gu_codes, const uint8_t* gu_scales,
+                const uint8_t* dn_codes, const uint8_t* dn_scales, void* stream,
+                moe_w2_planes** out) {
+  if (!out) return MOE_W2_EINVAL;
+  *out = nullptr;
+  if (!gu_codes || !gu_scales || !dn_codes || !dn_scales) return MOE_W2_EINVAL;
+  if (E < 0 || K < 0 || I < 0) return MOE_W2_EINVAL;
+  if (!shape_ok(E, K, I)) return MOE_W2_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t n_gu = (size_t)E * 2 * I * K;
+  const size_t n_dn = (size_t)E * K * I;
+  size_t o = 0;
+  const size_t o_guc = o; o += align_up(n_gu / 4);
+  const size_t o_gus = o; o += align_up(n_gu / 32);
+  const size_t o_dnc = o; o += align_up(n_dn / 4);
+  const size_t o_dns = o; o += align_up(n_dn / 32);
+  const size_t o_e0 = o;  o += align_up((size_t)E * K * 4);
+  const size_t o_flag = o; o += align_up(4);
+  moe_w2_planes* p = new (std::nothrow) moe_w2_planes;
+  if (!p) return MOE_W2_ENOMEM;
+  memset(p, 0, sizeof(*p));
+  p->E = E; p->K = K; p->I = I;
+  if (hipGetDevice(&p->device) != hipSuccess) { delete p; return MOE_W2_EHIP; }
+  if (hipMalloc(&p->base, o) != hipSuccess) { (void)hipGetLastError(); delete p; return MOE_W2_ENOMEM; }
+  p->bytes = o;
+  uint8_t* b = (uint8_t*)p->base;
+  p->gu_codes = b + o_guc; p->gu_scales = b + o_gus;
+  p->dn_codes = b + o_dnc; p->dn_scales = b + o_dns;
+  p->dn_e0 = (int32_t*)(b + o_e0); p->flag = (int32_t*)(b + o_flag);
+  hipError_t err = launch_pack(p, gu_codes, gu_scales, dn_codes, dn_scales, s);
+  int32_t flag = 0;
+  if (err == hipSuccess) err = hipMemcpyAsync(&flag, p->flag, 4, hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess) { (void)hipFree(p->base); delete p; return MOE_W2_EHIP; }
+  if (flag & (kFlagGuScale | kFlagDnScale)) { (void)hipFree(p->base); delete p; return MOE_W2_ESCALE; }
+  if (flag & kFlagDnSpan) { (void)hipFree(p->base); delete p; return MOE_W2_EUNSUPPORTED; }
+  *out = p;
+  return MOE_W2_OK;
+}
+
+int moe_w2_unpack(const moe_w2_planes* p, uint8_t* gu_codes, uint8_t* gu_scales,
+                  uint8_t* dn_codes, uint8_t* dn_scales, void* stream) {
+  if (!p || !gu_codes || !gu_scales || !dn_codes || !dn_scales) return MOE_W2_EINVAL;
+  return hip_status(launch_unpack(p, gu_codes, gu_scales, dn_codes, dn_scales, (hipStream_t)stream));
+}
+
+void moe_w2_planes_free(moe_w2_planes* p) {
+  if (!p) return;
+  (void)hipDeviceSynchronize();
+  (void)hipFree(p->base);
+  delete p;
+}
+
+int moe_w2_planes_info(const moe_w2_planes* p, int* E, int* K, int* I, size_t* bytes) {
+  if (!p) return MOE_W2_EINVAL;
+  if (E) *E = p->E;
+  if (K) *K = p->K;
+  if (I) *I = p->I;
+  if (bytes) *bytes = p->bytes;
+  return MOE_W2_OK;
+}
+
+size_t moe_w2_workspace_bytes(const moe_w2_planes* p, int T, int top_k) {
+  if (!p || T < 0 || top_k < 1 || top_k > 32) return 0;
+  return workspace_layout(p->E, p->K, p->I, T, top_k).total;
+}
+
+size_t moe_w2_route_workspace_bytes(int E, int T, int top_k) {
+  if (E < 1 || E > 1024 || T < 0 || top_k < 1 || top_k > 32) return 0;
+  const int P = T * top_k;
+  const int max_tiles = P / kGemmBM + (E < P ? E : P) + 1;
+  return align_up((size_t)E * 4) + align_up(8 * 4) + align_up((size_t)max_tiles * 2 * 4) +
+         route_scratch_bytes(E, P);
+}
+
+int moe_w2_route(int E, int T, int top_k, const int32_t* topk_ids, int32_t* offsets, int32_t* perm,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (E < 1 || T < 0 || top_k < 1) return MOE_W2_EINVAL;
+  if (E > 1024 || top_k > 32) return MOE_W2_EUNSUPPORTED;
+  if (!offsets || (T > 0 && (!topk_ids || !perm))) return MOE_W2_EINVAL;
+  const size_t need = moe_w2_route_workspace_bytes(E, T, top_k);
+  if (!workspace || workspace_bytes < need) return MOE_W2_EWORKSPACE;
+  const int P = T * top_k;
+  const int max_tiles = P / kGemmBM + (E < P ? E : P) + 1;
+  uint8_t* w = (uint8_t*)workspace;
+  RouteOut o;
+  o.offsets = offsets;
+  o.perm = perm;
+  o.active = (int32_t*)w;  w += align_up((size_t)E * 4);
+  o.meta = (int32_t*)w;    w += align_up(8 * 4);
+  o.tiles = (int32_t*)w;   w += align_up((size_t)max_tiles * 2 * 4);
+  o.chunk_cnt = (int32_t*)w;
+  o.rank = (int32_t*)(w + route_scratch_bytes(E, P) - align_up((size_t)P * 4));
+  o.counters = nullptr;
+  o.max_tiles = max_tiles;
+  return hip_status(launch_route(E, T, top_k, topk_ids, o, (hipStream_t)stream));
+}
+
+int moe_w2_forward(const moe_w2_planes* p, int T, int top_k, const void* x, const int32_t* topk_ids,
+                   const float* topk_w, void* y, int out_dtype, void* workspace,
+                   size_t workspace_bytes, int path, void* stream) {
+  if (!p || T < 0 || top_k < 1) return MOE_W2_EINVAL;
+  if (top_k > 32) return MOE_W2_EUNSUPPORTED;
+  if (out_dtype != MOE_W2_OUT_BF16 && out_dtype != MOE_W2_OUT_F32) return MOE_W2_EINVAL;
+  if (path != MOE_W2_PATH_AUTO && path != MOE_W2_PATH_DECODE && path != MOE_W2_PATH_GEMM) return MOE_W2_EINVAL;
+  if (T > 0 && (!x || !topk_ids || !topk_w || !y)) return MOE_W2_EINVAL;
+  if ((long long)T * top_k > (1LL << 30)) return MOE_W2_EUNSUPPORTED;
+  const Workspace ws = workspace_layout(p->E, p->K, p->I, T, top_k);
+  if (!workspace || workspace_bytes < ws.total) return MOE_W2_EWORKSPACE;
+  if (T == 0) return MOE_W2_OK;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* wsb = (uint8_t*)workspace;
+  RouteOut o;
+  o.offsets = (int32_t*)(wsb + ws.offsets);
+  o.perm = (int32_t*)(wsb + ws.perm);
+  o.active = (int32_t*)(wsb + ws.active);
+  o.meta = (int32_t*)(wsb + ws.meta);
+  o.tiles = (int32_t*)(wsb + ws.tiles);
+  o.counters = (long long*)(wsb + ws.counters);
+  o.chunk_cnt = (int32_t*)(wsb + ws.chunk_cnt);
+  o.rank = (int32_t*)(wsb + ws.rank);
+  o.max_tiles = ws.max_tiles;
+  hipError_t err = launch_route(p->E, T, top_k, topk_ids, o, s);
+  if (err != hipSuccess) return MOE_W2_EHIP;
+  bool decode = path == MOE_W2_PATH_DECODE ||
+                (path == MOE_W2_PATH_AUTO && (long long)T * top_k <= kDecodeMaxPairs);
+  if (decode) {
+    err = launch_decode_gate_up(p, T, top_k, x, ws, wsb, s);
+    if (err == hipSuccess) err = launch_decode_down(p, T, top_k, ws, wsb, s);
+  } else {
+    err = launch_gemm_gate_up(p, T, top_k, x, ws, wsb, s);
+    if (err == hipSuccess) err = launch_gemm_down(p, T, top_k, ws, wsb, s);
+  }
+  if (err == hipSuccess)
+    err = launch_combine(T, top_k, p->E, p->K, topk_ids, topk_w, (const float*)(wsb + ws.pair_out), y,
+                         out_dtype, s);
+  return hip_status(err);
+}
+
+int moe_w2_read_counters(const void* workspace, int64_t* invalid_pairs, int64_t* act_overflow,
+                         void* stream) {
+  if (!workspace) return MOE_W2_EINVAL;
+  long long c[2] = {0, 0};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = hipMemcpyAsync(c, workspace, sizeof(c), hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return MOE_W2_EHIP;
+  if (invalid_pairs) *invalid_pairs = c[0];
+  if (act_overflow) *act_overflow = c[1];
+  return MOE_W2_OK;
+}
+
+int nvfp4_to_w2(int n, int R, int C, const uint8_t* e2m1, const uint8_t* e4m3, const float* scale_2,
+                uint8_t* codes, uint8_t* scales, void* stream) {
+  if (n < 0 || R < 0 || C < 0) return MOE_W2_EINVAL;
+  if (C % 32) return MOE_W2_EUNSUPPORTED;
+  const long long nb = (long long)n * R * (C / 32);
+  if (nb == 0) return MOE_W2_OK;
+  if (!e2m1 || !e4m3 || !scale_2 || !codes || !scales) return MOE_W2_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* dflag = nullptr;
+  if (hipMalloc(&dflag, sizeof(int32_t)) != hipSuccess) { (void)hipGetLastError(); return MOE_W2_ENOMEM; }
+  int32_t flag = 0;
+  hipError_t err = hipMemsetAsync(dflag, 0, sizeof(int32_t), s);
+  if (err == hipSuccess) err = launch_nvfp4_to_w2(n, R, C, e2m1, e4m3, scale_2, codes, scales, dflag, s);
+  if (err == hipSuccess) err = hipMemcpyAsync(&flag, dflag, 4, hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  (void)hipFree(dflag);
+  if (err != hipSuccess) return MOE_W2_EHIP;
+  return flag ? MOE_W2_ENVFP4 : MOE_W2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Host-side internals of libmoew2: the planes object, the workspace layout and the kernel
+// launchers implemented in the .hip files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_w2.h"
+
+struct moe_w2_planes {
+  int E, K, I;
+  int device;
+  void* base;          // single device allocation
+  size_t bytes;
+  uint8_t* gu_codes;   // [E][2I/16][K/256][1024]
+  uint8_t* gu_scales;  // [E][2I/16][K/256][128]
+  uint8_t* dn_codes;   // [E][K/16][I/256][1024]
+  uint8_t* dn_scales;  // [E][K/16][I/256][128]  (canonical byte - E0 of the row)
+  int32_t* dn_e0;      // [E][K] per-row power-of-two offset of the down weights
+  int32_t* flag;       // pack-time validation flags (device)
+};
+
+namespace moew2 {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Pack-time validation flags
+enum { kFlagGuScale = 1, kFlagDnScale = 2, kFlagDnSpan = 4 };
+
+// Workspace layout of one forward.
+struct Workspace {
+  // counters: [0] invalid pairs, [1] act overflow (int64)
+  size_t counters;
+  size_t offsets;     // int32 [E+1]
+  size_t perm;        // int32 [P]
+  size_t active;      // int32 [E]   expert of each active slot
+  size_t meta;        // int32 [8]   [0] = number of active experts, [1] = number of GEMM M-tiles
+  size_t tiles;       // int32 [max_tiles][2] (expert, first sorted row) GEMM M-tiles
+  size_t chunk_cnt;   // int32 [nchunks][E+1] per-chunk counts (large routing)
+  size_t rank;        // int32 [P] rank of a pair within its chunk and expert
+  size_t act;         // fp16 [P][I] gated intermediate, sorted order
+  size_t pair_out;    // fp32 [P][K] per-pair down outputs, indexed by pair id
+  size_t total;
+  int P, nchunks, max_tiles;
+};
+
+constexpr int kRouteChunk = 256;       // pairs per routing chunk
+constexpr int kRouteSmallMax = 1024;   // single-workgroup routing up to this many pairs
+constexpr int kGemmBM = 128;           // GEMM M-tile (sorted pair rows)
+constexpr int kDecodeMaxPairs = 512;   // AUTO path: decode kernels up to this many pairs
+
+Workspace workspace_layout(int E, int K, int I, int T, int top_k);
+size_t route_scratch_bytes(int E, int P);
+
+// Launchers (return hipError_t of the launch)
+hipError_t launch_pack(const moe_w2_planes* p, const uint8_t* gu_codes, const uint8_t* gu_scales,
+                       const uint8_t* dn_codes, const uint8_t* dn_scales, hipStream_t s);
+hipError_t launch_unpack(const moe_w2_planes* p, uint8_t* gu_codes, uint8_t* gu_scales,
+                         uint8_t* dn_codes, uint8_t* dn_scales, hipStream_t s);
+
+// Routing: writes offsets/perm (+ active list, tiles, counters when the pointers are non-null).
+struct RouteOut {
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* active;    // may be null
+  int32_t* meta;      // may be null
+  int32_t* tiles;     // may be null
+  long long* counters;  // may be null
+  int32_t* chunk_cnt; // scratch for P > kRouteSmallMax
+  int32_t* rank;      // scratch for P > kRouteSmallMax
+  int max_tiles;
+};
+hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const RouteOut& o, hipStream_t s);
+
+// Decode path (small groups): gate_up + SiLU, down, combine.
+hipError_t launch_decode_gate_up(const moe_w2_planes* p, int T, int top_k, const void* x,
+                                 const Workspace& ws, uint8_t* wsb, hipStream_t s);
+hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const Workspace& ws,
+                              uint8_t* wsb, hipStream_t s);
+// GEMM path (large groups)
+hipError_t launch_gemm_gate_up(const moe_w2_planes* p, int T, int top_k, const void* x,
+                               const Workspace& ws, uint8_t* wsb, hipStream_t s);
+hipError_t launch_gemm_down(const moe_w2_planes* p, int T, int top_k, const Workspace& ws,
+                            uint8_t* wsb, hipStream_t s);
+hipError_t launch_combine(int T, int top_k, int E, int K, const int32_t* ids, const float* w,
+                          const float* pair_out, void* y, int out_dtype, hipStream_t s);
+
+// Re-quantizer
+hipError_t launch_nvfp4_to_w2(int n, int R, int C, const uint8_t* e2m1, const uint8_t* e4m3,
+                              const float* scale_2, uint8_t* codes, uint8_t* scales, int32_t* flag,
+                              hipStream_t s);
+
+}  // namespace moew2

@@ -1,0 +1,133 @@
+// nvfp4_to_w2: load-time re-quantizer NVFP4 -> sign-symmetric 2-bit planes.
+//
+// "The v0.24.0 port", section "Our hooks", modelopt.py bullet: modelopt NVFP4 experts (e2m1
+// codes, f8e4m3 scales per 16 elements, fp32 per-tensor weight_scale_2) are dequantized exactly
+// and re-quantized to the codebook {-4,-1,1,4}; the UE8M0 block-32 output scales absorb scale_2.
+//
+// One thread per 32-element block. Every element is held exactly as N * 2^P with N < 2^32
+// (N = twice the e2m1 magnitude x the e4m3 significand x the fp32 significand), so the squared
+// error comparisons are exact integer arithmetic, never rounded:
+//   D(e) = SSE(e) - sum|x|^2 = Q(e) 4^e - 2^(e+1) A(e),  Q = sum q^2,  A = sum q |x|,
+// and the optimum lies in [top-6, top] with top = ceil(log2 max|x|): above top every magnitude
+// is 1 and the error grows with e; below max|x|/37 doubling the step always lowers the error.
+#include "common.h"
+#include "internal.h"
+
+namespace moew2 {
+namespace {
+
+__device__ __forceinline__ int ilog2_u32(uint32_t v) { return 31 - __clz(v); }  // v > 0
+
+// N * 2^d > 5 (exact) for N < 2^32
+__device__ __forceinline__ bool above_midpoint(uint32_t N, int d) {
+  if (N == 0) return false;
+  if (d >= 3) return true;
+  if (d >= 0) return ((uint64_t)N << d) > 5u;
+  if (d <= -33) return false;
+  return (uint64_t)N > ((uint64_t)5 << (-d));
+}
+
+__global__ void __launch_bounds__(256)
+nvfp4_to_w2_kernel(long long nblocks, long long blocks_per_tensor,
+                   const uint8_t* __restrict__ e2m1, const uint8_t* __restrict__ e4m3,
+                   const float* __restrict__ scale_2, uint8_t* __restrict__ codes,
+                   uint8_t* __restrict__ scales, int32_t* __restrict__ flag) {
+  const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const long long tensor = b / blocks_per_tensor;
+  // fp32 scale_2 = F * 2^G
+  const uint32_t su = __builtin_bit_cast(uint32_t, scale_2[tensor]);
+  const int sexp = (su >> 23) & 255;
+  const uint32_t neg2 = su >> 31;
+  uint32_t F;
+  int G;
+  if (sexp == 255) { atomicOr(flag, 1); *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{0, 0}; scales[b] = 0; return; }
+  if (sexp == 0) { F = su & 0x7fffffu; G = -149; } else { F = (su & 0x7fffffu) | 0x800000u; G = sexp - 150; }
+  // e4m3 per half: significand S (<= 15) and exponent
+  const uint16_t sb = *reinterpret_cast<const uint16_t*>(e4m3 + 2 * b);
+  uint32_t SF[2];
+  int P[2];
+  uint32_t nsg[2];
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t byte = (sb >> (8 * j)) & 0xffu;
+    const int ex = (byte >> 3) & 15, mt = byte & 7;
+    if (ex == 15 && mt == 7) { atomicOr(flag, 1); *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{0, 0}; scales[b] = 0; return; }
+    uint32_t S;
+    int pe;
+    if (ex == 0) { S = mt; pe = -9; } else { S = 8 + mt; pe = ex - 10; }
+    SF[j] = S * F;               // < 2^28
+    P[j] = pe + G - 1;           // the -1 undoes the doubled e2m1 magnitude
+    nsg[j] = (byte >> 7) ^ neg2;
+  }
+  const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(e2m1 + 16 * b);
+  // twice the e2m1 magnitude of nibble n&7: 0,1,2,3,4,6,8,12
+  constexpr uint64_t kTwiceMag = 0x0C08060403020100ull;
+  uint32_t N[32];
+  uint32_t neg = 0;
+  int top = -100000;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t word = raw[k >> 3];
+    const uint32_t nib = (word >> (4 * (k & 7))) & 15u;
+    const int j = k >> 4;
+    const uint32_t m2 = (uint32_t)((kTwiceMag >> (8 * (nib & 7))) & 0xff);
+    N[k] = m2 * SF[j];
+    neg |= (((nib >> 3) ^ nsg[j]) & 1u) << k;
+    if (N[k]) {
+      const int c = P[j] + ilog2_u32(N[k]) + ((N[k] & (N[k] - 1)) ? 1 : 0);
+      top = c > top ? c : top;
+    }
+  }
+  int best = -127;
+  if (top != -100000) {
+    int lo = max(-127, min(127, top - 6));
+    int hi = max(-127, min(127, top));
+    const int Pm = min(P[0], P[1]);
+    const int Z = min(2 * lo, lo + 1 + Pm);
+    __int128 best_v = 0;
+    for (int e = lo; e <= hi; ++e) {
+      uint64_t A0 = 0, A1 = 0;
+      int n4 = 0;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const int j = k >> 4;
+        const bool q4 = above_midpoint(N[k], P[j] - e + 1);
+        const uint64_t v = q4 ? 4ull * N[k] : (uint64_t)N[k];
+        if (j == 0) A0 += v; else A1 += v;
+        n4 += q4 ? 1 : 0;
+      }
+      const __int128 A = ((__int128)A0 << (P[0] - Pm)) + ((__int128)A1 << (P[1] - Pm));
+      // D(e) = Q 2^(2e) - A 2^(e+1+Pm), scaled by 2^-Z with Z below both exponents for every
+      // candidate, so both shifts are non-negative and every value is an exact integer.
+      const __int128 Q = 32 + 15 * n4;
+      const __int128 v = (Q << (2 * e - Z)) - (A << (e + 1 + Pm - Z));
+      if (e == lo || v < best_v) { best_v = v; best = e; }
+    }
+  }
+  uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const bool q4 = above_midpoint(N[k], P[k >> 4] - best + 1);
+    const bool ng = (neg >> k) & 1u;
+    const uint32_t c = ng ? (q4 ? 0u : 1u) : (q4 ? 3u : 2u);
+    if (k < 16) c0 |= c << (2 * k); else c1 |= c << (2 * (k - 16));
+  }
+  *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{c0, c1};
+  scales[b] = (uint8_t)(best + 127);
+}
+
+}  // namespace
+
+hipError_t launch_nvfp4_to_w2(int n, int R, int C, const uint8_t* e2m1, const uint8_t* e4m3,
+                              const float* scale_2, uint8_t* codes, uint8_t* scales, int32_t* flag,
+                              hipStream_t s) {
+  const long long bpt = (long long)R * (C / 32);
+  const long long nb = (long long)n * bpt;
+  if (nb == 0) return hipSuccess;
+  const int B = 256;
+  hipLaunchKernelGGL(nvfp4_to_w2_kernel, dim3((unsigned)((nb + B - 1) / B)), dim3(B), 0, s, nb, bpt,
+                     e2m1, e4m3, scale_2, codes, scales, flag);
+  return hipGetLastError();
+}
+
+}  // namespace moew2

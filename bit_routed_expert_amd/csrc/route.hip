@@ -1,0 +1,259 @@
+// Token-sort / expert-offset pass: a stable counting sort of the pairs p = t*top_k + j by
+// expert id. Valid sorted ids form a permutation of token*top_k+j ("The v0.24.0 port",
+// section "Our hooks", bullet "Deterministic unpermute"); ids outside [0, E) are placed last.
+//
+// The rank of a pair among the pairs of its expert is computed without atomics on counts:
+// within a round of 256 pairs every pair sets its bit in a 256-bit mask of its expert (LDS),
+// and its rank is the popcount of the mask bits below it. This keeps the sort stable and the
+// output independent of scheduling.
+#include "common.h"
+#include "internal.h"
+
+namespace moew2 {
+namespace {
+
+constexpr int kRoundThreads = 256;   // pairs per round
+constexpr int kMaskWords = kRoundThreads / 32;
+constexpr int kChunkRounds = 4;      // rounds per chunk in the multi-kernel path
+constexpr int kChunkPairs = kRoundThreads * kChunkRounds;
+constexpr int kSmallMaxPairs = 4096; // single-workgroup path
+
+__device__ __forceinline__ int bin_of(int id, int E) { return (id >= 0 && id < E) ? id : E; }
+
+// In-place exclusive scan of n ints in LDS by the whole block; returns the total.
+__device__ int block_exclusive_scan(int* data, int n, int* scratch /* blockDim ints */) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int b0 = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i) if (b0 + i < n) local += data[b0 + i];
+  scratch[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {
+    int v = tid >= off ? scratch[tid - off] : 0;
+    __syncthreads();
+    scratch[tid] += v;
+    __syncthreads();
+  }
+  int run = scratch[tid] - local;  // exclusive prefix of this thread's segment
+  for (int i = 0; i < per; ++i) {
+    if (b0 + i < n) { int v = data[b0 + i]; data[b0 + i] = run; run += v; }
+  }
+  int total = scratch[nt - 1];
+  __syncthreads();
+  return total;
+}
+
+// Offsets, active-expert list, GEMM M-tile list and counters from per-bin totals held in LDS
+// (`cnt` has E+1 entries and is overwritten by its exclusive scan). Shared by both paths.
+__device__ void finish_routing(int* cnt, int E, int P, int* scratch, int* tmp,
+                               int32_t* offsets, int32_t* active, int32_t* meta, int32_t* tiles,
+                               long long* counters, int max_tiles) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  // per-expert activity and tile counts
+  for (int b = tid; b < E; b += nt) tmp[b] = cnt[b] > 0 ? 1 : 0;
+  __syncthreads();
+  int n_active = block_exclusive_scan(tmp, E, scratch);
+  for (int b = tid; b < E; b += nt) {
+    int n = cnt[b];
+    if (n > 0) active[tmp[b]] = b;  // tmp[b] = slot
+  }
+  __syncthreads();
+  for (int b = tid; b < E; b += nt) tmp[b] = (cnt[b] + kGemmBM - 1) / kGemmBM;
+  __syncthreads();
+  int n_tiles = block_exclusive_scan(tmp, E, scratch);
+  // offsets: exclusive scan of the E+1 bins (the last bin holds the invalid pairs)
+  int tot = block_exclusive_scan(cnt, E + 1, scratch);
+  (void)tot;
+  for (int b = tid; b <= E; b += nt) offsets[b] = b < E ? cnt[b] : cnt[E];
+  if (tid == 0) offsets[E] = cnt[E];  // = number of valid pairs
+  for (int b = tid; b < E; b += nt) {
+    int n = cnt[b + 1] - cnt[b];
+    int t0 = tmp[b];
+    for (int m = 0; m * kGemmBM < n; ++m) {
+      if (t0 + m < max_tiles) { tiles[2 * (t0 + m)] = b; tiles[2 * (t0 + m) + 1] = cnt[b] + m * kGemmBM; }
+    }
+  }
+  if (tid == 0) {
+    meta[0] = n_active;
+    meta[1] = n_tiles < max_tiles ? n_tiles : max_tiles;
+    if (counters) { counters[0] = (long long)(P - cnt[E]); counters[1] = 0; }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Single-workgroup routing for P <= kSmallMaxPairs.
+// LDS: masks[(E+1)][8] words, running[E+1], cnt[E+1], tmp[E], rank[P], scratch[256].
+// ---------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(kRoundThreads)
+route_small_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __restrict__ offsets,
+                   int32_t* __restrict__ perm, int32_t* active, int32_t* meta, int32_t* tiles,
+                   long long* counters, int max_tiles) {
+  extern __shared__ int lds[];
+  const int nb = E + 1;
+  uint32_t* masks = reinterpret_cast<uint32_t*>(lds);
+  int* running = lds + nb * kMaskWords;
+  int* cnt = running + nb;
+  int* tmp = cnt + nb;
+  int* rank = tmp + nb;
+  int* scratch = rank + kSmallMaxPairs;
+  const int tid = threadIdx.x;
+  for (int b = tid; b < nb; b += kRoundThreads) running[b] = 0;
+  const int rounds = (P + kRoundThreads - 1) / kRoundThreads;
+  for (int r = 0; r < rounds; ++r) {
+    for (int i = tid; i < nb * kMaskWords; i += kRoundThreads) masks[i] = 0;
+    __syncthreads();
+    const int p = r * kRoundThreads + tid;
+    int bin = -1;
+    if (p < P) {
+      bin = bin_of(ids[p], E);
+      atomicOr(&masks[bin * kMaskWords + tid / 32], 1u << (tid % 32));
+    }
+    __syncthreads();
+    if (bin >= 0) {
+      const uint32_t* m = masks + bin * kMaskWords;
+      int rk = running[bin];
+      for (int w = 0; w < tid / 32; ++w) rk += __popc(m[w]);
+      rk += __popc(m[tid / 32] & ((1u << (tid % 32)) - 1u));
+      rank[p] = rk;
+    }
+    __syncthreads();
+    for (int b = tid; b < nb; b += kRoundThreads) {
+      int c = 0;
+      for (int w = 0; w < kMaskWords; ++w) c += __popc(masks[b * kMaskWords + w]);
+      running[b] += c;
+    }
+    __syncthreads();
+  }
+  for (int b = tid; b < nb; b += kRoundThreads) cnt[b] = running[b];
+  __syncthreads();
+  finish_routing(cnt, E, P, scratch, tmp, offsets, active, meta, tiles, counters, max_tiles);
+  __syncthreads();
+  // cnt now holds the exclusive scan over bins (bin start positions)
+  for (int p = tid; p < P; p += kRoundThreads) {
+    const int bin = bin_of(ids[p], E);
+    perm[cnt[bin] + rank[p]] = p;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Multi-kernel routing for larger P: per-chunk ranks and counts, a scan, then the scatter.
+// ---------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(kRoundThreads)
+route_chunk_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __restrict__ chunk_cnt,
+                   int32_t* __restrict__ rank) {
+  extern __shared__ int lds[];
+  const int nb = E + 1;
+  uint32_t* masks = reinterpret_cast<uint32_t*>(lds);
+  int* running = lds + nb * kMaskWords;
+  const int tid = threadIdx.x, c = blockIdx.x;
+  for (int b = tid; b < nb; b += kRoundThreads) running[b] = 0;
+  for (int r = 0; r < kChunkRounds; ++r) {
+    for (int i = tid; i < nb * kMaskWords; i += kRoundThreads) masks[i] = 0;
+    __syncthreads();
+    const int p = c * kChunkPairs + r * kRoundThreads + tid;
+    int bin = -1;
+    if (p < P) {
+      bin = bin_of(ids[p], E);
+      atomicOr(&masks[bin * kMaskWords + tid / 32], 1u << (tid % 32));
+    }
+    __syncthreads();
+    if (bin >= 0) {
+      const uint32_t* m = masks + bin * kMaskWords;
+      int rk = running[bin];
+      for (int w = 0; w < tid / 32; ++w) rk += __popc(m[w]);
+      rk += __popc(m[tid / 32] & ((1u << (tid % 32)) - 1u));
+      rank[p] = rk;
+    }
+    __syncthreads();
+    for (int b = tid; b < nb; b += kRoundThreads) {
+      int cc = 0;
+      for (int w = 0; w < kMaskWords; ++w) cc += __popc(masks[b * kMaskWords + w]);
+      running[b] += cc;
+    }
+    __syncthreads();
+  }
+  for (int b = tid; b < nb; b += kRoundThreads) chunk_cnt[(long long)c * nb + b] = running[b];
+}
+
+// One workgroup: per-bin exclusive prefix over chunks (in place) and the routing summary.
+__global__ void __launch_bounds__(1024)
+route_scan_kernel(int E, int P, int nchunks, int32_t* __restrict__ chunk_cnt,
+                  int32_t* __restrict__ offsets, int32_t* active, int32_t* meta, int32_t* tiles,
+                  long long* counters, int max_tiles) {
+  extern __shared__ int lds[];
+  const int nb = E + 1;
+  int* cnt = lds;
+  int* tmp = cnt + nb;
+  int* scratch = tmp + nb;
+  const int tid = threadIdx.x;
+  for (int b = tid; b < nb; b += blockDim.x) {
+    int run = 0;
+    int c = 0;
+    for (; c + 8 <= nchunks; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = chunk_cnt[(long long)(c + u) * nb + b];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) { chunk_cnt[(long long)(c + u) * nb + b] = run; run += v[u]; }
+    }
+    for (; c < nchunks; ++c) {
+      int v = chunk_cnt[(long long)c * nb + b];
+      chunk_cnt[(long long)c * nb + b] = run;
+      run += v;
+    }
+    cnt[b] = run;
+  }
+  __syncthreads();
+  finish_routing(cnt, E, P, scratch, tmp, offsets, active, meta, tiles, counters, max_tiles);
+  __syncthreads();
+  // keep the bin start positions for the scatter in offsets' spare copy: chunk_cnt row nchunks
+  for (int b = tid; b < nb; b += blockDim.x) chunk_cnt[(long long)nchunks * nb + b] = cnt[b];
+}
+
+__global__ void __launch_bounds__(kRoundThreads)
+route_scatter_kernel(const int32_t* __restrict__ ids, int E, int P, int nchunks,
+                     const int32_t* __restrict__ chunk_cnt, const int32_t* __restrict__ rank,
+                     int32_t* __restrict__ perm) {
+  const int nb = E + 1;
+  const int c = blockIdx.x;
+  for (int r = 0; r < kChunkRounds; ++r) {
+    const int p = c * kChunkPairs + r * kRoundThreads + threadIdx.x;
+    if (p >= P) return;
+    const int bin = bin_of(ids[p], E);
+    const int pos = chunk_cnt[(long long)nchunks * nb + bin] + chunk_cnt[(long long)c * nb + bin] + rank[p];
+    perm[pos] = p;
+  }
+}
+
+}  // namespace
+
+size_t route_scratch_bytes(int E, int P) {
+  const int nb = E + 1;
+  const int nchunks = (P + kChunkPairs - 1) / kChunkPairs;
+  return align_up((size_t)(nchunks + 1) * nb * sizeof(int32_t)) + align_up((size_t)P * sizeof(int32_t));
+}
+
+hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const RouteOut& o, hipStream_t s) {
+  const int P = T * top_k;
+  const int nb = E + 1;
+  if (P <= kSmallMaxPairs) {
+    size_t lds = (size_t)nb * kMaskWords * 4 + (size_t)3 * nb * 4 + (size_t)kSmallMaxPairs * 4 +
+                 kRoundThreads * 4;
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kRoundThreads), lds, s, ids, E, P,
+                       o.offsets, o.perm, o.active, o.meta, o.tiles, o.counters, o.max_tiles);
+    return hipGetLastError();
+  }
+  const int nchunks = (P + kChunkPairs - 1) / kChunkPairs;
+  size_t lds1 = (size_t)nb * kMaskWords * 4 + (size_t)nb * 4;
+  hipLaunchKernelGGL(route_chunk_kernel, dim3(nchunks), dim3(kRoundThreads), lds1, s, ids, E, P,
+                     o.chunk_cnt, o.rank);
+  size_t lds2 = (size_t)2 * nb * 4 + 1024 * 4;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), lds2, s, E, P, nchunks, o.chunk_cnt,
+                     o.offsets, o.active, o.meta, o.tiles, o.counters, o.max_tiles);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(kRoundThreads), 0, s, ids, E, P,
+                     nchunks, o.chunk_cnt, o.rank, o.perm);
+  return hipGetLastError();
+}
+
+}  // namespace moew2

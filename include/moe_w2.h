@@ -1,0 +1,174 @@
+/*
+ * moe_w2.h - C ABI of libmoew2.so: the routed Mixture-of-Experts expert forward over
+ * sign-symmetric 2-bit weights, and the load-time NVFP4 -> 2-bit re-quantizer, for AMD MI355X
+ * (gfx950).
+ *
+ * The method is the one described for vLLM-Moet ("The v0.24.0 port" page, section "Our hooks";
+ * README bullets "2-bit expert planes - the sign-bias finding" and "The kernels"): routed expert
+ * weights are 2-bit codes over the codebook {-4, -1, 1, 4} with one UE8M0 power-of-two scale per
+ * 32 elements along each GEMM's reduction axis; the forward routes pairs (token, expert) to a
+ * grouped gate/up GEMM, a SiLU-gated product, a grouped down GEMM and a router-weighted,
+ * deterministic combine; NVFP4 experts (e2m1 x e4m3 block-16 x fp32 per-tensor scale_2) are
+ * re-quantized to those planes at load time.
+ *
+ * Conventions (all entry points):
+ *  - Pointers are HIP device pointers unless a parameter says "host". The caller owns every
+ *    buffer it passes and keeps it alive until the stream has passed the call. The library owns
+ *    the native planes (moe_w2_planes), created by moe_w2_pack and freed by moe_w2_planes_free.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls are
+ *    asynchronous on it unless marked "synchronous".
+ *  - Every entry point returns a status (enum moe_w2_status). Host-detectable problems (null
+ *    pointers, unsupported shapes, too small workspace) return a negative status before anything
+ *    is enqueued. No call prints, aborts or throws.
+ *  - Shapes: K (hidden size) and I (expert intermediate size) must be multiples of 256;
+ *    1 <= E <= 1024; 1 <= top_k <= 32; T >= 0 (T = 0 is a no-op).
+ *
+ * Canonical plane layout (the input of moe_w2_pack, the output of nvfp4_to_w2):
+ *  - codes: 4 per byte along the row's reduction axis, element k at bits 2*(k%4)..+1 (LSB
+ *    first); code c in 0..3 has value {-4, -1, +1, +4}[c] (code order from the starlog article,
+ *    section "Technical Insight"; c and 3-c are negatives).
+ *  - scales: one UE8M0 byte per 32 elements along the reduction axis: value 2^(b-127).
+ *  - gate_up[e] has 2I rows of K: rows 0..I-1 are the gate projection, rows I..2I-1 the up
+ *    projection. down[e] has K rows of I.
+ */
+#ifndef MOE_W2_H
+#define MOE_W2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_w2_status {
+  MOE_W2_OK = 0,
+  MOE_W2_EINVAL = -1,        /* null pointer, negative size or bad enum value */
+  MOE_W2_EUNSUPPORTED = -2,  /* shape outside the supported set (see conventions above) */
+  MOE_W2_ESCALE = -3,        /* a scale byte outside the range the planes can hold */
+  MOE_W2_ENOMEM = -4,        /* device allocation failed */
+  MOE_W2_EHIP = -5,          /* a HIP runtime call failed */
+  MOE_W2_EWORKSPACE = -6,    /* workspace null or smaller than moe_w2_workspace_bytes() */
+  MOE_W2_ENVFP4 = -7         /* NaN e4m3 byte or NaN / infinite scale_2 in nvfp4_to_w2 input */
+};
+
+enum moe_w2_out_dtype { MOE_W2_OUT_BF16 = 0, MOE_W2_OUT_F32 = 1 };
+
+/* Which kernels moe_w2_forward uses. AUTO picks DECODE for T*top_k <= 512, else GEMM. */
+enum moe_w2_path { MOE_W2_PATH_AUTO = 0, MOE_W2_PATH_DECODE = 1, MOE_W2_PATH_GEMM = 2 };
+
+typedef struct moe_w2_planes moe_w2_planes; /* opaque; library-owned native planes */
+
+/* ABI version of this header (increases on incompatible change). */
+int moe_w2_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* moe_w2_status_string(int status);
+
+/*
+ * moe_w2_pack - build the native planes of one MoE layer from canonical planes.
+ * Source: "The v0.24.0 port", section "Our hooks" (planes are built when weights are processed
+ * after loading; four sections per expert: gate_up codes, gate_up scales, down codes, down
+ * scales).
+ *   gu_codes  [E][2I][K/4]   gu_scales [E][2I][K/32]
+ *   dn_codes  [E][K][I/4]    dn_scales [E][K][I/32]
+ * The native layout is opaque (tiles of 32 rows x 256 reduction elements in matrix-core
+ * fragment order; gate and up rows interleaved in groups of 32). Gate_up scale bytes must be
+ * <= 252 (4 * 2^(b-127) must fit bf16). Down weights are held as fp16 with a per-row power-of-two
+ * offset; the scale bytes of one down row must lie within a window of 38 consecutive values
+ * ([c, c+37]) so every weight of the row is exact in fp16, and must be <= 254.
+ * Synchronous (validates the scale bytes on the device). On success *out receives the planes;
+ * on failure nothing is allocated and *out is NULL.
+ */
+int moe_w2_pack(int E, int K, int I,
+                const uint8_t* gu_codes, const uint8_t* gu_scales,
+                const uint8_t* dn_codes, const uint8_t* dn_scales,
+                void* stream, moe_w2_planes** out);
+
+/* Inverse of moe_w2_pack into canonical buffers of the shapes above (asynchronous; exact). */
+int moe_w2_unpack(const moe_w2_planes* planes,
+                  uint8_t* gu_codes, uint8_t* gu_scales,
+                  uint8_t* dn_codes, uint8_t* dn_scales, void* stream);
+
+/* Free the planes (synchronous: waits for the device). NULL is a no-op. */
+void moe_w2_planes_free(moe_w2_planes* planes);
+
+/* Shape and device footprint of the planes. Host outputs; any of them may be NULL. */
+int moe_w2_planes_info(const moe_w2_planes* planes, int* E, int* K, int* I, size_t* bytes);
+
+/*
+ * Workspace needed by moe_w2_forward for T tokens and top_k experts per token, in bytes
+ * (0 on bad arguments). The workspace also holds the two device counters of moe_w2_read_counters.
+ */
+size_t moe_w2_workspace_bytes(const moe_w2_planes* planes, int T, int top_k);
+
+/*
+ * moe_w2_route - the token-sort / expert-offset pass on its own.
+ * Source: "The v0.24.0 port", section "Our hooks", bullet "Deterministic unpermute": valid
+ * sorted ids form a permutation of token*top_k+j.
+ *   topk_ids [T][top_k] int32.  offsets [E+1] int32: offsets[e] = number of valid pairs with an
+ *   expert id < e.  perm [T*top_k] int32: the pair indices p = t*top_k + j sorted by expert id,
+ *   ascending p within an expert (stable); pairs whose id is outside [0, E) follow, ascending.
+ *   workspace: device scratch of moe_w2_route_workspace_bytes(E, T, top_k) bytes.
+ */
+size_t moe_w2_route_workspace_bytes(int E, int T, int top_k);
+int moe_w2_route(int E, int T, int top_k, const int32_t* topk_ids,
+                 int32_t* offsets, int32_t* perm,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_w2_forward - y = sum_j w[t,j] * D_e (silu(G_e x_t) * (U_e x_t)), e = topk_ids[t,j].
+ * Source: the method statement (top-k routed grouped GEMM: gate/up projection, SiLU-gated
+ * product, down projection, router-weighted combine); README bullet "The kernels"; "The v0.24.0
+ * port", bullet "Deterministic unpermute" (bijective per-pair placement, fixed-order sum).
+ *   x        [T][K] bf16 (row-major)
+ *   topk_ids [T][top_k] int32; ids outside [0, E) contribute nothing and are counted
+ *   topk_w   [T][top_k] fp32 router weights
+ *   y        [T][K] bf16 (MOE_W2_OUT_BF16, round-to-nearest-even of the fp32 result) or fp32
+ *   workspace: device memory of at least moe_w2_workspace_bytes(planes, T, top_k) bytes; it
+ *   must not be shared by forwards that may run concurrently.
+ * Arithmetic: gate/up in bf16 x bf16 -> fp32; the gated product is rounded to fp16; down in
+ * fp16 x fp16 -> fp32; combine in fp32 with j ascending. The result does not depend on the
+ * order in which pairs are processed and repeated calls are bit-identical. An intermediate
+ * |silu(g) * u| above the fp16 range becomes +-inf and is counted (act_overflow).
+ * Asynchronous; no host synchronisation and no allocation.
+ */
+int moe_w2_forward(const moe_w2_planes* planes, int T, int top_k,
+                   const void* x, const int32_t* topk_ids, const float* topk_w,
+                   void* y, int out_dtype,
+                   void* workspace, size_t workspace_bytes, int path, void* stream);
+
+/*
+ * Device counters of the last forward that used `workspace` (synchronous: waits for `stream`).
+ * invalid_pairs: pairs whose id was outside [0, E). act_overflow: gated intermediates that
+ * overflowed fp16. Host outputs.
+ */
+int moe_w2_read_counters(const void* workspace, int64_t* invalid_pairs, int64_t* act_overflow,
+                         void* stream);
+
+/*
+ * nvfp4_to_w2 - load-time re-quantizer NVFP4 -> canonical 2-bit planes.
+ * Source: "The v0.24.0 port", section "Our hooks", modelopt.py bullet (exact f64 dequant of
+ * e2m1 codes x f8e4m3 block-16 scales x per-tensor weight_scale_2; re-quantization to the
+ * sign-symmetric codebook; UE8M0 block-32 output scales absorb scale_2); README opening
+ * paragraph.
+ *   e2m1    [n][R][C/2]  two e2m1 codes per byte, low nibble = even element
+ *   e4m3    [n][R][C/16] E4M3FN block scales (one per 16 elements)
+ *   scale_2 [n]          fp32 per-tensor scale
+ *   codes   [n][R][C/4]  canonical codes;  scales [n][R][C/32] UE8M0 bytes
+ * Per 32-element block: x = e2m1 * e4m3 * scale_2 (exact); the exponent e in [-127, 127] and
+ * per-element magnitudes q in {1, 4} minimise sum (|x| - q 2^e)^2 exactly; equal errors take the
+ * lower exponent; |x| exactly 2.5 * 2^e takes q = 1; the code sign is the sign bit of x (-0 is
+ * negative). C must be a multiple of 32; n, R >= 0.
+ * Synchronous; returns MOE_W2_ENVFP4 if any e4m3 byte is NaN (0x7F/0xFF) or a scale_2 is NaN or
+ * infinite (outputs for the affected blocks are then unspecified).
+ */
+int nvfp4_to_w2(int n, int R, int C,
+                const uint8_t* e2m1, const uint8_t* e4m3, const float* scale_2,
+                uint8_t* codes, uint8_t* scales, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W2_H */

@@ -1,0 +1,175 @@
+"""GPU parity of moe_w2_forward (decode and GEMM kernels) against the f64 oracle, plus exact
+invariants of the GPU path. Bar: max |y_gpu - y_oracle| <= 1e-2 * rms(y_oracle) on the fp32
+output; the bf16 output must be the round-to-nearest-even of the fp32 output, bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import bit_routed_expert_amd as moe
+from oracle import formats, forward as oracle_fwd
+import workloads
+
+from gpu_helpers import bf16_rne_bits, dev, forward, pack, rel_max_err
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+PATHS = [moe.PATH_DECODE, moe.PATH_GEMM]
+
+
+def _oracle(case, tokens=None):
+    x = formats.bf16_bits_to_f64(case["x"])
+    return oracle_fwd.moe_forward(x, case["topk_ids"], case["topk_w"], case["gu_codes"], case["gu_scales"],
+                                  case["dn_codes"], case["dn_scales"], tokens=tokens)
+
+
+def _case(T, K, I, E, top_k, seed, zipf=False):
+    rng = np.random.default_rng(seed)
+    planes = workloads.draw_planes(rng, E, K, I)
+    x = workloads.draw_x(rng, T, K)
+    if zipf:
+        ids, w = workloads.zipf_routing(rng, T, E, top_k, rank_perm=rng.permutation(E))
+    else:
+        ids, w = workloads.uniform_routing(rng, T, E, top_k)
+    return dict(planes, x=x, topk_ids=ids, topk_w=w)
+
+
+@pytest.fixture(scope="module")
+def tiny(gpu):
+    d = workloads.tiny()
+    return d, pack(d), _oracle(d)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_tiny_layer_parity(tiny, path):
+    d, h, y_ref = tiny
+    y = forward(h, d["x"], d["topk_ids"], d["topk_w"], moe.OUT_F32, path).cpu().numpy()
+    err = rel_max_err(y, y_ref)
+    print(f"tiny path={path} rel max err {err:.2e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_bf16_output_is_rne_of_f32(tiny, path):
+    d, h, _ = tiny
+    y32 = forward(h, d["x"], d["topk_ids"], d["topk_w"], moe.OUT_F32, path).cpu().numpy()
+    y16 = forward(h, d["x"], d["topk_ids"], d["topk_w"], moe.OUT_BF16, path)
+    bits = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(bits, bf16_rne_bits(y32))
+
+
+CASES = [
+    # several tiles along every axis with ragged tails: (T, K, I, E, top_k, seed, zipf)
+    (37, 512, 768, 16, 4, 21, False),
+    (300, 768, 512, 8, 2, 22, False),
+    (200, 1024, 256, 32, 8, 23, True),
+    (3, 256, 256, 4, 4, 24, False),     # top_k == E
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"T{c[0]}K{c[1]}I{c[2]}E{c[3]}k{c[4]}" for c in CASES])
+@pytest.mark.parametrize("path", PATHS)
+def test_mid_size_parity(gpu, case, path):
+    T, K, I, E, top_k, seed, zipf = case
+    c = _case(T, K, I, E, top_k, seed, zipf)
+    y_ref = _oracle(c)
+    h = pack(c)
+    y = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path).cpu().numpy()
+    err = rel_max_err(y, y_ref)
+    print(f"{case} path={path} rel max err {err:.2e}")
+    assert err <= TOL
+
+
+def test_paths_agree_closely(gpu):
+    c = _case(64, 512, 512, 8, 4, 31)
+    h = pack(c)
+    a = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, moe.PATH_DECODE).cpu().numpy()
+    b = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, moe.PATH_GEMM).cpu().numpy()
+    rms = np.sqrt(np.mean(a.astype(np.float64) ** 2))
+    assert np.max(np.abs(a - b)) <= 1e-3 * rms
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_repeats_are_bit_identical(gpu, path):
+    c = _case(96, 512, 512, 16, 8, 41, zipf=True)
+    h = pack(c)
+    ws = moe.alloc_workspace(h, 96, 8)
+    ys = [forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path, ws).cpu().numpy() for _ in range(6)]
+    for y in ys[1:]:
+        assert np.array_equal(y.view(np.uint32), ys[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_down_scale_doubling_is_exact_and_negation_nearly(gpu, path):
+    c = _case(40, 512, 512, 8, 2, 51)
+    y = forward(pack(c), c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path).cpu().numpy()
+    c2 = dict(c, dn_scales=(c["dn_scales"] + 1).astype(np.uint8))
+    y2 = forward(pack(c2), c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path).cpu().numpy()
+    assert np.array_equal(y2, 2 * y)
+    c3 = dict(c, dn_codes=(~c["dn_codes"]).astype(np.uint8))
+    y3 = forward(pack(c3), c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path).cpu().numpy()
+    # The matrix cores' fp32 accumulation is not sign-symmetric in its last bit, so negating the
+    # down weights negates y up to last-bit rounding (exact would need symmetric rounding).
+    d = np.abs(y3.astype(np.float64) + y)
+    ulp = np.spacing(np.abs(y).astype(np.float32)).astype(np.float64)
+    print(f"negation: {np.count_nonzero(d)} of {d.size} entries differ, max {np.max(d / ulp):.1f} ulp")
+    assert np.max(d) <= 1e-5 * np.sqrt(np.mean(y.astype(np.float64) ** 2))
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_invalid_ids_contribute_nothing_and_are_counted(gpu, path):
+    c = _case(20, 256, 512, 8, 4, 61)
+    ids = c["topk_ids"].copy()
+    ids[::3, 1] = -1
+    ids[1::5, 3] = 8       # == E, out of range
+    n_bad = int(((ids < 0) | (ids >= 8)).sum())
+    h = pack(c)
+    ws = moe.alloc_workspace(h, 20, 4)
+    y = forward(h, c["x"], ids, c["topk_w"], moe.OUT_F32, path, ws).cpu().numpy()
+    inv, ovf = moe.moe_w2_read_counters(ws)
+    assert inv == n_bad and ovf == 0
+    y_ref = oracle_fwd.moe_forward(formats.bf16_bits_to_f64(c["x"]), ids, c["topk_w"], c["gu_codes"], c["gu_scales"],
+                                   c["dn_codes"], c["dn_scales"])
+    assert rel_max_err(y, y_ref) <= TOL
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_duplicate_ids_are_summed(gpu, path):
+    c = _case(16, 256, 256, 4, 2, 71)
+    ids = np.stack([c["topk_ids"][:, 0]] * 2, axis=1).astype(np.int32)
+    y = forward(pack(c), c["x"], ids, c["topk_w"], moe.OUT_F32, path).cpu().numpy()
+    y_ref = oracle_fwd.moe_forward(formats.bf16_bits_to_f64(c["x"]), ids, c["topk_w"], c["gu_codes"], c["gu_scales"],
+                                   c["dn_codes"], c["dn_scales"])
+    assert rel_max_err(y, y_ref) <= TOL
+
+
+def test_zero_tokens_is_a_noop(gpu):
+    c = _case(4, 256, 256, 4, 2, 81)
+    h = pack(c)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    y = moe.moe_w2_forward(h, x, ids, w, out_dtype=moe.OUT_F32)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 256)
+
+
+def test_workspace_too_small_is_rejected(gpu):
+    c = _case(4, 256, 256, 4, 2, 82)
+    h = pack(c)
+    ws = torch.empty(moe.moe_w2_workspace_bytes(h, 4, 2) - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(moe.MoeW2Error) as ei:
+        forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, moe.PATH_AUTO, ws)
+    assert ei.value.status == -6
+
+
+def test_down_rows_with_large_exponent_offsets(gpu):
+    """Down scale bytes far from 127 (rows needing a per-row fp16 offset) stay exact."""
+    c = _case(24, 256, 512, 4, 2, 91)
+    rng = np.random.default_rng(92)
+    base = rng.integers(20, 220, size=(4, 256, 1))
+    c["dn_scales"] = (base + rng.integers(0, 30, size=(4, 256, 16))).astype(np.uint8)
+    y_ref = _oracle(c)
+    h = pack(c)
+    for path in PATHS:
+        y = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path).cpu().numpy()
+        assert rel_max_err(y, y_ref) <= TOL
