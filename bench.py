@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of the 2-bit routed-expert MoE forward on one MI355X.
+
+Default workload (the decode shape the metric is quoted on): one MoE layer with K=4096, I=2048,
+E=256, top-8, uniform routing, 2-bit codes uniform over {-4,-1,1,4}, UE8M0 block-32 exponents
+uniform in [-10,-6], bf16 N(0,1) activations. One step runs the whole forward (route, gate_up +
+SiLU, down, combine) once for each decode batch T = 1, 8 and 32 (41 tokens per step), each call on
+a fresh routing instance (cycling through --instances seeded instances) and on alternating copies
+of the layer's planes, so consecutive calls never find their weights in the 256 MB last-level
+cache. Inputs are resident in HBM before timing. The timed steps are captured in one HIP graph and
+replayed (a serving loop replays captured decode steps the same way); value = tokens per second
+over that replay, wall clock between two device synchronisations. eager_tokens_per_s is the same
+work launched call by call from Python.
+
+The JSON line also carries:
+  roofline      - the dominant kernel (the decode gate_up kernel): algorithmic bytes (weights of
+                  the activated experts, x read, gated intermediate written) / its average launch
+                  duration, from HIP events around a graph of back-to-back launches of that stage
+                  (same inputs, same launch configuration) on the stream it runs on;
+  per_batch     - per-T forward time and whole-forward algorithmic HBM rate;
+  prefill       - the 8192-token prefill workload (K=6144, Zipf(1.1) routing): tokens/s and matrix
+                  core rate of the two grouped GEMMs against the dense bf16/fp16 peak;
+  cpu_baseline  - the f64 CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
+DECODE_TS = (1, 8, 32)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--instances", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-iters", type=int, default=5)
+    return ap.parse_args()
+
+
+def expert_bytes(K, I):
+    """Bytes of one expert's 2-bit planes: codes (2 bits) + one UE8M0 byte per 32 weights."""
+    gu = 2 * I * K // 4 + 2 * I * K // 32
+    dn = K * I // 4 + K * I // 32
+    return gu, dn
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "bit_routed_expert_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(name, src_hash):
+    """HBM traffic per launch from a committed counter summary, if it was taken on this source."""
+    p = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("source_hash") != src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_routed_expert_amd as moe
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    c = workloads.DECODE
+    K, I, E, top_k = c["K"], c["I"], c["E"], c["top_k"]
+    canon = workloads.decode_layer()
+    d_canon = [dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")]
+    layers = [moe.moe_w2_pack(*d_canon), moe.moe_w2_pack(*d_canon)]   # two copies at distinct addresses
+    del d_canon
+    torch.cuda.empty_cache()
+
+    R = args.instances
+    inst = {}
+    for T in DECODE_TS:
+        lst = []
+        for d in workloads.decode_instances(T, R):
+            lst.append(dict(
+                x=torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).cuda(),
+                ids=dev(d["topk_ids"]), w=dev(d["topk_w"]), ids_np=d["topk_ids"], host=d))
+        inst[T] = lst
+    ws = {T: moe.alloc_workspace(layers[0], T, top_k) for T in DECODE_TS}
+    ys = {T: torch.empty((T, K), dtype=torch.bfloat16, device="cuda") for T in DECODE_TS}
+    gu_b, dn_b = expert_bytes(K, I)
+
+    def n_active(ids):
+        v = ids[(ids >= 0) & (ids < E)]
+        return len(np.unique(v))
+
+    # algorithmic bytes per call
+    def call_bytes(T, ids):
+        na = n_active(ids)
+        gate_up = na * gu_b + T * K * 2 + T * top_k * I * 2
+        full = na * (gu_b + dn_b) + 2 * T * K * 2 + T * top_k * 8
+        return gate_up, full
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def fwd(s, i, T):
+        call = 3 * s + i
+        d = inst[T][s % R]
+        moe.moe_w2_forward(layers[call % 2], d["x"], d["ids"], d["w"], workspace=ws[T], y=ys[T])
+
+    for s in range(args.warmup):
+        for i, T in enumerate(DECODE_TS):
+            fwd(s, i, T)
+    torch.cuda.synchronize()
+    # eager reference: the same steps launched one by one from Python
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, T in enumerate(DECODE_TS):
+            fwd(s, i, T)
+    torch.cuda.synchronize()
+    eager_elapsed = time.perf_counter() - t0
+    # ---- timed region: the K steps captured once in a HIP graph and replayed; nothing else runs ----
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(args.steps):
+            for i, T in enumerate(DECODE_TS):
+                fwd(s, i, T)
+    graph.replay()          # warm replay (untimed)
+    torch.cuda.synchronize()
+    g0, g1 = ev(), ev()
+    t0 = time.perf_counter()
+    g0.record(stream)
+    graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    tokens = sum(DECODE_TS) * args.steps
+    value = tokens / elapsed
+
+    # ---- per-kernel timing: each stage launched back-to-back between one pair of events ----
+    # (an event between two launches leaves an idle gap on the stream, so none is placed there)
+    kws = {T: [moe.alloc_workspace(layers[0], T, top_k) for _ in range(R)] for T in DECODE_TS}
+    for T in DECODE_TS:
+        for r in range(R):
+            d = inst[T][r]
+            moe.moe_w2_forward(layers[0], d["x"], d["ids"], d["w"], workspace=kws[T][r], y=ys[T])
+    torch.cuda.synchronize()
+    n_rep = max(2, args.steps)
+    per_batch, gu_bytes_all, gu_ms_all, n_gu = {}, 0, 0.0, 0
+    for T in DECODE_TS:
+        res = {}
+        for name, stage in (("gate_up", moe.STAGE_GATE_UP), ("down", moe.STAGE_DOWN), ("forward", None)):
+            a0, a1 = ev(), ev()
+            nbytes_gu = nbytes_full = 0
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for k in range(n_rep):
+                    r = k % R
+                    d = inst[T][r]
+                    layer = layers[k % 2]
+                    if stage is None:
+                        moe.moe_w2_forward(layer, d["x"], d["ids"], d["w"], workspace=kws[T][r], y=ys[T])
+                    else:
+                        moe.moe_w2_forward_stage(stage, layer, d["x"], d["ids"], d["w"], ys[T], kws[T][r])
+                    gb, fb = call_bytes(T, d["ids_np"])
+                    nbytes_gu += gb
+                    nbytes_full += fb
+            g.replay()
+            torch.cuda.synchronize()
+            a0.record(stream)
+            g.replay()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            del g
+            ms = a0.elapsed_time(a1) / n_rep
+            res[name] = ms
+            if name == "gate_up":
+                gu_bytes_all += nbytes_gu
+                gu_ms_all += ms * n_rep
+                n_gu += n_rep
+                res["gu_GBps"] = nbytes_gu / n_rep / (ms * 1e-3) / 1e9
+            if name == "forward":
+                res["fwd_GBps"] = nbytes_full / n_rep / (ms * 1e-3) / 1e9
+        per_batch[f"T{T}"] = dict(
+            fwd_us=round(res["forward"] * 1e3, 2), gate_up_us=round(res["gate_up"] * 1e3, 2),
+            down_us=round(res["down"] * 1e3, 2), fwd_hbm_GBps=round(res["fwd_GBps"], 1),
+            gate_up_hbm_GBps=round(res["gu_GBps"], 1), tokens_per_s=round(T / (res["forward"] * 1e-3), 1))
+    achieved = gu_bytes_all / (gu_ms_all * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profiles("decode_gate_up", src_hash)
+    roofline = dict(bound="hbm", kernel="decode_kernel<gate_up>", achieved=round(achieved, 1),
+                    peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
+                    traffic=traffic, launches=n_gu, avg_launch_us=round(gu_ms_all / n_gu * 1e3, 3),
+                    algorithmic_bytes_per_launch=int(gu_bytes_all / n_gu))
+    del kws
+
+    out = {
+        "metric": "routed-expert tokens/sec (decode, K=4096 I=2048 E=256 top-8, T in {1,8,32})",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "gpu_ms_per_step": round(g0.elapsed_time(g1) / args.steps, 4),
+        "eager_tokens_per_s": round(tokens / eager_elapsed, 1),
+        "timing": "timed steps captured in one HIP graph and replayed; per-kernel times from graphs "
+                  "of back-to-back launches of that stage between one event pair",
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "moe_w2 decode: K=4096 I=2048 E=256 top-8 uniform routing, "
+                               "one forward each at T=1,8,32 per step (41 tokens)",
+                   "tokens_per_step": sum(DECODE_TS), "routing_instances": R, "plane_copies": 2},
+        "roofline": roofline,
+        "per_batch": per_batch,
+        "source_hash": src_hash,
+    }
+
+    if not args.no_prefill:
+        out["prefill"] = bench_prefill(args, moe, workloads, torch, dev)
+
+    # free GPU memory before the CPU baseline
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(canon, inst)
+    print(json.dumps(out), flush=True)
+
+
+def bench_prefill(args, moe, workloads, torch, dev):
+    c = workloads.PREFILL
+    T, K, I, E, top_k = c["T"], c["K"], c["I"], c["E"], c["top_k"]
+    canon = workloads.zipf_layer(c["seed"], K, I, E)
+    planes = moe.moe_w2_pack(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")])
+    del canon
+    d = workloads.zipf_instances(T, 1, c["seed"], K, E, top_k)[0]
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).cuda()
+    ids, w = dev(d["topk_ids"]), dev(d["topk_w"])
+    ws = moe.alloc_workspace(planes, T, top_k)
+    y = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    a = (planes, x, ids, w, y, ws)
+    for _ in range(2):
+        moe.moe_w2_forward(planes, x, ids, w, workspace=ws, y=y)
+    torch.cuda.synchronize()
+    t = {}
+    n = args.prefill_iters
+    for name, stage in (("forward", None), ("route", moe.STAGE_ROUTE), ("gate_up", moe.STAGE_GATE_UP),
+                        ("down", moe.STAGE_DOWN), ("combine", moe.STAGE_COMBINE)):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(n):
+            if stage is None:
+                moe.moe_w2_forward(planes, x, ids, w, workspace=ws, y=y)
+            else:
+                moe.moe_w2_forward_stage(stage, *a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t[name] = e0.elapsed_time(e1) / n
+    fwd, rt, gu, dn, cb = t["forward"], t["route"], t["gate_up"], t["down"], t["combine"]
+    P = T * top_k
+    f_gu = 2.0 * P * 2 * I * K
+    f_dn = 2.0 * P * K * I
+    gemm_tflops = (f_gu + f_dn) / ((gu + dn) * 1e-3) / 1e12
+    fwd_tflops = (f_gu + f_dn) / (fwd * 1e-3) / 1e12
+    del planes, ws
+    torch.cuda.empty_cache()
+    return dict(
+        workload="moe_w2 prefill: T=8192 K=6144 I=2048 E=256 top-8 Zipf(1.1)",
+        tokens_per_s=round(T / (fwd * 1e-3), 1), fwd_ms=round(float(fwd), 4),
+        route_ms=round(float(rt), 4), gate_up_ms=round(float(gu), 4), down_ms=round(float(dn), 4),
+        combine_ms=round(float(cb), 4),
+        gate_up_tflops=round(f_gu / (gu * 1e-3) / 1e12, 1), down_tflops=round(f_dn / (dn * 1e-3) / 1e12, 1),
+        gemm_tflops=round(gemm_tflops, 1), gemm_mfma_frac=round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        fwd_tflops=round(fwd_tflops, 1), fwd_mfma_frac=round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        peak_tflops=MFMA_BF16_PEAK_TFLOPS, iters=args.prefill_iters)
+
+
+def cpu_baseline(canon, inst):
+    """The f64 oracle on one routing instance at T=1 and one at T=8 of the decode workload."""
+    from threadpoolctl import threadpool_info
+    from oracle import formats, forward
+
+    t0 = time.perf_counter()
+    tokens = 0
+    for T in (1, 8):
+        h = inst[T][0]["host"]
+        forward.moe_forward(formats.bf16_bits_to_f64(h["x"]), h["topk_ids"], h["topk_w"], canon["gu_codes"],
+                            canon["gu_scales"], canon["dn_codes"], canon["dn_scales"])
+        tokens += T
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return dict(value=round(tokens / dt, 3), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample="one routing instance each at T=1 and T=8 of the decode workload (9 tokens, "
+                       f"all activated experts dequantized in f64), {dt:.1f} s wall; "
+                       f"host has {os.cpu_count()} logical CPUs")
+
+
+if __name__ == "__main__":
+    main()

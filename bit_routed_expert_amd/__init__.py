@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoew2.so
 
 OUT_BF16, OUT_F32 = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_GEMM = 0, 1, 2
+STAGE_ROUTE, STAGE_GATE_UP, STAGE_DOWN, STAGE_COMBINE = 0, 1, 2, 3
 
 STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ESCALE", -4: "ENOMEM", -5: "EHIP",
           -6: "EWORKSPACE", -7: "ENVFP4"}
@@ -49,6 +50,7 @@ def _lib():
             "moe_w2_route_workspace_bytes": ([I32, I32, I32], SZ),
             "moe_w2_route": ([I32, I32, I32, P, P, P, P, SZ, P], I32),
             "moe_w2_forward": ([P, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
+            "moe_w2_forward_stage": ([P, I32, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
             "moe_w2_read_counters": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), P], I32),
             "nvfp4_to_w2": ([I32, I32, I32, P, P, P, P, P, P], I32),
         }
@@ -172,6 +174,16 @@ def moe_w2_forward(planes, x, topk_ids, topk_w, out_dtype=OUT_BF16, workspace=No
                                  ctypes.c_void_p(y.data_ptr()), int(out_dtype), _dev(workspace, torch.uint8, "workspace"),
                                  workspace.numel(), int(path), _stream()), "moe_w2_forward")
     return y
+
+
+def moe_w2_forward_stage(stage, planes, x, topk_ids, topk_w, y, workspace, out_dtype=OUT_BF16, path=PATH_AUTO):
+    """One stage of moe_w2_forward (all tensors preallocated on the device); stages 0..3 in order
+    on one stream and workspace are exactly moe_w2_forward."""
+    T, _ = x.shape
+    _check(_lib().moe_w2_forward_stage(planes.handle, int(stage), T, topk_ids.shape[1], ctypes.c_void_p(x.data_ptr()),
+                                       ctypes.c_void_p(topk_ids.data_ptr()), ctypes.c_void_p(topk_w.data_ptr()),
+                                       ctypes.c_void_p(y.data_ptr()), int(out_dtype), ctypes.c_void_p(workspace.data_ptr()),
+                                       workspace.numel(), int(path), _stream()), "moe_w2_forward_stage")
 
 
 def moe_w2_read_counters(workspace):

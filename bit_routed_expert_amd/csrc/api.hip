@@ -156,10 +156,11 @@ int moe_w2_route(int E, int T, int top_k, const int32_t* topk_ids, int32_t* offs
   return hip_status(launch_route(E, T, top_k, topk_ids, o, (hipStream_t)stream));
 }
 
-int moe_w2_forward(const moe_w2_planes* p, int T, int top_k, const void* x, const int32_t* topk_ids,
-                   const float* topk_w, void* y, int out_dtype, void* workspace,
-                   size_t workspace_bytes, int path, void* stream) {
+int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, const void* x,
+                         const int32_t* topk_ids, const float* topk_w, void* y, int out_dtype,
+                         void* workspace, size_t workspace_bytes, int path, void* stream) {
   if (!p || T < 0 || top_k < 1) return MOE_W2_EINVAL;
+  if (stage < MOE_W2_STAGE_ROUTE || stage > MOE_W2_STAGE_COMBINE) return MOE_W2_EINVAL;
   if (top_k > 32) return MOE_W2_EUNSUPPORTED;
   if (out_dtype != MOE_W2_OUT_BF16 && out_dtype != MOE_W2_OUT_F32) return MOE_W2_EINVAL;
   if (path != MOE_W2_PATH_AUTO && path != MOE_W2_PATH_DECODE && path != MOE_W2_PATH_GEMM) return MOE_W2_EINVAL;
@@ -170,31 +171,47 @@ int moe_w2_forward(const moe_w2_planes* p, int T, int top_k, const void* x, cons
   if (T == 0) return MOE_W2_OK;
   hipStream_t s = (hipStream_t)stream;
   uint8_t* wsb = (uint8_t*)workspace;
-  RouteOut o;
-  o.offsets = (int32_t*)(wsb + ws.offsets);
-  o.perm = (int32_t*)(wsb + ws.perm);
-  o.active = (int32_t*)(wsb + ws.active);
-  o.meta = (int32_t*)(wsb + ws.meta);
-  o.tiles = (int32_t*)(wsb + ws.tiles);
-  o.counters = (long long*)(wsb + ws.counters);
-  o.chunk_cnt = (int32_t*)(wsb + ws.chunk_cnt);
-  o.rank = (int32_t*)(wsb + ws.rank);
-  o.max_tiles = ws.max_tiles;
-  hipError_t err = launch_route(p->E, T, top_k, topk_ids, o, s);
-  if (err != hipSuccess) return MOE_W2_EHIP;
-  bool decode = path == MOE_W2_PATH_DECODE ||
-                (path == MOE_W2_PATH_AUTO && (long long)T * top_k <= kDecodeMaxPairs);
-  if (decode) {
-    err = launch_decode_gate_up(p, T, top_k, x, ws, wsb, s);
-    if (err == hipSuccess) err = launch_decode_down(p, T, top_k, ws, wsb, s);
-  } else {
-    err = launch_gemm_gate_up(p, T, top_k, x, ws, wsb, s);
-    if (err == hipSuccess) err = launch_gemm_down(p, T, top_k, ws, wsb, s);
+  const bool decode = path == MOE_W2_PATH_DECODE ||
+                      (path == MOE_W2_PATH_AUTO && (long long)T * top_k <= kDecodeMaxPairs);
+  hipError_t err = hipSuccess;
+  switch (stage) {
+    case MOE_W2_STAGE_ROUTE: {
+      RouteOut o;
+      o.offsets = (int32_t*)(wsb + ws.offsets);
+      o.perm = (int32_t*)(wsb + ws.perm);
+      o.active = (int32_t*)(wsb + ws.active);
+      o.meta = (int32_t*)(wsb + ws.meta);
+      o.tiles = (int32_t*)(wsb + ws.tiles);
+      o.counters = (long long*)(wsb + ws.counters);
+      o.chunk_cnt = (int32_t*)(wsb + ws.chunk_cnt);
+      o.rank = (int32_t*)(wsb + ws.rank);
+      o.max_tiles = ws.max_tiles;
+      err = launch_route(p->E, T, top_k, topk_ids, o, s);
+      break;
+    }
+    case MOE_W2_STAGE_GATE_UP:
+      err = decode ? launch_decode_gate_up(p, T, top_k, x, ws, wsb, s)
+                   : launch_gemm_gate_up(p, T, top_k, x, ws, wsb, s);
+      break;
+    case MOE_W2_STAGE_DOWN:
+      err = decode ? launch_decode_down(p, T, top_k, ws, wsb, s) : launch_gemm_down(p, T, top_k, ws, wsb, s);
+      break;
+    default:
+      err = launch_combine(T, top_k, p->E, p->K, topk_ids, topk_w, (const float*)(wsb + ws.pair_out), y,
+                           out_dtype, s);
   }
-  if (err == hipSuccess)
-    err = launch_combine(T, top_k, p->E, p->K, topk_ids, topk_w, (const float*)(wsb + ws.pair_out), y,
-                         out_dtype, s);
   return hip_status(err);
+}
+
+int moe_w2_forward(const moe_w2_planes* p, int T, int top_k, const void* x, const int32_t* topk_ids,
+                   const float* topk_w, void* y, int out_dtype, void* workspace,
+                   size_t workspace_bytes, int path, void* stream) {
+  for (int stage = MOE_W2_STAGE_ROUTE; stage <= MOE_W2_STAGE_COMBINE; ++stage) {
+    int st = moe_w2_forward_stage(p, stage, T, top_k, x, topk_ids, topk_w, y, out_dtype, workspace,
+                                  workspace_bytes, path, stream);
+    if (st != MOE_W2_OK) return st;
+  }
+  return MOE_W2_OK;
 }
 
 int moe_w2_read_counters(const void* workspace, int64_t* invalid_pairs, int64_t* act_overflow,

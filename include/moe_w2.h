@@ -57,6 +57,14 @@ enum moe_w2_out_dtype { MOE_W2_OUT_BF16 = 0, MOE_W2_OUT_F32 = 1 };
 /* Which kernels moe_w2_forward uses. AUTO picks DECODE for T*top_k <= 512, else GEMM. */
 enum moe_w2_path { MOE_W2_PATH_AUTO = 0, MOE_W2_PATH_DECODE = 1, MOE_W2_PATH_GEMM = 2 };
 
+/* The four stages of moe_w2_forward, in order (see moe_w2_forward_stage). */
+enum moe_w2_stage {
+  MOE_W2_STAGE_ROUTE = 0,    /* token sort / expert offsets / tile lists, into the workspace */
+  MOE_W2_STAGE_GATE_UP = 1,  /* grouped gate/up GEMM + SiLU-gated product -> workspace */
+  MOE_W2_STAGE_DOWN = 2,     /* grouped down GEMM -> per-pair rows in the workspace */
+  MOE_W2_STAGE_COMBINE = 3   /* router-weighted fixed-order combine -> y */
+};
+
 typedef struct moe_w2_planes moe_w2_planes; /* opaque; library-owned native planes */
 
 /* ABI version of this header (increases on incompatible change). */
@@ -72,8 +80,8 @@ const char* moe_w2_status_string(int status);
  * scales).
  *   gu_codes  [E][2I][K/4]   gu_scales [E][2I][K/32]
  *   dn_codes  [E][K][I/4]    dn_scales [E][K][I/32]
- * The native layout is opaque (tiles of 32 rows x 256 reduction elements in matrix-core
- * fragment order; gate and up rows interleaved in groups of 32). Gate_up scale bytes must be
+ * The native layout is opaque (tiles of 16 rows x 256 reduction elements in matrix-core
+ * fragment order; gate and up rows interleaved in groups of 16). Gate_up scale bytes must be
  * <= 252 (4 * 2^(b-127) must fit bf16). Down weights are held as fp16 with a per-row power-of-two
  * offset; the scale bytes of one down row must lie within a window of 38 consecutive values
  * ([c, c+37]) so every weight of the row is exact in fp16, and must be <= 254.
@@ -137,6 +145,17 @@ int moe_w2_forward(const moe_w2_planes* planes, int T, int top_k,
                    const void* x, const int32_t* topk_ids, const float* topk_w,
                    void* y, int out_dtype,
                    void* workspace, size_t workspace_bytes, int path, void* stream);
+
+/*
+ * moe_w2_forward_stage - one stage of moe_w2_forward, with the same arguments. Calling stages
+ * ROUTE, GATE_UP, DOWN, COMBINE in this order on one stream with one workspace is exactly
+ * moe_w2_forward; each stage reads what the previous ones left in the workspace. Lets a caller
+ * place events or other work between the stages. Asynchronous; no allocation.
+ */
+int moe_w2_forward_stage(const moe_w2_planes* planes, int stage, int T, int top_k,
+                         const void* x, const int32_t* topk_ids, const float* topk_w,
+                         void* y, int out_dtype,
+                         void* workspace, size_t workspace_bytes, int path, void* stream);
 
 /*
  * Device counters of the last forward that used `workspace` (synchronous: waits for `stream`).
