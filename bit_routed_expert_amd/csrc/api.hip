@@ -173,9 +173,12 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
   uint8_t* wsb = (uint8_t*)workspace;
   const bool decode = path == MOE_W2_PATH_DECODE ||
                       (path == MOE_W2_PATH_AUTO && (long long)T * top_k <= kDecodeMaxPairs);
+  // the direct decode organisation needs no routing pass and combines inside the down stage
+  const bool direct = decode && (long long)T * top_k <= kDirectMaxPairs;
   hipError_t err = hipSuccess;
   switch (stage) {
     case MOE_W2_STAGE_ROUTE: {
+      if (direct) break;
       RouteOut o;
       o.offsets = (int32_t*)(wsb + ws.offsets);
       o.perm = (int32_t*)(wsb + ws.perm);
@@ -190,15 +193,18 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
       break;
     }
     case MOE_W2_STAGE_GATE_UP:
-      err = decode ? launch_decode_gate_up(p, T, top_k, x, ws, wsb, s)
+      err = decode ? launch_decode_gate_up(p, T, top_k, x, topk_ids, ws, wsb, direct, s)
                    : launch_gemm_gate_up(p, T, top_k, x, ws, wsb, s);
       break;
     case MOE_W2_STAGE_DOWN:
-      err = decode ? launch_decode_down(p, T, top_k, ws, wsb, s) : launch_gemm_down(p, T, top_k, ws, wsb, s);
+      err = decode ? launch_decode_down(p, T, top_k, topk_ids, topk_w, y, out_dtype, ws, wsb, direct, s)
+                   : launch_gemm_down(p, T, top_k, ws, wsb, s);
       break;
     default:
-      err = launch_combine(T, top_k, p->E, p->K, topk_ids, topk_w, (const float*)(wsb + ws.pair_out), y,
-                           out_dtype, s);
+      // the direct decode down stage already combined into y
+      if (!direct)
+        err = launch_combine(T, top_k, p->E, p->K, topk_ids, topk_w, (const float*)(wsb + ws.pair_out), y,
+                             out_dtype, s);
   }
   return hip_status(err);
 }

@@ -49,6 +49,7 @@ constexpr int kRouteChunk = 256;       // pairs per routing chunk
 constexpr int kRouteSmallMax = 1024;   // single-workgroup routing up to this many pairs
 constexpr int kGemmBM = 128;           // GEMM M-tile (sorted pair rows)
 constexpr int kDecodeMaxPairs = 512;   // AUTO path: decode kernels up to this many pairs
+constexpr int kDirectMaxPairs = 8;     // decode without a routing pass up to this many pairs
 
 Workspace workspace_layout(int E, int K, int I, int T, int top_k);
 size_t route_scratch_bytes(int E, int P);
@@ -74,10 +75,14 @@ struct RouteOut {
 hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const RouteOut& o, hipStream_t s);
 
 // Decode path (small groups): gate_up + SiLU, down, combine.
+// direct = no routing pass (P <= kDirectMaxPairs); the direct down launch also writes y.
 hipError_t launch_decode_gate_up(const moe_w2_planes* p, int T, int top_k, const void* x,
-                                 const Workspace& ws, uint8_t* wsb, hipStream_t s);
-hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const Workspace& ws,
-                              uint8_t* wsb, hipStream_t s);
+                                 const int32_t* ids, const Workspace& ws, uint8_t* wsb, bool direct,
+                                 hipStream_t s);
+hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const int32_t* ids, const float* w,
+                              void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, bool direct,
+                              hipStream_t s);
+size_t decode_direct_lds(int I);
 // GEMM path (large groups)
 hipError_t launch_gemm_gate_up(const moe_w2_planes* p, int T, int top_k, const void* x,
                                const Workspace& ws, uint8_t* wsb, hipStream_t s);

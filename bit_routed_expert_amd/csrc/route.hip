@@ -137,6 +137,75 @@ route_small_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __res
 }
 
 // ---------------------------------------------------------------------------------------
+// One-round routing for P <= 1024 pairs and E <= 256 experts (decode batches): one thread per
+// pair, a 1024-bit mask per expert, and a single block scan of three packed prefix sums per
+// expert (pair count, GEMM M-tiles, active flag).
+// ---------------------------------------------------------------------------------------
+constexpr int kFastThreads = 1024;
+constexpr int kFastWords = kFastThreads / 32;
+
+__global__ void __launch_bounds__(kFastThreads)
+route_fast_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __restrict__ offsets,
+                  int32_t* __restrict__ perm, int32_t* active, int32_t* meta, int32_t* tiles,
+                  long long* counters, int max_tiles) {
+  extern __shared__ int lds[];
+  const int nb = E + 1;
+  uint32_t* masks = reinterpret_cast<uint32_t*>(lds);     // [nb][32]
+  int* start = lds + nb * kFastWords;                      // [nb]
+  int* wsum = start + nb;                                  // [16]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int i = tid; i < nb * kFastWords; i += kFastThreads) masks[i] = 0;
+  __syncthreads();
+  const int bin = tid < P ? bin_of(ids[tid], E) : -1;
+  if (bin >= 0) atomicOr(&masks[bin * kFastWords + tid / 32], 1u << (tid % 32));
+  __syncthreads();
+  int rank = 0;
+  if (bin >= 0) {
+    const uint32_t* m = masks + bin * kFastWords;
+    for (int w = 0; w < tid / 32; ++w) rank += __popc(m[w]);
+    rank += __popc(m[tid / 32] & ((1u << (tid % 32)) - 1u));
+  }
+  int c = 0;
+  uint32_t v = 0;
+  if (tid < nb) {
+    for (int w = 0; w < kFastWords; ++w) c += __popc(masks[tid * kFastWords + w]);
+    v = (uint32_t)c << 20;
+    if (tid < E && c > 0) v |= ((uint32_t)((c + kGemmBM - 1) / kGemmBM) << 10) | 1u;
+  }
+  // block exclusive scan of the packed values (fields never carry into each other)
+  uint32_t incl = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[wv] = (int)incl;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < kFastThreads / 64; ++i) { int t = wsum[i]; wsum[i] = run; run += t; }
+  }
+  __syncthreads();
+  const uint32_t excl = incl - v + (uint32_t)wsum[wv];
+  if (tid < nb) {
+    const int s0 = (int)(excl >> 20), t0 = (int)((excl >> 10) & 1023u), a0 = (int)(excl & 1023u);
+    start[tid] = s0;
+    offsets[tid] = s0;
+    if (tid < E && c > 0) {
+      active[a0] = tid;
+      for (int m = 0; m * kGemmBM < c; ++m)
+        if (t0 + m < max_tiles) { tiles[2 * (t0 + m)] = tid; tiles[2 * (t0 + m) + 1] = s0 + m * kGemmBM; }
+    }
+    if (tid == E) {
+      meta[0] = a0;
+      meta[1] = t0 < max_tiles ? t0 : max_tiles;
+      if (counters) { counters[0] = (long long)(P - s0); counters[1] = 0; }
+    }
+  }
+  __syncthreads();
+  if (bin >= 0) perm[start[bin] + rank] = tid;
+}
+
+// ---------------------------------------------------------------------------------------
 // Multi-kernel routing for larger P: per-chunk ranks and counts, a scan, then the scatter.
 // ---------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(kRoundThreads)
@@ -237,6 +306,12 @@ size_t route_scratch_bytes(int E, int P) {
 hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const RouteOut& o, hipStream_t s) {
   const int P = T * top_k;
   const int nb = E + 1;
+  if (P <= kFastThreads && E <= 256) {
+    size_t lds = (size_t)nb * kFastWords * 4 + (size_t)nb * 4 + 16 * 4;
+    hipLaunchKernelGGL(route_fast_kernel, dim3(1), dim3(kFastThreads), lds, s, ids, E, P, o.offsets, o.perm,
+                       o.active, o.meta, o.tiles, o.counters, o.max_tiles);
+    return hipGetLastError();
+  }
   if (P <= kSmallMaxPairs) {
     size_t lds = (size_t)nb * kMaskWords * 4 + (size_t)3 * nb * 4 + (size_t)kSmallMaxPairs * 4 +
                  kRoundThreads * 4;

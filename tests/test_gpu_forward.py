@@ -173,3 +173,29 @@ def test_down_rows_with_large_exponent_offsets(gpu):
     for path in PATHS:
         y = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path).cpu().numpy()
         assert rel_max_err(y, y_ref) <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_tiny_batch_direct_path(gpu, T):
+    """P = T*top_k <= 8 runs without a routing pass; invalid and duplicate ids included."""
+    c = _case(T, 512, 512, 16, 4, 101 + T)
+    ids = c["topk_ids"].copy()
+    ids[0, 1] = -1
+    ids[0, 2] = ids[0, 3]           # duplicate expert within a token
+    h = pack(c)
+    ws = moe.alloc_workspace(h, T, 4)
+    for path in (moe.PATH_AUTO, moe.PATH_DECODE):
+        y = forward(h, c["x"], ids, c["topk_w"], moe.OUT_F32, path, ws).cpu().numpy()
+        y_ref = oracle_fwd.moe_forward(formats.bf16_bits_to_f64(c["x"]), ids, c["topk_w"], c["gu_codes"],
+                                       c["gu_scales"], c["dn_codes"], c["dn_scales"])
+        assert rel_max_err(y, y_ref) <= TOL
+        inv, ovf = moe.moe_w2_read_counters(ws)
+        assert inv == 1 and ovf == 0
+
+
+def test_all_ids_invalid_gives_zero(gpu):
+    for T in (1, 16):
+        c = _case(T, 256, 256, 4, 2, 111)
+        ids = np.full((T, 2), -1, np.int32)
+        y = forward(pack(c), c["x"], ids, c["topk_w"], moe.OUT_F32, moe.PATH_AUTO).cpu().numpy()
+        assert np.all(y == 0)
