@@ -48,6 +48,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-iters", type=int, default=5)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every timed call from Python instead of replaying HIP graphs (for profilers)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run three 1 GiB device-to-device copies (a plain copy kernel of known size, "
+                         "to scale the HBM byte counters of a profile)")
     return ap.parse_args()
 
 
@@ -93,6 +98,13 @@ def main():
 
     torch.cuda.set_device(0)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     c = workloads.DECODE
     K, I, E, top_k = c["K"], c["I"], c["E"], c["top_k"]
     canon = workloads.decode_layer()
@@ -145,17 +157,23 @@ def main():
     torch.cuda.synchronize()
     eager_elapsed = time.perf_counter() - t0
     # ---- timed region: the K steps captured once in a HIP graph and replayed; nothing else runs ----
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    def timed_steps():
         for s in range(args.steps):
             for i, T in enumerate(DECODE_TS):
                 fwd(s, i, T)
-    graph.replay()          # warm replay (untimed)
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            timed_steps()
+        graph.replay()          # warm replay (untimed)
     torch.cuda.synchronize()
     g0, g1 = ev(), ev()
     t0 = time.perf_counter()
     g0.record(stream)
-    graph.replay()
+    if args.eager:
+        timed_steps()
+    else:
+        graph.replay()
     g1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -177,9 +195,8 @@ def main():
         res = {}
         for name, stage in (("gate_up", moe.STAGE_GATE_UP), ("down", moe.STAGE_DOWN), ("forward", None)):
             a0, a1 = ev(), ev()
-            nbytes_gu = nbytes_full = 0
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+            def loop():
+                nb_gu = nb_full = 0
                 for k in range(n_rep):
                     r = k % R
                     d = inst[T][r]
@@ -189,15 +206,25 @@ def main():
                     else:
                         moe.moe_w2_forward_stage(stage, layer, d["x"], d["ids"], d["w"], ys[T], kws[T][r])
                     gb, fb = call_bytes(T, d["ids_np"])
-                    nbytes_gu += gb
-                    nbytes_full += fb
-            g.replay()
+                    nb_gu += gb
+                    nb_full += fb
+                return nb_gu, nb_full
+            if args.eager:
+                loop()
+                torch.cuda.synchronize()
+                a0.record(stream)
+                nbytes_gu, nbytes_full = loop()
+                a1.record(stream)
+            else:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    nbytes_gu, nbytes_full = loop()
+                g.replay()
+                torch.cuda.synchronize()
+                a0.record(stream)
+                g.replay()
+                a1.record(stream)
             torch.cuda.synchronize()
-            a0.record(stream)
-            g.replay()
-            a1.record(stream)
-            torch.cuda.synchronize()
-            del g
             ms = a0.elapsed_time(a1) / n_rep
             res[name] = ms
             if name == "gate_up":
@@ -230,8 +257,9 @@ def main():
         "ms_per_step": round(elapsed / args.steps * 1e3, 4),
         "gpu_ms_per_step": round(g0.elapsed_time(g1) / args.steps, 4),
         "eager_tokens_per_s": round(tokens / eager_elapsed, 1),
-        "timing": "timed steps captured in one HIP graph and replayed; per-kernel times from graphs "
-                  "of back-to-back launches of that stage between one event pair",
+        "timing": ("eager launches" if args.eager else
+                   "timed steps captured in one HIP graph and replayed; per-kernel times from graphs "
+                   "of back-to-back launches of that stage between one event pair"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

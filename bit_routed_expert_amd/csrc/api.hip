@@ -166,6 +166,8 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
   if (path != MOE_W2_PATH_AUTO && path != MOE_W2_PATH_DECODE && path != MOE_W2_PATH_GEMM) return MOE_W2_EINVAL;
   if (T > 0 && (!x || !topk_ids || !topk_w || !y)) return MOE_W2_EINVAL;
   if ((long long)T * top_k > (1LL << 30)) return MOE_W2_EUNSUPPORTED;
+  if ((long long)T * p->K >= (1LL << 31) || (long long)T * top_k * p->I >= (1LL << 31))
+    return MOE_W2_EUNSUPPORTED;  // the GEMM kernels index x and the intermediate in 32 bits
   const Workspace ws = workspace_layout(p->E, p->K, p->I, T, top_k);
   if (!workspace || workspace_bytes < ws.total) return MOE_W2_EWORKSPACE;
   if (T == 0) return MOE_W2_OK;

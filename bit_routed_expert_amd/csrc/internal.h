@@ -47,7 +47,7 @@ struct Workspace {
 
 constexpr int kRouteChunk = 256;       // pairs per routing chunk
 constexpr int kRouteSmallMax = 1024;   // single-workgroup routing up to this many pairs
-constexpr int kGemmBM = 128;           // GEMM M-tile (sorted pair rows)
+constexpr int kGemmBM = 64;            // GEMM M-tile (sorted pair rows)
 constexpr int kDecodeMaxPairs = 512;   // AUTO path: decode kernels up to this many pairs
 constexpr int kDirectMaxPairs = 8;     // decode without a routing pass up to this many pairs
 
