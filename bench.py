@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
 DECODE_TS = (1, 8, 32)
+DIRECT_MAX_PAIRS = 8            # pairs up to which the forward takes the two-kernel direct path
 
 
 def parse():
@@ -63,27 +64,34 @@ def expert_bytes(K, I):
     return gu, dn
 
 
-def kernel_source_hash():
+DECODE_SOURCES = ("common.h", "internal.h", "decode.hip")
+
+
+def kernel_source_hash(files=DECODE_SOURCES):
+    """Hash of the sources a kernel is built from: a counter summary taken on other sources is stale."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "bit_routed_expert_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in files:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(name, src_hash):
-    """HBM traffic per launch from a committed counter summary, if it was taken on this source."""
-    p = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    """HBM bytes per launch from a committed counter summary (profiles/<name>_traffic.txt, lines
+    `source_hash: <hex>` and `bytes_per_launch: <int>`), if it was taken on these sources."""
+    p = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
     if not os.path.exists(p):
         return None
-    try:
-        d = json.load(open(p))
-    except Exception:
+    fields = {}
+    with open(p) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_hash") != src_hash or "bytes_per_launch" not in fields:
         return None
-    if d.get("source_hash") != src_hash:
-        return None
-    return d.get("bytes_per_launch")
+    return int(fields["bytes_per_launch"])
 
 
 def main():
@@ -227,7 +235,8 @@ def main():
             torch.cuda.synchronize()
             ms = a0.elapsed_time(a1) / n_rep
             res[name] = ms
-            if name == "gate_up":
+            if name == "gate_up" and T * top_k > DIRECT_MAX_PAIRS:
+                # the routed decode gate/up kernel (T = 1 takes the direct kernel instead)
                 gu_bytes_all += nbytes_gu
                 gu_ms_all += ms * n_rep
                 n_gu += n_rep
@@ -241,7 +250,8 @@ def main():
     achieved = gu_bytes_all / (gu_ms_all * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     traffic = traffic_from_profiles("decode_gate_up", src_hash)
-    roofline = dict(bound="hbm", kernel="decode_kernel<gate_up>", achieved=round(achieved, 1),
+    roofline = dict(bound="hbm", kernel="decode_gate_up_kernel<4,false> (T=8 and T=32 calls)",
+                    achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
                     traffic=traffic, launches=n_gu, avg_launch_us=round(gu_ms_all / n_gu * 1e3, 3),
                     algorithmic_bytes_per_launch=int(gu_bytes_all / n_gu))
