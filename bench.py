@@ -343,13 +343,13 @@ def bench_prefill(args, moe, workloads, torch, dev):
 
 
 def cpu_baseline(canon, inst):
-    """The f64 oracle on one routing instance at T=1 and one at T=8 of the decode workload."""
+    """The f64 oracle on one bench step: routing instance 0 at T = 1, 8 and 32 of the decode workload."""
     from threadpoolctl import threadpool_info
     from oracle import formats, forward
 
     t0 = time.perf_counter()
     tokens = 0
-    for T in (1, 8):
+    for T in DECODE_TS:
         h = inst[T][0]["host"]
         forward.moe_forward(formats.bf16_bits_to_f64(h["x"]), h["topk_ids"], h["topk_w"], canon["gu_codes"],
                             canon["gu_scales"], canon["dn_codes"], canon["dn_scales"])
@@ -357,8 +357,8 @@ def cpu_baseline(canon, inst):
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return dict(value=round(tokens / dt, 3), unit="tokens/s", cores=int(threads), kind="oracle",
-                sample="one routing instance each at T=1 and T=8 of the decode workload (9 tokens, "
-                       f"all activated experts dequantized in f64), {dt:.1f} s wall; "
+                sample=f"one bench step: routing instance 0 at T=1, 8 and 32 of the decode workload "
+                       f"({tokens} tokens, every activated expert dequantized in f64), {dt:.1f} s wall; "
                        f"host has {os.cpu_count()} logical CPUs")
 
 

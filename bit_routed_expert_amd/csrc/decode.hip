@@ -1,6 +1,6 @@
 // Decode-shaped expert GEMMs: few tokens per expert, the whole activated expert set streamed
-// from HBM once per call. Decode is bound by the weight stream (README bullet "FP4 recovery -
-// used surgically": decode is HBM-bound), so the kernels are organised around keeping enough
+// from HBM once per call. Decode time is set by the weight bytes read from HBM (README bullet
+// "FP4 recovery - used surgically"), so the kernels are organised around keeping enough
 // weight tiles in flight: every wave streams its tiles through a 4-deep register ring while the
 // matrix cores consume the previous ones, with the expert's tokens (up to kChunk at a time) as
 // the 16-row A operand staged in LDS.
