@@ -235,12 +235,13 @@ def main():
             torch.cuda.synchronize()
             ms = a0.elapsed_time(a1) / n_rep
             res[name] = ms
-            if name == "gate_up" and T * top_k > DIRECT_MAX_PAIRS:
-                # the routed decode gate/up kernel (T = 1 takes the direct kernel instead)
-                gu_bytes_all += nbytes_gu
-                gu_ms_all += ms * n_rep
-                n_gu += n_rep
+            if name == "gate_up":
                 res["gu_GBps"] = nbytes_gu / n_rep / (ms * 1e-3) / 1e9
+                if T * top_k > DIRECT_MAX_PAIRS:
+                    # the routed decode gate/up kernel (T = 1 takes the direct kernel instead)
+                    gu_bytes_all += nbytes_gu
+                    gu_ms_all += ms * n_rep
+                    n_gu += n_rep
             if name == "forward":
                 res["fwd_GBps"] = nbytes_full / n_rep / (ms * 1e-3) / 1e9
         per_batch[f"T{T}"] = dict(

@@ -30,8 +30,11 @@ Workspace workspace_layout(int E, int K, int I, int T, int top_k) {
   return w;
 }
 
+// The decode kernels address one expert's gate_up plane (2I x K codes, 2 bits each) as a buffer of
+// at most 2^31 - 1 bytes.
 static bool shape_ok(int E, int K, int I) {
-  return E >= 1 && E <= 1024 && K >= 256 && I >= 256 && K % 256 == 0 && I % 256 == 0;
+  return E >= 1 && E <= 1024 && K >= 256 && I >= 256 && K % 256 == 0 && I % 256 == 0 &&
+         (long long)I * K / 2 < (1LL << 31);
 }
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_W2_OK : MOE_W2_EHIP; }

@@ -101,6 +101,25 @@ MOEW2_DEV float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u;
 MOEW2_DEV u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 MOEW2_DEV u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 
+// Raw buffer view of one expert's weight plane (at most 2^31 - 1 bytes). A load at offset
+// kOutOfRange lies past the buffer's size and returns zeros without a memory access: issuing it
+// instead of branching around the load keeps every wave's load sequence fixed, so the compiler's
+// wait counts stay exact while a ring of tiles is in flight. Weight loads carry the nontemporal
+// policy (each byte is read once per call).
+constexpr int kBufferWord3 = 0x00020000;   // raw (untyped) buffer, gfx9-family descriptor word 3
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kPolicyNT = 2;               // cache policy bits: nt
+MOEW2_DEV __amdgpu_buffer_rsrc_t buffer_view(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+// voffset (per lane, range-checked) + soffset (wave-uniform byte offset added to the base)
+MOEW2_DEV u32x4_t buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kPolicyNT));
+}
+MOEW2_DEV u32x2_t buf_ld8_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kPolicyNT));
+}
+
 // Round-to-nearest-even fp32 -> bf16 bits (finite and infinite inputs; NaN stays NaN).
 MOEW2_DEV uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);

@@ -1,14 +1,20 @@
 // Decode-shaped expert GEMMs: few tokens per expert, the whole activated expert set streamed
 // from HBM once per call. Decode time is set by the weight bytes read from HBM (README bullet
-// "FP4 recovery - used surgically"), so the kernels are organised around keeping enough
-// weight tiles in flight: every wave streams its tiles through a 4-deep register ring while the
-// matrix cores consume the previous ones, with the expert's tokens (up to kChunk at a time) as
-// the 16-row A operand staged in LDS.
+// "FP4 recovery - used surgically"), so the kernels are organised around keeping enough weight
+// tiles in flight: every wave streams its tiles through a 4-deep register ring while the matrix
+// cores consume the previous ones, with the expert's tokens (up to kChunk at a time) as the
+// 16-row A operand staged in LDS.
 //
 // gate_up: weights bf16 (2-bit codes -> e2m1 -> bf16, UE8M0 scale folded in by the MX
 //          conversion instruction), x bf16, fp32 accumulation; a = silu(g) * u rounded to fp16.
 // down:    weights fp16 (same decode; the per-row offset E0 is applied in the epilogue), a fp16.
 // combine: y[t] = sum over j ascending of w[t, j] * o[t*top_k + j] in fp32.
+//
+// Load ordering: a workgroup first issues its staging loads (x or the gated rows), then the
+// first kRing weight tiles of every wave, and only then waits - for the staging loads alone -
+// before writing LDS. Weight tiles are raw buffer loads; a tile past the end of a wave's range is
+// requested at an out-of-range offset (no memory access), so the load sequence never branches
+// and the ring's waits stay exact.
 //
 // Two organisations ("The v0.24.0 port", bullet "Deterministic unpermute": per-pair outputs are
 // placed bijectively and summed in a fixed order, no atomics on values):
@@ -28,20 +34,39 @@ constexpr int kChunk = 4;     // token rows per pass (valid rows of the 16-row M
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRing = 4;      // weight tiles in flight per wave
+constexpr int kStage = 4;     // 16-byte staging pieces per thread per memory round trip
 
 struct TileRegs {
   u32x4_t c[2];   // codes of up to two row groups (gate, up) for one k-tile
   u32x2_t s[2];   // their scale bytes (8 blocks of this lane's row)
 };
 
+// One expert's planes as buffer views, and the tile index (within the expert) of k-tile 0 of
+// each of the wave's NB row groups.
 template <int NB>
-MOEW2_DEV void load_tile(TileRegs& r, const uint8_t* codes, const uint8_t* scales, const long long* tile_idx,
-                         int kt, int lane) {
+struct WaveTiles {
+  __amdgpu_buffer_rsrc_t codes, scales;
+  uint32_t tile[NB];
+};
+
+template <int NB>
+MOEW2_DEV WaveTiles<NB> wave_tiles(const uint8_t* codes, const uint8_t* scales, int e, uint32_t tiles_per_expert) {
+  WaveTiles<NB> wt;
+  wt.codes = buffer_view(codes + (size_t)e * tiles_per_expert * kTileCodeBytes, tiles_per_expert * kTileCodeBytes);
+  wt.scales = buffer_view(scales + (size_t)e * tiles_per_expert * kTileScaleBytes, tiles_per_expert * kTileScaleBytes);
+  return wt;
+}
+
+// The tile's byte offset goes in the scalar offset; the lane's offset (shifted out of range when
+// the tile is not wanted - a wave-uniform condition) in the range-checked vector offset.
+template <int NB>
+MOEW2_DEV void load_tile(TileRegs& r, const WaveTiles<NB>& wt, int kt, bool valid, int lane) {
+  const uint32_t oob = valid ? 0u : kOutOfRange;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const long long t = tile_idx[b] + kt;
-    r.c[b] = ld16(codes + t * kTileCodeBytes + 16 * lane);
-    r.s[b] = ld8(scales + t * kTileScaleBytes + 8 * (lane & 15));
+    const uint32_t t = wt.tile[b] + (uint32_t)kt;
+    r.c[b] = buf_ld16_nt(wt.codes, (16u * (uint32_t)lane) | oob, t * kTileCodeBytes);
+    r.s[b] = buf_ld8_nt(wt.scales, (8u * (uint32_t)(lane & 15)) | oob, t * kTileScaleBytes);
   }
 }
 
@@ -73,36 +98,79 @@ MOEW2_DEV void mma_tile(const TileRegs& r, const uint8_t* a_row, int kt, f32x4_t
   }
 }
 
-// Stream k-tiles [kb, ke) of NB row groups through a kRing-deep register ring.
+// ring[i] <- k-tile kb + i (out-of-range requests past ke)
+template <int NB>
+MOEW2_DEV void prime_ring(TileRegs (&ring)[kRing], const WaveTiles<NB>& wt, int kb, int ke, int lane) {
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) load_tile<NB>(ring[i], wt, kb + i, kb + i < ke, lane);
+}
+
+// Consume k-tiles [kb, ke) from the primed ring; each consumed slot is refilled with the tile
+// kRing further on (or an out-of-range request), so every iteration issues the same loads.
 template <class Op, int NB>
-MOEW2_DEV void stream_k(TileRegs (&ring)[kRing], const uint8_t* codes, const uint8_t* scales,
-                        const long long* tile_idx, int kb, int ke, const uint8_t* a_row, f32x4_t* acc,
-                        int lane) {
+MOEW2_DEV void stream_k(TileRegs (&ring)[kRing], const WaveTiles<NB>& wt, int kb, int ke, const uint8_t* a_row,
+                        f32x4_t* acc, int lane) {
   for (int k0 = kb; k0 < ke; k0 += kRing) {
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       const int kt = k0 + i;
-      if (kt < ke) {
-        mma_tile<Op, NB>(ring[i], a_row, kt, acc);
-        if (kt + kRing < ke) load_tile<NB>(ring[i], codes, scales, tile_idx, kt + kRing, lane);
-      }
+      if (kt < ke) mma_tile<Op, NB>(ring[i], a_row, kt, acc);
+      load_tile<NB>(ring[i], wt, kt + kRing, kt + kRing < ke, lane);
     }
   }
 }
 
-template <int NB>
-MOEW2_DEV void prime_ring(TileRegs (&ring)[kRing], const uint8_t* codes, const uint8_t* scales,
-                          const long long* tile_idx, int kb, int ke, int lane) {
+// Staging of n rows (row length `len` 16-bit elements, a multiple of 256) into LDS rows of
+// `stride` bytes; row m starts at element row_off(m) of src. Piece idx (16 bytes) of the flat
+// [n][len/8] range goes to thread idx % NT; a batch covers kStage pieces per thread, issued
+// together (stage_issue) and written to LDS together (stage_commit).
+struct Stage {
+  u32x4_t v[kStage];
+};
+
+template <int NT, class RowOff>
+MOEW2_DEV void stage_issue(Stage& st, const uint16_t* src, int len, int n, int base, RowOff row_off, int tid) {
+  const int per_row = len / 8, total = n * per_row;
 #pragma unroll
-  for (int i = 0; i < kRing; ++i)
-    if (kb + i < ke) load_tile<NB>(ring[i], codes, scales, tile_idx, kb + i, lane);
+  for (int i = 0; i < kStage; ++i) {
+    const int idx = base + i * NT + tid;
+    if (idx < total) {
+      const int m = idx / per_row, c8 = idx - m * per_row;
+      st.v[i] = ld16(src + row_off(m) + (size_t)c8 * 8);
+    }
+  }
 }
 
-// Work group of rows: expert e, n pairs; pair m's index and its row in the gated-intermediate
-// buffer.
-struct Group {
-  int e, n, row0;
-};
+template <int NT>
+MOEW2_DEV void stage_commit(const Stage& st, uint8_t* lds, int stride, int len, int n, int base, int tid) {
+  const int per_row = len / 8, total = n * per_row;
+#pragma unroll
+  for (int i = 0; i < kStage; ++i) {
+    const int idx = base + i * NT + tid;
+    if (idx < total) {
+      const int m = idx / per_row, c8 = idx - m * per_row;
+      *reinterpret_cast<u32x4_t*>(lds + (size_t)m * stride + (size_t)c8 * 16) = st.v[i];
+    }
+  }
+}
+
+// Stage n rows while the weight ring is primed. Batches beyond the first (rows longer than
+// kStage * NT / n pieces) go first, one round trip each; the first batch is issued just before
+// the prime and written after it. Every path thus reaches the streaming loop with the same loads
+// outstanding, which keeps the compiler's waits inside the loop exact.
+template <int NT, int NB, class RowOff>
+MOEW2_DEV void stage_and_prime(TileRegs (&ring)[kRing], const WaveTiles<NB>& wt, int kb, int ke, int lane,
+                               uint8_t* lds, int stride, const uint16_t* src, int len, int n, RowOff row_off,
+                               int tid) {
+  Stage st;
+  for (int base = kStage * NT; base < n * (len / 8); base += kStage * NT) {
+    stage_issue<NT>(st, src, len, n, base, row_off, tid);
+    stage_commit<NT>(st, lds, stride, len, n, base, tid);
+  }
+  stage_issue<NT>(st, src, len, n, 0, row_off, tid);
+  prime_ring<NB>(ring, wt, kb, ke, lane);
+  stage_commit<NT>(st, lds, stride, len, n, 0, tid);
+}
 
 // ---------------------------------------------------------------------------------------------
 // gate_up: grid (I / (16*NP), groups). Wave w handles row-pair q = blockIdx.x*NP + w/KS (gate row
@@ -120,44 +188,46 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
                       int E, int K, int I, int top_k) {
   constexpr int KS = kWaves / NP;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  Group g;
+  int e, n_total, row0;
   if (DIRECT) {
-    const int p = blockIdx.y;
-    g.e = ids[p];
-    if (g.e < 0 || g.e >= E) return;
-    g.n = 1;
-    g.row0 = p;
+    row0 = blockIdx.y;             // the pair
+    e = ids[row0];
+    if (e < 0 || e >= E) return;
+    n_total = 1;
   } else {
     if ((int)blockIdx.y >= meta[0]) return;
-    g.e = active[blockIdx.y];
-    g.row0 = offsets[g.e];
-    g.n = offsets[g.e + 1] - g.row0;
+    e = active[blockIdx.y];
+    row0 = offsets[e];
+    n_total = offsets[e + 1] - row0;
   }
   const int nkt = K / kTileK, nrg = 2 * I / kTileRows;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
   const int pw = w / KS, ks = w % KS;
   const int q = blockIdx.x * NP + pw;
-  long long tile_idx[2] = {((long long)g.e * nrg + 2 * q) * nkt, ((long long)g.e * nrg + 2 * q + 1) * nkt};
+  WaveTiles<2> wt = wave_tiles<2>(codes, scales, e, (uint32_t)(nrg * nkt));
+  wt.tile[0] = (uint32_t)(2 * q * nkt);
+  wt.tile[1] = (uint32_t)((2 * q + 1) * nkt);
   const int kb = ks * nkt / KS, ke = (ks + 1) * nkt / KS;
   const int stride = K * 2 + 16;
   float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][2][4][16]
   TileRegs ring[kRing];
-  for (int c0 = 0; c0 < g.n; c0 += kChunk) {
-    const int n = min(kChunk, g.n - c0);
-    prime_ring<2>(ring, codes, scales, tile_idx, kb, ke, lane);
-    const int per_row = K / 8;
-    for (int idx = tid; idx < n * per_row; idx += kThreads) {
-      const int m = idx / per_row, c8 = idx - m * per_row;
-      const int p = DIRECT ? g.row0 : perm[g.row0 + c0 + m];
-      const int t = p / top_k;
-      *reinterpret_cast<u32x4_t*>(lds + (size_t)m * stride + (size_t)c8 * 16) =
-          ld16(x + (size_t)t * K + (size_t)c8 * 8);
-    }
+  for (int c0 = 0; c0 < n_total; c0 += kChunk) {
+    const int n = min(kChunk, n_total - c0);
+    // token of each staged row (wave-uniform loads)
+    int tk[kChunk];
+#pragma unroll
+    for (int m = 0; m < kChunk; ++m) tk[m] = (DIRECT ? row0 : perm[row0 + c0 + min(m, n - 1)]) / top_k;
+    auto row_off = [&](int m) -> size_t {
+      const int t = m == 0 ? tk[0] : m == 1 ? tk[1] : m == 2 ? tk[2] : tk[3];
+      return (size_t)t * K;
+    };
+    stage_and_prime<kThreads, 2>(ring, wt, kb, ke, lane, lds, stride, x, K, n, row_off, tid);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
     const uint8_t* a_row = lds + (size_t)ma * stride + (size_t)(8 * (lane >> 4)) * 2;
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    stream_k<Bf16Op, 2>(ring, codes, scales, tile_idx, kb, ke, a_row, acc, lane);
+    stream_k<Bf16Op, 2>(ring, wt, kb, ke, a_row, acc, lane);
     if (KS > 1) {
       if (ks > 0 && lane < 16) {
 #pragma unroll
@@ -185,7 +255,7 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
           const float a = silu_mul(acc[0][r], acc[1][r]);
           const _Float16 h = (_Float16)a;
           if (__builtin_isinf((float)h) && !__builtin_isinf(a)) atomicAdd((unsigned long long*)&counters[1], 1ull);
-          const int row = DIRECT ? g.row0 : g.row0 + c0 + r;
+          const int row = DIRECT ? row0 : row0 + c0 + r;
           act[(size_t)row * I + 16 * q + lane] = h;
         }
       }
@@ -208,34 +278,31 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
                    float* __restrict__ pair_out, int E, int K, int I, int top_k) {
   constexpr int KS = kWaves / NP;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int n_active = meta[0];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if ((int)blockIdx.y >= n_active) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
+  if ((int)blockIdx.y >= meta[0]) return;
   const int e = active[blockIdx.y];
   const int row0 = offsets[e];
   const int n_e = offsets[e + 1] - row0;
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int pw = w / KS, ks = w % KS;
   const int rg = blockIdx.x * NP + pw;
-  long long tile_idx[1] = {((long long)e * nrg + rg) * nkt};
+  WaveTiles<1> wt = wave_tiles<1>(codes, scales, e, (uint32_t)(nrg * nkt));
+  wt.tile[0] = (uint32_t)(rg * nkt);
   const int kb = ks * nkt / KS, ke = (ks + 1) * nkt / KS;
   const int stride = I * 2 + 16;
   float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][4][16]
+  const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
   TileRegs ring[kRing];
   for (int c0 = 0; c0 < n_e; c0 += kChunk) {
     const int n = min(kChunk, n_e - c0);
-    prime_ring<1>(ring, codes, scales, tile_idx, kb, ke, lane);
-    const int per_row = I / 8;
-    for (int idx = tid; idx < n * per_row; idx += kThreads) {
-      const int m = idx / per_row, c8 = idx - m * per_row;
-      *reinterpret_cast<u32x4_t*>(lds + (size_t)m * stride + (size_t)c8 * 16) =
-          ld16(act + (size_t)(row0 + c0 + m) * I + (size_t)c8 * 8);
-    }
+    auto row_off = [&](int m) -> size_t { return (size_t)(row0 + c0 + m) * I; };
+    stage_and_prime<kThreads, 1>(ring, wt, kb, ke, lane, lds, stride, act16, I, n, row_off, tid);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
     const uint8_t* a_row = lds + (size_t)ma * stride + (size_t)(8 * (lane >> 4)) * 2;
     f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    stream_k<F16Op, 1>(ring, codes, scales, tile_idx, kb, ke, a_row, acc, lane);
+    stream_k<F16Op, 1>(ring, wt, kb, ke, a_row, acc, lane);
     if (KS > 1) {
       if (ks > 0 && lane < 16) {
 #pragma unroll
@@ -268,8 +335,9 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
 
 // ---------------------------------------------------------------------------------------------
 // direct down + combine for tiny batches: grid (K/16). The workgroup covers one row group of 16
-// output columns for every pair; wave w takes pairs w, w+4, ...; per-pair results meet in LDS and
-// are combined per token in j order. Also records the two counters (single writer: block 0).
+// output columns for every pair; wave w takes pair w/2 and half w%2 of the reduction; per-pair
+// results meet in LDS and are combined per token in j order. Block 0 also records the two
+// counters (single writer).
 // ---------------------------------------------------------------------------------------------
 constexpr int kDirectWaves = 2 * kDirectMaxPairs;   // two reduction halves per pair
 constexpr int kDirectThreads = 64 * kDirectWaves;
@@ -282,30 +350,26 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
                           int T, int E, int K, int I, int top_k) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int P = T * top_k;                         // <= kDirectMaxPairs
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int rg = blockIdx.x, col = 16 * rg + (lane & 15);
   const int stride = I * 2 + 16;
   float* o = reinterpret_cast<float*>(lds + (size_t)kDirectMaxPairs * stride);  // [P][16]
   float* red = o + kDirectMaxPairs * 16;                                        // [P][4][16]
-  // wave w: pair p = w / 2, reduction half w % 2; its tiles are requested before anything else
+  // wave w: pair p = w / 2, reduction half w % 2
   const int p = w >> 1, hk = w & 1;
   const int id = p < P ? ids[p] : -1;
   const bool valid = id >= 0 && id < E;
-  const long long tb = valid ? ((long long)id * nrg + rg) * nkt : 0;
+  WaveTiles<1> wt = wave_tiles<1>(codes, scales, valid ? id : 0, (uint32_t)(nrg * nkt));
+  wt.tile[0] = (uint32_t)(rg * nkt);
   const int kb = hk * nkt / 2, ke = valid ? (hk + 1) * nkt / 2 : kb;
-  TileRegs ring[kRing];
-  prime_ring<1>(ring, codes, scales, &tb, kb, ke, lane);
   const int e0 = valid ? dn_e0[(size_t)id * K + col] : 0;
-  // stage the gated rows of all valid pairs
-  const int per_row = I / 8;
-  for (int idx = tid; idx < P * per_row; idx += kDirectThreads) {
-    const int pp = idx / per_row, c8 = idx - pp * per_row;
-    const int ii = ids[pp];
-    if (ii >= 0 && ii < E)
-      *reinterpret_cast<u32x4_t*>(lds + (size_t)pp * stride + (size_t)c8 * 16) =
-          ld16(act + (size_t)pp * I + (size_t)c8 * 8);
-  }
+  // gated rows of all pairs (rows of invalid pairs are staged but never read)
+  const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
+  auto row_off = [&](int m) -> size_t { return (size_t)m * I; };
+  TileRegs ring[kRing];
+  stage_and_prime<kDirectThreads, 1>(ring, wt, kb, ke, lane, lds, stride, act16, I, P, row_off, tid);
   __syncthreads();
   if (blockIdx.x == 0) {
     // counters: invalid pairs, and gated intermediates that are infinite (from the staged rows)
@@ -327,11 +391,9 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
     if (tid == 0) { counters[0] = cnt[0]; counters[1] = cnt[1]; }
   }
   f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  if (valid) {
-    const uint8_t* a_row = lds + (size_t)p * stride + (size_t)(8 * (lane >> 4)) * 2;
-    stream_k<F16Op, 1>(ring, codes, scales, &tb, kb, ke, a_row, acc, lane);
-    if (hk == 1 && lane < 16) red[p * 16 + lane] = acc[0][0];
-  }
+  const uint8_t* a_row = lds + (size_t)(p < P ? p : 0) * stride + (size_t)(8 * (lane >> 4)) * 2;
+  stream_k<F16Op, 1>(ring, wt, kb, ke, a_row, acc, lane);
+  if (valid && hk == 1 && lane < 16) red[p * 16 + lane] = acc[0][0];
   __syncthreads();
   if (valid && hk == 0 && lane < 16) o[p * 16 + lane] = __builtin_ldexpf(acc[0][0] + red[p * 16 + lane], e0);
   __syncthreads();

@@ -20,7 +20,8 @@
  *  - Every entry point returns a status (enum moe_w2_status). Host-detectable problems (null
  *    pointers, unsupported shapes, too small workspace) return a negative status before anything
  *    is enqueued. No call prints, aborts or throws.
- *  - Shapes: K (hidden size) and I (expert intermediate size) must be multiples of 256;
+ *  - Shapes: K (hidden size) and I (expert intermediate size) must be multiples of 256 with
+ *    I*K < 2^32;
  *    1 <= E <= 1024; 1 <= top_k <= 32; T >= 0 (T = 0 is a no-op). A forward also needs
  *    T*K < 2^31 and T*top_k*I < 2^31 (element counts of x and of the gated intermediate).
  *
