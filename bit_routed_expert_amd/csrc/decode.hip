@@ -265,9 +265,9 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------------------------
-// routed down: grid (K / (16*NP), active slots). Wave w handles row group rg = blockIdx.x*NP +
-// w/KS over the reduction slice w%KS. Per-pair rows go to pair_out at the pair index (bijective);
-// combine_kernel then sums them per token in j order.
+// routed down: grid (K / (32*NP), active slots). Wave w handles row groups 2*rq and 2*rq + 1,
+// rq = blockIdx.x*NP + w/KS, over the reduction slice w%KS. Per-pair rows go to pair_out at the
+// pair index (bijective); combine_kernel then sums them per token in j order.
 // ---------------------------------------------------------------------------------------------
 template <int NP>
 __global__ void __launch_bounds__(kThreads)
@@ -286,46 +286,54 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
   const int n_e = offsets[e + 1] - row0;
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int pw = w / KS, ks = w % KS;
-  const int rg = blockIdx.x * NP + pw;
-  WaveTiles<1> wt = wave_tiles<1>(codes, scales, e, (uint32_t)(nrg * nkt));
-  wt.tile[0] = (uint32_t)(rg * nkt);
+  const int rq = blockIdx.x * NP + pw;
+  WaveTiles<2> wt = wave_tiles<2>(codes, scales, e, (uint32_t)(nrg * nkt));
+  wt.tile[0] = (uint32_t)(2 * rq * nkt);
+  wt.tile[1] = (uint32_t)((2 * rq + 1) * nkt);
   const int kb = ks * nkt / KS, ke = (ks + 1) * nkt / KS;
   const int stride = I * 2 + 16;
-  float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][4][16]
+  float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][2][4][16]
   const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
   TileRegs ring[kRing];
   for (int c0 = 0; c0 < n_e; c0 += kChunk) {
     const int n = min(kChunk, n_e - c0);
     auto row_off = [&](int m) -> size_t { return (size_t)(row0 + c0 + m) * I; };
-    stage_and_prime<kThreads, 1>(ring, wt, kb, ke, lane, lds, stride, act16, I, n, row_off, tid);
+    stage_and_prime<kThreads, 2>(ring, wt, kb, ke, lane, lds, stride, act16, I, n, row_off, tid);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
     const uint8_t* a_row = lds + (size_t)ma * stride + (size_t)(8 * (lane >> 4)) * 2;
-    f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    stream_k<F16Op, 1>(ring, wt, kb, ke, a_row, acc, lane);
+    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    stream_k<F16Op, 2>(ring, wt, kb, ke, a_row, acc, lane);
     if (KS > 1) {
       if (ks > 0 && lane < 16) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[(w * 4 + r) * 16 + lane] = acc[0][r];
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[((w * 2 + b) * 4 + r) * 16 + lane] = acc[b][r];
       }
       __syncthreads();
       if (ks == 0 && lane < 16) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = acc[0][r];
-          for (int kk = 1; kk < KS; ++kk) v += red[((w + kk) * 4 + r) * 16 + lane];
-          acc[0][r] = v;
-        }
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v = acc[b][r];
+            for (int kk = 1; kk < KS; ++kk) v += red[(((w + kk) * 2 + b) * 4 + r) * 16 + lane];
+            acc[b][r] = v;
+          }
       }
     }
     if (ks == 0 && lane < 16) {
-      const int col = 16 * rg + lane;
-      const int e0 = dn_e0[(size_t)e * K + col];
 #pragma unroll
-      for (int r = 0; r < kChunk; ++r) {
-        if (r < n) {
-          const int p = perm[row0 + c0 + r];
-          pair_out[(size_t)p * K + col] = __builtin_ldexpf(acc[0][r], e0);
+      for (int b = 0; b < 2; ++b) {
+        const int col = 16 * (2 * rq + b) + lane;
+        const int e0 = dn_e0[(size_t)e * K + col];
+#pragma unroll
+        for (int r = 0; r < kChunk; ++r) {
+          if (r < n) {
+            const int p = perm[row0 + c0 + r];
+            pair_out[(size_t)p * K + col] = __builtin_ldexpf(acc[b][r], e0);
+          }
         }
       }
     }
@@ -414,22 +422,37 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
 }
 
 // y[t] = sum_j (ascending) w[t, j] * o[t*top_k + j]; ids outside [0, E) contribute nothing.
-// One thread per 4 output columns of one token (used after the GEMM path).
+// One thread per 4 output columns of one token. A group of up to 8 pairs has its ids, weights and
+// pair rows requested together (rows of invalid pairs are read but not used), so a token costs
+// one memory round trip per 8 pairs; the sum itself runs in ascending j.
 __global__ void combine_kernel(const int32_t* __restrict__ ids, const float* __restrict__ wts,
                                const float* __restrict__ pair_out, void* __restrict__ y,
                                int T, int top_k, int E, int K, int out_dtype) {
+  constexpr int G = 8;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int q = K / 4;
   if (gid >= (long long)T * q) return;
   const int t = (int)(gid / q), c = (int)(gid - (long long)t * q) * 4;
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-  for (int j = 0; j < top_k; ++j) {
-    const int p = t * top_k + j;
-    const int id = ids[p];
-    if (id < 0 || id >= E) continue;
-    const float w = wts[p];
-    const float4 o = *reinterpret_cast<const float4*>(pair_out + (size_t)p * K + c);
-    acc0 += w * o.x; acc1 += w * o.y; acc2 += w * o.z; acc3 += w * o.w;
+  for (int j0 = 0; j0 < top_k; j0 += G) {
+    int id[G];
+    float w[G];
+    float4 o[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (j0 + i < top_k) {
+        const int p = t * top_k + j0 + i;
+        id[i] = ids[p];
+        w[i] = wts[p];
+        o[i] = *reinterpret_cast<const float4*>(pair_out + (size_t)p * K + c);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (j0 + i < top_k && id[i] >= 0 && id[i] < E) {
+        acc0 += w[i] * o[i].x; acc1 += w[i] * o[i].y; acc2 += w[i] * o[i].z; acc3 += w[i] * o[i].w;
+      }
+    }
   }
   if (out_dtype == MOE_W2_OUT_F32) {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)t * K + c) = make_float4(acc0, acc1, acc2, acc3);
@@ -487,7 +510,7 @@ hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const in
     return hipGetLastError();
   }
   const int slots = min(p->E, P);
-  const size_t lds = (size_t)kChunk * (p->I * 2 + 16) + (size_t)kWaves * 4 * 16 * 4;
+  const size_t lds = (size_t)kChunk * (p->I * 2 + 16) + (size_t)kWaves * 2 * 4 * 16 * 4;
   const int np = pick_np(slots);
   auto args = [&](auto kern, int gx) {
     hipLaunchKernelGGL(kern, dim3(gx, slots), dim3(kThreads), lds, s,
@@ -496,8 +519,8 @@ hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const in
                        (const int32_t*)(wsb + ws.active), (const int32_t*)(wsb + ws.meta),
                        (float*)(wsb + ws.pair_out), p->E, p->K, p->I, top_k);
   };
-  if (np == 4) args(decode_down_kernel<4>, p->K / 64);
-  else args(decode_down_kernel<1>, p->K / 16);
+  if (np == 4) args(decode_down_kernel<4>, p->K / 128);
+  else args(decode_down_kernel<1>, p->K / 32);
   return hipGetLastError();
 }
 
