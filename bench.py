@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-iters", type=int, default=5)
+    ap.add_argument("--no-requant", action="store_true")
+    ap.add_argument("--requant-iters", type=int, default=5)
     ap.add_argument("--eager", action="store_true",
                     help="launch every timed call from Python instead of replaying HIP graphs (for profilers)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -286,6 +288,8 @@ def main():
 
     if not args.no_prefill:
         out["prefill"] = bench_prefill(args, moe, workloads, torch, dev)
+    if not args.no_requant:
+        out["requant"] = bench_requant(args, moe, workloads, torch, dev)
 
     # free GPU memory before the CPU baseline
     if not args.no_cpu_baseline:
@@ -341,6 +345,43 @@ def bench_prefill(args, moe, workloads, torch, dev):
         gemm_tflops=round(gemm_tflops, 1), gemm_mfma_frac=round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         fwd_tflops=round(fwd_tflops, 1), fwd_mfma_frac=round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         peak_tflops=MFMA_BF16_PEAK_TFLOPS, iters=args.prefill_iters)
+
+
+def bench_requant(args, moe, workloads, torch, dev):
+    """nvfp4_to_w2 over the n=256 tensors of [2048, 6144]: one synchronous call per iteration,
+    timed with events on its stream (the call's flag clear, kernel and status read-back)."""
+    c = workloads.REQUANT
+    n, R, C = c["n"], c["R"], c["C"]
+    e2m1 = torch.empty((n, R, C // 2), dtype=torch.uint8, device="cuda")
+    e4m3 = torch.empty((n, R, C // 16), dtype=torch.uint8, device="cuda")
+    s2 = np.zeros(n, np.float32)
+    for i in range(n):
+        a, b, s = workloads.nvfp4_tensor(i)
+        e2m1[i].copy_(torch.from_numpy(a))
+        e4m3[i].copy_(torch.from_numpy(b))
+        s2[i] = s
+    s2d = dev(s2)
+    codes = torch.empty((n, R, C // 4), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, R, C // 32), dtype=torch.uint8, device="cuda")
+    moe.nvfp4_to_w2(e2m1, e4m3, s2d, codes, scales)
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(args.requant_iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        moe.nvfp4_to_w2(e2m1, e4m3, s2d, codes, scales)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    nbytes = n * R * (C // 2 + C // 16 + C // 4 + C // 32) + 4 * n
+    blocks = n * R * (C // 32)
+    del e2m1, e4m3, codes, scales
+    torch.cuda.empty_cache()
+    return dict(workload="nvfp4_to_w2: 256 tensors of [2048, 6144] (e2m1 x e4m3/16 x fp32 scale_2 -> 2-bit + UE8M0/32)",
+                ms=round(ms, 4), hbm_GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                blocks_per_s=round(blocks / (ms * 1e-3), 1), algorithmic_bytes=nbytes, iters=args.requant_iters)
 
 
 def cpu_baseline(canon, inst):
