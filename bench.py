@@ -25,6 +25,7 @@ The JSON line also carries:
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -175,7 +176,11 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             timed_steps()
-        graph.replay()          # warm replay (untimed)
+        # untimed warm replays, at least ~50 ms of GPU work: the GPU idles while the graph is
+        # captured, and its clocks take a few milliseconds of load to come back up
+        replay_s = max(eager_elapsed, 1e-4)     # one replay runs about as long as the eager steps
+        for _ in range(max(2, int(math.ceil(0.05 / replay_s)))):
+            graph.replay()
     torch.cuda.synchronize()
     g0, g1 = ev(), ev()
     t0 = time.perf_counter()
