@@ -24,6 +24,7 @@ Workspace workspace_layout(int E, int K, int I, int T, int top_k) {
   w.chunk_cnt = o;
   w.rank = o + (rs - align_up((size_t)P * 4));
   o += rs;
+  w.xq = o;        o += align_up((size_t)T * (2 * (size_t)K + K / 16));
   w.act = o;       o += align_up((size_t)P * I * 2);
   w.pair_out = o;  o += align_up((size_t)P * K * 4);
   w.total = o;

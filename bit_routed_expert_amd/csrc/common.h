@@ -18,17 +18,19 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 // Native plane layout (built by moe_w2_pack):
 //   A weight matrix of NR rows (output features) and reduction length KR is stored as tiles of
 //   16 rows x 256 reduction elements; tile (rg, kt) holds 1024 code bytes at
-//   (rg * (KR/256) + kt) * 1024. Lane l (0..63) of a wave owns row 16*rg + l%16 and the
-//   8-element group g = l/16 of every 32-element block; its 16 bytes sit at tile + 16*l, so one
-//   16-byte load per lane is one fully coalesced 1 KiB wave load.
-//   Dword j (0..3) of a lane covers blocks b = 2j and 2j+1 of the tile, elements
-//   k = 256*kt + 32*b + 8*g + i (i = 0..7), as bit pairs: bit 4i+3 = sign (block 2j, i),
-//   bit 4i+2 = |value|==4 (block 2j, i), bit 4i+1 = sign (block 2j+1, i), bit 4i+0 = |value|==4
-//   (block 2j+1, i). So (dw & 0xCCCCCCCC) | 0x22222222 is eight e2m1 codes (+-1 = 0b?010,
-//   +-4 = 0b?110) of block 2j and ((dw << 2) & 0xCCCCCCCC) | 0x22222222 those of block 2j+1; byte
-//   q of such a word holds elements 2q (low nibble) and 2q+1, which is exactly the 8-element B
-//   operand of v_mfma_f32_16x16x32 for lane l (column l%16, k = 8*(l/16) .. +7).
-//   Scale tile (rg, kt): 128 bytes at (rg * (KR/256) + kt) * 128, row-major [16 rows][8 blocks].
+//   (rg * (KR/256) + kt) * 1024 and 128 scale bytes at (rg * (KR/256) + kt) * 128. Lane l
+//   (0..63) of a wave owns row 16*rg + l%16 and reads the 16 code bytes at tile + 16*l, so one
+//   16-byte load per lane is one fully coalesced 1 KiB wave load. With g = l/16, each of the
+//   lane's 4 dwords holds 16 values as bit pairs: for value slot i = 0..7 and sub-slot s = 0, 1,
+//   bit 4i+3-2s = sign and bit 4i+2-2s = |value|==4. So (dw & 0xCCCCCCCC) | 0x22222222 is eight
+//   e2m1 codes (+-1 = 0b?010, +-4 = 0b?110) of sub-slot 0 and ((dw << 2) & 0xCCCCCCCC) |
+//   0x22222222 those of sub-slot 1, value i in nibble i (low nibble first).
+//   Two assignments of values to slots:
+//   * k-group layout (down matrices), for v_mfma_f32_16x16x32: dword j, sub-slot s covers block
+//     b = 2j+s, k = 256kt + 32b + 8g + i; scale tile row-major [16 rows][8 blocks].
+//   * block layout (gate_up matrices), for the block-scaled fp4 instruction: dwords 0,1 cover
+//     block 8kt + g and dwords 2,3 block 8kt + 4 + g; dword j, sub-slot s holds values
+//     16*(j%2) + 8s + i of its block; scale byte 2*l + c = block 8kt + 4c + g of row l%16.
 //   Gate_up matrices interleave rows in groups of 16: row group 2q = gate rows 16q..16q+15,
 //   row group 2q+1 = up rows 16q..16q+15. Down scale bytes are stored minus a per-row offset E0
 //   (kept separately) so that every down weight is exact in fp16.
@@ -38,7 +40,7 @@ constexpr int kTileK = 256;
 constexpr int kTileCodeBytes = 1024;
 constexpr int kTileScaleBytes = 128;
 
-// Two e2m1 words (8 codes each, blocks 2j and 2j+1) from one native dword.
+// Two e2m1 words (8 codes each: sub-slots 0 and 1) from one native dword.
 MOEW2_DEV void native_to_fp4(uint32_t dw, uint32_t& blk0, uint32_t& blk1) {
   blk0 = (dw & 0xCCCCCCCCu) | 0x22222222u;
   blk1 = ((dw << 2) & 0xCCCCCCCCu) | 0x22222222u;
@@ -95,6 +97,76 @@ struct F16Op {
 // k = 8*(l/16) .. +7; B lane l holds column l%16, the same k; accumulator register r (0..3) of
 // lane l holds row 4*(l/16) + r, column l%16.
 
+// ------------------------------------------------------------------------------------------
+// Block-scaled (MX) matrix instruction v_mfma_scale_f32_16x16x128_f8f6f4 with A = fp8 (OCP
+// e4m3) and B = fp4 (e2m1); layout checked on the device. With g = l/16, one instruction covers
+// 128 k = 4 blocks of 32:
+//   B lane l: column l%16, all 32 values of block g in k order (nibble i of the 128-bit operand
+//             = value i; low nibble first).
+//   A lane l: row l%16; operand bytes 0..15 = k 16g .. 16g+15, bytes 16..31 = k 64+16g .. +15.
+//   scales: lane l supplies the E8M0 byte of (row/column l%16, block g), selected from its
+//           32-bit scale register by op_sel (0..3).
+//   accumulator: as for v_mfma_f32_16x16x32.
+// The gate_up planes use this operand order (see the planes' layout note above): in k-tile kt,
+// lane l holds blocks 8kt + g (instruction 0) and 8kt + 4 + g (instruction 1) of its row.
+// ------------------------------------------------------------------------------------------
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4e_t __attribute__((ext_vector_type(4)));
+
+constexpr int kFmtFp8 = 0;   // A operand format: OCP e4m3
+constexpr int kFmtFp4 = 4;   // B operand format: e2m1
+
+// B operand of one instruction from the lane's two native dwords of a block (values 0..15 and
+// 16..31): four e2m1 words.
+MOEW2_DEV i32x8_t mx_b_operand(uint32_t d0, uint32_t d1) {
+  uint32_t a0, a1, b0, b1;
+  native_to_fp4(d0, a0, a1);
+  native_to_fp4(d1, b0, b1);
+  i32x8_t v = {(int)a0, (int)a1, (int)b0, (int)b1, 0, 0, 0, 0};
+  return v;
+}
+
+template <int OPA, int OPB>
+MOEW2_DEV f32x4_t mx_mfma(const i32x8_t& a, const i32x8_t& b, f32x4_t c, uint32_t sa, uint32_t sb) {
+  const f32x4e_t r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+      a, b, __builtin_bit_cast(f32x4e_t, c), kFmtFp8, kFmtFp4, OPA, (int)sa, OPB, (int)sb);
+  return __builtin_bit_cast(f32x4_t, r);
+}
+
+// x as two e4m3 parts for the A operand. Per 32-element block with |x| <= amax: scale byte
+// sx = max(0, exponent field of amax - 7), so |x| / 2^(sx-127) < 256 fits e4m3 (max 448);
+// hi = RNE_e4m3(x / 2^(sx-127)); lo = RNE_e4m3(16 * (x / 2^(sx-127) - hi)) with scale byte sx - 4.
+// A bf16 value (8 significant bits) is the exact sum of the two parts whenever it is at least
+// 2^-11 of the block maximum (hi holds the top 4 bits, the remainder has at most 4); smaller
+// values keep an error below 2^-21 of the block maximum. sx < 4 (a block maximum below 2^-116)
+// drops the lo part.
+MOEW2_DEV uint32_t x_scale_byte(float amax) {
+  const int ef = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 255u);
+  return (uint32_t)(ef > 7 ? ef - 7 : 0);
+}
+MOEW2_DEV uint32_t x_lo_scale_byte(uint32_t sx) { return sx >= 4 ? sx - 4 : 0; }
+
+// Four values -> four hi bytes and four lo bytes (one dword each), given the block's scale byte.
+MOEW2_DEV void x_split4(float v0, float v1, float v2, float v3, uint32_t sx, uint32_t& hi, uint32_t& lo) {
+  const int sh = 127 - (int)sx, sl = 131 - (int)sx;
+  const float t0 = __builtin_ldexpf(v0, sh), t1 = __builtin_ldexpf(v1, sh);
+  const float t2 = __builtin_ldexpf(v2, sh), t3 = __builtin_ldexpf(v3, sh);
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, h, true);
+  const float r0 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(h, 0), -16.f, __builtin_ldexpf(v0, sl));
+  const float r1 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(h, 1), -16.f, __builtin_ldexpf(v1, sl));
+  const float r2 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(h, 2), -16.f, __builtin_ldexpf(v2, sl));
+  const float r3 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(h, 3), -16.f, __builtin_ldexpf(v3, sl));
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, l, true);
+  hi = (uint32_t)h;
+  lo = sx >= 4 ? (uint32_t)l : 0u;
+}
+
+// bf16 bits -> float
+MOEW2_DEV float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+MOEW2_DEV float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
 MOEW2_DEV float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // 16-byte global load / store helpers
@@ -118,6 +190,9 @@ MOEW2_DEV u32x4_t buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t 
 }
 MOEW2_DEV u32x2_t buf_ld8_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kPolicyNT));
+}
+MOEW2_DEV uint32_t buf_ld2_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, kPolicyNT);
 }
 
 // Round-to-nearest-even fp32 -> bf16 bits (finite and infinite inputs; NaN stays NaN).

@@ -173,6 +173,112 @@ MOEW2_DEV void stage_and_prime(TileRegs (&ring)[kRing], const WaveTiles<NB>& wt,
 }
 
 // ---------------------------------------------------------------------------------------------
+// gate_up on the block-scaled matrix instruction (fp8 x, fp4 weights; operand order in common.h).
+// The staged x rows are split into hi and lo e4m3 parts while they are written to LDS:
+//   row layout in LDS: hi [K] bytes | lo [K] bytes | scale words [K/256][4 lane groups][4 bytes:
+//   hi chunk 0, hi chunk 1, lo chunk 0, lo chunk 1] | pad.
+// ---------------------------------------------------------------------------------------------
+__host__ __device__ inline int gu_row_stride(int K) { return 2 * K + K / 16 + 64; }
+
+struct GuTileRegs {
+  u32x4_t c[2];     // codes of the gate and up row groups (block layout)
+  uint32_t s[2];    // their two scale bytes (chunks 0 and 1)
+};
+
+MOEW2_DEV void load_gu_tile(GuTileRegs& r, const WaveTiles<2>& wt, int kt, bool valid, int lane) {
+  const uint32_t oob = valid ? 0u : kOutOfRange;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint32_t t = wt.tile[b] + (uint32_t)kt;
+    r.c[b] = buf_ld16_nt(wt.codes, (16u * (uint32_t)lane) | oob, t * kTileCodeBytes);
+    r.s[b] = buf_ld2_nt(wt.scales, (2u * (uint32_t)lane) | oob, t * kTileScaleBytes);
+  }
+}
+
+template <int C>
+MOEW2_DEV void mma_gu_chunk(const GuTileRegs& r, const uint8_t* hi, const uint8_t* lo, uint32_t sa, int g,
+                            f32x4_t* acc) {
+  const u32x4_t h0 = *reinterpret_cast<const u32x4_t*>(hi + 128 * C + 16 * g);
+  const u32x4_t h1 = *reinterpret_cast<const u32x4_t*>(hi + 128 * C + 64 + 16 * g);
+  const u32x4_t l0 = *reinterpret_cast<const u32x4_t*>(lo + 128 * C + 16 * g);
+  const u32x4_t l1 = *reinterpret_cast<const u32x4_t*>(lo + 128 * C + 64 + 16 * g);
+  const i32x8_t ah = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+  const i32x8_t al = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const i32x8_t bo = mx_b_operand(r.c[b][2 * C], r.c[b][2 * C + 1]);
+    acc[b] = mx_mfma<C, C>(ah, bo, acc[b], sa, r.s[b]);
+    acc[b] = mx_mfma<2 + C, C>(al, bo, acc[b], sa, r.s[b]);
+  }
+}
+
+// One k-tile: `arow` is the lane's staged row (hi part at +0, lo at +K, scale words at +2K).
+MOEW2_DEV void mma_gu_tile(const GuTileRegs& r, const uint8_t* arow, int K, int kt, int g, f32x4_t* acc) {
+  const uint8_t* hi = arow + kt * kTileK;
+  const uint8_t* lo = hi + K;
+  const uint32_t sa = *reinterpret_cast<const uint32_t*>(arow + 2 * K + kt * 16 + 4 * g);
+  mma_gu_chunk<0>(r, hi, lo, sa, g, acc);
+  mma_gu_chunk<1>(r, hi, lo, sa, g, acc);
+}
+
+MOEW2_DEV void prime_gu(GuTileRegs (&ring)[kRing], const WaveTiles<2>& wt, int kb, int ke, int lane) {
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) load_gu_tile(ring[i], wt, kb + i, kb + i < ke, lane);
+}
+
+MOEW2_DEV void stream_gu(GuTileRegs (&ring)[kRing], const WaveTiles<2>& wt, int kb, int ke, const uint8_t* arow,
+                         int K, int g, f32x4_t* acc, int lane) {
+  for (int k0 = kb; k0 < ke; k0 += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      const int kt = k0 + i;
+      if (kt < ke) mma_gu_tile(ring[i], arow, K, kt, g, acc);
+      load_gu_tile(ring[i], wt, kt + kRing, kt + kRing < ke, lane);
+    }
+  }
+}
+
+// Quantizing commit of staged bf16 pieces (8 values each): the 4 pieces of a 32-value block sit
+// in 4 consecutive lanes, which agree on the block maximum through two lane swaps.
+template <int NT>
+MOEW2_DEV void stage_commit_x8(const Stage& st, uint8_t* lds, int stride, int K, int n, int base, int tid) {
+  const int per_row = K / 8, total = n * per_row;
+#pragma unroll
+  for (int i = 0; i < kStage; ++i) {
+    const int idx = base + i * NT + tid;
+    const bool ok = idx < total;
+    const u32x4_t v = st.v[i];
+    float a = 0.f;
+    if (ok) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[q])), __builtin_fabsf(bf16_hi(v[q]))));
+    }
+    a = __builtin_fmaxf(a, __shfl_xor(a, 1, 64));
+    a = __builtin_fmaxf(a, __shfl_xor(a, 2, 64));
+    if (ok) {
+      const int m = idx / per_row, c8 = idx - m * per_row;
+      const uint32_t sx = x_scale_byte(a);
+      uint32_t h0, l0, h1, l1;
+      x_split4(bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1]), sx, h0, l0);
+      x_split4(bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3]), sx, h1, l1);
+      uint8_t* row = lds + (size_t)m * stride;
+      *reinterpret_cast<u32x2_t*>(row + 8 * c8) = u32x2_t{h0, h1};
+      *reinterpret_cast<u32x2_t*>(row + K + 8 * c8) = u32x2_t{l0, l1};
+      if ((c8 & 3) == 0) {
+        const int b = c8 >> 2, kt = b >> 3, d = b & 7, gg = d & 3, c = d >> 2;
+        uint8_t* sw = row + 2 * K + kt * 16 + 4 * gg;
+        sw[c] = (uint8_t)sx;
+        sw[2 + c] = (uint8_t)x_lo_scale_byte(sx);
+      }
+    }
+    // one piece at a time: interleaving the pieces' conversions would raise the register peak
+    // while the weight ring is in flight
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // gate_up: grid (I / (16*NP), groups). Wave w handles row-pair q = blockIdx.x*NP + w/KS (gate row
 // group 2q, up row group 2q+1) over the reduction slice w%KS of KS = 4/NP.
 // DIRECT: group = pair p (expert ids[p]); act row = p. Otherwise group = active slot; act row =
@@ -209,9 +315,9 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
   wt.tile[0] = (uint32_t)(2 * q * nkt);
   wt.tile[1] = (uint32_t)((2 * q + 1) * nkt);
   const int kb = ks * nkt / KS, ke = (ks + 1) * nkt / KS;
-  const int stride = K * 2 + 16;
+  const int stride = gu_row_stride(K);
   float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][2][4][16]
-  TileRegs ring[kRing];
+  GuTileRegs ring[kRing];
   for (int c0 = 0; c0 < n_total; c0 += kChunk) {
     const int n = min(kChunk, n_total - c0);
     // token of each staged row (wave-uniform loads)
@@ -222,12 +328,24 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
       const int t = m == 0 ? tk[0] : m == 1 ? tk[1] : m == 2 ? tk[2] : tk[3];
       return (size_t)t * K;
     };
-    stage_and_prime<kThreads, 2>(ring, wt, kb, ke, lane, lds, stride, x, K, n, row_off, tid);
+    // staging (extra batches first, the last one overlapped with the ring prime; see
+    // stage_and_prime), quantized to the hi / lo parts on the way into LDS. The thread index
+    // is passed through an empty asm so that the staging addresses are recomputed here instead
+    // of being hoisted out of the chunk loop and held in registers across the stream.
+    int st_tid = tid;
+    asm volatile("" : "+v"(st_tid));
+    Stage st;
+    for (int base = kStage * kThreads; base < n * (K / 8); base += kStage * kThreads) {
+      stage_issue<kThreads>(st, x, K, n, base, row_off, st_tid);
+      stage_commit_x8<kThreads>(st, lds, stride, K, n, base, st_tid);
+    }
+    stage_issue<kThreads>(st, x, K, n, 0, row_off, st_tid);
+    prime_gu(ring, wt, kb, ke, lane);
+    stage_commit_x8<kThreads>(st, lds, stride, K, n, 0, st_tid);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
-    const uint8_t* a_row = lds + (size_t)ma * stride + (size_t)(8 * (lane >> 4)) * 2;
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    stream_k<Bf16Op, 2>(ring, wt, kb, ke, a_row, acc, lane);
+    stream_gu(ring, wt, kb, ke, lds + (size_t)ma * stride, K, lane >> 4, acc, lane);
     if (KS > 1) {
       if (ks > 0 && lane < 16) {
 #pragma unroll
@@ -476,7 +594,7 @@ hipError_t launch_decode_gate_up(const moe_w2_planes* p, int T, int top_k, const
   const int P = T * top_k;
   const int slots = direct ? P : min(p->E, P);
   if (slots == 0) return hipSuccess;
-  const size_t lds = (size_t)kChunk * (p->K * 2 + 16) + (size_t)kWaves * 2 * 4 * 16 * 4;
+  const size_t lds = (size_t)kChunk * gu_row_stride(p->K) + (size_t)kWaves * 2 * 4 * 16 * 4;
   const uint16_t* xb = (const uint16_t*)x;
   const int32_t* off = (const int32_t*)(wsb + ws.offsets);
   const int32_t* perm = (const int32_t*)(wsb + ws.perm);

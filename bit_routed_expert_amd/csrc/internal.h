@@ -39,6 +39,8 @@ struct Workspace {
   size_t tiles;       // int32 [max_tiles][2] (expert, first sorted row) GEMM M-tiles
   size_t chunk_cnt;   // int32 [nchunks][E+1] per-chunk counts (large routing)
   size_t rank;        // int32 [P] rank of a pair within its chunk and expert
+  size_t xq;          // x split for the block-scaled instruction (GEMM path): hi [T][K] e4m3,
+                      // lo [T][K] e4m3, scale words [T][K/256][4][4] (hi c0, hi c1, lo c0, lo c1)
   size_t act;         // fp16 [P][I] gated intermediate, sorted order
   size_t pair_out;    // fp32 [P][K] per-pair down outputs, indexed by pair id
   size_t total;

@@ -16,6 +16,13 @@ __device__ __forceinline__ int canonical_row(int nr, int I, bool gate_up) {
   return (rg & 1) ? I + 16 * q + j : 16 * q + j;
 }
 
+// Row k of value slot 0 of dword j, sub-slot s, for lane group g in k-tile kt (the two tile
+// layouts of the planes; gate_up matrices use the block layout, down matrices the k-group one).
+__device__ __forceinline__ int slot_k0(int kt, int j, int s, int g, bool block_layout) {
+  return kt * kTileK + (block_layout ? 32 * ((j >> 1) * 4 + g) + 16 * (j & 1) + 8 * s
+                                     : 32 * (2 * j + s) + 8 * g);
+}
+
 // code c (0..3, value {-4,-1,1,4}[c]) -> (sign, |value|==4) bit pair
 __device__ __forceinline__ uint32_t code_sign(uint32_t c) { return (c >> 1) ^ 1u; }
 __device__ __forceinline__ uint32_t code_mag4(uint32_t c) { return ((c >> 1) ^ (c & 1u)) ^ 1u; }
@@ -41,7 +48,7 @@ __global__ void pack_codes_kernel(const uint8_t* __restrict__ canon, uint8_t* __
     uint32_t v = 0;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int k0 = kt * kTileK + 32 * (2 * j + s) + 8 * g;  // multiple of 8
+      const int k0 = slot_k0(kt, j, s, g, gate_up != 0);  // multiple of 8
       const uint32_t bits = (uint32_t)row[k0 / 4] | ((uint32_t)row[k0 / 4 + 1] << 8);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -78,7 +85,7 @@ __global__ void unpack_codes_kernel(const uint8_t* __restrict__ native, uint8_t*
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int k0 = kt * kTileK + 32 * (2 * j + s) + 8 * g;
+      const int k0 = slot_k0(kt, j, s, g, gate_up != 0);
       uint32_t bits = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -138,10 +145,17 @@ __global__ void pack_scales_kernel(const uint8_t* __restrict__ canon, uint8_t* _
     out[d] = (uint8_t)(b - off);
   }
   if (bad) atomicOr(flag, kFlagGuScale);
-  uint8_t* dst = native + ((long long)e * nrg * nkt + (long long)rg * nkt + kt) * kTileScaleBytes + 8 * j;
-  u32x2_t v = {(uint32_t)out[0] | ((uint32_t)out[1] << 8) | ((uint32_t)out[2] << 16) | ((uint32_t)out[3] << 24),
-               (uint32_t)out[4] | ((uint32_t)out[5] << 8) | ((uint32_t)out[6] << 16) | ((uint32_t)out[7] << 24)};
-  *reinterpret_cast<u32x2_t*>(dst) = v;
+  uint8_t* tile = native + ((long long)e * nrg * nkt + (long long)rg * nkt + kt) * kTileScaleBytes;
+  if (gate_up) {
+    // block layout: byte 2*(16g + j) + c holds block 4c + g
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<uint16_t*>(tile + 2 * (16 * g + j)) = (uint16_t)(out[g] | (out[4 + g] << 8));
+  } else {
+    u32x2_t v = {(uint32_t)out[0] | ((uint32_t)out[1] << 8) | ((uint32_t)out[2] << 16) | ((uint32_t)out[3] << 24),
+                 (uint32_t)out[4] | ((uint32_t)out[5] << 8) | ((uint32_t)out[6] << 16) | ((uint32_t)out[7] << 24)};
+    *reinterpret_cast<u32x2_t*>(tile + 8 * j) = v;
+  }
 }
 
 __global__ void unpack_scales_kernel(const uint8_t* __restrict__ native, uint8_t* __restrict__ canon,
@@ -159,10 +173,13 @@ __global__ void unpack_scales_kernel(const uint8_t* __restrict__ native, uint8_t
   const int nr = rg * kTileRows + j;
   const int cr = canonical_row(nr, I, gate_up != 0);
   const int off = gate_up ? 0 : e0[(long long)e * NR + cr];
-  const uint8_t* src = native + ((long long)e * nrg * nkt + (long long)rg * nkt + kt) * kTileScaleBytes + 8 * j;
+  const uint8_t* tile = native + ((long long)e * nrg * nkt + (long long)rg * nkt + kt) * kTileScaleBytes;
   uint8_t* dst = canon + ((long long)e * NR + cr) * nblk + kt * 8;
 #pragma unroll
-  for (int d = 0; d < 8; ++d) dst[d] = (uint8_t)(src[d] + off);
+  for (int d = 0; d < 8; ++d) {
+    const int at = gate_up ? 2 * (16 * (d & 3) + j) + (d >> 2) : 8 * j + d;
+    dst[d] = (uint8_t)(tile[at] + off);
+  }
 }
 
 inline unsigned grid_for(long long n, int block) { return (unsigned)((n + block - 1) / block); }
