@@ -26,6 +26,7 @@ Workspace workspace_layout(int E, int K, int I, int T, int top_k) {
   o += rs;
   w.xq = o;        o += align_up((size_t)T * (2 * (size_t)K + K / 16));
   w.act = o;       o += align_up((size_t)P * I * 2);
+  w.aq = o;        o += align_up((size_t)P * (3 * (size_t)I + I / 8));
   w.pair_out = o;  o += align_up((size_t)P * K * 4);
   w.total = o;
   return w;
@@ -78,7 +79,6 @@ int moe_w2_pack(int E, int K, int I, const uint8_t* gu_codes, const uint8_t* gu_
   const size_t o_gus = o; o += align_up(n_gu / 32);
   const size_t o_dnc = o; o += align_up(n_dn / 4);
   const size_t o_dns = o; o += align_up(n_dn / 32);
-  const size_t o_e0 = o;  o += align_up((size_t)E * K * 4);
   const size_t o_flag = o; o += align_up(4);
   moe_w2_planes* p = new (std::nothrow) moe_w2_planes;
   if (!p) return MOE_W2_ENOMEM;
@@ -90,14 +90,13 @@ int moe_w2_pack(int E, int K, int I, const uint8_t* gu_codes, const uint8_t* gu_
   uint8_t* b = (uint8_t*)p->base;
   p->gu_codes = b + o_guc; p->gu_scales = b + o_gus;
   p->dn_codes = b + o_dnc; p->dn_scales = b + o_dns;
-  p->dn_e0 = (int32_t*)(b + o_e0); p->flag = (int32_t*)(b + o_flag);
+  p->flag = (int32_t*)(b + o_flag);
   hipError_t err = launch_pack(p, gu_codes, gu_scales, dn_codes, dn_scales, s);
   int32_t flag = 0;
   if (err == hipSuccess) err = hipMemcpyAsync(&flag, p->flag, 4, hipMemcpyDeviceToHost, s);
   if (err == hipSuccess) err = hipStreamSynchronize(s);
   if (err != hipSuccess) { (void)hipFree(p->base); delete p; return MOE_W2_EHIP; }
-  if (flag & (kFlagGuScale | kFlagDnScale)) { (void)hipFree(p->base); delete p; return MOE_W2_ESCALE; }
-  if (flag & kFlagDnSpan) { (void)hipFree(p->base); delete p; return MOE_W2_EUNSUPPORTED; }
+  if (flag & kFlagScale) { (void)hipFree(p->base); delete p; return MOE_W2_ESCALE; }
   *out = p;
   return MOE_W2_OK;
 }

@@ -3,11 +3,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
-typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
@@ -15,87 +10,32 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 #define MOEW2_DEV __device__ __forceinline__
 
 // ------------------------------------------------------------------------------------------
-// Native plane layout (built by moe_w2_pack):
+// Native plane layout (built by moe_w2_pack), in the operand order of the block-scaled matrix
+// instruction described below:
 //   A weight matrix of NR rows (output features) and reduction length KR is stored as tiles of
 //   16 rows x 256 reduction elements; tile (rg, kt) holds 1024 code bytes at
 //   (rg * (KR/256) + kt) * 1024 and 128 scale bytes at (rg * (KR/256) + kt) * 128. Lane l
 //   (0..63) of a wave owns row 16*rg + l%16 and reads the 16 code bytes at tile + 16*l, so one
-//   16-byte load per lane is one fully coalesced 1 KiB wave load. With g = l/16, each of the
-//   lane's 4 dwords holds 16 values as bit pairs: for value slot i = 0..7 and sub-slot s = 0, 1,
-//   bit 4i+3-2s = sign and bit 4i+2-2s = |value|==4. So (dw & 0xCCCCCCCC) | 0x22222222 is eight
-//   e2m1 codes (+-1 = 0b?010, +-4 = 0b?110) of sub-slot 0 and ((dw << 2) & 0xCCCCCCCC) |
-//   0x22222222 those of sub-slot 1, value i in nibble i (low nibble first).
-//   Two assignments of values to slots:
-//   * k-group layout (down matrices), for v_mfma_f32_16x16x32: dword j, sub-slot s covers block
-//     b = 2j+s, k = 256kt + 32b + 8g + i; scale tile row-major [16 rows][8 blocks].
-//   * block layout (gate_up matrices), for the block-scaled fp4 instruction: dwords 0,1 cover
-//     block 8kt + g and dwords 2,3 block 8kt + 4 + g; dword j, sub-slot s holds values
-//     16*(j%2) + 8s + i of its block; scale byte 2*l + c = block 8kt + 4c + g of row l%16.
+//   16-byte load per lane is one fully coalesced 1 KiB wave load. With g = l/16, the lane's dwords
+//   0,1 hold block 8kt + g of its row and dwords 2,3 block 8kt + 4 + g; dword j holds values
+//   16*(j%2) .. 16*(j%2) + 15 of its block as bit pairs: value 8s + i (i = 0..7, s = 0, 1) has its
+//   sign at bit 4i+3-2s and |value|==4 at bit 4i+2-2s. So (dw & 0xCCCCCCCC) | 0x22222222 is the
+//   eight e2m1 codes (+-1 = 0b?010, +-4 = 0b?110) of values 0..7 of the dword and
+//   ((dw << 2) & 0xCCCCCCCC) | 0x22222222 those of values 8..15, value i in nibble i.
+//   Scale byte 2*l + c of a tile = UE8M0 byte of block 8kt + 4c + g of row l%16.
 //   Gate_up matrices interleave rows in groups of 16: row group 2q = gate rows 16q..16q+15,
-//   row group 2q+1 = up rows 16q..16q+15. Down scale bytes are stored minus a per-row offset E0
-//   (kept separately) so that every down weight is exact in fp16.
+//   row group 2q+1 = up rows 16q..16q+15.
 // ------------------------------------------------------------------------------------------
 constexpr int kTileRows = 16;
 constexpr int kTileK = 256;
 constexpr int kTileCodeBytes = 1024;
 constexpr int kTileScaleBytes = 128;
 
-// Two e2m1 words (8 codes each: sub-slots 0 and 1) from one native dword.
+// Two e2m1 words (values 0..7 and 8..15 of a native dword, 8 codes each).
 MOEW2_DEV void native_to_fp4(uint32_t dw, uint32_t& blk0, uint32_t& blk1) {
   blk0 = (dw & 0xCCCCCCCCu) | 0x22222222u;
   blk1 = ((dw << 2) & 0xCCCCCCCCu) | 0x22222222u;
 }
-
-// A float whose exponent field is byte D of `sw`. The MX conversion instructions scale by
-// 2^(exponent field - 127) and ignore the sign and mantissa of their scale operand, so this is
-// the UE8M0 scale 2^(b-127) for every byte b in 0..254 with one shift.
-template <int D>
-MOEW2_DEV float ue8m0_scale_operand(uint32_t sw) {
-  uint32_t v = D == 0 ? (sw << 23) : D == 1 ? (sw << 15) : D == 2 ? (sw << 7) : (sw >> 1);
-  return __builtin_bit_cast(float, v);
-}
-
-MOEW2_DEV bf16x8_t fp4x8_to_bf16(uint32_t f, float scale) {
-  bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, scale, 0);
-  bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, scale, 1);
-  bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, scale, 2);
-  bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, scale, 3);
-  bf16x8_t r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
-MOEW2_DEV f16x8_t fp4x8_to_f16(uint32_t f, float scale) {
-  f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(f, scale, 0);
-  f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(f, scale, 1);
-  f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(f, scale, 2);
-  f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(f, scale, 3);
-  f16x8_t r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
-// Element type traits: gate_up runs in bf16, down in fp16.
-struct Bf16Op {
-  typedef bf16x8_t vec;
-  MOEW2_DEV static vec dequant(uint32_t fp4, float scale) { return fp4x8_to_bf16(fp4, scale); }
-  MOEW2_DEV static f32x4_t mfma(vec a, vec b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-struct F16Op {
-  typedef f16x8_t vec;
-  MOEW2_DEV static vec dequant(uint32_t fp4, float scale) { return fp4x8_to_f16(fp4, scale); }
-  MOEW2_DEV static f32x4_t mfma(vec a, vec b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
-
-// v_mfma_f32_16x16x32 operand layout (checked on the device): A lane l holds row l%16,
-// k = 8*(l/16) .. +7; B lane l holds column l%16, the same k; accumulator register r (0..3) of
-// lane l holds row 4*(l/16) + r, column l%16.
 
 // ------------------------------------------------------------------------------------------
 // Block-scaled (MX) matrix instruction v_mfma_scale_f32_16x16x128_f8f6f4 with A = fp8 (OCP
@@ -106,9 +46,9 @@ struct F16Op {
 //   A lane l: row l%16; operand bytes 0..15 = k 16g .. 16g+15, bytes 16..31 = k 64+16g .. +15.
 //   scales: lane l supplies the E8M0 byte of (row/column l%16, block g), selected from its
 //           32-bit scale register by op_sel (0..3).
-//   accumulator: as for v_mfma_f32_16x16x32.
-// The gate_up planes use this operand order (see the planes' layout note above): in k-tile kt,
-// lane l holds blocks 8kt + g (instruction 0) and 8kt + 4 + g (instruction 1) of its row.
+//   accumulator register r (0..3) of lane l: row 4*(l/16) + r, column l%16.
+// The planes use this operand order (layout note above): in k-tile kt, lane l holds blocks
+// 8kt + g (instruction 0) and 8kt + 4 + g (instruction 1) of its row.
 // ------------------------------------------------------------------------------------------
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4e_t __attribute__((ext_vector_type(4)));
@@ -163,15 +103,52 @@ MOEW2_DEV void x_split4(float v0, float v1, float v2, float v3, uint32_t sx, uin
   lo = sx >= 4 ? (uint32_t)l : 0u;
 }
 
+// The gated intermediate (fp16, 11 significant bits) as three e4m3 parts with scale bytes sa,
+// sa - 4 and sa - 8 (sa = x_scale_byte of the block maximum): p0 = RNE(t), p1 = RNE(16 (t - p0)),
+// p2 = RNE(16 (16 (t - p0) - p1)) with t = a / 2^(sa-127). Each remainder has at most 4
+// significant bits left, so the three parts are exact for every value at least 2^-10 of the block
+// maximum; smaller values keep an error below 2^-24 of the block maximum. sa < 8 drops the parts
+// whose scale would go below 0.
+MOEW2_DEV void a_split4(float v0, float v1, float v2, float v3, uint32_t sa, uint32_t& p0, uint32_t& p1,
+                        uint32_t& p2) {
+  const int sh = 127 - (int)sa, sm = 131 - (int)sa;
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(v0, sh), __builtin_ldexpf(v1, sh), 0, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(v2, sh), __builtin_ldexpf(v3, sh), h, true);
+  const float r0 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(h, 0), -16.f, __builtin_ldexpf(v0, sm));
+  const float r1 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(h, 1), -16.f, __builtin_ldexpf(v1, sm));
+  const float r2 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(h, 2), -16.f, __builtin_ldexpf(v2, sm));
+  const float r3 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(h, 3), -16.f, __builtin_ldexpf(v3, sm));
+  int m = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+  m = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, m, true);
+  const float q0 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(m, 0), -16.f, 16.f * r0);
+  const float q1 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(m, 1), -16.f, 16.f * r1);
+  const float q2 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(m, 2), -16.f, 16.f * r2);
+  const float q3 = __builtin_fmaf(__builtin_amdgcn_cvt_f32_fp8(m, 3), -16.f, 16.f * r3);
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, l, true);
+  p0 = (uint32_t)h;
+  p1 = sa >= 4 ? (uint32_t)m : 0u;
+  p2 = sa >= 8 ? (uint32_t)l : 0u;
+}
+// scale word pair of one (row, k-tile, lane group) for the three parts: word 0 = (p0 c0, p0 c1,
+// p1 c0, p1 c1), word 1 = (p2 c0, p2 c1, 0, 0); c = chunk (instruction 0 or 1 of the k-tile)
+MOEW2_DEV uint32_t a_part_scale(uint32_t sa, int part) {
+  const int v = (int)sa - 4 * part;
+  return v > 0 ? (uint32_t)v : 0u;
+}
+
+// fp16 bits -> float
+MOEW2_DEV float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+MOEW2_DEV float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
 // bf16 bits -> float
 MOEW2_DEV float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 MOEW2_DEV float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 MOEW2_DEV float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// 16-byte global load / store helpers
+// 16-byte global load helper
 MOEW2_DEV u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
-MOEW2_DEV u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 
 // Raw buffer view of one expert's weight plane (at most 2^31 - 1 bytes). A load at offset
 // kOutOfRange lies past the buffer's size and returns zeros without a memory access: issuing it
@@ -187,9 +164,6 @@ MOEW2_DEV __amdgpu_buffer_rsrc_t buffer_view(const void* base, uint32_t bytes) {
 // voffset (per lane, range-checked) + soffset (wave-uniform byte offset added to the base)
 MOEW2_DEV u32x4_t buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kPolicyNT));
-}
-MOEW2_DEV u32x2_t buf_ld8_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kPolicyNT));
 }
 MOEW2_DEV uint32_t buf_ld2_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, kPolicyNT);

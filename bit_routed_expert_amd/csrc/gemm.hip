@@ -12,7 +12,8 @@
 //  gate_up: block-scaled fp8 x fp4 instruction; x is first split into two e4m3 parts by
 //           quant_x_kernel (one pass over x), the weights' codes become e2m1 operands with two
 //           bit operations per 8 values and their UE8M0 bytes are the instruction's B scales.
-//  down:    fp16 instruction on the gated intermediate (fp16) and the fp16-decoded weights.
+//  down:    the same instruction with the gated intermediate (fp16) split into three e4m3 parts
+//           by quant_act_kernel.
 #include <type_traits>
 
 #include "common.h"
@@ -230,51 +231,100 @@ gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restr
 }
 
 // ------------------------------------------------------------------------------------------------
-// down (fp16). LDS row of one k-tile: 256 fp16 values | pad.
+// gated intermediate split: one thread per 32-value block of act [P][I] (fp16), three parts
+// (layout of the workspace region in internal.h).
 // ------------------------------------------------------------------------------------------------
-constexpr int kAStride = kTileK * 2 + 16;
-constexpr int kABytes = BM * kAStride;
+__global__ void __launch_bounds__(256)
+quant_act_kernel(const uint16_t* __restrict__ act, uint8_t* __restrict__ aq, int P, int I) {
+  const int nb = I / 32;
+  const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= (long long)P * nb) return;
+  const int r = (int)(b / nb), blk = (int)(b - (long long)r * nb);
+  const uint16_t* src = act + (size_t)r * I + 32 * blk;
+  u32x4_t v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = ld16(src + 8 * q);
+  float a = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(f16_lo(v[q][j])), __builtin_fabsf(f16_hi(v[q][j]))));
+  const uint32_t sa = x_scale_byte(a);
+  uint32_t p0[8], p1[8], p2[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    a_split4(f16_lo(v[q][0]), f16_hi(v[q][0]), f16_lo(v[q][1]), f16_hi(v[q][1]), sa, p0[2 * q], p1[2 * q], p2[2 * q]);
+    a_split4(f16_lo(v[q][2]), f16_hi(v[q][2]), f16_lo(v[q][3]), f16_hi(v[q][3]), sa, p0[2 * q + 1], p1[2 * q + 1],
+             p2[2 * q + 1]);
+  }
+  const size_t part = (size_t)P * I;
+  uint8_t* d0 = aq + (size_t)r * I + 32 * blk;
+  *reinterpret_cast<u32x4_t*>(d0) = u32x4_t{p0[0], p0[1], p0[2], p0[3]};
+  *reinterpret_cast<u32x4_t*>(d0 + 16) = u32x4_t{p0[4], p0[5], p0[6], p0[7]};
+  *reinterpret_cast<u32x4_t*>(d0 + part) = u32x4_t{p1[0], p1[1], p1[2], p1[3]};
+  *reinterpret_cast<u32x4_t*>(d0 + part + 16) = u32x4_t{p1[4], p1[5], p1[6], p1[7]};
+  *reinterpret_cast<u32x4_t*>(d0 + 2 * part) = u32x4_t{p2[0], p2[1], p2[2], p2[3]};
+  *reinterpret_cast<u32x4_t*>(d0 + 2 * part + 16) = u32x4_t{p2[4], p2[5], p2[6], p2[7]};
+  const int kt = blk >> 3, d = blk & 7, g = d & 3, c = d >> 2;
+  uint8_t* sw = aq + 3 * part + ((size_t)r * (I / kTileK) + kt) * 32 + 8 * g;
+  sw[c] = (uint8_t)sa;
+  sw[2 + c] = (uint8_t)a_part_scale(sa, 1);
+  sw[4 + c] = (uint8_t)a_part_scale(sa, 2);
+}
+
+// ------------------------------------------------------------------------------------------------
+// down (block-scaled, three parts). LDS row of one k-tile: part 0 [256] | part 1 [256] |
+// part 2 [256] | scale words [4][8] | pad.
+// ------------------------------------------------------------------------------------------------
+constexpr int kDnStride = 3 * kTileK + 32 + 16;
+constexpr int kDnABytes = BM * kDnStride;
+constexpr int kDnPieces = BM * 48 / kThreads;   // 16-byte part pieces per thread per k-tile
+static_assert(kDnPieces == 6, "down A staging layout");
 
 __global__ void __launch_bounds__(kThreads, 1)
-gemm_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                 const int32_t* __restrict__ dn_e0, const _Float16* __restrict__ act_in,
-                 const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-                 const int32_t* __restrict__ tiles, const int32_t* __restrict__ meta,
-                 float* __restrict__ pair_out, int K, int I, int n_blocks) {
-  typedef F16Op Op;
-  typedef typename Op::vec vec;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kABytes];
+gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                    const uint8_t* __restrict__ aq, const int32_t* __restrict__ offsets,
+                    const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
+                    const int32_t* __restrict__ meta, float* __restrict__ pair_out, int P, int K, int I,
+                    int n_blocks) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const TileMap tm = map_tile(tiles, meta, offsets, n_blocks);
   if (!tm.live) return;
   const int e = tm.e, rs = tm.rs, rows_valid = tm.rows_valid;
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
   const int rg0 = 4 * (tm.nb * kWaves + w);
   const bool wave_active = rg0 < nrg;
 
-  // ---- A staging: thread t copies 16-byte piece (t % 32) of rows t/32 + 16*i, i = 0..3 ----
-  const int piece = tid & 31;
-  const uint16_t* asrc = reinterpret_cast<const uint16_t*>(act_in);
-  uint32_t arow[4];
+  // ---- A staging: thread t copies 16-byte slot t % 16 of part q of rows t/16 and t/16 + 32
+  //      (pieces i = 0..5: q = i/2, row half i%2); threads 0..127 also copy half (t % 2) of
+  //      row t/2's 32 scale-word bytes ----
+  const size_t part = (size_t)P * I;
+  const int sl = tid & 15;
+  size_t arow[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = tid / 32 + 16 * i;
-    arow[i] = (uint32_t)(rs + min(r, rows_valid - 1)) * (uint32_t)I;
-  }
-  u32x4_t areg[4];
+  for (int h = 0; h < 2; ++h) arow[h] = (size_t)(rs + min((tid >> 4) + 32 * h, rows_valid - 1)) * I + 16 * sl;
+  const int srow = min(tid >> 1, BM - 1);
+  const uint8_t* ssrc = aq + 3 * part + (size_t)(rs + min(srow, rows_valid - 1)) * (nkt * 32) + 16 * (tid & 1);
+  u32x4_t areg[kDnPieces], sreg;
   auto load_a = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) areg[i] = ld16(asrc + arow[i] + kt * kTileK + piece * 8);
+    for (int i = 0; i < kDnPieces; ++i) areg[i] = ld16(aq + (i >> 1) * part + arow[i & 1] + kt * kTileK);
+    if (tid < 2 * BM) sreg = ld16(ssrc + kt * 32);
   };
   auto store_a = [&](int buf) {
+    uint8_t* base = lds + buf * kDnABytes + (tid >> 4) * kDnStride + 16 * sl;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4_t*>(lds + buf * kABytes + (tid / 32 + 16 * i) * kAStride + piece * 16) = areg[i];
+    for (int i = 0; i < kDnPieces; ++i)
+      *reinterpret_cast<u32x4_t*>(base + (i & 1) * 32 * kDnStride + (i >> 1) * kTileK) = areg[i];
+    if (tid < 2 * BM) *reinterpret_cast<u32x4_t*>(lds + buf * kDnABytes + (tid >> 1) * kDnStride + 3 * kTileK + 16 * (tid & 1)) = sreg;
   };
 
   const size_t tb0 = (size_t)e * nrg * nkt + (size_t)(wave_active ? rg0 : 0) * nkt;
-  struct BRegs { u32x4_t c[4]; u32x2_t s[4]; };
+  struct BRegs { u32x4_t c[4]; uint32_t s[4]; };
   BRegs bA, bB;
   auto load_b = [&](int kt, BRegs& r) {
     if (!wave_active) return;
@@ -282,7 +332,7 @@ gemm_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
     for (int t = 0; t < 4; ++t) {
       const size_t ti = tb0 + (size_t)t * nkt + kt;
       r.c[t] = ld16(codes + ti * kTileCodeBytes + 16 * lane);
-      r.s[t] = ld8(scales + ti * kTileScaleBytes + 8 * (lane & 15));
+      r.s[t] = *reinterpret_cast<const uint16_t*>(scales + ti * kTileScaleBytes + 2 * lane);
     }
   };
 
@@ -292,31 +342,27 @@ gemm_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // one k-tile = 8 blocks of 32 = native dwords 0..3 (two blocks each, k-group layout)
-  auto compute = [&](const uint8_t* abuf, const BRegs& br) {
+  auto chunk = [&](const uint8_t* abuf, const BRegs& br, auto cc) {
+    constexpr int C = decltype(cc)::value;
+    i32x8_t bo[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      vec b0[4], b1[4];
+    for (int t = 0; t < 4; ++t) bo[t] = mx_b_operand(br.c[t][2 * C], br.c[t][2 * C + 1]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint32_t f0, f1;
-        native_to_fp4(br.c[t][j], f0, f1);
-        const uint32_t sw = j < 2 ? br.s[t][0] : br.s[t][1];
-        const float s0 = (j & 1) == 0 ? ue8m0_scale_operand<0>(sw) : ue8m0_scale_operand<2>(sw);
-        const float s1 = (j & 1) == 0 ? ue8m0_scale_operand<1>(sw) : ue8m0_scale_operand<3>(sw);
-        b0[t] = Op::dequant(f0, s0);
-        b1[t] = Op::dequant(f1, s1);
+    for (int m = 0; m < 4; ++m) {
+      const uint8_t* ar = abuf + (m * 16 + (lane & 15)) * kDnStride;
+      const u32x2_t sw = *reinterpret_cast<const u32x2_t*>(ar + 3 * kTileK + 8 * g);
+      i32x8_t ap[3];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(ar + q * kTileK + 128 * C + 16 * g);
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(ar + q * kTileK + 128 * C + 64 + 16 * g);
+        ap[q] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint8_t* ar = abuf + (m * 16 + (lane & 15)) * kAStride + (8 * (lane >> 4)) * 2;
-        const vec a0 = *reinterpret_cast<const vec*>(ar + (32 * (2 * j)) * 2);
-        const vec a1 = *reinterpret_cast<const vec*>(ar + (32 * (2 * j + 1)) * 2);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          acc[m][t] = Op::mfma(a0, b0[t], acc[m][t]);
-          acc[m][t] = Op::mfma(a1, b1[t], acc[m][t]);
-        }
+      for (int t = 0; t < 4; ++t) {
+        acc[m][t] = mx_mfma<C, C>(ap[0], bo[t], acc[m][t], sw[0], br.s[t]);
+        acc[m][t] = mx_mfma<2 + C, C>(ap[1], bo[t], acc[m][t], sw[0], br.s[t]);
+        acc[m][t] = mx_mfma<C, C>(ap[2], bo[t], acc[m][t], sw[1], br.s[t]);
       }
     }
   };
@@ -324,7 +370,10 @@ gemm_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
     const bool more = kt + 1 < nkt;
     if (more) { load_b(kt + 1, nxt); load_a(kt + 1); }
     __builtin_amdgcn_sched_barrier(0);
-    if (wave_active) compute(lds + (kt & 1) * kABytes, cur);
+    if (wave_active) {
+      chunk(lds + (kt & 1) * kDnABytes, cur, std::integral_constant<int, 0>());
+      chunk(lds + (kt & 1) * kDnABytes, cur, std::integral_constant<int, 1>());
+    }
     if (more) store_a((kt + 1) & 1);
     __syncthreads();
   };
@@ -339,7 +388,7 @@ gemm_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
   }
   if (!wave_active) return;
 
-  // ---- epilogue: per-pair rows (times 2^E0 of the output row) at the pair index ----
+  // ---- epilogue: per-pair rows at the pair index ----
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -348,10 +397,7 @@ gemm_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
       if (row >= rows_valid) continue;
       const int p = perm[rs + row];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int col = 16 * (rg0 + t) + (lane & 15);
-        pair_out[(size_t)p * K + col] = __builtin_ldexpf(acc[m][t][r], dn_e0[(size_t)e * K + col]);
-      }
+      for (int t = 0; t < 4; ++t) pair_out[(size_t)p * K + 16 * (rg0 + t) + (lane & 15)] = acc[m][t][r];
     }
   }
 }
@@ -381,12 +427,16 @@ hipError_t launch_gemm_gate_up(const moe_w2_planes* p, int T, int top_k, const v
 hipError_t launch_gemm_down(const moe_w2_planes* p, int T, int top_k, const Workspace& ws,
                             uint8_t* wsb, hipStream_t s) {
   if (ws.max_tiles == 0) return hipSuccess;
+  const int P = T * top_k;
+  const long long nblk32 = (long long)P * (p->I / 32);
+  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)((nblk32 + 255) / 256)), dim3(256), 0, s,
+                     (const uint16_t*)(wsb + ws.act), wsb + ws.aq, P, p->I);
   const int nblk = (p->K + BN - 1) / BN;
-  hipLaunchKernelGGL(gemm_down_kernel, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads), 0, s,
-                     p->dn_codes, p->dn_scales, p->dn_e0, (const _Float16*)(wsb + ws.act),
+  hipLaunchKernelGGL(gemm_down_mx_kernel, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads), 2 * kDnABytes, s,
+                     p->dn_codes, p->dn_scales, (const uint8_t*)(wsb + ws.aq),
                      (const int32_t*)(wsb + ws.offsets), (const int32_t*)(wsb + ws.perm),
                      (const int32_t*)(wsb + ws.tiles), (const int32_t*)(wsb + ws.meta),
-                     (float*)(wsb + ws.pair_out), p->K, p->I, nblk);
+                     (float*)(wsb + ws.pair_out), P, p->K, p->I, nblk);
   return hipGetLastError();
 }
 

@@ -15,8 +15,7 @@ struct moe_w2_planes {
   uint8_t* gu_codes;   // [E][2I/16][K/256][1024]
   uint8_t* gu_scales;  // [E][2I/16][K/256][128]
   uint8_t* dn_codes;   // [E][K/16][I/256][1024]
-  uint8_t* dn_scales;  // [E][K/16][I/256][128]  (canonical byte - E0 of the row)
-  int32_t* dn_e0;      // [E][K] per-row power-of-two offset of the down weights
+  uint8_t* dn_scales;  // [E][K/16][I/256][128]
   int32_t* flag;       // pack-time validation flags (device)
 };
 
@@ -26,7 +25,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Pack-time validation flags
-enum { kFlagGuScale = 1, kFlagDnScale = 2, kFlagDnSpan = 4 };
+enum { kFlagScale = 1 };   // pack: a scale byte above 252
 
 // Workspace layout of one forward.
 struct Workspace {
@@ -42,6 +41,9 @@ struct Workspace {
   size_t xq;          // x split for the block-scaled instruction (GEMM path): hi [T][K] e4m3,
                       // lo [T][K] e4m3, scale words [T][K/256][4][4] (hi c0, hi c1, lo c0, lo c1)
   size_t act;         // fp16 [P][I] gated intermediate, sorted order
+  size_t aq;          // gated intermediate split for the block-scaled instruction (GEMM path):
+                      // parts 0, 1, 2 [P][I] e4m3 each, scale words [P][I/256][4][8]
+                      // (part 0 c0, c1, part 1 c0, c1, part 2 c0, c1, 0, 0)
   size_t pair_out;    // fp32 [P][K] per-pair down outputs, indexed by pair id
   size_t total;
   int P, nchunks, max_tiles;

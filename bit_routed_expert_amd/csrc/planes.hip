@@ -16,11 +16,9 @@ __device__ __forceinline__ int canonical_row(int nr, int I, bool gate_up) {
   return (rg & 1) ? I + 16 * q + j : 16 * q + j;
 }
 
-// Row k of value slot 0 of dword j, sub-slot s, for lane group g in k-tile kt (the two tile
-// layouts of the planes; gate_up matrices use the block layout, down matrices the k-group one).
-__device__ __forceinline__ int slot_k0(int kt, int j, int s, int g, bool block_layout) {
-  return kt * kTileK + (block_layout ? 32 * ((j >> 1) * 4 + g) + 16 * (j & 1) + 8 * s
-                                     : 32 * (2 * j + s) + 8 * g);
+// Row k of value slot 0 of dword j, sub-slot s, for lane group g in k-tile kt (block layout).
+__device__ __forceinline__ int slot_k0(int kt, int j, int s, int g) {
+  return kt * kTileK + 32 * ((j >> 1) * 4 + g) + 16 * (j & 1) + 8 * s;
 }
 
 // code c (0..3, value {-4,-1,1,4}[c]) -> (sign, |value|==4) bit pair
@@ -48,7 +46,7 @@ __global__ void pack_codes_kernel(const uint8_t* __restrict__ canon, uint8_t* __
     uint32_t v = 0;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int k0 = slot_k0(kt, j, s, g, gate_up != 0);  // multiple of 8
+      const int k0 = slot_k0(kt, j, s, g);  // multiple of 8
       const uint32_t bits = (uint32_t)row[k0 / 4] | ((uint32_t)row[k0 / 4 + 1] << 8);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -85,7 +83,7 @@ __global__ void unpack_codes_kernel(const uint8_t* __restrict__ native, uint8_t*
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int k0 = slot_k0(kt, j, s, g, gate_up != 0);
+      const int k0 = slot_k0(kt, j, s, g);
       uint32_t bits = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -100,29 +98,11 @@ __global__ void unpack_codes_kernel(const uint8_t* __restrict__ native, uint8_t*
   }
 }
 
-// Down rows: per-row offset E0 so that every weight of the row is exact in fp16.
-// Native byte nb = b - E0 must lie in [103, 140]: +-1 * 2^(nb-127) >= 2^-24 (smallest fp16
-// subnormal) and 4 * 2^(nb-127) <= 2^15.
-__global__ void down_offset_kernel(const uint8_t* __restrict__ scales, int32_t* __restrict__ e0,
-                                   int nrows, int nblk, int32_t* __restrict__ flag) {
-  int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= nrows) return;
-  const uint8_t* s = scales + (long long)r * nblk;
-  int mn = 255, mx = 0;
-  for (int b = 0; b < nblk; ++b) { int v = s[b]; mn = v < mn ? v : mn; mx = v > mx ? v : mx; }
-  int off = 0;
-  if (mx > 254) atomicOr(flag, kFlagDnScale);
-  if (mn < 103 || mx > 140) {
-    off = mx - 140;
-    if (mn - off < 103) atomicOr(flag, kFlagDnSpan);
-  }
-  e0[r] = off;
-}
-
-// One thread per (matrix, tile, row): 8 scale bytes.
+// One thread per (matrix, tile, row): the row's 8 scale bytes of the k-tile. Byte 2*(16g + j) + c
+// of the tile holds block 4c + g of row j (block layout). A byte above 252 is flagged: its
+// weights (up to 4 * 2^(b-127)) would not be finite in fp32.
 __global__ void pack_scales_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ native,
-                                   const int32_t* __restrict__ e0, int nmat, int NR, int KR, int I,
-                                   int gate_up, int32_t* __restrict__ flag) {
+                                   int nmat, int NR, int KR, int I, int gate_up, int32_t* __restrict__ flag) {
   const int nkt = KR / kTileK, nrg = NR / kTileRows, nblk = KR / 32;
   const long long total = (long long)nmat * nrg * nkt * kTileRows;
   long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -132,35 +112,21 @@ __global__ void pack_scales_kernel(const uint8_t* __restrict__ canon, uint8_t* _
   const int kt = (int)(t % nkt); t /= nkt;
   const int rg = (int)(t % nrg);
   const int e = (int)(t / nrg);
-  const int nr = rg * kTileRows + j;
-  const int cr = canonical_row(nr, I, gate_up != 0);
+  const int cr = canonical_row(rg * kTileRows + j, I, gate_up != 0);
   const uint8_t* src = canon + ((long long)e * NR + cr) * nblk + kt * 8;
-  const int off = gate_up ? 0 : e0[(long long)e * NR + cr];
-  uint8_t out[8];
+  uint8_t* tile = native + ((long long)e * nrg * nkt + (long long)rg * nkt + kt) * kTileScaleBytes;
   int bad = 0;
 #pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    int b = src[d];
-    if (gate_up && b > 252) bad = 1;
-    out[d] = (uint8_t)(b - off);
+  for (int g = 0; g < 4; ++g) {
+    const int b0 = src[g], b1 = src[4 + g];
+    bad |= (b0 > 252) | (b1 > 252);
+    *reinterpret_cast<uint16_t*>(tile + 2 * (16 * g + j)) = (uint16_t)(b0 | (b1 << 8));
   }
-  if (bad) atomicOr(flag, kFlagGuScale);
-  uint8_t* tile = native + ((long long)e * nrg * nkt + (long long)rg * nkt + kt) * kTileScaleBytes;
-  if (gate_up) {
-    // block layout: byte 2*(16g + j) + c holds block 4c + g
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<uint16_t*>(tile + 2 * (16 * g + j)) = (uint16_t)(out[g] | (out[4 + g] << 8));
-  } else {
-    u32x2_t v = {(uint32_t)out[0] | ((uint32_t)out[1] << 8) | ((uint32_t)out[2] << 16) | ((uint32_t)out[3] << 24),
-                 (uint32_t)out[4] | ((uint32_t)out[5] << 8) | ((uint32_t)out[6] << 16) | ((uint32_t)out[7] << 24)};
-    *reinterpret_cast<u32x2_t*>(tile + 8 * j) = v;
-  }
+  if (bad) atomicOr(flag, kFlagScale);
 }
 
 __global__ void unpack_scales_kernel(const uint8_t* __restrict__ native, uint8_t* __restrict__ canon,
-                                     const int32_t* __restrict__ e0, int nmat, int NR, int KR, int I,
-                                     int gate_up) {
+                                     int nmat, int NR, int KR, int I, int gate_up) {
   const int nkt = KR / kTileK, nrg = NR / kTileRows, nblk = KR / 32;
   const long long total = (long long)nmat * nrg * nkt * kTileRows;
   long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -170,16 +136,11 @@ __global__ void unpack_scales_kernel(const uint8_t* __restrict__ native, uint8_t
   const int kt = (int)(t % nkt); t /= nkt;
   const int rg = (int)(t % nrg);
   const int e = (int)(t / nrg);
-  const int nr = rg * kTileRows + j;
-  const int cr = canonical_row(nr, I, gate_up != 0);
-  const int off = gate_up ? 0 : e0[(long long)e * NR + cr];
+  const int cr = canonical_row(rg * kTileRows + j, I, gate_up != 0);
   const uint8_t* tile = native + ((long long)e * nrg * nkt + (long long)rg * nkt + kt) * kTileScaleBytes;
   uint8_t* dst = canon + ((long long)e * NR + cr) * nblk + kt * 8;
 #pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    const int at = gate_up ? 2 * (16 * (d & 3) + j) + (d >> 2) : 8 * j + d;
-    dst[d] = (uint8_t)(tile[at] + off);
-  }
+  for (int d = 0; d < 8; ++d) dst[d] = tile[2 * (16 * (d & 3) + j) + (d >> 2)];
 }
 
 inline unsigned grid_for(long long n, int block) { return (unsigned)((n + block - 1) / block); }
@@ -192,9 +153,6 @@ hipError_t launch_pack(const moe_w2_planes* p, const uint8_t* gu_codes, const ui
   const int B = 256;
   hipError_t err = hipMemsetAsync(p->flag, 0, sizeof(int32_t), s);
   if (err != hipSuccess) return err;
-  long long n_dn_rows = (long long)E * K;
-  hipLaunchKernelGGL(down_offset_kernel, dim3(grid_for(n_dn_rows, B)), dim3(B), 0, s,
-                     dn_scales, p->dn_e0, (int)n_dn_rows, I / 32, p->flag);
   long long n1 = (long long)E * (2 * I / kTileRows) * (K / 256) * 64;
   hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for(n1, B)), dim3(B), 0, s,
                      gu_codes, p->gu_codes, E, 2 * I, K, I, 1);
@@ -203,10 +161,10 @@ hipError_t launch_pack(const moe_w2_planes* p, const uint8_t* gu_codes, const ui
                      dn_codes, p->dn_codes, E, K, I, I, 0);
   long long n3 = (long long)E * (2 * I / kTileRows) * (K / 256) * kTileRows;
   hipLaunchKernelGGL(pack_scales_kernel, dim3(grid_for(n3, B)), dim3(B), 0, s,
-                     gu_scales, p->gu_scales, p->dn_e0, E, 2 * I, K, I, 1, p->flag);
+                     gu_scales, p->gu_scales, E, 2 * I, K, I, 1, p->flag);
   long long n4 = (long long)E * (K / kTileRows) * (I / 256) * kTileRows;
   hipLaunchKernelGGL(pack_scales_kernel, dim3(grid_for(n4, B)), dim3(B), 0, s,
-                     dn_scales, p->dn_scales, p->dn_e0, E, K, I, I, 0, p->flag);
+                     dn_scales, p->dn_scales, E, K, I, I, 0, p->flag);
   return hipGetLastError();
 }
 
@@ -222,10 +180,10 @@ hipError_t launch_unpack(const moe_w2_planes* p, uint8_t* gu_codes, uint8_t* gu_
                      p->dn_codes, dn_codes, E, K, I, I, 0);
   long long n3 = (long long)E * (2 * I / kTileRows) * (K / 256) * kTileRows;
   hipLaunchKernelGGL(unpack_scales_kernel, dim3(grid_for(n3, B)), dim3(B), 0, s,
-                     p->gu_scales, gu_scales, p->dn_e0, E, 2 * I, K, I, 1);
+                     p->gu_scales, gu_scales, E, 2 * I, K, I, 1);
   long long n4 = (long long)E * (K / kTileRows) * (I / 256) * kTileRows;
   hipLaunchKernelGGL(unpack_scales_kernel, dim3(grid_for(n4, B)), dim3(B), 0, s,
-                     p->dn_scales, dn_scales, p->dn_e0, E, K, I, I, 0);
+                     p->dn_scales, dn_scales, E, K, I, I, 0);
   return hipGetLastError();
 }
 

@@ -82,11 +82,10 @@ const char* moe_w2_status_string(int status);
  * scales).
  *   gu_codes  [E][2I][K/4]   gu_scales [E][2I][K/32]
  *   dn_codes  [E][K][I/4]    dn_scales [E][K][I/32]
- * The native layout is opaque (tiles of 16 rows x 256 reduction elements in matrix-core
- * fragment order; gate and up rows interleaved in groups of 16). Gate_up scale bytes must be
- * <= 252 (4 * 2^(b-127) must fit bf16). Down weights are held as fp16 with a per-row power-of-two
- * offset; the scale bytes of one down row must lie within a window of 38 consecutive values
- * ([c, c+37]) so every weight of the row is exact in fp16, and must be <= 254.
+ * The native layout is opaque (tiles of 16 rows x 256 reduction elements in the operand order
+ * of the block-scaled matrix instruction; gate and up rows interleaved in groups of 16). Every
+ * scale byte must be <= 252 (a weight 4 * 2^(b-127) must be finite in fp32); MOE_W2_ESCALE
+ * otherwise.
  * Synchronous (validates the scale bytes on the device). On success *out receives the planes;
  * on failure nothing is allocated and *out is NULL.
  */

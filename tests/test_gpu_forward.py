@@ -162,8 +162,8 @@ def test_workspace_too_small_is_rejected(gpu):
     assert ei.value.status == -6
 
 
-def test_down_rows_with_large_exponent_offsets(gpu):
-    """Down scale bytes far from 127 (rows needing a per-row fp16 offset) stay exact."""
+def test_down_rows_with_large_exponent_spread(gpu):
+    """Down rows whose scale bytes lie far from 127 and spread over up to 30 exponents."""
     c = _case(24, 256, 512, 4, 2, 91)
     rng = np.random.default_rng(92)
     base = rng.integers(20, 220, size=(4, 256, 1))

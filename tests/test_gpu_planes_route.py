@@ -21,11 +21,12 @@ def _planes(E, K, I, seed):
 def test_pack_unpack_roundtrip_is_exact(gpu, shape):
     E, K, I = shape
     p = _planes(E, K, I, 5)
-    # include down rows that need an exponent offset and extreme gate_up bytes
+    # include extreme scale bytes (0 and 252) in both matrices
     p["dn_scales"][0] = 30
     p["dn_scales"][1, :, :] = np.arange(I // 32, dtype=np.uint8)[None, :] % 30 + 200
     p["gu_scales"][0, 0, 0] = 252
     p["gu_scales"][0, 1, 0] = 0
+    p["dn_scales"][2 % E, 0, 0] = 252
     h = pack(p)
     out = [t.cpu().numpy() for t in moe.moe_w2_unpack(h)]
     torch.cuda.synchronize()
@@ -46,12 +47,13 @@ def test_pack_rejects_bad_scales(gpu):
         pack(q)
     assert ei.value.status == -3
     q = dict(p, dn_scales=p["dn_scales"].copy())
-    q["dn_scales"][0, 7, 0] = 100
-    q["dn_scales"][0, 7, 1] = 138      # span 38 > 37 in one down row
+    q["dn_scales"][0, 5, 1] = 253      # 4 * 2^126 is not finite in fp32
     with pytest.raises(moe.MoeW2Error) as ei:
         pack(q)
-    assert ei.value.status == -2
-    q["dn_scales"][0, 7, 1] = 137      # span 37 fits
+    assert ei.value.status == -3
+    q["dn_scales"][0, 5, 1] = 252      # the largest accepted byte
+    q["dn_scales"][0, 7, 0] = 0        # and the smallest, in the same row as 252: any spread
+    q["dn_scales"][0, 7, 1] = 252
     pack(q)
 
 
