@@ -79,6 +79,29 @@ def test_mid_size_parity(gpu, case, path):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_wide_dynamic_range_inputs(gpu, path):
+    """The A operand is split into e4m3 parts per 32-value block: x blocks holding one large value
+    and values 2^-6 .. 2^-24 of it, gated intermediates of widely different size (scale bytes
+    40 .. 200 spread over rows and blocks; gate_up bytes 110 .. 125 keep |a| within fp16), and a
+    block whose x is all zero stay within the bar."""
+    c = _case(40, 512, 512, 8, 4, 51)
+    rng = np.random.default_rng(52)
+    xf = rng.standard_normal((40, 512)).astype(np.float32) * np.exp2(-rng.integers(6, 25, size=(40, 512)))
+    xf[:, ::32] = np.where(rng.random((40, 16)) < 0.5, 8.0, -8.0)
+    xf[3, 64:96] = 0.0
+    c["x"] = workloads.f32_to_bf16_bits(xf)
+    c["gu_scales"] = rng.integers(110, 126, size=c["gu_scales"].shape).astype(np.uint8)
+    c["dn_scales"] = rng.integers(40, 200, size=c["dn_scales"].shape).astype(np.uint8)
+    y_ref = _oracle(c)
+    h = pack(c)
+    y = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path).cpu().numpy()
+    err = rel_max_err(y, y_ref)
+    print(f"wide dynamic range path={path} rel max err {err:.2e}")
+    assert np.all(np.isfinite(y))
+    assert err <= TOL
+
+
 def test_paths_agree_closely(gpu):
     c = _case(64, 512, 512, 8, 4, 31)
     h = pack(c)
