@@ -178,12 +178,15 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
   uint8_t* wsb = (uint8_t*)workspace;
   const bool decode = path == MOE_W2_PATH_DECODE ||
                       (path == MOE_W2_PATH_AUTO && (long long)T * top_k <= kDecodeMaxPairs);
-  // the direct decode organisation needs no routing pass and combines inside the down stage
+  // every decode workgroup scans all ids itself (two per thread)
+  if (decode && (long long)T * top_k > kDecodeMaxPairs) return MOE_W2_EUNSUPPORTED;
+  // the decode kernels find their pairs from the ids themselves (no routing pass); the direct
+  // organisation also combines inside the down stage
   const bool direct = decode && (long long)T * top_k <= kDirectMaxPairs;
   hipError_t err = hipSuccess;
   switch (stage) {
     case MOE_W2_STAGE_ROUTE: {
-      if (direct) break;
+      if (decode) break;
       RouteOut o;
       o.offsets = (int32_t*)(wsb + ws.offsets);
       o.perm = (int32_t*)(wsb + ws.perm);

@@ -22,8 +22,9 @@
 //
 // Two organisations ("The v0.24.0 port", bullet "Deterministic unpermute": per-pair outputs are
 // placed bijectively and summed in a fixed order, no atomics on values):
-//  * routed (after the routing pass): one group per active expert holding all its pairs; the
-//    down kernel writes per-pair rows o[p] and combine_kernel sums them in j order per token.
+//  * routed (8 < P <= kDecodeMaxPairs): one group per active expert holding all its pairs, found
+//    by each workgroup from the ids (no routing pass, see pair_group); the down kernel writes per-pair rows o[p]
+//    and combine_kernel sums them in j order per token.
 //  * direct (tiny batches, P = T*top_k <= kDirectMaxPairs): no routing pass; gate_up runs one
 //    group per pair, and one down kernel covers every pair of a column block and combines in LDS.
 #include "common.h"
@@ -106,9 +107,10 @@ MOEW2_DEV void stage_issue(Stage& st, const uint16_t* src, int len, int n, int b
 
 // Splitting commit: the 4 pieces of a 32-value block sit in 4 consecutive lanes, which agree on
 // the block maximum through two lane swaps. NP = 2: bf16 source (x); NP = 3: fp16 source (the
-// gated intermediate).
+// gated intermediate). With count_inf, ninf gains the number of infinite source values.
 template <int NT, int NP>
-MOEW2_DEV void stage_commit_split(const Stage& st, uint8_t* lds, int stride, int KR, int n, int base, int tid) {
+MOEW2_DEV void stage_commit_split(const Stage& st, uint8_t* lds, int stride, int KR, int n, int base, int tid,
+                                  bool count_inf, int& ninf) {
   const int per_row = KR / 8, total = n * per_row;
 #pragma unroll
   for (int i = 0; i < kStage; ++i) {
@@ -129,6 +131,10 @@ MOEW2_DEV void stage_commit_split(const Stage& st, uint8_t* lds, int stride, int
     a = __builtin_fmaxf(a, __shfl_xor(a, 1, 64));
     a = __builtin_fmaxf(a, __shfl_xor(a, 2, 64));
     if (ok) {
+      if (count_inf) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ninf += __builtin_isinf(f[q]) ? 1 : 0;
+      }
       const int m = idx / per_row, c8 = idx - m * per_row;
       const uint32_t sx = x_scale_byte(a);
       uint8_t* row = lds + (size_t)m * stride;
@@ -218,21 +224,22 @@ MOEW2_DEV void stream_k(TileRegs<NB> (&ring)[kRing], const WaveTiles& wt, int kb
 // after it, so every path reaches the streaming loop with the same loads outstanding (the
 // compiler's waits inside the loop stay exact). The thread index is passed through an empty asm
 // so that the staging addresses are recomputed per call instead of being hoisted out of an
-// enclosing loop and held in registers across the stream.
+// enclosing loop and held in registers across the stream. With count_inf, ninf gains the number
+// of infinite staged values.
 template <int NT, int NP, int NB, class RowOff>
 MOEW2_DEV void stage_and_prime(TileRegs<NB> (&ring)[kRing], const WaveTiles& wt, int kb, int ke, int lane,
                                uint8_t* lds, int stride, const uint16_t* src, int KR, int n, RowOff row_off,
-                               int tid) {
+                               int tid, bool count_inf, int& ninf) {
   int st_tid = tid;
   asm volatile("" : "+v"(st_tid));
   Stage st;
   for (int base = kStage * NT; base < n * (KR / 8); base += kStage * NT) {
     stage_issue<NT>(st, src, KR, n, base, row_off, st_tid);
-    stage_commit_split<NT, NP>(st, lds, stride, KR, n, base, st_tid);
+    stage_commit_split<NT, NP>(st, lds, stride, KR, n, base, st_tid, count_inf, ninf);
   }
   stage_issue<NT>(st, src, KR, n, 0, row_off, st_tid);
   prime_ring<NB>(ring, wt, kb, ke, lane);
-  stage_commit_split<NT, NP>(st, lds, stride, KR, n, 0, st_tid);
+  stage_commit_split<NT, NP>(st, lds, stride, KR, n, 0, st_tid, count_inf, ninf);
 }
 
 // Cross-wave sum of split-K partial accumulators (KS waves per row pair) into the ks == 0 wave.
@@ -259,36 +266,108 @@ MOEW2_DEV void reduce_split_k(f32x4_t* acc, float* red, int w, int ks, int lane)
 }
 
 // ---------------------------------------------------------------------------------------------
+// Routing inside the decode kernels (8 < P <= kDecodeMaxPairs, no routing pass): workgroup row p
+// (blockIdx.y) takes expert e = ids[p] when p is the first pair routed to e, and finds all of
+// e's pairs in ascending pair order with wave ballots over the ids - the order of the routing
+// pass's stable sort ("The v0.24.0 port", bullet "Deterministic unpermute"). Rows whose pair is
+// not the first of its expert, or whose id is outside [0, E), exit at once. Pair p's gated row is
+// act[p].
+// ---------------------------------------------------------------------------------------------
+constexpr int kScanBallots = kDecodeMaxPairs / 64;   // 64 pairs per ballot
+static_assert(kDecodeMaxPairs == 2 * kThreads, "two ids per thread");
+
+struct ScanLds {
+  uint64_t ball[kScanBallots];    // pairs of the selected expert, ballot i = pairs 64i .. 64i+63
+  int bad[kWaves];                // invalid ids seen by each wave
+};
+
+// Index of the k-th (from 0) set bit of v (v has more than k set bits).
+MOEW2_DEV int select_bit64(uint64_t v, int k) {
+  int pos = 0;
+#pragma unroll
+  for (int width = 32; width >= 1; width >>= 1) {
+    const int c = __popcll(v & ((1ull << width) - 1ull));
+    if (k >= c) { k -= c; v >>= width; pos += width; }
+  }
+  return pos;
+}
+
+// Selects the group of workgroup row p: its expert e and pair count n; false (for the whole
+// workgroup) when p does not start a group. With `counters` non-null the workgroup also records
+// the invalid pair count and clears the overflow count.
+MOEW2_DEV bool pair_group(const int32_t* ids, int P, int E, int p, ScanLds& sh, int tid, int lane, int w,
+                          long long* counters, int& e, int& n) {
+  e = ids[p];
+  const int id0 = tid < P ? ids[tid] : -1;
+  const int id1 = tid + kThreads < P ? ids[tid + kThreads] : -1;
+  const uint64_t b0 = __ballot(id0 == e), b1 = __ballot(id1 == e);
+  int bad = 0;
+  if (counters)
+    bad = __popcll(__ballot(tid < P && (id0 < 0 || id0 >= E))) +
+          __popcll(__ballot(tid + kThreads < P && (id1 < 0 || id1 >= E)));
+  if (lane == 0) {
+    sh.ball[w] = b0;
+    sh.ball[kWaves + w] = b1;
+    sh.bad[w] = bad;
+  }
+  __syncthreads();
+  if (counters && tid == 0) {
+    int total = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) total += sh.bad[i];
+    counters[0] = total;
+    counters[1] = 0;
+  }
+  if (e < 0 || e >= E) return false;
+  const int word = p >> 6;
+  for (int i = 0; i < word; ++i)
+    if (sh.ball[i]) return false;
+  if (sh.ball[word] & ((1ull << (p & 63)) - 1ull)) return false;
+  n = 0;
+#pragma unroll
+  for (int i = 0; i < kScanBallots; ++i) n += __popcll(sh.ball[i]);
+  return true;
+}
+
+// Pair index of the m-th pair (from 0) of the selected group.
+MOEW2_DEV int pair_at(const ScanLds& sh, int m) {
+#pragma unroll
+  for (int i = 0; i < kScanBallots; ++i) {
+    const int c = __popcll(sh.ball[i]);
+    if (m < c) return 64 * i + select_bit64(sh.ball[i], m);
+    m -= c;
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------------------------
 // gate_up: grid (I / (16*NP), groups). Wave w handles row-pair q = blockIdx.x*NP + w/KS (gate row
 // group 2q, up row group 2q+1) over the reduction slice w%KS of KS = 4/NP.
-// DIRECT: group = pair p (expert ids[p]); act row = p. Otherwise group = active slot; act row =
-// sorted position.
+// DIRECT: group = pair blockIdx.y (expert ids[p]). Otherwise group = all pairs of expert
+// ids[blockIdx.y] when blockIdx.y is the first of them (pair_group). The gated row of pair p is
+// act[p] in both.
 // ---------------------------------------------------------------------------------------------
 template <int NPW, bool DIRECT>
 __global__ void __launch_bounds__(kThreads)
 decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                       const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
-                      const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-                      const int32_t* __restrict__ active, const int32_t* __restrict__ meta,
                       _Float16* __restrict__ act, long long* __restrict__ counters,
-                      int E, int K, int I, int top_k) {
+                      int P, int E, int K, int I, int top_k) {
   constexpr int KS = kWaves / NPW;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  int e, n_total, row0;
+  __shared__ ScanLds sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
+  int e, n_total;
   if (DIRECT) {
-    row0 = blockIdx.y;             // the pair
-    e = ids[row0];
+    e = ids[blockIdx.y];
     if (e < 0 || e >= E) return;
     n_total = 1;
   } else {
-    if ((int)blockIdx.y >= meta[0]) return;
-    e = active[blockIdx.y];
-    row0 = offsets[e];
-    n_total = offsets[e + 1] - row0;
+    long long* cnt = blockIdx.x == 0 && blockIdx.y == 0 ? counters : nullptr;
+    if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, cnt, e, n_total)) return;
   }
   const int nkt = K / kTileK, nrg = 2 * I / kTileRows;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
   const int pw = w / KS, ks = w % KS;
   const int q = blockIdx.x * NPW + pw;
   WaveTiles wt = wave_tiles(codes, scales, e, (uint32_t)(nrg * nkt));
@@ -300,15 +379,16 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
   TileRegs<2> ring[kRing];
   for (int c0 = 0; c0 < n_total; c0 += kChunk) {
     const int n = min(kChunk, n_total - c0);
-    // token of each staged row (wave-uniform loads)
-    int tk[kChunk];
+    // pair and token of each staged row (the same in every lane)
+    int pr[kChunk];
 #pragma unroll
-    for (int m = 0; m < kChunk; ++m) tk[m] = (DIRECT ? row0 : perm[row0 + c0 + min(m, n - 1)]) / top_k;
+    for (int m = 0; m < kChunk; ++m) pr[m] = DIRECT ? (int)blockIdx.y : pair_at(sh, c0 + min(m, n - 1));
     auto row_off = [&](int m) -> size_t {
-      const int t = m == 0 ? tk[0] : m == 1 ? tk[1] : m == 2 ? tk[2] : tk[3];
-      return (size_t)t * K;
+      const int pp = m == 0 ? pr[0] : m == 1 ? pr[1] : m == 2 ? pr[2] : pr[3];
+      return (size_t)(pp / top_k) * K;
     };
-    stage_and_prime<kThreads, 2, 2>(ring, wt, kb, ke, lane, lds, stride, x, K, n, row_off, tid);
+    int ninf = 0;
+    stage_and_prime<kThreads, 2, 2>(ring, wt, kb, ke, lane, lds, stride, x, K, n, row_off, tid, false, ninf);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -319,11 +399,8 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
 #pragma unroll
       for (int r = 0; r < kChunk; ++r) {
         if (r < n) {
-          const float a = silu_mul(acc[0][r], acc[1][r]);
-          const _Float16 h = (_Float16)a;
-          if (__builtin_isinf((float)h) && !__builtin_isinf(a)) atomicAdd((unsigned long long*)&counters[1], 1ull);
-          const int row = DIRECT ? row0 : row0 + c0 + r;
-          act[(size_t)row * I + 16 * q + lane] = h;
+          const int pp = r == 0 ? pr[0] : r == 1 ? pr[1] : r == 2 ? pr[2] : pr[3];
+          act[(size_t)pp * I + 16 * q + lane] = (_Float16)silu_mul(acc[0][r], acc[1][r]);
         }
       }
     }
@@ -332,25 +409,24 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------------------------
-// routed down: grid (K / (32*NP), active slots). Wave w handles row groups 2*rq and 2*rq + 1,
-// rq = blockIdx.x*NP + w/KS, over the reduction slice w%KS. Per-pair rows go to pair_out at the
-// pair index (bijective); combine_kernel then sums them per token in j order.
+// routed down: grid (K / (32*NP), P). The group is that of the gate_up stage (pair_group); wave w handles row groups 2*rq and 2*rq + 1, rq = blockIdx.x*NP + w/KS, over the
+// reduction slice w%KS. Per-pair rows go to pair_out at the pair index (bijective);
+// combine_kernel then sums them per token in j order. The blockIdx.x == 0 workgroups count the
+// gated intermediates that overflowed fp16 (each pair belongs to one group).
 // ---------------------------------------------------------------------------------------------
 template <int NPW>
 __global__ void __launch_bounds__(kThreads)
 decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                   const _Float16* __restrict__ act, const int32_t* __restrict__ offsets,
-                   const int32_t* __restrict__ perm, const int32_t* __restrict__ active,
-                   const int32_t* __restrict__ meta, float* __restrict__ pair_out, int E, int K, int I,
-                   int top_k) {
+                   const _Float16* __restrict__ act, const int32_t* __restrict__ ids,
+                   float* __restrict__ pair_out, long long* __restrict__ counters, int P, int E, int K,
+                   int I) {
   constexpr int KS = kWaves / NPW;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ ScanLds sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
-  if ((int)blockIdx.y >= meta[0]) return;
-  const int e = active[blockIdx.y];
-  const int row0 = offsets[e];
-  const int n_e = offsets[e + 1] - row0;
+  int e, n_e;
+  if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, nullptr, e, n_e)) return;
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int pw = w / KS, ks = w % KS;
   const int rq = blockIdx.x * NPW + pw;
@@ -364,8 +440,17 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
   TileRegs<2> ring[kRing];
   for (int c0 = 0; c0 < n_e; c0 += kChunk) {
     const int n = min(kChunk, n_e - c0);
-    auto row_off = [&](int m) -> size_t { return (size_t)(row0 + c0 + m) * I; };
-    stage_and_prime<kThreads, 3, 2>(ring, wt, kb, ke, lane, lds, stride, act16, I, n, row_off, tid);
+    int pr[kChunk];
+#pragma unroll
+    for (int m = 0; m < kChunk; ++m) pr[m] = pair_at(sh, c0 + min(m, n - 1));
+    auto row_off = [&](int m) -> size_t {
+      const int pp = m == 0 ? pr[0] : m == 1 ? pr[1] : m == 2 ? pr[2] : pr[3];
+      return (size_t)pp * I;
+    };
+    int ninf = 0;
+    stage_and_prime<kThreads, 3, 2>(ring, wt, kb, ke, lane, lds, stride, act16, I, n, row_off, tid,
+                                    blockIdx.x == 0, ninf);
+    if (ninf) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)ninf);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -377,7 +462,10 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
         const int col = 16 * (2 * rq + b) + lane;
 #pragma unroll
         for (int r = 0; r < kChunk; ++r) {
-          if (r < n) pair_out[(size_t)perm[row0 + c0 + r] * K + col] = acc[b][r];
+          if (r < n) {
+            const int pp = r == 0 ? pr[0] : r == 1 ? pr[1] : r == 2 ? pr[2] : pr[3];
+            pair_out[(size_t)pp * K + col] = acc[b][r];
+          }
         }
       }
     }
@@ -420,7 +508,9 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
   const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
   auto row_off = [&](int m) -> size_t { return (size_t)m * I; };
   TileRegs<1> ring[kRing];
-  stage_and_prime<kDirectThreads, 3, 1>(ring, wt, kb, ke, lane, lds, stride, act16, I, P, row_off, tid);
+  int ninf = 0;
+  stage_and_prime<kDirectThreads, 3, 1>(ring, wt, kb, ke, lane, lds, stride, act16, I, P, row_off, tid, false,
+                                        ninf);
   __syncthreads();
   if (blockIdx.x == 0) {
     // counters: invalid pairs, and gated intermediates that are infinite (from the source rows)
@@ -516,25 +606,21 @@ hipError_t launch_decode_gate_up(const moe_w2_planes* p, int T, int top_k, const
                                  const int32_t* ids, const Workspace& ws, uint8_t* wsb, bool direct,
                                  hipStream_t s) {
   const int P = T * top_k;
-  const int slots = direct ? P : min(p->E, P);
-  if (slots == 0) return hipSuccess;
+  if (P == 0) return hipSuccess;
+  const int groups = direct ? P : min(p->E, P);   // at most this many workgroup rows do work
   const size_t lds = (size_t)kChunk * MxRow<2>::stride(p->K) + (size_t)kWaves * 2 * 4 * 16 * 4;
   const uint16_t* xb = (const uint16_t*)x;
-  const int32_t* off = (const int32_t*)(wsb + ws.offsets);
-  const int32_t* perm = (const int32_t*)(wsb + ws.perm);
-  const int32_t* act_list = (const int32_t*)(wsb + ws.active);
-  const int32_t* meta = (const int32_t*)(wsb + ws.meta);
   _Float16* act = (_Float16*)(wsb + ws.act);
   long long* cnt = (long long*)(wsb + ws.counters);
   if (direct) {
-    hipLaunchKernelGGL((decode_gate_up_kernel<1, true>), dim3(p->I / 16, slots), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, off, perm, act_list, meta, act, cnt, p->E, p->K, p->I, top_k);
-  } else if (pick_np(slots) == 4) {
-    hipLaunchKernelGGL((decode_gate_up_kernel<4, false>), dim3(p->I / 64, slots), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, off, perm, act_list, meta, act, cnt, p->E, p->K, p->I, top_k);
+    hipLaunchKernelGGL((decode_gate_up_kernel<1, true>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k);
+  } else if (pick_np(groups) == 4) {
+    hipLaunchKernelGGL((decode_gate_up_kernel<4, false>), dim3(p->I / 64, P), dim3(kThreads), lds, s,
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k);
   } else {
-    hipLaunchKernelGGL((decode_gate_up_kernel<1, false>), dim3(p->I / 16, slots), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, off, perm, act_list, meta, act, cnt, p->E, p->K, p->I, top_k);
+    hipLaunchKernelGGL((decode_gate_up_kernel<1, false>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k);
   }
   return hipGetLastError();
 }
@@ -545,24 +631,21 @@ hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const in
   const int P = T * top_k;
   if (P == 0) return hipSuccess;
   const _Float16* act = (const _Float16*)(wsb + ws.act);
+  long long* cnt = (long long*)(wsb + ws.counters);
   if (direct) {
     hipLaunchKernelGGL(decode_down_direct_kernel, dim3(p->K / 16), dim3(kDirectThreads), decode_direct_lds(p->I), s,
-                       p->dn_codes, p->dn_scales, act, ids, w, y, (long long*)(wsb + ws.counters),
-                       out_dtype, T, p->E, p->K, p->I, top_k);
+                       p->dn_codes, p->dn_scales, act, ids, w, y, cnt, out_dtype, T, p->E, p->K, p->I, top_k);
     return hipGetLastError();
   }
-  const int slots = min(p->E, P);
+  const int groups = min(p->E, P);
   const size_t lds = (size_t)kChunk * MxRow<3>::stride(p->I) + (size_t)kWaves * 2 * 4 * 16 * 4;
-  const int np = pick_np(slots);
-  auto args = [&](auto kern, int gx) {
-    hipLaunchKernelGGL(kern, dim3(gx, slots), dim3(kThreads), lds, s,
-                       p->dn_codes, p->dn_scales, act,
-                       (const int32_t*)(wsb + ws.offsets), (const int32_t*)(wsb + ws.perm),
-                       (const int32_t*)(wsb + ws.active), (const int32_t*)(wsb + ws.meta),
-                       (float*)(wsb + ws.pair_out), p->E, p->K, p->I, top_k);
-  };
-  if (np == 4) args(decode_down_kernel<4>, p->K / 128);
-  else args(decode_down_kernel<1>, p->K / 32);
+  float* po = (float*)(wsb + ws.pair_out);
+  if (pick_np(groups) == 4)
+    hipLaunchKernelGGL(decode_down_kernel<4>, dim3(p->K / 128, P), dim3(kThreads), lds, s,
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I);
+  else
+    hipLaunchKernelGGL(decode_down_kernel<1>, dim3(p->K / 32, P), dim3(kThreads), lds, s,
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I);
   return hipGetLastError();
 }
 

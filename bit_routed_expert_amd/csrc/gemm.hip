@@ -222,7 +222,7 @@ gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restr
       for (int pr = 0; pr < 2; ++pr) {
         const float a = silu_mul(acc[m][2 * pr][r], acc[m][2 * pr + 1][r]);
         const _Float16 h = (_Float16)a;
-        if (__builtin_isinf((float)h) && !__builtin_isinf(a)) atomicAdd((unsigned long long*)&counters[1], 1ull);
+        if (__builtin_isinf((float)h)) atomicAdd((unsigned long long*)&counters[1], 1ull);
         const int col = 16 * (rg0 / 2 + pr) + (lane & 15);
         act[(size_t)sr * I + col] = h;
       }

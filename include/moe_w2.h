@@ -56,7 +56,8 @@ enum moe_w2_status {
 
 enum moe_w2_out_dtype { MOE_W2_OUT_BF16 = 0, MOE_W2_OUT_F32 = 1 };
 
-/* Which kernels moe_w2_forward uses. AUTO picks DECODE for T*top_k <= 512, else GEMM. */
+/* Which kernels moe_w2_forward uses. AUTO picks DECODE for T*top_k <= 512, else GEMM. DECODE
+ * supports T*top_k <= 512 only (MOE_W2_EUNSUPPORTED above). */
 enum moe_w2_path { MOE_W2_PATH_AUTO = 0, MOE_W2_PATH_DECODE = 1, MOE_W2_PATH_GEMM = 2 };
 
 /* The four stages of moe_w2_forward, in order (see moe_w2_forward_stage). */
@@ -136,10 +137,15 @@ int moe_w2_route(int E, int T, int top_k, const int32_t* topk_ids,
  *   y        [T][K] bf16 (MOE_W2_OUT_BF16, round-to-nearest-even of the fp32 result) or fp32
  *   workspace: device memory of at least moe_w2_workspace_bytes(planes, T, top_k) bytes; it
  *   must not be shared by forwards that may run concurrently.
- * Arithmetic: gate/up in bf16 x bf16 -> fp32; the gated product is rounded to fp16; down in
- * fp16 x fp16 -> fp32; combine in fp32 with j ascending. The result does not depend on the
- * order in which pairs are processed and repeated calls are bit-identical. An intermediate
- * |silu(g) * u| above the fp16 range becomes +-inf and is counted (act_overflow).
+ * Arithmetic: both projections run on the block-scaled fp8 x fp4 matrix instruction with fp32
+ * accumulation. The weights enter exactly (codes as e2m1 values +-0.5, +-2 under their UE8M0
+ * block scale times 2). Each 32-value block of x is split into two e4m3 parts (one hi part and
+ * its residual, power-of-two block scales), which hold every bf16 value of the block within
+ * 2^-11 of the block's largest magnitude; the gated product silu(g) * u is rounded to fp16 and
+ * split into three e4m3 parts, exact for every fp16 value within 2^-10 of its block's largest
+ * magnitude. Combine in fp32 with j ascending. The result does not depend on the order in which
+ * pairs are processed and repeated calls are bit-identical. An intermediate |silu(g) * u| above
+ * the fp16 range becomes +-inf and is counted (act_overflow).
  * Asynchronous; no host synchronisation and no allocation.
  */
 int moe_w2_forward(const moe_w2_planes* planes, int T, int top_k,
