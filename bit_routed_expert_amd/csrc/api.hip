@@ -171,6 +171,9 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
   if ((long long)T * top_k > (1LL << 30)) return MOE_W2_EUNSUPPORTED;
   if ((long long)T * p->K >= (1LL << 31) || (long long)T * top_k * p->I >= (1LL << 31))
     return MOE_W2_EUNSUPPORTED;  // the GEMM kernels index x and the intermediate in 32 bits
+  if ((long long)T * (2LL * p->K + p->K / 16) >= (1LL << 32) ||
+      (long long)T * top_k * (3LL * p->I + p->I / 8) >= (1LL << 32))
+    return MOE_W2_EUNSUPPORTED;  // ... and their split copies with 32-bit byte offsets
   const Workspace ws = workspace_layout(p->E, p->K, p->I, T, top_k);
   if (!workspace || workspace_bytes < ws.total) return MOE_W2_EWORKSPACE;
   if (T == 0) return MOE_W2_OK;

@@ -66,6 +66,33 @@ MOEW2_DEV i32x8_t mx_b_operand(uint32_t d0, uint32_t d1) {
   return v;
 }
 
+// The same expansion as one bit-field insert per output dword (plus a shift for the second):
+// v_bfi_b32 takes the selector mask from a scalar register. Make the masks once per kernel with
+// fp4_masks().
+struct Fp4Masks {
+  uint32_t sel;   // scalar register: 0xCCCCCCCC
+  uint32_t one;   // 0x22222222
+};
+MOEW2_DEV Fp4Masks fp4_masks() {
+  Fp4Masks f;
+  asm volatile("s_mov_b32 %0, 0xcccccccc" : "=s"(f.sel));
+  f.one = 0x22222222u;
+  return f;
+}
+MOEW2_DEV uint32_t bfi_sel(uint32_t sel, uint32_t a, uint32_t b) {   // (a & sel) | (b & ~sel)
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(sel), "v"(a), "v"(b));
+  return r;
+}
+MOEW2_DEV i32x8_t mx_b_operand(uint32_t d0, uint32_t d1, const Fp4Masks& f) {
+  const uint32_t a0 = bfi_sel(f.sel, d0, f.one);
+  const uint32_t a1 = bfi_sel(f.sel, d0 << 2, f.one);
+  const uint32_t b0 = bfi_sel(f.sel, d1, f.one);
+  const uint32_t b1 = bfi_sel(f.sel, d1 << 2, f.one);
+  i32x8_t v = {(int)a0, (int)a1, (int)b0, (int)b1, 0, 0, 0, 0};
+  return v;
+}
+
 template <int OPA, int OPB>
 MOEW2_DEV f32x4_t mx_mfma(const i32x8_t& a, const i32x8_t& b, f32x4_t c, uint32_t sa, uint32_t sb) {
   const f32x4e_t r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(

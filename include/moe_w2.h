@@ -23,7 +23,8 @@
  *  - Shapes: K (hidden size) and I (expert intermediate size) must be multiples of 256 with
  *    I*K < 2^32;
  *    1 <= E <= 1024; 1 <= top_k <= 32; T >= 0 (T = 0 is a no-op). A forward also needs
- *    T*K < 2^31 and T*top_k*I < 2^31 (element counts of x and of the gated intermediate).
+ *    T*K < 2^31 and T*top_k*I < 2^31 (element counts of x and of the gated intermediate),
+ *    T*(2K + K/16) < 2^32 and T*top_k*(3I + I/8) < 2^32 (bytes of their split copies).
  *
  * Canonical plane layout (the input of moe_w2_pack, the output of nvfp4_to_w2):
  *  - codes: 4 per byte along the row's reduction axis, element k at bits 2*(k%4)..+1 (LSB
