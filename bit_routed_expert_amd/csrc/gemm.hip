@@ -119,10 +119,10 @@ MOEW2_DEV void static_for(F&& f) {
   }
 }
 
-// The loads of one k-tile for one wave, as kItems single instructions: the stage's DMA
-// instructions (waves whose last instruction index lies past the stage repeat the stage's last
-// instruction - the same bytes to the same chunks - so every wave issues kPerWave), then the B
-// code and scale loads. Group i of the computing k-tile issues items [i*kItems/8, (i+1)*kItems/8)
+// The loads of one k-tile for one wave, as kItems single instructions: the B code and scale loads,
+// then the stage's DMA instructions (waves whose last instruction index lies past the stage
+// repeat the stage's last instruction - the same bytes to the same chunks - so every wave issues
+// kPerWave). Group i of the computing k-tile issues items [i*kItems/8, (i+1)*kItems/8)
 // of the k-tile two ahead, so the loads spread over the step instead of queueing behind the
 // barrier.
 template <class AT>
@@ -137,17 +137,18 @@ struct KLoads {
 
   template <int N>
   MOEW2_DEV void item(int kt, uint8_t* stage, BRegs& r) const {
-    if constexpr (N < AT::kPerWave) {
-      const int j = min(w + kWaves * N, AT::kInstr - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(abase + (aoff[N] + (uint32_t)kt * AT::kSrcBytes)),
-                                       (__attribute__((address_space(3))) void*)(stage + 1024 * j), 16, 0, 0);
-    } else {
-      constexpr int t = (N - AT::kPerWave) / 2;
+    if constexpr (N < kBLoads) {       // B first: it comes from HBM, A mostly from L2
+      constexpr int t = N / 2;
       const size_t ti = tb0 + (size_t)t * nkt + kt;
-      if constexpr ((N - AT::kPerWave) % 2 == 0)
+      if constexpr (N % 2 == 0)
         r.c[t] = ld16(codes + ti * kTileCodeBytes + 16 * lane);
       else
         r.s[t] = *reinterpret_cast<const uint16_t*>(scales + ti * kTileScaleBytes + 2 * lane);
+    } else {
+      constexpr int n = N - kBLoads;
+      const int j = min(w + kWaves * n, AT::kInstr - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(abase + (aoff[n] + (uint32_t)kt * AT::kSrcBytes)),
+                                       (__attribute__((address_space(3))) void*)(stage + 1024 * j), 16, 0, 0);
     }
   }
   template <int N0, int N1>
