@@ -197,11 +197,11 @@ MOEW2_DEV void mma_tile(const TileRegs<NB>& r, const uint8_t* arow, int KR, int 
   mma_chunk<1, NP, NB>(r, kbase, KR, w0, w1, g, acc);
 }
 
-// ring[i] <- k-tile kb + i (out-of-range requests past ke)
-template <int NB>
+// ring[i] <- k-tile kb + i for i in [I0, I1) (out-of-range requests past ke)
+template <int NB, int I0 = 0, int I1 = kRing>
 MOEW2_DEV void prime_ring(TileRegs<NB> (&ring)[kRing], const WaveTiles& wt, int kb, int ke, int lane) {
 #pragma unroll
-  for (int i = 0; i < kRing; ++i) load_tile<NB>(ring[i], wt, kb + i, kb + i < ke, lane);
+  for (int i = I0; i < I1; ++i) load_tile<NB>(ring[i], wt, kb + i, kb + i < ke, lane);
 }
 
 // Consume k-tiles [kb, ke) from the primed ring; each consumed slot is refilled with the tile
@@ -226,7 +226,12 @@ MOEW2_DEV void stream_k(TileRegs<NB> (&ring)[kRing], const WaveTiles& wt, int kb
 // so that the staging addresses are recomputed per call instead of being hoisted out of an
 // enclosing loop and held in registers across the stream. With count_inf, ninf gains the number
 // of infinite staged values.
-template <int NT, int NP, int NB, class RowOff>
+// SPLIT: ring slots primed before the staged rows are committed (the rest after). For a kernel
+// whose every workgroup starts at once and reads the same few rows (the tiny-batch organisation),
+// priming the whole ring first puts the entire weight volume in the memory queues ahead of those
+// row loads; committing first leaves the memory idle while every workgroup waits for the same
+// rows. Half and half keeps half the weights streaming while the rows arrive.
+template <int NT, int NP, int NB, int SPLIT = kRing, class RowOff>
 MOEW2_DEV void stage_and_prime(TileRegs<NB> (&ring)[kRing], const WaveTiles& wt, int kb, int ke, int lane,
                                uint8_t* lds, int stride, const uint16_t* src, int KR, int n, RowOff row_off,
                                int tid, bool count_inf, int& ninf) {
@@ -238,8 +243,10 @@ MOEW2_DEV void stage_and_prime(TileRegs<NB> (&ring)[kRing], const WaveTiles& wt,
     stage_commit_split<NT, NP>(st, lds, stride, KR, n, base, st_tid, count_inf, ninf);
   }
   stage_issue<NT>(st, src, KR, n, 0, row_off, st_tid);
-  prime_ring<NB>(ring, wt, kb, ke, lane);
+  prime_ring<NB, 0, SPLIT>(ring, wt, kb, ke, lane);
+  __builtin_amdgcn_sched_barrier(0);   // the first ring loads go out before the commit waits
   stage_commit_split<NT, NP>(st, lds, stride, KR, n, 0, st_tid, count_inf, ninf);
+  prime_ring<NB, SPLIT, kRing>(ring, wt, kb, ke, lane);
 }
 
 // Cross-wave sum of split-K partial accumulators (KS waves per row pair) into the ks == 0 wave.
@@ -359,9 +366,13 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
   int e, n_total;
+  bool valid = true;
   if (DIRECT) {
-    e = ids[blockIdx.y];
-    if (e < 0 || e >= E) return;
+    // no early exit: the x row is requested together with the id (an invalid pair streams no
+    // weights and gets a row of zeros, which the down stage stages like any other)
+    const int id = ids[blockIdx.y];
+    valid = id >= 0 && id < E;
+    e = valid ? id : 0;
     n_total = 1;
   } else {
     long long* cnt = blockIdx.x == 0 && blockIdx.y == 0 ? counters : nullptr;
@@ -373,7 +384,7 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
   WaveTiles wt = wave_tiles(codes, scales, e, (uint32_t)(nrg * nkt));
   wt.tile[0] = (uint32_t)(2 * q * nkt);
   wt.tile[1] = (uint32_t)((2 * q + 1) * nkt);
-  const int kb = ks * nkt / KS, ke = (ks + 1) * nkt / KS;
+  const int kb = ks * nkt / KS, ke = valid ? (ks + 1) * nkt / KS : kb;
   const int stride = MxRow<2>::stride(K);
   float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][2][4][16]
   TileRegs<2> ring[kRing];
@@ -388,7 +399,8 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
       return (size_t)(pp / top_k) * K;
     };
     int ninf = 0;
-    stage_and_prime<kThreads, 2, 2>(ring, wt, kb, ke, lane, lds, stride, x, K, n, row_off, tid, false, ninf);
+    stage_and_prime<kThreads, 2, 2, DIRECT ? kRing / 2 : kRing>(ring, wt, kb, ke, lane, lds, stride, x, K, n,
+                                                                row_off, tid, false, ninf);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -400,7 +412,7 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
       for (int r = 0; r < kChunk; ++r) {
         if (r < n) {
           const int pp = r == 0 ? pr[0] : r == 1 ? pr[1] : r == 2 ? pr[2] : pr[3];
-          act[(size_t)pp * I + 16 * q + lane] = (_Float16)silu_mul(acc[0][r], acc[1][r]);
+          act[(size_t)pp * I + 16 * q + lane] = valid ? (_Float16)silu_mul(acc[0][r], acc[1][r]) : (_Float16)0.f;
         }
       }
     }
@@ -504,35 +516,38 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
   wt.tile[0] = (uint32_t)(rg * nkt);
   wt.tile[1] = 0;
   const int kb = hk * nkt / 2, ke = valid ? (hk + 1) * nkt / 2 : kb;
-  // gated rows of all pairs (rows of invalid pairs are staged but never read)
+  // ids and router weights of the combine, read now rather than after the stream
+  __shared__ int cid[kDirectMaxPairs];
+  __shared__ float cw[kDirectMaxPairs];
+  __shared__ int cnt[2];
+  if (tid < P) {
+    cid[tid] = ids[tid];
+    cw[tid] = wts[tid];
+  }
+  if (tid < 2) cnt[tid] = 0;
+  // gated rows of all pairs (rows of invalid pairs are staged but never read); block 0 counts the
+  // infinite ones while staging them
   const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
   auto row_off = [&](int m) -> size_t { return (size_t)m * I; };
   TileRegs<1> ring[kRing];
   int ninf = 0;
-  stage_and_prime<kDirectThreads, 3, 1>(ring, wt, kb, ke, lane, lds, stride, act16, I, P, row_off, tid, false,
-                                        ninf);
+  stage_and_prime<kDirectThreads, 3, 1, kRing / 2>(ring, wt, kb, ke, lane, lds, stride, act16, I, P, row_off,
+                                                   tid, blockIdx.x == 0, ninf);
   __syncthreads();
   if (blockIdx.x == 0) {
-    // counters: invalid pairs, and gated intermediates that are infinite (from the source rows)
-    __shared__ int cnt[2];
-    if (tid < 2) cnt[tid] = 0;
-    __syncthreads();
-    int bad = 0, inf = 0;
-    for (int pp = 0; pp < P; ++pp) {
-      const int ii = ids[pp];
-      if (ii < 0 || ii >= E) { bad += tid == 0 ? 1 : 0; continue; }
-      for (int c = tid; c < I; c += kDirectThreads)
-        if (__builtin_isinf((float)act[(size_t)pp * I + c])) ++inf;
-    }
-    if (bad) atomicAdd(&cnt[0], bad);
-    if (inf) atomicAdd(&cnt[1], inf);
-    __syncthreads();
-    if (tid == 0) { counters[0] = cnt[0]; counters[1] = cnt[1]; }
+    // counters: invalid pairs, and infinite gated intermediates (the rows of invalid pairs are
+    // zeros, written by the gate_up stage)
+    if (ninf) atomicAdd(&cnt[1], ninf);
+    if (tid < P && (cid[tid] < 0 || cid[tid] >= E)) atomicAdd(&cnt[0], 1);
   }
   f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
   stream_k<3, 1>(ring, wt, kb, ke, lds + (size_t)(p < P ? p : 0) * stride, I, lane >> 4, acc, lane);
   if (valid && hk == 1 && lane < 16) red[p * 16 + lane] = acc[0][0];
   __syncthreads();
+  if (blockIdx.x == 0 && tid == 0) {
+    counters[0] = cnt[0];
+    counters[1] = cnt[1];
+  }
   if (valid && hk == 0 && lane < 16) o[p * 16 + lane] = acc[0][0] + red[p * 16 + lane];
   __syncthreads();
   // combine: y[t][16*rg + c] = sum_j w[t,j] * o[t*top_k+j][c]
@@ -541,9 +556,9 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
     float sum = 0.f;
     for (int j = 0; j < top_k; ++j) {
       const int pp = t * top_k + j;
-      const int ii = ids[pp];
+      const int ii = cid[pp];
       if (ii < 0 || ii >= E) continue;
-      sum += wts[pp] * o[pp * 16 + c];
+      sum += cw[pp] * o[pp * 16 + c];
     }
     const size_t yo = (size_t)t * K + 16 * rg + c;
     if (out_dtype == MOE_W2_OUT_F32) reinterpret_cast<float*>(y)[yo] = sum;
