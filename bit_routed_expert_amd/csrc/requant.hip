@@ -5,11 +5,15 @@
 // and re-quantized to the codebook {-4,-1,1,4}; the UE8M0 block-32 output scales absorb scale_2.
 //
 // One thread per 32-element block. Every element is held exactly as N * 2^P with N < 2^32
-// (N = twice the e2m1 magnitude x the e4m3 significand x the fp32 significand), so the squared
-// error comparisons are exact integer arithmetic, never rounded:
+// (N = twice the e2m1 magnitude m2 x the e4m3 significand x the fp32 significand; the last two
+// are one factor SF per half-block), so the squared error comparisons are exact integer
+// arithmetic, never rounded:
 //   D(e) = SSE(e) - sum|x|^2 = Q(e) 4^e - 2^(e+1) A(e),  Q = sum q^2,  A = sum q |x|,
 // and the optimum lies in [top-6, top] with top = ceil(log2 max|x|): above top every magnitude
 // is 1 and the error grows with e; below max|x|/37 doubling the step always lowers the error.
+// An element takes magnitude 4 at exponent e exactly when |x| > 2.5 * 2^e, i.e. when e is below
+// its threshold t = P + floor(log2 N) - 1 + [4N > 5 * 2^floor(log2 N)] (ties go to 1), so each
+// candidate needs only the per-half sums of m2 over the elements above it.
 #include "common.h"
 #include "internal.h"
 
@@ -17,15 +21,6 @@ namespace moew2 {
 namespace {
 
 __device__ __forceinline__ int ilog2_u32(uint32_t v) { return 31 - __clz(v); }  // v > 0
-
-// N * 2^d > 5 (exact) for N < 2^32
-__device__ __forceinline__ bool above_midpoint(uint32_t N, int d) {
-  if (N == 0) return false;
-  if (d >= 3) return true;
-  if (d >= 0) return ((uint64_t)N << d) > 5u;
-  if (d <= -33) return false;
-  return (uint64_t)N > ((uint64_t)5 << (-d));
-}
 
 __global__ void __launch_bounds__(256)
 nvfp4_to_w2_kernel(long long nblocks, long long blocks_per_tensor,
@@ -62,40 +57,46 @@ nvfp4_to_w2_kernel(long long nblocks, long long blocks_per_tensor,
   const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(e2m1 + 16 * b);
   // twice the e2m1 magnitude of nibble n&7: 0,1,2,3,4,6,8,12
   constexpr uint64_t kTwiceMag = 0x0C08060403020100ull;
-  uint32_t N[32];
-  uint32_t neg = 0;
-  int top = -100000;
+  constexpr int kNone = -100000;
+  uint32_t m2[32];
+  int t[32];
+  uint32_t neg = 0, tot[2] = {0, 0};
+  int top = kNone;
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
     const uint32_t word = raw[k >> 3];
     const uint32_t nib = (word >> (4 * (k & 7))) & 15u;
     const int j = k >> 4;
-    const uint32_t m2 = (uint32_t)((kTwiceMag >> (8 * (nib & 7))) & 0xff);
-    N[k] = m2 * SF[j];
+    m2[k] = (uint32_t)((kTwiceMag >> (8 * (nib & 7))) & 0xff);
+    tot[j] += m2[k];
     neg |= (((nib >> 3) ^ nsg[j]) & 1u) << k;
-    if (N[k]) {
-      const int c = P[j] + ilog2_u32(N[k]) + ((N[k] & (N[k] - 1)) ? 1 : 0);
+    const uint32_t N = m2[k] * SF[j];
+    t[k] = kNone;
+    if (N) {
+      const int L = ilog2_u32(N);
+      t[k] = P[j] + L - 1 + (4ull * N > (5ull << L) ? 1 : 0);
+      const int c = P[j] + L + ((N & (N - 1)) ? 1 : 0);
       top = c > top ? c : top;
     }
   }
   int best = -127;
-  if (top != -100000) {
+  if (top != kNone) {
     int lo = max(-127, min(127, top - 6));
     int hi = max(-127, min(127, top));
     const int Pm = min(P[0], P[1]);
     const int Z = min(2 * lo, lo + 1 + Pm);
     __int128 best_v = 0;
     for (int e = lo; e <= hi; ++e) {
-      uint64_t A0 = 0, A1 = 0;
-      int n4 = 0;
+      // m2 sums of the elements above their threshold, and their count (bits 16 up)
+      uint32_t acc0 = 0, acc1 = 0;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const int j = k >> 4;
-        const bool q4 = above_midpoint(N[k], P[j] - e + 1);
-        const uint64_t v = q4 ? 4ull * N[k] : (uint64_t)N[k];
-        if (j == 0) A0 += v; else A1 += v;
-        n4 += q4 ? 1 : 0;
-      }
+      for (int k = 0; k < 16; ++k) acc0 += t[k] > e ? m2[k] + 65536u : 0u;
+#pragma unroll
+      for (int k = 16; k < 32; ++k) acc1 += t[k] > e ? m2[k] + 65536u : 0u;
+      const int n4 = (int)((acc0 >> 16) + (acc1 >> 16));
+      // A_j = SF_j * sum over the half of (q4 ? 4 : 1) * m2
+      const uint64_t A0 = (uint64_t)SF[0] * (tot[0] + 3u * (acc0 & 0xffffu));
+      const uint64_t A1 = (uint64_t)SF[1] * (tot[1] + 3u * (acc1 & 0xffffu));
       const __int128 A = ((__int128)A0 << (P[0] - Pm)) + ((__int128)A1 << (P[1] - Pm));
       // D(e) = Q 2^(2e) - A 2^(e+1+Pm), scaled by 2^-Z with Z below both exponents for every
       // candidate, so both shifts are non-negative and every value is an exact integer.
@@ -107,7 +108,7 @@ nvfp4_to_w2_kernel(long long nblocks, long long blocks_per_tensor,
   uint32_t c0 = 0, c1 = 0;
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    const bool q4 = above_midpoint(N[k], P[k >> 4] - best + 1);
+    const bool q4 = t[k] > best;
     const bool ng = (neg >> k) & 1u;
     const uint32_t c = ng ? (q4 ? 0u : 1u) : (q4 ? 3u : 2u);
     if (k < 16) c0 |= c << (2 * k); else c1 |= c << (2 * (k - 16));
