@@ -22,15 +22,16 @@ namespace moew2 {
 namespace {
 
 constexpr int BM = kGemmBM;     // 64 sorted pair rows (4 MFMA row tiles)
-constexpr int kWaves = 4;       // each wave: all BM rows x 64 weight rows (4 row groups of 16)
-constexpr int BN = 64 * kWaves; // 256 weight rows per workgroup
+constexpr int kWaves = 8;       // each wave: all BM rows x 64 weight rows (4 row groups of 16)
+constexpr int BN = 64 * kWaves; // 512 weight rows per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWgPerCu = 2;     // two workgroups share a CU (LDS and registers sized for it)
+constexpr int kWgPerCu = 1;
 
 // Tile shape: the 2-bit weights cost 0.28 byte per element against 2 bytes for the activations,
-// so the workgroup tile is wide in N (256 weight rows) and short in M (64 rows). Two workgroups
-// run on each CU, so every SIMD holds waves of two workgroups that do not wait at each other's
-// barriers: one's loads, barrier waits and epilogue stores overlap the other's matrix work.
+// so the workgroup tile is wide in N (512 weight rows) and short in M (64 rows): per k-tile a
+// workgroup moves 39 KB of split activations and 37 KB of weights into the CU. (Two workgroups
+// of 64 x 256 per CU moved 1.5x the bytes per flop and measured no faster, nor did 32 x 128 wave
+// tiles, which halve the LDS operand reads.)
 //
 // The workgroup -> tile mapping is XCD-aware: consecutive workgroup ids are dispatched to the
 // 8 XCDs in turn, so workgroup b takes logical tile (b % 8) * per_xcd + b / 8. Each XCD then walks
@@ -263,7 +264,7 @@ static_assert(kA6Bytes % 16 == 0, "split record is whole chunks");
 // one accumulator are 4 instructions apart (back-to-back dependent instructions stall).
 template <class Part>
 MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][4], const uint8_t* abuf, const BRegs& br, Part part, bool mma,
-                        int lane, const Fp4Masks& fm) {
+                        int rows_valid, int lane, const Fp4Masks& fm) {
   const int g = lane >> 4;
   const uint8_t* arow = abuf + (lane & 15) * kA6Stride;
   static_for<0, 2>([&](auto cc) {
@@ -277,7 +278,8 @@ MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][4], const uint8_t* abuf, const BRegs& 
       if constexpr (m < 3) nxt = a6_load(arow + (m + 1) * 16 * kA6Stride, C, g);
       part(std::integral_constant<int, 4 * C + m>());
       __builtin_amdgcn_sched_barrier(0);
-      if (mma) {
+      // a row tile with no valid row (the ragged end of an expert's group) skips its instructions
+      if (mma && 16 * m < rows_valid) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[m][t] = mx6_mfma<0, C>(cur.p[0], bo[t], acc[m][t], cur.s, br.s[t]);
 #pragma unroll
@@ -327,7 +329,7 @@ gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restr
   const Fp4Masks fm = fp4_masks();
   const KLoads<A6Tile> ld{xq, aoff, codes, scales, tb0, nkt, w, lane};
   k_loop<A6Tile>(lds, ld, nkt, wave_active, [&](const uint8_t* abuf, const BRegs& br, auto part, bool mma) {
-    a6_ktile(acc, abuf, br, part, mma, lane, fm);
+    a6_ktile(acc, abuf, br, part, mma, rows_valid, lane, fm);
   });
   if (!wave_active) return;
 
@@ -388,7 +390,7 @@ gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict
   const Fp4Masks fm = fp4_masks();
   const KLoads<A6Tile> ld{aq, aoff, codes, scales, tb0, nkt, w, lane};
   k_loop<A6Tile>(lds, ld, nkt, wave_active, [&](const uint8_t* abuf, const BRegs& br, auto part, bool mma) {
-    a6_ktile(acc, abuf, br, part, mma, lane, fm);
+    a6_ktile(acc, abuf, br, part, mma, rows_valid, lane, fm);
   });
   if (!wave_active) return;
 
