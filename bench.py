@@ -20,6 +20,7 @@ The JSON line also carries:
   per_batch     - per-T forward time and whole-forward algorithmic HBM rate;
   prefill       - the 8192-token prefill workload (K=6144, Zipf(1.1) routing): tokens/s and matrix
                   core rate of the two grouped GEMMs against the dense bf16/fp16 peak;
+  slots         - the expert-slot forward against the plain forward at T=8 and 32;
   cpu_baseline  - the f64 CPU oracle on a bounded sample of the same workload.
 """
 import argparse
@@ -51,6 +52,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-iters", type=int, default=5)
     ap.add_argument("--no-requant", action="store_true")
+    ap.add_argument("--no-slots", action="store_true")
     ap.add_argument("--requant-iters", type=int, default=5)
     ap.add_argument("--eager", action="store_true",
                     help="launch every timed call from Python instead of replaying HIP graphs (for profilers)")
@@ -291,6 +293,8 @@ def main():
         "source_hash": src_hash,
     }
 
+    if not args.no_slots:
+        out["slots"] = bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K)
     if not args.no_prefill:
         out["prefill"] = bench_prefill(args, moe, workloads, torch, dev)
     if not args.no_requant:
@@ -300,6 +304,71 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(canon, inst)
     print(json.dumps(out), flush=True)
+
+
+def bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K):
+    """Expert-slot forward (moe_w2_forward_slots) on the decode workload: every expert resident in
+    a permuted slot (so each call streams what moe_w2_forward streams), against moe_w2_forward on
+    expert-ordered planes, both timed as graphs of back-to-back calls over two plane copies. The
+    difference is the cost of the id -> slot pass; the outputs are compared bit for bit."""
+    rng = np.random.default_rng(11)
+    K_, I = canon["gu_codes"].shape[2] * 4, canon["gu_codes"].shape[1] // 2
+    plain, slotted = [], []
+    for c in range(2):
+        d_canon = [dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")]
+        plain.append(moe.moe_w2_pack(*d_canon))
+        perm = rng.permutation(E).astype(np.int32)
+        h = moe.moe_w2_planes_create(E, K_, I)
+        for e in range(E):
+            moe.moe_w2_pack_slot(h, int(perm[e]), *[t[e] for t in d_canon])
+        slotted.append((h, dev(perm)))
+        del d_canon
+    torch.cuda.empty_cache()
+    stream = torch.cuda.current_stream()
+    n_rep = max(2, args.steps)
+    res = {}
+    for T in (8, 32):
+        R = len(inst[T])
+        ws = [moe.alloc_workspace(plain[0], T, top_k) for _ in range(R)]
+        y = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+        y2 = torch.empty_like(y)
+        d0 = inst[T][0]
+        moe.moe_w2_forward(plain[0], d0["x"], d0["ids"], d0["w"], workspace=ws[0], y=y)
+        moe.moe_w2_forward_slots(slotted[0][0], slotted[0][1], d0["x"], d0["ids"], d0["w"], workspace=ws[1 % R], y=y2)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(y.view(torch.int16), y2.view(torch.int16)))
+        out = {"forward": [], "forward_slots": []}
+        for name in ("forward", "forward_slots") * 3:   # alternated; medians reported
+            def loop():
+                for k in range(n_rep):
+                    d = inst[T][k % R]
+                    if name == "forward":
+                        moe.moe_w2_forward(plain[k % 2], d["x"], d["ids"], d["w"], workspace=ws[k % R], y=y)
+                    else:
+                        h, m = slotted[k % 2]
+                        moe.moe_w2_forward_slots(h, m, d["x"], d["ids"], d["w"], workspace=ws[k % R], y=y)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                loop()
+            g.replay()
+            torch.cuda.synchronize()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            g.replay()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            out[name].append(a0.elapsed_time(a1) / n_rep * 1e3)
+        f, fs = float(np.median(out["forward"])), float(np.median(out["forward_slots"]))
+        res[f"T{T}"] = dict(fwd_us=round(f, 2), slots_fwd_us=round(fs, 2), slot_pass_us=round(fs - f, 2),
+                            bit_identical=same)
+        del ws
+    for h, _ in slotted:
+        h.free()
+    for h in plain:
+        h.free()
+    torch.cuda.empty_cache()
+    return dict(workload="moe_w2_forward_slots: decode layer K=4096 I=2048 E=256 top-8, all experts "
+                         "resident in permuted slots", **res)
 
 
 def bench_prefill(args, moe, workloads, torch, dev):

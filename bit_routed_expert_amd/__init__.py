@@ -5,7 +5,8 @@ torch device tensors' pointers and the current HIP stream to the C ABI and turns
 exceptions. There is no fallback: if the library is missing or no GPU is present, calls fail.
 
 Functions keep the C names: moe_w2_pack, moe_w2_unpack, moe_w2_workspace_bytes, moe_w2_route,
-moe_w2_forward, moe_w2_read_counters, nvfp4_to_w2.
+moe_w2_forward, moe_w2_read_counters, nvfp4_to_w2, and the expert-slot entry points
+moe_w2_planes_create, moe_w2_pack_slot, moe_w2_forward_slots, moe_w2_read_miss_counter.
 """
 import ctypes
 import os
@@ -53,6 +54,10 @@ def _lib():
             "moe_w2_forward_stage": ([P, I32, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
             "moe_w2_read_counters": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), P], I32),
             "nvfp4_to_w2": ([I32, I32, I32, P, P, P, P, P, P], I32),
+            "moe_w2_planes_create": ([I32, I32, I32, P, ctypes.POINTER(P)], I32),
+            "moe_w2_pack_slot": ([P, I32, P, P, P, P, P], I32),
+            "moe_w2_forward_slots": ([P, I32, P, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
+            "moe_w2_read_miss_counter": ([P, ctypes.POINTER(ctypes.c_int64), P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -191,6 +196,51 @@ def moe_w2_read_counters(workspace):
     _check(_lib().moe_w2_read_counters(_dev(workspace, torch.uint8, "workspace"), ctypes.byref(inv), ctypes.byref(ovf),
                                        _stream()), "moe_w2_read_counters")
     return inv.value, ovf.value
+
+
+def moe_w2_planes_create(S, K, I):
+    """Planes of S empty expert slots (contents unspecified until moe_w2_pack_slot)."""
+    h = ctypes.c_void_p()
+    _check(_lib().moe_w2_planes_create(int(S), int(K), int(I), _stream(), ctypes.byref(h)), "moe_w2_planes_create")
+    return Planes(h, S, K, I)
+
+
+def moe_w2_pack_slot(planes, slot, gu_codes, gu_scales, dn_codes, dn_scales):
+    """One expert's canonical device planes (gu_codes [2I, K/4], gu_scales [2I, K/32], dn_codes [K, I/4],
+    dn_scales [K, I/32], uint8) into slot `slot`."""
+    K, I = planes.K, planes.I
+    if tuple(gu_codes.shape) != (2 * I, K // 4) or tuple(gu_scales.shape) != (2 * I, K // 32) \
+            or tuple(dn_codes.shape) != (K, I // 4) or tuple(dn_scales.shape) != (K, I // 32):
+        raise ValueError("inconsistent plane shapes")
+    _check(_lib().moe_w2_pack_slot(planes.handle, int(slot), _dev(gu_codes, torch.uint8, "gu_codes"),
+                                   _dev(gu_scales, torch.uint8, "gu_scales"), _dev(dn_codes, torch.uint8, "dn_codes"),
+                                   _dev(dn_scales, torch.uint8, "dn_scales"), _stream()), "moe_w2_pack_slot")
+
+
+def moe_w2_forward_slots(planes, slot_of_expert, x, topk_ids, topk_w, out_dtype=OUT_BF16, workspace=None,
+                         path=PATH_AUTO, y=None):
+    """moe_w2_forward over experts reached through slot_of_expert [E] int32 (device; entries outside
+    [0, planes.E) = not resident)."""
+    T, K = x.shape
+    top_k = topk_ids.shape[1]
+    E = slot_of_expert.shape[0]
+    if workspace is None:
+        workspace = alloc_workspace(planes, T, top_k)
+    if y is None:
+        y = torch.empty((T, K), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32, device="cuda")
+    _check(_lib().moe_w2_forward_slots(planes.handle, E, _dev(slot_of_expert, torch.int32, "slot_of_expert"), T, top_k,
+                                       _dev(x, torch.bfloat16, "x"), _dev(topk_ids, torch.int32, "topk_ids"),
+                                       _dev(topk_w, torch.float32, "topk_w"), ctypes.c_void_p(y.data_ptr()),
+                                       int(out_dtype), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                       int(path), _stream()), "moe_w2_forward_slots")
+    return y
+
+
+def moe_w2_read_miss_counter(workspace):
+    m = ctypes.c_int64(0)
+    _check(_lib().moe_w2_read_miss_counter(_dev(workspace, torch.uint8, "workspace"), ctypes.byref(m), _stream()),
+           "moe_w2_read_miss_counter")
+    return m.value
 
 
 def nvfp4_to_w2(e2m1, e4m3, scale_2, codes=None, scales=None):

@@ -14,7 +14,7 @@ Workspace workspace_layout(int E, int K, int I, int T, int top_k) {
   w.P = P;
   w.max_tiles = P > 0 ? P / kGemmBM + (E < P ? E : P) + 1 : 0;
   size_t o = 0;
-  w.counters = o;  o += align_up(2 * sizeof(long long));
+  w.counters = o;  o += align_up(3 * sizeof(long long));
   w.offsets = o;   o += align_up((size_t)(E + 1) * 4);
   w.perm = o;      o += align_up((size_t)P * 4);
   w.active = o;    o += align_up((size_t)E * 4);
@@ -28,6 +28,7 @@ Workspace workspace_layout(int E, int K, int I, int T, int top_k) {
   w.act = o;       o += align_up((size_t)P * I * 2);
   w.aq = o;        o += align_up((size_t)P * (I / kTileK) * kA6Bytes);
   w.pair_out = o;  o += align_up((size_t)P * K * 4);
+  w.slot_ids = o;  o += align_up((size_t)P * 4);
   w.total = o;
   return w;
 }
@@ -41,6 +42,63 @@ static bool shape_ok(int E, int K, int I) {
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_W2_OK : MOE_W2_EHIP; }
 
+// One device allocation holding E experts' (or slots') native planes and the validation flag.
+static int planes_alloc(int E, int K, int I, moe_w2_planes** out) {
+  const size_t n_gu = (size_t)E * 2 * I * K;
+  const size_t n_dn = (size_t)E * K * I;
+  size_t o = 0;
+  const size_t o_guc = o; o += align_up(n_gu / 4);
+  const size_t o_gus = o; o += align_up(n_gu / 32);
+  const size_t o_dnc = o; o += align_up(n_dn / 4);
+  const size_t o_dns = o; o += align_up(n_dn / 32);
+  const size_t o_flag = o; o += align_up(4);
+  moe_w2_planes* p = new (std::nothrow) moe_w2_planes;
+  if (!p) return MOE_W2_ENOMEM;
+  memset(p, 0, sizeof(*p));
+  p->E = E; p->K = K; p->I = I;
+  if (hipGetDevice(&p->device) != hipSuccess) { delete p; return MOE_W2_EHIP; }
+  if (hipMalloc(&p->base, o) != hipSuccess) { (void)hipGetLastError(); delete p; return MOE_W2_ENOMEM; }
+  p->bytes = o;
+  uint8_t* b = (uint8_t*)p->base;
+  p->gu_codes = b + o_guc; p->gu_scales = b + o_gus;
+  p->dn_codes = b + o_dnc; p->dn_scales = b + o_dns;
+  p->flag = (int32_t*)(b + o_flag);
+  *out = p;
+  return MOE_W2_OK;
+}
+
+// Reads the pack validation flag (synchronous).
+static int pack_status(const moe_w2_planes* p, hipError_t err, hipStream_t s) {
+  int32_t flag = 0;
+  if (err == hipSuccess) err = hipMemcpyAsync(&flag, p->flag, 4, hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return MOE_W2_EHIP;
+  return (flag & kFlagScale) ? MOE_W2_ESCALE : MOE_W2_OK;
+}
+
+// Host-side checks shared by every forward entry point (nothing is enqueued).
+static int forward_check(const moe_w2_planes* p, int T, int top_k, const void* x, const int32_t* topk_ids,
+                         const float* topk_w, const void* y, int out_dtype, const void* workspace,
+                         size_t workspace_bytes, int path) {
+  if (!p || T < 0 || top_k < 1) return MOE_W2_EINVAL;
+  if (top_k > 32) return MOE_W2_EUNSUPPORTED;
+  if (out_dtype != MOE_W2_OUT_BF16 && out_dtype != MOE_W2_OUT_F32) return MOE_W2_EINVAL;
+  if (path != MOE_W2_PATH_AUTO && path != MOE_W2_PATH_DECODE && path != MOE_W2_PATH_GEMM) return MOE_W2_EINVAL;
+  if (T > 0 && (!x || !topk_ids || !topk_w || !y)) return MOE_W2_EINVAL;
+  if ((long long)T * top_k > (1LL << 30)) return MOE_W2_EUNSUPPORTED;
+  if ((long long)T * p->K >= (1LL << 31) || (long long)T * top_k * p->I >= (1LL << 31))
+    return MOE_W2_EUNSUPPORTED;  // the GEMM kernels index x and the intermediate in 32 bits
+  if ((long long)T * (p->K / kTileK) * kA6Bytes >= (1LL << 32) ||
+      (long long)T * top_k * (p->I / kTileK) * kA6Bytes >= (1LL << 32))
+    return MOE_W2_EUNSUPPORTED;  // ... and their split copies with 32-bit byte offsets
+  const Workspace ws = workspace_layout(p->E, p->K, p->I, T, top_k);
+  if (!workspace || workspace_bytes < ws.total) return MOE_W2_EWORKSPACE;
+  const bool decode = path == MOE_W2_PATH_DECODE ||
+                      (path == MOE_W2_PATH_AUTO && (long long)T * top_k <= kDecodeMaxPairs);
+  // every decode workgroup scans all ids itself (two per thread)
+  if (decode && (long long)T * top_k > kDecodeMaxPairs) return MOE_W2_EUNSUPPORTED;
+  return MOE_W2_OK;
+}
 }  // namespace moew2
 
 using namespace moew2;
@@ -72,33 +130,30 @@ int moe_w2_pack(int E, int K, int I, const uint8_t* gu_codes, const uint8_t* gu_
   if (E < 0 || K < 0 || I < 0) return MOE_W2_EINVAL;
   if (!shape_ok(E, K, I)) return MOE_W2_EUNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
-  const size_t n_gu = (size_t)E * 2 * I * K;
-  const size_t n_dn = (size_t)E * K * I;
-  size_t o = 0;
-  const size_t o_guc = o; o += align_up(n_gu / 4);
-  const size_t o_gus = o; o += align_up(n_gu / 32);
-  const size_t o_dnc = o; o += align_up(n_dn / 4);
-  const size_t o_dns = o; o += align_up(n_dn / 32);
-  const size_t o_flag = o; o += align_up(4);
-  moe_w2_planes* p = new (std::nothrow) moe_w2_planes;
-  if (!p) return MOE_W2_ENOMEM;
-  memset(p, 0, sizeof(*p));
-  p->E = E; p->K = K; p->I = I;
-  if (hipGetDevice(&p->device) != hipSuccess) { delete p; return MOE_W2_EHIP; }
-  if (hipMalloc(&p->base, o) != hipSuccess) { (void)hipGetLastError(); delete p; return MOE_W2_ENOMEM; }
-  p->bytes = o;
-  uint8_t* b = (uint8_t*)p->base;
-  p->gu_codes = b + o_guc; p->gu_scales = b + o_gus;
-  p->dn_codes = b + o_dnc; p->dn_scales = b + o_dns;
-  p->flag = (int32_t*)(b + o_flag);
-  hipError_t err = launch_pack(p, gu_codes, gu_scales, dn_codes, dn_scales, s);
-  int32_t flag = 0;
-  if (err == hipSuccess) err = hipMemcpyAsync(&flag, p->flag, 4, hipMemcpyDeviceToHost, s);
-  if (err == hipSuccess) err = hipStreamSynchronize(s);
-  if (err != hipSuccess) { (void)hipFree(p->base); delete p; return MOE_W2_EHIP; }
-  if (flag & kFlagScale) { (void)hipFree(p->base); delete p; return MOE_W2_ESCALE; }
+  moe_w2_planes* p = nullptr;
+  int st = planes_alloc(E, K, I, &p);
+  if (st != MOE_W2_OK) return st;
+  st = pack_status(p, launch_pack(p, gu_codes, gu_scales, dn_codes, dn_scales, s), s);
+  if (st != MOE_W2_OK) { (void)hipFree(p->base); delete p; return st; }
   *out = p;
   return MOE_W2_OK;
+}
+
+int moe_w2_planes_create(int S, int K, int I, void* stream, moe_w2_planes** out) {
+  (void)stream;
+  if (!out) return MOE_W2_EINVAL;
+  *out = nullptr;
+  if (S < 0 || K < 0 || I < 0) return MOE_W2_EINVAL;
+  if (!shape_ok(S, K, I)) return MOE_W2_EUNSUPPORTED;
+  return planes_alloc(S, K, I, out);
+}
+
+int moe_w2_pack_slot(moe_w2_planes* p, int slot, const uint8_t* gu_codes, const uint8_t* gu_scales,
+                     const uint8_t* dn_codes, const uint8_t* dn_scales, void* stream) {
+  if (!p || !gu_codes || !gu_scales || !dn_codes || !dn_scales) return MOE_W2_EINVAL;
+  if (slot < 0 || slot >= p->E) return MOE_W2_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  return pack_status(p, launch_pack_experts(p, slot, 1, gu_codes, gu_scales, dn_codes, dn_scales, s), s);
 }
 
 int moe_w2_unpack(const moe_w2_planes* p, uint8_t* gu_codes, uint8_t* gu_scales,
@@ -162,27 +217,15 @@ int moe_w2_route(int E, int T, int top_k, const int32_t* topk_ids, int32_t* offs
 int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, const void* x,
                          const int32_t* topk_ids, const float* topk_w, void* y, int out_dtype,
                          void* workspace, size_t workspace_bytes, int path, void* stream) {
-  if (!p || T < 0 || top_k < 1) return MOE_W2_EINVAL;
   if (stage < MOE_W2_STAGE_ROUTE || stage > MOE_W2_STAGE_COMBINE) return MOE_W2_EINVAL;
-  if (top_k > 32) return MOE_W2_EUNSUPPORTED;
-  if (out_dtype != MOE_W2_OUT_BF16 && out_dtype != MOE_W2_OUT_F32) return MOE_W2_EINVAL;
-  if (path != MOE_W2_PATH_AUTO && path != MOE_W2_PATH_DECODE && path != MOE_W2_PATH_GEMM) return MOE_W2_EINVAL;
-  if (T > 0 && (!x || !topk_ids || !topk_w || !y)) return MOE_W2_EINVAL;
-  if ((long long)T * top_k > (1LL << 30)) return MOE_W2_EUNSUPPORTED;
-  if ((long long)T * p->K >= (1LL << 31) || (long long)T * top_k * p->I >= (1LL << 31))
-    return MOE_W2_EUNSUPPORTED;  // the GEMM kernels index x and the intermediate in 32 bits
-  if ((long long)T * (p->K / kTileK) * kA6Bytes >= (1LL << 32) ||
-      (long long)T * top_k * (p->I / kTileK) * kA6Bytes >= (1LL << 32))
-    return MOE_W2_EUNSUPPORTED;  // ... and their split copies with 32-bit byte offsets
+  const int st = forward_check(p, T, top_k, x, topk_ids, topk_w, y, out_dtype, workspace, workspace_bytes, path);
+  if (st != MOE_W2_OK) return st;
   const Workspace ws = workspace_layout(p->E, p->K, p->I, T, top_k);
-  if (!workspace || workspace_bytes < ws.total) return MOE_W2_EWORKSPACE;
   if (T == 0) return MOE_W2_OK;
   hipStream_t s = (hipStream_t)stream;
   uint8_t* wsb = (uint8_t*)workspace;
   const bool decode = path == MOE_W2_PATH_DECODE ||
                       (path == MOE_W2_PATH_AUTO && (long long)T * top_k <= kDecodeMaxPairs);
-  // every decode workgroup scans all ids itself (two per thread)
-  if (decode && (long long)T * top_k > kDecodeMaxPairs) return MOE_W2_EUNSUPPORTED;
   // the decode kernels find their pairs from the ids themselves (no routing pass); the direct
   // organisation also combines inside the down stage
   const bool direct = decode && (long long)T * top_k <= kDirectMaxPairs;
@@ -228,6 +271,35 @@ int moe_w2_forward(const moe_w2_planes* p, int T, int top_k, const void* x, cons
                                   workspace_bytes, path, stream);
     if (st != MOE_W2_OK) return st;
   }
+  return MOE_W2_OK;
+}
+
+int moe_w2_forward_slots(const moe_w2_planes* p, int E, const int32_t* slot_of_expert, int T, int top_k,
+                         const void* x, const int32_t* topk_ids, const float* topk_w, void* y, int out_dtype,
+                         void* workspace, size_t workspace_bytes, int path, void* stream) {
+  if (E < 1) return MOE_W2_EINVAL;
+  if (E > (1 << 30)) return MOE_W2_EUNSUPPORTED;
+  if (T > 0 && !slot_of_expert) return MOE_W2_EINVAL;
+  int st = forward_check(p, T, top_k, x, topk_ids, topk_w, y, out_dtype, workspace, workspace_bytes, path);
+  if (st != MOE_W2_OK || T == 0) return st;
+  const Workspace ws = workspace_layout(p->E, p->K, p->I, T, top_k);
+  uint8_t* wsb = (uint8_t*)workspace;
+  int32_t* sids = (int32_t*)(wsb + ws.slot_ids);
+  hipError_t err = launch_slot_ids(T * top_k, E, p->E, topk_ids, slot_of_expert, sids, (long long*)(wsb + ws.counters),
+                                   (hipStream_t)stream);
+  if (err != hipSuccess) return MOE_W2_EHIP;
+  // the forward proper, on the slot ids: the planes' experts are the slots
+  return moe_w2_forward(p, T, top_k, x, sids, topk_w, y, out_dtype, workspace, workspace_bytes, path, stream);
+}
+
+int moe_w2_read_miss_counter(const void* workspace, int64_t* miss_pairs, void* stream) {
+  if (!workspace) return MOE_W2_EINVAL;
+  long long c = 0;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = hipMemcpyAsync(&c, (const long long*)workspace + 2, sizeof(c), hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return MOE_W2_EHIP;
+  if (miss_pairs) *miss_pairs = c;
   return MOE_W2_OK;
 }
 

@@ -29,7 +29,7 @@ enum { kFlagScale = 1 };   // pack: a scale byte above 252
 
 // Workspace layout of one forward.
 struct Workspace {
-  // counters: [0] invalid pairs, [1] act overflow (int64)
+  // counters: [0] invalid pairs, [1] act overflow, [2] slot misses (int64)
   size_t counters;
   size_t offsets;     // int32 [E+1]
   size_t perm;        // int32 [P]
@@ -44,6 +44,7 @@ struct Workspace {
   size_t aq;          // gated intermediate split (GEMM path): one 608-byte three-part e2m3
                       // record per (sorted row, k-tile)
   size_t pair_out;    // fp32 [P][K] per-pair down outputs, indexed by pair id
+  size_t slot_ids;    // int32 [P] the ids mapped to slots (slot forward)
   size_t total;
   int P, nchunks, max_tiles;
 };
@@ -60,6 +61,13 @@ size_t route_scratch_bytes(int E, int P);
 // Launchers (return hipError_t of the launch)
 hipError_t launch_pack(const moe_w2_planes* p, const uint8_t* gu_codes, const uint8_t* gu_scales,
                        const uint8_t* dn_codes, const uint8_t* dn_scales, hipStream_t s);
+hipError_t launch_pack_experts(const moe_w2_planes* p, int e0, int n, const uint8_t* gu_codes,
+                               const uint8_t* gu_scales, const uint8_t* dn_codes, const uint8_t* dn_scales,
+                               hipStream_t s);
+// Slot forward: slot_ids[p] = slot_of_expert[ids[p]] (-1 for ids outside [0, E) and for experts
+// in no slot); counters[2] = number of misses.
+hipError_t launch_slot_ids(int P, int E, int S, const int32_t* ids, const int32_t* slot_of_expert,
+                           int32_t* slot_ids, long long* counters, hipStream_t s);
 hipError_t launch_unpack(const moe_w2_planes* p, uint8_t* gu_codes, uint8_t* gu_scales,
                          uint8_t* dn_codes, uint8_t* dn_scales, hipStream_t s);
 

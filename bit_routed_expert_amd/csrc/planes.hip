@@ -147,25 +147,33 @@ inline unsigned grid_for(long long n, int block) { return (unsigned)((n + block 
 
 }  // namespace
 
-hipError_t launch_pack(const moe_w2_planes* p, const uint8_t* gu_codes, const uint8_t* gu_scales,
-                       const uint8_t* dn_codes, const uint8_t* dn_scales, hipStream_t s) {
-  const int E = p->E, K = p->K, I = p->I;
+// Packs experts [e0, e0 + n) of the planes from canonical planes holding those n experts.
+hipError_t launch_pack_experts(const moe_w2_planes* p, int e0, int n, const uint8_t* gu_codes,
+                               const uint8_t* gu_scales, const uint8_t* dn_codes, const uint8_t* dn_scales,
+                               hipStream_t s) {
+  const int K = p->K, I = p->I;
   const int B = 256;
+  const size_t gu = (size_t)2 * I * K, dn = (size_t)K * I;   // weights per expert
   hipError_t err = hipMemsetAsync(p->flag, 0, sizeof(int32_t), s);
   if (err != hipSuccess) return err;
-  long long n1 = (long long)E * (2 * I / kTileRows) * (K / 256) * 64;
+  long long n1 = (long long)n * (2 * I / kTileRows) * (K / 256) * 64;
   hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for(n1, B)), dim3(B), 0, s,
-                     gu_codes, p->gu_codes, E, 2 * I, K, I, 1);
-  long long n2 = (long long)E * (K / kTileRows) * (I / 256) * 64;
+                     gu_codes, p->gu_codes + (size_t)e0 * gu / 4, n, 2 * I, K, I, 1);
+  long long n2 = (long long)n * (K / kTileRows) * (I / 256) * 64;
   hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for(n2, B)), dim3(B), 0, s,
-                     dn_codes, p->dn_codes, E, K, I, I, 0);
-  long long n3 = (long long)E * (2 * I / kTileRows) * (K / 256) * kTileRows;
+                     dn_codes, p->dn_codes + (size_t)e0 * dn / 4, n, K, I, I, 0);
+  long long n3 = (long long)n * (2 * I / kTileRows) * (K / 256) * kTileRows;
   hipLaunchKernelGGL(pack_scales_kernel, dim3(grid_for(n3, B)), dim3(B), 0, s,
-                     gu_scales, p->gu_scales, E, 2 * I, K, I, 1, p->flag);
-  long long n4 = (long long)E * (K / kTileRows) * (I / 256) * kTileRows;
+                     gu_scales, p->gu_scales + (size_t)e0 * gu / 32, n, 2 * I, K, I, 1, p->flag);
+  long long n4 = (long long)n * (K / kTileRows) * (I / 256) * kTileRows;
   hipLaunchKernelGGL(pack_scales_kernel, dim3(grid_for(n4, B)), dim3(B), 0, s,
-                     dn_scales, p->dn_scales, E, K, I, I, 0, p->flag);
+                     dn_scales, p->dn_scales + (size_t)e0 * dn / 32, n, K, I, I, 0, p->flag);
   return hipGetLastError();
+}
+
+hipError_t launch_pack(const moe_w2_planes* p, const uint8_t* gu_codes, const uint8_t* gu_scales,
+                       const uint8_t* dn_codes, const uint8_t* dn_scales, hipStream_t s) {
+  return launch_pack_experts(p, 0, p->E, gu_codes, gu_scales, dn_codes, dn_scales, s);
 }
 
 hipError_t launch_unpack(const moe_w2_planes* p, uint8_t* gu_codes, uint8_t* gu_scales,

@@ -331,4 +331,45 @@ hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const Route
   return hipGetLastError();
 }
 
+// Slot forward: each pair's expert id becomes its slot index through the device map; a pair
+// whose expert sits in no slot (a miss) or whose id is outside [0, E) gets -1, which every
+// forward path treats as a pair that contributes nothing. One workgroup, so the miss count has a
+// single writer and needs no clearing beforehand (the call can be captured in a graph).
+// Source: the README paragraph on the base cache (a missing expert's contribution is zeroed and
+// an in-graph miss counter bumped).
+namespace {
+constexpr int kSlotThreads = 1024;
+__global__ void __launch_bounds__(kSlotThreads)
+slot_ids_kernel(int P, int E, int S, const int32_t* __restrict__ ids, const int32_t* __restrict__ slot_of_expert,
+                int32_t* __restrict__ slot_ids, long long* __restrict__ counters) {
+  __shared__ int part[kSlotThreads / 64];
+  int miss = 0;
+  for (int p = threadIdx.x; p < P; p += kSlotThreads) {
+    const int id = ids[p];
+    int sl = -1;
+    if (id >= 0 && id < E) {
+      sl = slot_of_expert[id];
+      if (sl < 0 || sl >= S) { sl = -1; ++miss; }
+    }
+    slot_ids[p] = sl;
+  }
+  // wave sums, then one thread writes the total
+  for (int off = 32; off > 0; off >>= 1) miss += __shfl_down(miss, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = miss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long total = 0;
+    for (int i = 0; i < kSlotThreads / 64; ++i) total += part[i];
+    counters[2] = total;
+  }
+}
+}  // namespace
+
+hipError_t launch_slot_ids(int P, int E, int S, const int32_t* ids, const int32_t* slot_of_expert,
+                           int32_t* slot_ids, long long* counters, hipStream_t s) {
+  hipLaunchKernelGGL(slot_ids_kernel, dim3(1), dim3(kSlotThreads), 0, s, P, E, S, ids, slot_of_expert, slot_ids,
+                     counters);
+  return hipGetLastError();
+}
+
 }  // namespace moew2

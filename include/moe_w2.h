@@ -24,7 +24,7 @@
  *    I*K < 2^32;
  *    1 <= E <= 1024; 1 <= top_k <= 32; T >= 0 (T = 0 is a no-op). A forward also needs
  *    T*K < 2^31 and T*top_k*I < 2^31 (element counts of x and of the gated intermediate),
- *    T*(2K + K/16) < 2^32 and T*top_k*(3I + I/8) < 2^32 (bytes of their split copies).
+ *    T*(K/256)*608 < 2^32 and T*top_k*(I/256)*608 < 2^32 (bytes of their split copies).
  *
  * Canonical plane layout (the input of moe_w2_pack, the output of nvfp4_to_w2):
  *  - codes: 4 per byte along the row's reduction axis, element k at bits 2*(k%4)..+1 (LSB
@@ -138,15 +138,18 @@ int moe_w2_route(int E, int T, int top_k, const int32_t* topk_ids,
  *   y        [T][K] bf16 (MOE_W2_OUT_BF16, round-to-nearest-even of the fp32 result) or fp32
  *   workspace: device memory of at least moe_w2_workspace_bytes(planes, T, top_k) bytes; it
  *   must not be shared by forwards that may run concurrently.
- * Arithmetic: both projections run on the block-scaled fp8 x fp4 matrix instruction with fp32
- * accumulation. The weights enter exactly (codes as e2m1 values +-0.5, +-2 under their UE8M0
- * block scale times 2). Each 32-value block of x is split into two e4m3 parts (one hi part and
- * its residual, power-of-two block scales), which hold every bf16 value of the block within
- * 2^-11 of the block's largest magnitude; the gated product silu(g) * u is rounded to fp16 and
- * split into three e4m3 parts, exact for every fp16 value within 2^-10 of its block's largest
- * magnitude. Combine in fp32 with j ascending. The result does not depend on the order in which
- * pairs are processed and repeated calls are bit-identical. An intermediate |silu(g) * u| above
- * the fp16 range becomes +-inf and is counted (act_overflow).
+ * Arithmetic: both projections run on the block-scaled matrix instruction (fp4 weights, fp8 or
+ * fp6 activations) with fp32 accumulation. The weights enter exactly (codes as e2m1 values +-1,
+ * +-4 under their UE8M0 block scale). The gated product silu(g) * u is rounded to fp16; an
+ * intermediate above the fp16 range becomes +-inf and is counted (act_overflow). Activations
+ * enter as parts with power-of-two scales per 32-value block:
+ *  - PATH_DECODE: x as two e4m3 parts, exact for every bf16 value within 2^-11 of its block's
+ *    largest magnitude; the fp16 gated product as three e4m3 parts, exact within 2^-10;
+ *  - PATH_GEMM: x and the fp16 gated product each as three e2m3 parts whose sum is within
+ *    2^-13 of the block's largest magnitude of every value.
+ * Combine in fp32 with j ascending. A pair's result does not depend on which other pairs share
+ * the call, the order in which pairs are processed, or where its expert's planes sit; repeated
+ * calls are bit-identical.
  * Asynchronous; no host synchronisation and no allocation.
  */
 int moe_w2_forward(const moe_w2_planes* planes, int T, int top_k,
@@ -172,6 +175,50 @@ int moe_w2_forward_stage(const moe_w2_planes* planes, int stage, int T, int top_
  */
 int moe_w2_read_counters(const void* workspace, int64_t* invalid_pairs, int64_t* act_overflow,
                          void* stream);
+
+/*
+ * Expert slots: planes of S slots, each holding one expert's planes, and a forward that reaches
+ * experts through a device map expert -> slot. Source: the README paragraph on the base cache
+ * (the GPU holds a cache of hot experts in the slot machinery; a missing expert's contribution
+ * is zeroed and an in-graph miss counter bumped; after the missing experts are fetched the step
+ * is replayed, bit-identical to a fully resident forward); "The v0.24.0 port", section "Our
+ * hooks", BASE cache bullet (slot table, four sections per expert slot); "vLLM-Moet: a 2-bit
+ * expert patch and a three-tier expert cache on SM120", section "A cache miss costs a replay".
+ *
+ * moe_w2_planes_create - planes of S empty slots for K and I (contents unspecified until packed).
+ * Synchronous. On failure *out is NULL.
+ */
+int moe_w2_planes_create(int S, int K, int I, void* stream, moe_w2_planes** out);
+
+/*
+ * moe_w2_pack_slot - pack one expert's canonical planes into slot `slot` of `planes`:
+ *   gu_codes [2I][K/4]  gu_scales [2I][K/32]  dn_codes [K][I/4]  dn_scales [K][I/32]
+ * (the layout of one expert of moe_w2_pack). Synchronous (validates the scale bytes); on
+ * MOE_W2_ESCALE the slot's contents are unspecified. Must not overlap a forward that reads the
+ * slot.
+ */
+int moe_w2_pack_slot(moe_w2_planes* planes, int slot,
+                     const uint8_t* gu_codes, const uint8_t* gu_scales,
+                     const uint8_t* dn_codes, const uint8_t* dn_scales, void* stream);
+
+/*
+ * moe_w2_forward_slots - moe_w2_forward over experts 0..E-1 reached through slot_of_expert
+ * [E] int32 (device): expert e's planes are in slot slot_of_expert[e] of `planes` (which has S
+ * slots), or nowhere when the entry is outside [0, S). A pair whose expert is in no slot (a
+ * miss) contributes nothing, like an id outside [0, E); both are counted in invalid_pairs, and
+ * misses alone in the miss counter (moe_w2_read_miss_counter). Every pair whose expert is
+ * resident gets exactly the result moe_w2_forward gives it on planes packed in expert order, so
+ * once the missing experts are packed into slots and the map updated, the same call is
+ * bit-identical to a fully resident forward. Workspace: moe_w2_workspace_bytes(planes, T, top_k).
+ * Other arguments and behaviour as moe_w2_forward. Asynchronous; no allocation.
+ */
+int moe_w2_forward_slots(const moe_w2_planes* planes, int E, const int32_t* slot_of_expert,
+                         int T, int top_k, const void* x, const int32_t* topk_ids,
+                         const float* topk_w, void* y, int out_dtype,
+                         void* workspace, size_t workspace_bytes, int path, void* stream);
+
+/* Misses of the last moe_w2_forward_slots that used `workspace` (synchronous). Host output. */
+int moe_w2_read_miss_counter(const void* workspace, int64_t* miss_pairs, void* stream);
 
 /*
  * nvfp4_to_w2 - load-time re-quantizer NVFP4 -> canonical 2-bit planes.

@@ -119,3 +119,24 @@ def moe_forward_act(x, topk_ids, gu_codes, gu_scales, tokens=None):
         xe = x[tokens[rows]]
         out[rows, js] = silu(xe @ w_gu[:I].T) * (xe @ w_gu[I:].T)
     return out
+
+
+def resident_ids(topk_ids, E, resident):
+    """Expert-cache reading of a forward (README paragraph on the base cache; "The v0.24.0 port",
+    BASE cache bullet): a pair whose expert is not resident contributes nothing and counts as a
+    miss. resident: bool [E]. Returns (ids with the non-resident experts' pairs set to -1, number
+    of misses); ids already outside [0, E) stay invalid and are not misses."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    res = np.asarray(resident, dtype=bool)
+    valid = (ids >= 0) & (ids < E)
+    hit = np.zeros_like(valid)
+    hit[valid] = res[ids[valid]]
+    miss = valid & ~hit
+    return np.where(hit, ids, -1).astype(np.int32), int(miss.sum())
+
+
+def moe_forward_resident(x, topk_ids, topk_w, gu_codes, gu_scales, dn_codes, dn_scales, resident, tokens=None):
+    """The forward with only the resident experts (resident: bool [E]); f64 [len(tokens), K]."""
+    E = gu_codes.shape[0]
+    ids, _ = resident_ids(topk_ids, E, resident)
+    return moe_forward(x, ids, topk_w, gu_codes, gu_scales, dn_codes, dn_scales, tokens)

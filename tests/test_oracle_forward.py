@@ -162,3 +162,33 @@ def test_token_subset_matches_full():
     ys = forward.moe_forward(x, d["topk_ids"], d["topk_w"], tokens=[3, 1], **P)
     # same arithmetic; BLAS may block a smaller batch differently, so allow f64 rounding
     np.testing.assert_allclose(ys, y[[3, 1]], rtol=1e-12, atol=1e-14 * np.abs(y).max())
+
+
+def test_resident_forward_reductions_and_additivity():
+    """Expert-cache reading (README paragraph on the base cache): non-resident experts' pairs
+    contribute nothing. With every expert resident it is the full forward; with none it is zero;
+    and two complementary resident sets add up to the full forward (each pair lands in exactly
+    one of them), which a mask on the wrong index (slot vs expert, token vs pair) breaks."""
+    d, x = _tiny_inputs(5)
+    E = d["gu_codes"].shape[0]
+    args = (d["gu_codes"], d["gu_scales"], d["dn_codes"], d["dn_scales"])
+    full = forward.moe_forward(x, d["topk_ids"], d["topk_w"], *args)
+    assert np.array_equal(forward.moe_forward_resident(x, d["topk_ids"], d["topk_w"], *args, np.ones(E, bool)), full)
+    assert not np.any(forward.moe_forward_resident(x, d["topk_ids"], d["topk_w"], *args, np.zeros(E, bool)))
+    rng = np.random.default_rng(6)
+    for _ in range(4):
+        res = rng.random(E) < 0.5
+        a = forward.moe_forward_resident(x, d["topk_ids"], d["topk_w"], *args, res)
+        b = forward.moe_forward_resident(x, d["topk_ids"], d["topk_w"], *args, ~res)
+        assert np.max(np.abs(a + b - full)) <= 1e-12 * np.max(np.abs(full))
+        assert not np.array_equal(a, full) or res.all() or not np.isin(d["topk_ids"], np.nonzero(~res)[0]).any()
+
+
+def test_resident_ids_hand_example():
+    """Misses are pairs with a valid id whose expert is not resident; invalid ids stay invalid and
+    are not misses."""
+    ids = np.array([[0, 3], [2, -1], [5, 1]], dtype=np.int32)   # E = 4: id 5 and -1 are invalid
+    resident = np.array([True, False, True, False])
+    got, miss = forward.resident_ids(ids, 4, resident)
+    assert np.array_equal(got, np.array([[0, -1], [2, -1], [-1, -1]], dtype=np.int32))
+    assert miss == 2   # ids 3 and 1
