@@ -21,6 +21,7 @@ The JSON line also carries:
   prefill       - the 8192-token prefill workload (K=6144, Zipf(1.1) routing): tokens/s and matrix
                   core rate of the two grouped GEMMs against the dense bf16/fp16 peak;
   slots         - the expert-slot forward against the plain forward at T=8 and 32;
+  w4            - the FP4 (MXFP4) expert planes: decode at T=1, 8, 32 and the prefill GEMMs;
   cpu_baseline  - the f64 CPU oracle on a bounded sample of the same workload.
 """
 import argparse
@@ -53,6 +54,7 @@ def parse():
     ap.add_argument("--prefill-iters", type=int, default=5)
     ap.add_argument("--no-requant", action="store_true")
     ap.add_argument("--no-slots", action="store_true")
+    ap.add_argument("--no-w4", action="store_true")
     ap.add_argument("--requant-iters", type=int, default=5)
     ap.add_argument("--eager", action="store_true",
                     help="launch every timed call from Python instead of replaying HIP graphs (for profilers)")
@@ -295,6 +297,8 @@ def main():
 
     if not args.no_slots:
         out["slots"] = bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K)
+    if not args.no_w4:
+        out["w4"] = bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I)
     if not args.no_prefill:
         out["prefill"] = bench_prefill(args, moe, workloads, torch, dev)
     if not args.no_requant:
@@ -304,6 +308,65 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(canon, inst)
     print(json.dumps(out), flush=True)
+
+
+def w4_expert_bytes(K, I):
+    """Bytes of one expert's FP4 planes: e2m1 codes (4 bits) + one UE8M0 byte per 32 weights."""
+    return 2 * I * K // 2 + 2 * I * K // 32, K * I // 2 + K * I // 32
+
+
+def bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I):
+    """FP4 expert planes on the decode workload (same routing instances and x as the 2-bit decode
+    leg; two plane copies alternated), each T timed as a graph of back-to-back forwards; and the
+    prefill GEMM stages on the 8192-token Zipf workload."""
+    rng = np.random.default_rng(12)
+    layers = []
+    for _ in range(2):
+        canon = workloads.draw_planes_fp4(rng, E, K, I)
+        layers.append(moe.moe_w4_pack(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")]))
+        del canon
+    torch.cuda.empty_cache()
+    gu_b, dn_b = w4_expert_bytes(K, I)
+    stream = torch.cuda.current_stream()
+    n_rep = max(2, args.steps)
+    res, total_us = {}, 0.0
+    for T in DECODE_TS:
+        R = len(inst[T])
+        ws = [moe.alloc_workspace(layers[0], T, top_k) for _ in range(R)]
+        y = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+        nbytes = 0
+        def loop():
+            nb = 0
+            for k in range(n_rep):
+                d = inst[T][k % R]
+                moe.moe_w4_forward(layers[k % 2], d["x"], d["ids"], d["w"], workspace=ws[k % R], y=y)
+                ids = d["ids_np"]
+                na = len(np.unique(ids[(ids >= 0) & (ids < E)]))
+                nb += na * (gu_b + dn_b) + 2 * T * K * 2 + T * top_k * 8
+            return nb
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            nbytes = loop()
+        g.replay()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        g.replay()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        ms = a0.elapsed_time(a1) / n_rep
+        total_us += ms * 1e3
+        res[f"T{T}"] = dict(fwd_us=round(ms * 1e3, 2), fwd_hbm_GBps=round(nbytes / n_rep / (ms * 1e-3) / 1e9, 1),
+                            tokens_per_s=round(T / (ms * 1e-3), 1))
+        del ws
+    for h in layers:
+        h.free()
+    torch.cuda.empty_cache()
+    out = dict(workload="moe_w4 (FP4 e2m1 + UE8M0/32 experts) decode: K=4096 I=2048 E=256 top-8 uniform "
+                        "routing, T=1,8,32", decode_tokens_per_s=round(sum(DECODE_TS) / (total_us * 1e-6), 1), **res)
+    if not args.no_prefill:
+        out["prefill"] = bench_prefill(args, moe, workloads, torch, dev, fp4=True)
+    return out
 
 
 def bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K):
@@ -371,11 +434,15 @@ def bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K):
                          "resident in permuted slots", **res)
 
 
-def bench_prefill(args, moe, workloads, torch, dev):
+def bench_prefill(args, moe, workloads, torch, dev, fp4=False):
     c = workloads.PREFILL
     T, K, I, E, top_k = c["T"], c["K"], c["I"], c["E"], c["top_k"]
-    canon = workloads.zipf_layer(c["seed"], K, I, E)
-    planes = moe.moe_w2_pack(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")])
+    if fp4:
+        canon = workloads.draw_planes_fp4(np.random.default_rng(13), E, K, I)
+        planes = moe.moe_w4_pack(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")])
+    else:
+        canon = workloads.zipf_layer(c["seed"], K, I, E)
+        planes = moe.moe_w2_pack(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")])
     del canon
     d = workloads.zipf_instances(T, 1, c["seed"], K, E, top_k)[0]
     x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).cuda()
@@ -411,7 +478,7 @@ def bench_prefill(args, moe, workloads, torch, dev):
     del planes, ws
     torch.cuda.empty_cache()
     return dict(
-        workload="moe_w2 prefill: T=8192 K=6144 I=2048 E=256 top-8 Zipf(1.1)",
+        workload=("moe_w4 (FP4)" if fp4 else "moe_w2") + " prefill: T=8192 K=6144 I=2048 E=256 top-8 Zipf(1.1)",
         tokens_per_s=round(T / (fwd * 1e-3), 1), fwd_ms=round(float(fwd), 4),
         route_ms=round(float(rt), 4), gate_up_ms=round(float(gu), 4), down_ms=round(float(dn), 4),
         combine_ms=round(float(cb), 4),

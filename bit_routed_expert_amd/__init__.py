@@ -55,6 +55,9 @@ def _lib():
             "moe_w2_read_counters": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), P], I32),
             "nvfp4_to_w2": ([I32, I32, I32, P, P, P, P, P, P], I32),
             "moe_w2_planes_create": ([I32, I32, I32, P, ctypes.POINTER(P)], I32),
+            "moe_w4_pack": ([I32, I32, I32, P, P, P, P, P, ctypes.POINTER(P)], I32),
+            "moe_w4_unpack": ([P, P, P, P, P, P], I32),
+            "moe_w4_forward": ([P, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
             "moe_w2_pack_slot": ([P, I32, P, P, P, P, P], I32),
             "moe_w2_forward_slots": ([P, I32, P, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
             "moe_w2_read_miss_counter": ([P, ctypes.POINTER(ctypes.c_int64), P], I32),
@@ -129,6 +132,48 @@ def moe_w2_pack(gu_codes, gu_scales, dn_codes, dn_scales):
                               _dev(dn_codes, torch.uint8, "dn_codes"), _dev(dn_scales, torch.uint8, "dn_scales"),
                               _stream(), ctypes.byref(h)), "moe_w2_pack")
     return Planes(h, E, K, I)
+
+
+def moe_w4_pack(gu_codes, gu_scales, dn_codes, dn_scales):
+    """Canonical FP4 device planes (uint8) -> Planes. Shapes: gu_codes [E, 2I, K/2] (two e2m1 codes per
+    byte, low nibble = even element), gu_scales [E, 2I, K/32], dn_codes [E, K, I/2], dn_scales [E, K, I/32]."""
+    E, two_i, k2 = gu_codes.shape
+    K, I = k2 * 2, two_i // 2
+    if tuple(gu_scales.shape) != (E, 2 * I, K // 32) or tuple(dn_codes.shape) != (E, K, I // 2) \
+            or tuple(dn_scales.shape) != (E, K, I // 32):
+        raise ValueError("inconsistent plane shapes")
+    h = ctypes.c_void_p()
+    _check(_lib().moe_w4_pack(E, K, I, _dev(gu_codes, torch.uint8, "gu_codes"), _dev(gu_scales, torch.uint8, "gu_scales"),
+                              _dev(dn_codes, torch.uint8, "dn_codes"), _dev(dn_scales, torch.uint8, "dn_scales"),
+                              _stream(), ctypes.byref(h)), "moe_w4_pack")
+    return Planes(h, E, K, I)
+
+
+def moe_w4_unpack(planes):
+    E, K, I = planes.E, planes.K, planes.I
+    d = torch.device("cuda")
+    out = (torch.empty((E, 2 * I, K // 2), dtype=torch.uint8, device=d),
+           torch.empty((E, 2 * I, K // 32), dtype=torch.uint8, device=d),
+           torch.empty((E, K, I // 2), dtype=torch.uint8, device=d),
+           torch.empty((E, K, I // 32), dtype=torch.uint8, device=d))
+    _check(_lib().moe_w4_unpack(planes.handle, *[ctypes.c_void_p(t.data_ptr()) for t in out], _stream()),
+           "moe_w4_unpack")
+    return out
+
+
+def moe_w4_forward(planes, x, topk_ids, topk_w, out_dtype=OUT_BF16, workspace=None, path=PATH_AUTO, y=None):
+    """moe_w2_forward on FP4 planes (moe_w4_pack)."""
+    T, K = x.shape
+    top_k = topk_ids.shape[1]
+    if workspace is None:
+        workspace = alloc_workspace(planes, T, top_k)
+    if y is None:
+        y = torch.empty((T, K), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32, device="cuda")
+    _check(_lib().moe_w4_forward(planes.handle, T, top_k, _dev(x, torch.bfloat16, "x"),
+                                 _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_w, torch.float32, "topk_w"),
+                                 ctypes.c_void_p(y.data_ptr()), int(out_dtype), _dev(workspace, torch.uint8, "workspace"),
+                                 workspace.numel(), int(path), _stream()), "moe_w4_forward")
+    return y
 
 
 def moe_w2_unpack(planes):

@@ -43,19 +43,20 @@ static bool shape_ok(int E, int K, int I) {
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_W2_OK : MOE_W2_EHIP; }
 
 // One device allocation holding E experts' (or slots') native planes and the validation flag.
-static int planes_alloc(int E, int K, int I, moe_w2_planes** out) {
+static int planes_alloc(int E, int K, int I, int fmt, moe_w2_planes** out) {
   const size_t n_gu = (size_t)E * 2 * I * K;
   const size_t n_dn = (size_t)E * K * I;
+  const int cb = code_bits(fmt);
   size_t o = 0;
-  const size_t o_guc = o; o += align_up(n_gu / 4);
+  const size_t o_guc = o; o += align_up(n_gu * cb / 8);
   const size_t o_gus = o; o += align_up(n_gu / 32);
-  const size_t o_dnc = o; o += align_up(n_dn / 4);
+  const size_t o_dnc = o; o += align_up(n_dn * cb / 8);
   const size_t o_dns = o; o += align_up(n_dn / 32);
   const size_t o_flag = o; o += align_up(4);
   moe_w2_planes* p = new (std::nothrow) moe_w2_planes;
   if (!p) return MOE_W2_ENOMEM;
   memset(p, 0, sizeof(*p));
-  p->E = E; p->K = K; p->I = I;
+  p->E = E; p->K = K; p->I = I; p->fmt = fmt;
   if (hipGetDevice(&p->device) != hipSuccess) { delete p; return MOE_W2_EHIP; }
   if (hipMalloc(&p->base, o) != hipSuccess) { (void)hipGetLastError(); delete p; return MOE_W2_ENOMEM; }
   p->bytes = o;
@@ -121,22 +122,35 @@ const char* moe_w2_status_string(int status) {
   }
 }
 
-int moe_w2_pack(int E, int K, int I, const uint8_t* gu_codes, const uint8_t* gu_scales,
-                const uint8_t* dn_codes, const uint8_t* dn_scales, void* stream,
-                moe_w2_planes** out) {
+static int pack_fmt(int fmt, int E, int K, int I, const uint8_t* gu_codes, const uint8_t* gu_scales,
+                    const uint8_t* dn_codes, const uint8_t* dn_scales, void* stream, moe_w2_planes** out) {
   if (!out) return MOE_W2_EINVAL;
   *out = nullptr;
   if (!gu_codes || !gu_scales || !dn_codes || !dn_scales) return MOE_W2_EINVAL;
   if (E < 0 || K < 0 || I < 0) return MOE_W2_EINVAL;
   if (!shape_ok(E, K, I)) return MOE_W2_EUNSUPPORTED;
+  // the decode kernels address one expert's gate_up codes as a buffer of at most 2^31 - 1 bytes
+  if (fmt == kFmtW4 && (long long)I * K >= (1LL << 31)) return MOE_W2_EUNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   moe_w2_planes* p = nullptr;
-  int st = planes_alloc(E, K, I, &p);
+  int st = planes_alloc(E, K, I, fmt, &p);
   if (st != MOE_W2_OK) return st;
   st = pack_status(p, launch_pack(p, gu_codes, gu_scales, dn_codes, dn_scales, s), s);
   if (st != MOE_W2_OK) { (void)hipFree(p->base); delete p; return st; }
   *out = p;
   return MOE_W2_OK;
+}
+
+int moe_w2_pack(int E, int K, int I, const uint8_t* gu_codes, const uint8_t* gu_scales,
+                const uint8_t* dn_codes, const uint8_t* dn_scales, void* stream,
+                moe_w2_planes** out) {
+  return pack_fmt(kFmtW2, E, K, I, gu_codes, gu_scales, dn_codes, dn_scales, stream, out);
+}
+
+int moe_w4_pack(int E, int K, int I, const uint8_t* gu_codes, const uint8_t* gu_scales,
+                const uint8_t* dn_codes, const uint8_t* dn_scales, void* stream,
+                moe_w2_planes** out) {
+  return pack_fmt(kFmtW4, E, K, I, gu_codes, gu_scales, dn_codes, dn_scales, stream, out);
 }
 
 int moe_w2_planes_create(int S, int K, int I, void* stream, moe_w2_planes** out) {
@@ -145,7 +159,7 @@ int moe_w2_planes_create(int S, int K, int I, void* stream, moe_w2_planes** out)
   *out = nullptr;
   if (S < 0 || K < 0 || I < 0) return MOE_W2_EINVAL;
   if (!shape_ok(S, K, I)) return MOE_W2_EUNSUPPORTED;
-  return planes_alloc(S, K, I, out);
+  return planes_alloc(S, K, I, kFmtW2, out);
 }
 
 int moe_w2_pack_slot(moe_w2_planes* p, int slot, const uint8_t* gu_codes, const uint8_t* gu_scales,
@@ -159,6 +173,14 @@ int moe_w2_pack_slot(moe_w2_planes* p, int slot, const uint8_t* gu_codes, const 
 int moe_w2_unpack(const moe_w2_planes* p, uint8_t* gu_codes, uint8_t* gu_scales,
                   uint8_t* dn_codes, uint8_t* dn_scales, void* stream) {
   if (!p || !gu_codes || !gu_scales || !dn_codes || !dn_scales) return MOE_W2_EINVAL;
+  if (p->fmt != kFmtW2) return MOE_W2_EINVAL;
+  return hip_status(launch_unpack(p, gu_codes, gu_scales, dn_codes, dn_scales, (hipStream_t)stream));
+}
+
+int moe_w4_unpack(const moe_w2_planes* p, uint8_t* gu_codes, uint8_t* gu_scales,
+                  uint8_t* dn_codes, uint8_t* dn_scales, void* stream) {
+  if (!p || !gu_codes || !gu_scales || !dn_codes || !dn_scales) return MOE_W2_EINVAL;
+  if (p->fmt != kFmtW4) return MOE_W2_EINVAL;
   return hip_status(launch_unpack(p, gu_codes, gu_scales, dn_codes, dn_scales, (hipStream_t)stream));
 }
 
@@ -290,6 +312,13 @@ int moe_w2_forward_slots(const moe_w2_planes* p, int E, const int32_t* slot_of_e
   if (err != hipSuccess) return MOE_W2_EHIP;
   // the forward proper, on the slot ids: the planes' experts are the slots
   return moe_w2_forward(p, T, top_k, x, sids, topk_w, y, out_dtype, workspace, workspace_bytes, path, stream);
+}
+
+int moe_w4_forward(const moe_w2_planes* p, int T, int top_k, const void* x, const int32_t* topk_ids,
+                   const float* topk_w, void* y, int out_dtype, void* workspace, size_t workspace_bytes,
+                   int path, void* stream) {
+  if (!p || p->fmt != kFmtW4) return MOE_W2_EINVAL;
+  return moe_w2_forward(p, T, top_k, x, topk_ids, topk_w, y, out_dtype, workspace, workspace_bytes, path, stream);
 }
 
 int moe_w2_read_miss_counter(const void* workspace, int64_t* miss_pairs, void* stream) {

@@ -31,6 +31,18 @@ constexpr int kTileK = 256;
 constexpr int kTileCodeBytes = 1024;
 constexpr int kTileScaleBytes = 128;
 
+// FP4 planes (e2m1 codes with UE8M0 block-32 scales, the instruction's own B format) use the same
+// tiles with 2048 code bytes: instruction c's operands at bytes [1024c, 1024c + 1024), lane l's
+// 16 bytes at 1024c + 16l holding the 32 e2m1 values of block 8kt + 4c + l/16 of row l%16 in
+// order (value i in nibble i, low nibble first) - one fully coalesced 1 KiB wave load per
+// instruction. Scale tiles are the 2-bit planes' (byte 2l + c).
+constexpr int kTileCodeBytesW4 = 2048;
+template <int FMT>
+struct WFmt {
+  static constexpr int kCodeBytes = FMT ? kTileCodeBytesW4 : kTileCodeBytes;
+  static constexpr int kLoads = FMT ? 2 : 1;   // 16-byte code loads per lane per tile
+};
+
 // Two e2m1 words (values 0..7 and 8..15 of a native dword, 8 codes each).
 MOEW2_DEV void native_to_fp4(uint32_t dw, uint32_t& blk0, uint32_t& blk1) {
   blk0 = (dw & 0xCCCCCCCCu) | 0x22222222u;
@@ -91,6 +103,28 @@ MOEW2_DEV i32x8_t mx_b_operand(uint32_t d0, uint32_t d1, const Fp4Masks& f) {
   const uint32_t b1 = bfi_sel(f.sel, d1 << 2, f.one);
   i32x8_t v = {(int)a0, (int)a1, (int)b0, (int)b1, 0, 0, 0, 0};
   return v;
+}
+
+// B operand of instruction C of a tile from the lane's code registers: the 2-bit codes expand to
+// e2m1 (W2), the fp4 codes are the operand (W4).
+template <int FMT, int C>
+MOEW2_DEV i32x8_t b_operand(const u32x4_t (&cr)[WFmt<FMT>::kLoads], const Fp4Masks& f) {
+  if constexpr (FMT == 0) {
+    return mx_b_operand(cr[0][2 * C], cr[0][2 * C + 1], f);
+  } else {
+    const u32x4_t& v = cr[C];
+    return i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+  }
+}
+
+template <int FMT, int C>
+MOEW2_DEV i32x8_t b_operand(const u32x4_t (&cr)[WFmt<FMT>::kLoads]) {
+  if constexpr (FMT == 0) {
+    return mx_b_operand(cr[0][2 * C], cr[0][2 * C + 1]);
+  } else {
+    const u32x4_t& v = cr[C];
+    return i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+  }
 }
 
 template <int OPA, int OPB>

@@ -46,30 +46,35 @@ struct WaveTiles {
   uint32_t tile[2];
 };
 
+template <int FMT>
 MOEW2_DEV WaveTiles wave_tiles(const uint8_t* codes, const uint8_t* scales, int e, uint32_t tiles_per_expert) {
+  constexpr uint32_t cb = WFmt<FMT>::kCodeBytes;
   WaveTiles wt;
-  wt.codes = buffer_view(codes + (size_t)e * tiles_per_expert * kTileCodeBytes, tiles_per_expert * kTileCodeBytes);
+  wt.codes = buffer_view(codes + (size_t)e * tiles_per_expert * cb, tiles_per_expert * cb);
   wt.scales = buffer_view(scales + (size_t)e * tiles_per_expert * kTileScaleBytes, tiles_per_expert * kTileScaleBytes);
   return wt;
 }
 
-// Weight tile registers of one k-tile: per row group (NB of them), the lane's 16 code bytes
-// (block layout) and its two scale bytes (instructions 0 and 1 of the k-tile).
-template <int NB>
+// Weight tile registers of one k-tile: per row group (NB of them), the lane's code bytes (16 for
+// 2-bit codes, 2 x 16 for fp4 codes; block layout) and its two scale bytes (instructions 0 and 1
+// of the k-tile).
+template <int NB, int FMT>
 struct TileRegs {
-  u32x4_t c[NB];
+  u32x4_t c[NB][WFmt<FMT>::kLoads];
   uint32_t s[NB];
 };
 
 // The tile's byte offset goes in the scalar offset; the lane's offset (shifted out of range when
 // the tile is not wanted - a wave-uniform condition) in the range-checked vector offset.
-template <int NB>
-MOEW2_DEV void load_tile(TileRegs<NB>& r, const WaveTiles& wt, int kt, bool valid, int lane) {
+template <int NB, int FMT>
+MOEW2_DEV void load_tile(TileRegs<NB, FMT>& r, const WaveTiles& wt, int kt, bool valid, int lane) {
   const uint32_t oob = valid ? 0u : kOutOfRange;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const uint32_t t = wt.tile[b] + (uint32_t)kt;
-    r.c[b] = buf_ld16_nt(wt.codes, (16u * (uint32_t)lane) | oob, t * kTileCodeBytes);
+#pragma unroll
+    for (int q = 0; q < WFmt<FMT>::kLoads; ++q)
+      r.c[b][q] = buf_ld16_nt(wt.codes, (16u * (uint32_t)lane) | oob, t * WFmt<FMT>::kCodeBytes + 1024u * q);
     r.s[b] = buf_ld2_nt(wt.scales, (2u * (uint32_t)lane) | oob, t * kTileScaleBytes);
   }
 }
@@ -170,8 +175,8 @@ MOEW2_DEV i32x8_t a_operand(const uint8_t* part, int c, int g) {
 }
 
 // Instruction C (0, 1) of one k-tile for the NB row groups, all NP parts.
-template <int C, int NP, int NB>
-MOEW2_DEV void mma_chunk(const TileRegs<NB>& r, const uint8_t* kbase, int KR, uint32_t w0, uint32_t w1, int g,
+template <int C, int NP, int NB, int FMT>
+MOEW2_DEV void mma_chunk(const TileRegs<NB, FMT>& r, const uint8_t* kbase, int KR, uint32_t w0, uint32_t w1, int g,
                          f32x4_t* acc) {
   const i32x8_t a0 = a_operand(kbase, C, g);
   const i32x8_t a1 = a_operand(kbase + KR, C, g);
@@ -179,7 +184,7 @@ MOEW2_DEV void mma_chunk(const TileRegs<NB>& r, const uint8_t* kbase, int KR, ui
   if (NP == 3) a2 = a_operand(kbase + 2 * KR, C, g);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const i32x8_t bo = mx_b_operand(r.c[b][2 * C], r.c[b][2 * C + 1]);
+    const i32x8_t bo = b_operand<FMT, C>(r.c[b]);
     acc[b] = mx_mfma<C, C>(a0, bo, acc[b], w0, r.s[b]);
     acc[b] = mx_mfma<2 + C, C>(a1, bo, acc[b], w0, r.s[b]);
     if (NP == 3) acc[b] = mx_mfma<C, C>(a2, bo, acc[b], w1, r.s[b]);
@@ -187,34 +192,34 @@ MOEW2_DEV void mma_chunk(const TileRegs<NB>& r, const uint8_t* kbase, int KR, ui
 }
 
 // One k-tile from the lane's staged row `arow`.
-template <int NP, int NB>
-MOEW2_DEV void mma_tile(const TileRegs<NB>& r, const uint8_t* arow, int KR, int kt, int g, f32x4_t* acc) {
+template <int NP, int NB, int FMT>
+MOEW2_DEV void mma_tile(const TileRegs<NB, FMT>& r, const uint8_t* arow, int KR, int kt, int g, f32x4_t* acc) {
   const uint8_t* kbase = arow + kt * kTileK;
   const uint8_t* sw = arow + NP * KR + (kt * 4 + g) * MxRow<NP>::kSW;
   const uint32_t w0 = *reinterpret_cast<const uint32_t*>(sw);
   const uint32_t w1 = NP == 3 ? *reinterpret_cast<const uint32_t*>(sw + 4) : 0u;
-  mma_chunk<0, NP, NB>(r, kbase, KR, w0, w1, g, acc);
-  mma_chunk<1, NP, NB>(r, kbase, KR, w0, w1, g, acc);
+  mma_chunk<0, NP, NB, FMT>(r, kbase, KR, w0, w1, g, acc);
+  mma_chunk<1, NP, NB, FMT>(r, kbase, KR, w0, w1, g, acc);
 }
 
 // ring[i] <- k-tile kb + i for i in [I0, I1) (out-of-range requests past ke)
-template <int NB, int I0 = 0, int I1 = kRing>
-MOEW2_DEV void prime_ring(TileRegs<NB> (&ring)[kRing], const WaveTiles& wt, int kb, int ke, int lane) {
+template <int NB, int FMT, int I0 = 0, int I1 = kRing>
+MOEW2_DEV void prime_ring(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt, int kb, int ke, int lane) {
 #pragma unroll
-  for (int i = I0; i < I1; ++i) load_tile<NB>(ring[i], wt, kb + i, kb + i < ke, lane);
+  for (int i = I0; i < I1; ++i) load_tile<NB, FMT>(ring[i], wt, kb + i, kb + i < ke, lane);
 }
 
 // Consume k-tiles [kb, ke) from the primed ring; each consumed slot is refilled with the tile
 // kRing further on (or an out-of-range request), so every iteration issues the same loads.
-template <int NP, int NB>
-MOEW2_DEV void stream_k(TileRegs<NB> (&ring)[kRing], const WaveTiles& wt, int kb, int ke, const uint8_t* arow,
+template <int NP, int NB, int FMT>
+MOEW2_DEV void stream_k(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt, int kb, int ke, const uint8_t* arow,
                         int KR, int g, f32x4_t* acc, int lane) {
   for (int k0 = kb; k0 < ke; k0 += kRing) {
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       const int kt = k0 + i;
-      if (kt < ke) mma_tile<NP, NB>(ring[i], arow, KR, kt, g, acc);
-      load_tile<NB>(ring[i], wt, kt + kRing, kt + kRing < ke, lane);
+      if (kt < ke) mma_tile<NP, NB, FMT>(ring[i], arow, KR, kt, g, acc);
+      load_tile<NB, FMT>(ring[i], wt, kt + kRing, kt + kRing < ke, lane);
     }
   }
 }
@@ -231,8 +236,8 @@ MOEW2_DEV void stream_k(TileRegs<NB> (&ring)[kRing], const WaveTiles& wt, int kb
 // priming the whole ring first puts the entire weight volume in the memory queues ahead of those
 // row loads; committing first leaves the memory idle while every workgroup waits for the same
 // rows. Half and half keeps half the weights streaming while the rows arrive.
-template <int NT, int NP, int NB, int SPLIT = kRing, class RowOff>
-MOEW2_DEV void stage_and_prime(TileRegs<NB> (&ring)[kRing], const WaveTiles& wt, int kb, int ke, int lane,
+template <int NT, int NP, int NB, int FMT, int SPLIT = kRing, class RowOff>
+MOEW2_DEV void stage_and_prime(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt, int kb, int ke, int lane,
                                uint8_t* lds, int stride, const uint16_t* src, int KR, int n, RowOff row_off,
                                int tid, bool count_inf, int& ninf) {
   int st_tid = tid;
@@ -243,10 +248,10 @@ MOEW2_DEV void stage_and_prime(TileRegs<NB> (&ring)[kRing], const WaveTiles& wt,
     stage_commit_split<NT, NP>(st, lds, stride, KR, n, base, st_tid, count_inf, ninf);
   }
   stage_issue<NT>(st, src, KR, n, 0, row_off, st_tid);
-  prime_ring<NB, 0, SPLIT>(ring, wt, kb, ke, lane);
+  prime_ring<NB, FMT, 0, SPLIT>(ring, wt, kb, ke, lane);
   __builtin_amdgcn_sched_barrier(0);   // the first ring loads go out before the commit waits
   stage_commit_split<NT, NP>(st, lds, stride, KR, n, 0, st_tid, count_inf, ninf);
-  prime_ring<NB, SPLIT, kRing>(ring, wt, kb, ke, lane);
+  prime_ring<NB, FMT, SPLIT, kRing>(ring, wt, kb, ke, lane);
 }
 
 // Cross-wave sum of split-K partial accumulators (KS waves per row pair) into the ks == 0 wave.
@@ -354,7 +359,7 @@ MOEW2_DEV int pair_at(const ScanLds& sh, int m) {
 // ids[blockIdx.y] when blockIdx.y is the first of them (pair_group). The gated row of pair p is
 // act[p] in both.
 // ---------------------------------------------------------------------------------------------
-template <int NPW, bool DIRECT>
+template <int NPW, bool DIRECT, int FMT>
 __global__ void __launch_bounds__(kThreads)
 decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                       const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
@@ -381,13 +386,13 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
   const int nkt = K / kTileK, nrg = 2 * I / kTileRows;
   const int pw = w / KS, ks = w % KS;
   const int q = blockIdx.x * NPW + pw;
-  WaveTiles wt = wave_tiles(codes, scales, e, (uint32_t)(nrg * nkt));
+  WaveTiles wt = wave_tiles<FMT>(codes, scales, e, (uint32_t)(nrg * nkt));
   wt.tile[0] = (uint32_t)(2 * q * nkt);
   wt.tile[1] = (uint32_t)((2 * q + 1) * nkt);
   const int kb = ks * nkt / KS, ke = valid ? (ks + 1) * nkt / KS : kb;
   const int stride = MxRow<2>::stride(K);
   float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][2][4][16]
-  TileRegs<2> ring[kRing];
+  TileRegs<2, FMT> ring[kRing];
   for (int c0 = 0; c0 < n_total; c0 += kChunk) {
     const int n = min(kChunk, n_total - c0);
     // pair and token of each staged row (the same in every lane)
@@ -399,12 +404,12 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
       return (size_t)(pp / top_k) * K;
     };
     int ninf = 0;
-    stage_and_prime<kThreads, 2, 2, DIRECT ? kRing / 2 : kRing>(ring, wt, kb, ke, lane, lds, stride, x, K, n,
+    stage_and_prime<kThreads, 2, 2, FMT, DIRECT ? kRing / 2 : kRing>(ring, wt, kb, ke, lane, lds, stride, x, K, n,
                                                                 row_off, tid, false, ninf);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    stream_k<2, 2>(ring, wt, kb, ke, lds + (size_t)ma * stride, K, lane >> 4, acc, lane);
+    stream_k<2, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, K, lane >> 4, acc, lane);
     reduce_split_k<KS>(acc, red, w, ks, lane);
     if (ks == 0 && lane < 16) {
       // accumulator register r of lanes 0..15 holds token row r, column lane
@@ -426,7 +431,7 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
 // combine_kernel then sums them per token in j order. The blockIdx.x == 0 workgroups count the
 // gated intermediates that overflowed fp16 (each pair belongs to one group).
 // ---------------------------------------------------------------------------------------------
-template <int NPW>
+template <int NPW, int FMT>
 __global__ void __launch_bounds__(kThreads)
 decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                    const _Float16* __restrict__ act, const int32_t* __restrict__ ids,
@@ -442,14 +447,14 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int pw = w / KS, ks = w % KS;
   const int rq = blockIdx.x * NPW + pw;
-  WaveTiles wt = wave_tiles(codes, scales, e, (uint32_t)(nrg * nkt));
+  WaveTiles wt = wave_tiles<FMT>(codes, scales, e, (uint32_t)(nrg * nkt));
   wt.tile[0] = (uint32_t)(2 * rq * nkt);
   wt.tile[1] = (uint32_t)((2 * rq + 1) * nkt);
   const int kb = ks * nkt / KS, ke = (ks + 1) * nkt / KS;
   const int stride = MxRow<3>::stride(I);
   float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][2][4][16]
   const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
-  TileRegs<2> ring[kRing];
+  TileRegs<2, FMT> ring[kRing];
   for (int c0 = 0; c0 < n_e; c0 += kChunk) {
     const int n = min(kChunk, n_e - c0);
     int pr[kChunk];
@@ -460,13 +465,13 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
       return (size_t)pp * I;
     };
     int ninf = 0;
-    stage_and_prime<kThreads, 3, 2>(ring, wt, kb, ke, lane, lds, stride, act16, I, n, row_off, tid,
+    stage_and_prime<kThreads, 3, 2, FMT>(ring, wt, kb, ke, lane, lds, stride, act16, I, n, row_off, tid,
                                     blockIdx.x == 0, ninf);
     if (ninf) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)ninf);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    stream_k<3, 2>(ring, wt, kb, ke, lds + (size_t)ma * stride, I, lane >> 4, acc, lane);
+    stream_k<3, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, I, lane >> 4, acc, lane);
     reduce_split_k<KS>(acc, red, w, ks, lane);
     if (ks == 0 && lane < 16) {
 #pragma unroll
@@ -494,6 +499,7 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
 constexpr int kDirectWaves = 2 * kDirectMaxPairs;   // two reduction halves per pair
 constexpr int kDirectThreads = 64 * kDirectWaves;
 
+template <int FMT>
 __global__ void __launch_bounds__(kDirectThreads)
 decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                           const _Float16* __restrict__ act, const int32_t* __restrict__ ids,
@@ -512,7 +518,7 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
   const int p = w >> 1, hk = w & 1;
   const int id = p < P ? ids[p] : -1;
   const bool valid = id >= 0 && id < E;
-  WaveTiles wt = wave_tiles(codes, scales, valid ? id : 0, (uint32_t)(nrg * nkt));
+  WaveTiles wt = wave_tiles<FMT>(codes, scales, valid ? id : 0, (uint32_t)(nrg * nkt));
   wt.tile[0] = (uint32_t)(rg * nkt);
   wt.tile[1] = 0;
   const int kb = hk * nkt / 2, ke = valid ? (hk + 1) * nkt / 2 : kb;
@@ -529,9 +535,9 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
   // infinite ones while staging them
   const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
   auto row_off = [&](int m) -> size_t { return (size_t)m * I; };
-  TileRegs<1> ring[kRing];
+  TileRegs<1, FMT> ring[kRing];
   int ninf = 0;
-  stage_and_prime<kDirectThreads, 3, 1, kRing / 2>(ring, wt, kb, ke, lane, lds, stride, act16, I, P, row_off,
+  stage_and_prime<kDirectThreads, 3, 1, FMT, kRing / 2>(ring, wt, kb, ke, lane, lds, stride, act16, I, P, row_off,
                                                    tid, blockIdx.x == 0, ninf);
   __syncthreads();
   if (blockIdx.x == 0) {
@@ -541,7 +547,7 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
     if (tid < P && (cid[tid] < 0 || cid[tid] >= E)) atomicAdd(&cnt[0], 1);
   }
   f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  stream_k<3, 1>(ring, wt, kb, ke, lds + (size_t)(p < P ? p : 0) * stride, I, lane >> 4, acc, lane);
+  stream_k<3, 1, FMT>(ring, wt, kb, ke, lds + (size_t)(p < P ? p : 0) * stride, I, lane >> 4, acc, lane);
   if (valid && hk == 1 && lane < 16) red[p * 16 + lane] = acc[0][0];
   __syncthreads();
   if (blockIdx.x == 0 && tid == 0) {
@@ -617,51 +623,67 @@ size_t decode_direct_lds(int I) {
   return (size_t)kDirectMaxPairs * MxRow<3>::stride(I) + (size_t)kDirectMaxPairs * 2 * 16 * 4;
 }
 
-hipError_t launch_decode_gate_up(const moe_w2_planes* p, int T, int top_k, const void* x,
-                                 const int32_t* ids, const Workspace& ws, uint8_t* wsb, bool direct,
-                                 hipStream_t s) {
+template <int FMT>
+static hipError_t decode_gate_up_fmt(const moe_w2_planes* p, int T, int top_k, const void* x,
+                                     const int32_t* ids, const Workspace& ws, uint8_t* wsb, bool direct,
+                                     hipStream_t s) {
   const int P = T * top_k;
-  if (P == 0) return hipSuccess;
   const int groups = direct ? P : min(p->E, P);   // at most this many workgroup rows do work
   const size_t lds = (size_t)kChunk * MxRow<2>::stride(p->K) + (size_t)kWaves * 2 * 4 * 16 * 4;
   const uint16_t* xb = (const uint16_t*)x;
   _Float16* act = (_Float16*)(wsb + ws.act);
   long long* cnt = (long long*)(wsb + ws.counters);
   if (direct) {
-    hipLaunchKernelGGL((decode_gate_up_kernel<1, true>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((decode_gate_up_kernel<1, true, FMT>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
                        p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k);
   } else if (pick_np(groups) == 4) {
-    hipLaunchKernelGGL((decode_gate_up_kernel<4, false>), dim3(p->I / 64, P), dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((decode_gate_up_kernel<4, false, FMT>), dim3(p->I / 64, P), dim3(kThreads), lds, s,
                        p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k);
   } else {
-    hipLaunchKernelGGL((decode_gate_up_kernel<1, false>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((decode_gate_up_kernel<1, false, FMT>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
                        p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const int32_t* ids, const float* w,
-                              void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, bool direct,
-                              hipStream_t s) {
+hipError_t launch_decode_gate_up(const moe_w2_planes* p, int T, int top_k, const void* x,
+                                 const int32_t* ids, const Workspace& ws, uint8_t* wsb, bool direct,
+                                 hipStream_t s) {
+  if (T * top_k == 0) return hipSuccess;
+  return p->fmt == kFmtW4 ? decode_gate_up_fmt<kFmtW4>(p, T, top_k, x, ids, ws, wsb, direct, s)
+                          : decode_gate_up_fmt<kFmtW2>(p, T, top_k, x, ids, ws, wsb, direct, s);
+}
+
+template <int FMT>
+static hipError_t decode_down_fmt(const moe_w2_planes* p, int T, int top_k, const int32_t* ids, const float* w,
+                                  void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, bool direct,
+                                  hipStream_t s) {
   const int P = T * top_k;
-  if (P == 0) return hipSuccess;
   const _Float16* act = (const _Float16*)(wsb + ws.act);
   long long* cnt = (long long*)(wsb + ws.counters);
   if (direct) {
-    hipLaunchKernelGGL(decode_down_direct_kernel, dim3(p->K / 16), dim3(kDirectThreads), decode_direct_lds(p->I), s,
-                       p->dn_codes, p->dn_scales, act, ids, w, y, cnt, out_dtype, T, p->E, p->K, p->I, top_k);
+    hipLaunchKernelGGL(decode_down_direct_kernel<FMT>, dim3(p->K / 16), dim3(kDirectThreads), decode_direct_lds(p->I),
+                       s, p->dn_codes, p->dn_scales, act, ids, w, y, cnt, out_dtype, T, p->E, p->K, p->I, top_k);
     return hipGetLastError();
   }
   const int groups = min(p->E, P);
   const size_t lds = (size_t)kChunk * MxRow<3>::stride(p->I) + (size_t)kWaves * 2 * 4 * 16 * 4;
   float* po = (float*)(wsb + ws.pair_out);
   if (pick_np(groups) == 4)
-    hipLaunchKernelGGL(decode_down_kernel<4>, dim3(p->K / 128, P), dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((decode_down_kernel<4, FMT>), dim3(p->K / 128, P), dim3(kThreads), lds, s,
                        p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I);
   else
-    hipLaunchKernelGGL(decode_down_kernel<1>, dim3(p->K / 32, P), dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((decode_down_kernel<1, FMT>), dim3(p->K / 32, P), dim3(kThreads), lds, s,
                        p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const int32_t* ids, const float* w,
+                              void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, bool direct,
+                              hipStream_t s) {
+  if (T * top_k == 0) return hipSuccess;
+  return p->fmt == kFmtW4 ? decode_down_fmt<kFmtW4>(p, T, top_k, ids, w, y, out_dtype, ws, wsb, direct, s)
+                          : decode_down_fmt<kFmtW2>(p, T, top_k, ids, w, y, out_dtype, ws, wsb, direct, s);
 }
 
 hipError_t launch_combine(int T, int top_k, int E, int K, const int32_t* ids, const float* w,

@@ -105,12 +105,15 @@ MOEW2_DEV void a_sources(uint32_t (&off)[AT::kPerWave], int w, int lane, RowOff 
   }
 }
 
-// B: the 4 row groups of a wave, one native k-tile
+// B: the 4 row groups of a wave, one native k-tile (code loads per row group: 1 for 2-bit codes,
+// 2 for fp4 codes)
+template <int FMT>
 struct BRegs {
-  u32x4_t c[4];
+  u32x4_t c[4][WFmt<FMT>::kLoads];
   uint32_t s[4];
 };
-constexpr int kBLoads = 8;   // vector memory instructions for one BRegs
+template <int FMT>
+constexpr int kBLoads = 4 * (WFmt<FMT>::kLoads + 1);   // vector memory instructions for one BRegs
 constexpr int kGroups = 8;   // instruction groups per k-tile: 2 columns C x 4 row tiles m
 
 template <int I, int N, class F>
@@ -127,9 +130,9 @@ MOEW2_DEV void static_for(F&& f) {
 // code and scale loads of k-tile kb. Group i of the computing k-tile issues items
 // [i*kItems/8, (i+1)*kItems/8), so the loads spread over the step instead of queueing behind the
 // barrier.
-template <class AT>
+template <class AT, int FMT>
 struct KLoads {
-  static constexpr int kItems = AT::kPerWave + kBLoads;
+  static constexpr int kItems = AT::kPerWave + kBLoads<FMT>;
   const uint8_t* abase;
   const uint32_t* aoff;
   const uint8_t* codes;
@@ -138,29 +141,30 @@ struct KLoads {
   int nkt, w, lane;
 
   template <int N>
-  MOEW2_DEV void item(int ka, uint8_t* stage, int kb, BRegs& r) const {
+  MOEW2_DEV void item(int ka, uint8_t* stage, int kb, BRegs<FMT>& r) const {
     if constexpr (N < AT::kPerWave) {
       const int j = min(w + kWaves * N, AT::kInstr - 1);
       __builtin_amdgcn_global_load_lds((const void*)(abase + (aoff[N] + (uint32_t)ka * AT::kSrcBytes)),
                                        (__attribute__((address_space(3))) void*)(stage + 1024 * j), 16, 0, 0);
     } else {
-      constexpr int n = N - AT::kPerWave, t = n / 2;
+      constexpr int L = WFmt<FMT>::kLoads;
+      constexpr int n = N - AT::kPerWave, t = n / (L + 1), q = n % (L + 1);
       const size_t ti = tb0 + (size_t)t * nkt + kb;
-      if constexpr (n % 2 == 0)
-        r.c[t] = ld16(codes + ti * kTileCodeBytes + 16 * lane);
+      if constexpr (q < L)
+        r.c[t][q] = ld16(codes + ti * WFmt<FMT>::kCodeBytes + 1024 * q + 16 * lane);
       else
         r.s[t] = *reinterpret_cast<const uint16_t*>(scales + ti * kTileScaleBytes + 2 * lane);
     }
   }
   template <int N0, int N1>
-  MOEW2_DEV void items(int ka, uint8_t* stage, int kb, BRegs& r) const {
+  MOEW2_DEV void items(int ka, uint8_t* stage, int kb, BRegs<FMT>& r) const {
     if constexpr (N0 < N1) {
       item<N0>(ka, stage, kb, r);
       items<N0 + 1, N1>(ka, stage, kb, r);
     }
   }
   template <int I>
-  MOEW2_DEV void group(int ka, uint8_t* stage, int kb, BRegs& r) const {
+  MOEW2_DEV void group(int ka, uint8_t* stage, int kb, BRegs<FMT>& r) const {
     items<I * kItems / kGroups, (I + 1) * kItems / kGroups>(ka, stage, kb, r);
   }
 };
@@ -169,12 +173,12 @@ struct KLoads {
 // issues load group I (COMPUTE calls it for I = 0..7 in order, always) and mma says whether the
 // step has a k-tile to multiply (not the first two steps, the tail of the last round or idle
 // waves). K-tile j uses A stage j % 2 and B register set j % 3.
-template <class AT, class Compute>
-MOEW2_DEV void k_loop(uint8_t* lds, const KLoads<AT>& ld, int nkt, bool active, Compute compute) {
-  BRegs b0, b1, b2;
-  auto step = [&](int kt, BRegs& cur, BRegs& ahead) {
+template <class AT, int FMT, class Compute>
+MOEW2_DEV void k_loop(uint8_t* lds, const KLoads<AT, FMT>& ld, int nkt, bool active, Compute compute) {
+  BRegs<FMT> b0, b1, b2;
+  auto step = [&](int kt, BRegs<FMT>& cur, BRegs<FMT>& ahead) {
     // k-tile kt has landed: its A was issued in the previous step before that step's B loads
-    wait_vm<kBLoads>();
+    wait_vm<kBLoads<FMT>>();
     __builtin_amdgcn_s_barrier();      // ... in every wave; and every wave is done with kt - 1
     const int ka = max(0, min(kt + 1, nkt - 1));
     const int kb = min(kt + 2, nkt - 1);
@@ -262,8 +266,8 @@ static_assert(kA6Bytes % 16 == 0, "split record is whole chunks");
 // instructions. The next row tile's operand is read from LDS while this one's 12 instructions
 // run, the group's share of the loads two k-tiles ahead goes out with it, and the three parts of
 // one accumulator are 4 instructions apart (back-to-back dependent instructions stall).
-template <class Part>
-MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][4], const uint8_t* abuf, const BRegs& br, Part part, bool mma,
+template <int FMT, class Part>
+MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][4], const uint8_t* abuf, const BRegs<FMT>& br, Part part, bool mma,
                         int rows_valid, int lane, const Fp4Masks& fm) {
   const int g = lane >> 4;
   const uint8_t* arow = abuf + (lane & 15) * kA6Stride;
@@ -271,7 +275,7 @@ MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][4], const uint8_t* abuf, const BRegs& 
     constexpr int C = decltype(cc)::value;
     i32x8_t bo[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) bo[t] = mx_b_operand(br.c[t][2 * C], br.c[t][2 * C + 1], fm);
+    for (int t = 0; t < 4; ++t) bo[t] = b_operand<FMT, C>(br.c[t], fm);
     A6Op cur = a6_load(arow, C, g), nxt;
     static_for<0, 4>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
@@ -295,6 +299,7 @@ MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][4], const uint8_t* abuf, const BRegs& 
 // ------------------------------------------------------------------------------------------------
 // gate_up: rows of the split x gathered through the sort permutation (token = pair / top_k).
 // ------------------------------------------------------------------------------------------------
+template <int FMT>
 __global__ void __launch_bounds__(kThreads, kWgPerCu)
 gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                        const uint8_t* __restrict__ xq, const int32_t* __restrict__ offsets,
@@ -327,8 +332,8 @@ gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restr
     for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const Fp4Masks fm = fp4_masks();
-  const KLoads<A6Tile> ld{xq, aoff, codes, scales, tb0, nkt, w, lane};
-  k_loop<A6Tile>(lds, ld, nkt, wave_active, [&](const uint8_t* abuf, const BRegs& br, auto part, bool mma) {
+  const KLoads<A6Tile, FMT> ld{xq, aoff, codes, scales, tb0, nkt, w, lane};
+  k_loop(lds, ld, nkt, wave_active, [&](const uint8_t* abuf, const BRegs<FMT>& br, auto part, bool mma) {
     a6_ktile(acc, abuf, br, part, mma, rows_valid, lane, fm);
   });
   if (!wave_active) return;
@@ -359,6 +364,7 @@ gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restr
 // ------------------------------------------------------------------------------------------------
 // down: rows of the split gated intermediate in sorted order; per-pair fp32 rows out.
 // ------------------------------------------------------------------------------------------------
+template <int FMT>
 __global__ void __launch_bounds__(kThreads, kWgPerCu)
 gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                     const uint8_t* __restrict__ aq, const int32_t* __restrict__ offsets,
@@ -388,8 +394,8 @@ gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict
     for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const Fp4Masks fm = fp4_masks();
-  const KLoads<A6Tile> ld{aq, aoff, codes, scales, tb0, nkt, w, lane};
-  k_loop<A6Tile>(lds, ld, nkt, wave_active, [&](const uint8_t* abuf, const BRegs& br, auto part, bool mma) {
+  const KLoads<A6Tile, FMT> ld{aq, aoff, codes, scales, tb0, nkt, w, lane};
+  k_loop(lds, ld, nkt, wave_active, [&](const uint8_t* abuf, const BRegs<FMT>& br, auto part, bool mma) {
     a6_ktile(acc, abuf, br, part, mma, rows_valid, lane, fm);
   });
   if (!wave_active) return;
@@ -422,7 +428,8 @@ hipError_t launch_gemm_gate_up(const moe_w2_planes* p, int T, int top_k, const v
   hipLaunchKernelGGL(quant_a6_kernel<true>, dim3((unsigned)((nblk32 + 255) / 256)), dim3(256), 0, s,
                      (const uint16_t*)x, wsb + ws.xq, T, p->K);
   const int nblk = (2 * p->I + BN - 1) / BN;
-  hipLaunchKernelGGL(gemm_gate_up_mx_kernel, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads),
+  auto kern = p->fmt == kFmtW4 ? gemm_gate_up_mx_kernel<kFmtW4> : gemm_gate_up_mx_kernel<kFmtW2>;
+  hipLaunchKernelGGL(kern, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads),
                      kAStages * A6Tile::kBytes, s,
                      p->gu_codes, p->gu_scales, (const uint8_t*)(wsb + ws.xq),
                      (const int32_t*)(wsb + ws.offsets), (const int32_t*)(wsb + ws.perm),
@@ -439,7 +446,8 @@ hipError_t launch_gemm_down(const moe_w2_planes* p, int T, int top_k, const Work
   hipLaunchKernelGGL(quant_a6_kernel<false>, dim3((unsigned)((nblk32 + 255) / 256)), dim3(256), 0, s,
                      (const uint16_t*)(wsb + ws.act), wsb + ws.aq, P, p->I);
   const int nblk = (p->K + BN - 1) / BN;
-  hipLaunchKernelGGL(gemm_down_mx_kernel, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads),
+  auto kern = p->fmt == kFmtW4 ? gemm_down_mx_kernel<kFmtW4> : gemm_down_mx_kernel<kFmtW2>;
+  hipLaunchKernelGGL(kern, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads),
                      kAStages * A6Tile::kBytes, s,
                      p->dn_codes, p->dn_scales, (const uint8_t*)(wsb + ws.aq),
                      (const int32_t*)(wsb + ws.offsets), (const int32_t*)(wsb + ws.perm),

@@ -9,17 +9,22 @@
 
 struct moe_w2_planes {
   int E, K, I;
+  int fmt;             // weight format: kFmtW2 (2-bit codes) or kFmtW4 (e2m1 codes), both UE8M0 / 32
   int device;
   void* base;          // single device allocation
   size_t bytes;
-  uint8_t* gu_codes;   // [E][2I/16][K/256][1024]
+  uint8_t* gu_codes;   // [E][2I/16][K/256][tile code bytes: 1024 (w2) or 2048 (w4)]
   uint8_t* gu_scales;  // [E][2I/16][K/256][128]
-  uint8_t* dn_codes;   // [E][K/16][I/256][1024]
+  uint8_t* dn_codes;   // [E][K/16][I/256][tile code bytes]
   uint8_t* dn_scales;  // [E][K/16][I/256][128]
   int32_t* flag;       // pack-time validation flags (device)
 };
 
 namespace moew2 {
+
+// Weight formats of the planes. W2: 2-bit sign-symmetric codes; W4: e2m1 (fp4) codes (MXFP4).
+enum { kFmtW2 = 0, kFmtW4 = 1 };
+inline int code_bits(int fmt) { return fmt == kFmtW4 ? 4 : 2; }
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }

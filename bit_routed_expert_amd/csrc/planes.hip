@@ -98,6 +98,29 @@ __global__ void unpack_codes_kernel(const uint8_t* __restrict__ native, uint8_t*
   }
 }
 
+// FP4 codes (canonical: two e2m1 codes per byte, low nibble = even element): one thread per
+// (matrix, tile, instruction c, lane); the lane's 16 operand bytes are the 32 codes of block
+// 8kt + 4c + g of its row, i.e. 16 consecutive canonical bytes (W4 tile layout in common.h).
+__global__ void pack_codes4_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ native,
+                                   int nmat, int NR, int KR, int I, int gate_up, int unpack) {
+  const int nkt = KR / kTileK, nrg = NR / kTileRows;
+  const long long total = (long long)nmat * nrg * nkt * 128;
+  long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int lane = (int)(gid & 63), c = (int)((gid >> 6) & 1);
+  long long t = gid >> 7;
+  const int kt = (int)(t % nkt); t /= nkt;
+  const int rg = (int)(t % nrg);
+  const int e = (int)(t / nrg);
+  const int cr = canonical_row(rg * kTileRows + (lane & 15), I, gate_up != 0);
+  uint8_t* row = const_cast<uint8_t*>(canon) + ((long long)e * NR + cr) * (KR / 2) + 16 * (8 * kt + 4 * c + (lane >> 4));
+  uint8_t* tile = native + ((long long)e * nrg * nkt + (long long)rg * nkt + kt) * kTileCodeBytesW4 + 1024 * c + 16 * lane;
+  if (unpack)
+    *reinterpret_cast<u32x4_t*>(row) = *reinterpret_cast<const u32x4_t*>(tile);
+  else
+    *reinterpret_cast<u32x4_t*>(tile) = *reinterpret_cast<const u32x4_t*>(row);
+}
+
 // One thread per (matrix, tile, row): the row's 8 scale bytes of the k-tile. Byte 2*(16g + j) + c
 // of the tile holds block 4c + g of row j (block layout). A byte above 252 is flagged: its
 // weights (up to 4 * 2^(b-127)) would not be finite in fp32.
@@ -154,14 +177,20 @@ hipError_t launch_pack_experts(const moe_w2_planes* p, int e0, int n, const uint
   const int K = p->K, I = p->I;
   const int B = 256;
   const size_t gu = (size_t)2 * I * K, dn = (size_t)K * I;   // weights per expert
+  const int cb = code_bits(p->fmt);                           // code bits per weight
   hipError_t err = hipMemsetAsync(p->flag, 0, sizeof(int32_t), s);
   if (err != hipSuccess) return err;
   long long n1 = (long long)n * (2 * I / kTileRows) * (K / 256) * 64;
-  hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for(n1, B)), dim3(B), 0, s,
-                     gu_codes, p->gu_codes + (size_t)e0 * gu / 4, n, 2 * I, K, I, 1);
   long long n2 = (long long)n * (K / kTileRows) * (I / 256) * 64;
-  hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for(n2, B)), dim3(B), 0, s,
-                     dn_codes, p->dn_codes + (size_t)e0 * dn / 4, n, K, I, I, 0);
+  uint8_t* guc = p->gu_codes + (size_t)e0 * gu * cb / 8;
+  uint8_t* dnc = p->dn_codes + (size_t)e0 * dn * cb / 8;
+  if (p->fmt == kFmtW4) {
+    hipLaunchKernelGGL(pack_codes4_kernel, dim3(grid_for(2 * n1, B)), dim3(B), 0, s, gu_codes, guc, n, 2 * I, K, I, 1, 0);
+    hipLaunchKernelGGL(pack_codes4_kernel, dim3(grid_for(2 * n2, B)), dim3(B), 0, s, dn_codes, dnc, n, K, I, I, 0, 0);
+  } else {
+    hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for(n1, B)), dim3(B), 0, s, gu_codes, guc, n, 2 * I, K, I, 1);
+    hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for(n2, B)), dim3(B), 0, s, dn_codes, dnc, n, K, I, I, 0);
+  }
   long long n3 = (long long)n * (2 * I / kTileRows) * (K / 256) * kTileRows;
   hipLaunchKernelGGL(pack_scales_kernel, dim3(grid_for(n3, B)), dim3(B), 0, s,
                      gu_scales, p->gu_scales + (size_t)e0 * gu / 32, n, 2 * I, K, I, 1, p->flag);
@@ -181,11 +210,18 @@ hipError_t launch_unpack(const moe_w2_planes* p, uint8_t* gu_codes, uint8_t* gu_
   const int E = p->E, K = p->K, I = p->I;
   const int B = 256;
   long long n1 = (long long)E * (2 * I / kTileRows) * (K / 256) * 64;
-  hipLaunchKernelGGL(unpack_codes_kernel, dim3(grid_for(n1, B)), dim3(B), 0, s,
-                     p->gu_codes, gu_codes, E, 2 * I, K, I, 1);
   long long n2 = (long long)E * (K / kTileRows) * (I / 256) * 64;
-  hipLaunchKernelGGL(unpack_codes_kernel, dim3(grid_for(n2, B)), dim3(B), 0, s,
-                     p->dn_codes, dn_codes, E, K, I, I, 0);
+  if (p->fmt == kFmtW4) {
+    hipLaunchKernelGGL(pack_codes4_kernel, dim3(grid_for(2 * n1, B)), dim3(B), 0, s, gu_codes, p->gu_codes, E, 2 * I,
+                       K, I, 1, 1);
+    hipLaunchKernelGGL(pack_codes4_kernel, dim3(grid_for(2 * n2, B)), dim3(B), 0, s, dn_codes, p->dn_codes, E, K, I,
+                       I, 0, 1);
+  } else {
+    hipLaunchKernelGGL(unpack_codes_kernel, dim3(grid_for(n1, B)), dim3(B), 0, s, p->gu_codes, gu_codes, E, 2 * I, K,
+                       I, 1);
+    hipLaunchKernelGGL(unpack_codes_kernel, dim3(grid_for(n2, B)), dim3(B), 0, s, p->dn_codes, dn_codes, E, K, I, I,
+                       0);
+  }
   long long n3 = (long long)E * (2 * I / kTileRows) * (K / 256) * kTileRows;
   hipLaunchKernelGGL(unpack_scales_kernel, dim3(grid_for(n3, B)), dim3(B), 0, s,
                      p->gu_scales, gu_scales, E, 2 * I, K, I, 1);

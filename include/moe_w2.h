@@ -96,8 +96,32 @@ int moe_w2_pack(int E, int K, int I,
                 const uint8_t* dn_codes, const uint8_t* dn_scales,
                 void* stream, moe_w2_planes** out);
 
-/* Inverse of moe_w2_pack into canonical buffers of the shapes above (asynchronous; exact). */
+/*
+ * moe_w4_pack - native planes of one MoE layer with FP4 (MXFP4) experts: e2m1 codes with one
+ * UE8M0 scale per 32 elements along each GEMM's reduction axis. Source: README bullet "FP4
+ * recovery - used surgically" (a delta tier keeps hot experts at FP4; an FP4 read is twice the
+ * bytes of the 2-bit planes) and bullet "The kernels" (the moe_w4_mm FP4 GEMM beside moe_w2_mm).
+ *   gu_codes  [E][2I][K/2]  two e2m1 codes per byte, low nibble = even element
+ *   gu_scales [E][2I][K/32] dn_codes [E][K][I/2] dn_scales [E][K][I/32]
+ * e2m1 code n: sign n>>3, magnitude {0, 0.5, 1, 1.5, 2, 3, 4, 6}[n & 7]; weight = value * 2^(b-127).
+ * Scale bytes must be <= 252 (MOE_W2_ESCALE otherwise); also needs I*K < 2^31. The planes work
+ * with moe_w2_forward / moe_w2_forward_stage / moe_w4_forward (same arithmetic, fp4 weights in
+ * place of the expanded 2-bit codes). Synchronous, like moe_w2_pack.
+ */
+int moe_w4_pack(int E, int K, int I,
+                const uint8_t* gu_codes, const uint8_t* gu_scales,
+                const uint8_t* dn_codes, const uint8_t* dn_scales,
+                void* stream, moe_w2_planes** out);
+
+/* Inverse of moe_w2_pack into canonical buffers of its shapes (asynchronous; exact).
+ * MOE_W2_EINVAL for planes made by moe_w4_pack. */
 int moe_w2_unpack(const moe_w2_planes* planes,
+                  uint8_t* gu_codes, uint8_t* gu_scales,
+                  uint8_t* dn_codes, uint8_t* dn_scales, void* stream);
+
+/* Inverse of moe_w4_pack into canonical FP4 buffers (asynchronous; exact). MOE_W2_EINVAL for
+ * planes made by moe_w2_pack. */
+int moe_w4_unpack(const moe_w2_planes* planes,
                   uint8_t* gu_codes, uint8_t* gu_scales,
                   uint8_t* dn_codes, uint8_t* dn_scales, void* stream);
 
@@ -157,6 +181,12 @@ int moe_w2_forward(const moe_w2_planes* planes, int T, int top_k,
                    void* y, int out_dtype,
                    void* workspace, size_t workspace_bytes, int path, void* stream);
 
+/* moe_w4_forward - moe_w2_forward on planes made by moe_w4_pack (MOE_W2_EINVAL for others). */
+int moe_w4_forward(const moe_w2_planes* planes, int T, int top_k,
+                   const void* x, const int32_t* topk_ids, const float* topk_w,
+                   void* y, int out_dtype,
+                   void* workspace, size_t workspace_bytes, int path, void* stream);
+
 /*
  * moe_w2_forward_stage - one stage of moe_w2_forward, with the same arguments. Calling stages
  * ROUTE, GATE_UP, DOWN, COMBINE in this order on one stream with one workspace is exactly
@@ -185,7 +215,8 @@ int moe_w2_read_counters(const void* workspace, int64_t* invalid_pairs, int64_t*
  * hooks", BASE cache bullet (slot table, four sections per expert slot); "vLLM-Moet: a 2-bit
  * expert patch and a three-tier expert cache on SM120", section "A cache miss costs a replay".
  *
- * moe_w2_planes_create - planes of S empty slots for K and I (contents unspecified until packed).
+ * moe_w2_planes_create - planes of S empty 2-bit slots for K and I (contents unspecified until
+ * packed).
  * Synchronous. On failure *out is NULL.
  */
 int moe_w2_planes_create(int S, int K, int I, void* stream, moe_w2_planes** out);

@@ -11,7 +11,8 @@ Sources:
   e2m1 and E4M3FN formats) are not printed on the pages.
 
 Canonical packing (a reading, the pages are silent): 4 codes per byte, element k of a row at bits
-2*(k%4)..2*(k%4)+1 (LSB first), along the row's reduction axis.
+2*(k%4)..2*(k%4)+1 (LSB first), along the row's reduction axis. FP4 (MXFP4) expert planes: two
+e2m1 codes per byte, low nibble = even element, with the same UE8M0 block-32 scales.
 """
 from fractions import Fraction
 
@@ -83,6 +84,17 @@ def pack_codes(codes):
         raise ValueError("codes must be in 0..3")
     c = codes.reshape(codes.shape[:-1] + (codes.shape[-1] // 4, 4))
     return (c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)).astype(np.uint8)
+
+
+def unpack_e2m1(packed):
+    """Canonical FP4 bytes [..., n/2] -> e2m1 nibbles [..., n]: element 2i in the low nibble of
+    byte i, element 2i+1 in the high nibble (the NVFP4 packing named for the re-quantizer input,
+    used for the FP4 expert planes too)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = packed & np.uint8(15)
+    out[..., 1::2] = packed >> np.uint8(4)
+    return out
 
 
 def bf16_bits_to_f64(bits):

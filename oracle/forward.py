@@ -21,9 +21,10 @@ Definition (reading of the pages; the plain reading is stated where they are sil
 """
 import numpy as np
 
-from .formats import CODEBOOK, unpack_codes
+from .formats import CODEBOOK, E2M1_MAGNITUDE, unpack_codes, unpack_e2m1
 
 _CODEBOOK = np.array(CODEBOOK, dtype=np.float64)
+_E2M1 = np.array([m for m in E2M1_MAGNITUDE] + [-m for m in E2M1_MAGNITUDE], dtype=np.float64)
 
 
 def dequant_rows(packed, scale_bytes):
@@ -35,6 +36,21 @@ def dequant_rows(packed, scale_bytes):
         raise ValueError("UE8M0 scale byte out of range")
     s = np.ldexp(1.0, sb - 127)
     return vals * np.repeat(s, 32, axis=-1)
+
+
+def dequant_rows_fp4(packed, scale_bytes):
+    """FP4 experts (README bullet "FP4 recovery - used surgically": hot experts kept at FP4):
+    packed e2m1 codes [rows, n/2] + UE8M0 scale bytes [rows, n/32] -> f64 weights [rows, n],
+    W = e2m1(code) * 2**(b - 127)."""
+    vals = _E2M1[unpack_e2m1(packed)]
+    sb = np.asarray(scale_bytes).astype(np.int64)
+    if sb.size and (sb.max() > 254 or sb.min() < 0):
+        raise ValueError("UE8M0 scale byte out of range")
+    return vals * np.repeat(np.ldexp(1.0, sb - 127), 32, axis=-1)
+
+
+def _dequant(fp4):
+    return dequant_rows_fp4 if fp4 else dequant_rows
 
 
 def route(topk_ids, E):
@@ -59,13 +75,15 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None):
+def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None, fp4=False):
     """Per-pair down-projection outputs o[(t, j)] in f64.
 
     x: [T, K] f64 (the bf16 activations' exact values). Returns an array [len(tokens), top_k, K];
     rows of invalid pairs are zero. ``tokens`` restricts the computation to a subset of tokens
-    (for spot checks of large workloads); default all tokens.
+    (for spot checks of large workloads); default all tokens. fp4: the planes hold e2m1 codes
+    (two per byte) instead of 2-bit codes.
     """
+    dq = _dequant(fp4)
     x = np.asarray(x, dtype=np.float64)
     ids = np.asarray(topk_ids, dtype=np.int64)
     T, K = x.shape
@@ -79,8 +97,8 @@ def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=N
         if e < 0 or e >= E:
             continue
         rows, js = np.nonzero(sel == e)
-        w_gu = dequant_rows(gu_codes[e], gu_scales[e])  # [2I, K]
-        w_dn = dequant_rows(dn_codes[e], dn_scales[e])  # [K, I]
+        w_gu = dq(gu_codes[e], gu_scales[e])  # [2I, K]
+        w_dn = dq(dn_codes[e], dn_scales[e])  # [K, I]
         xe = x[tokens[rows]]                              # [n_e, K]
         g = xe @ w_gu[:I].T                               # [n_e, I]
         u = xe @ w_gu[I:].T
@@ -89,9 +107,9 @@ def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=N
     return out
 
 
-def moe_forward(x, topk_ids, topk_w, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None):
+def moe_forward(x, topk_ids, topk_w, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None, fp4=False):
     """y[t] = sum_j (ascending) w[t, j] * o_(t, j); f64 [len(tokens), K]."""
-    o = pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens)
+    o = pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens, fp4)
     w = np.asarray(topk_w, dtype=np.float64)
     tokens = np.arange(o.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
     w = w[tokens]

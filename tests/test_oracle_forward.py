@@ -192,3 +192,56 @@ def test_resident_ids_hand_example():
     got, miss = forward.resident_ids(ids, 4, resident)
     assert np.array_equal(got, np.array([[0, -1], [2, -1], [-1, -1]], dtype=np.int32))
     assert miss == 2   # ids 3 and 1
+
+
+def test_unpack_e2m1_hand_bytes():
+    """FP4 packing: element 2i in the low nibble of byte i. 0x8A -> nibbles 0xA (-1.0), 0x8 (-0.0);
+    0x21 -> 0x1 (0.5), 0x2 (1.0)."""
+    n = formats.unpack_e2m1(np.array([[0x8A, 0x21]], np.uint8))
+    assert n.tolist() == [[0xA, 0x8, 0x1, 0x2]]
+    vals = [formats.e2m1_value(v) for v in n[0]]
+    assert vals == [-1.0, -0.0, 0.5, 1.0] and np.signbit(vals[1])
+
+
+def _dense_fp4_independent(packed, scale_bytes):
+    """FP4 weights from the e2m1 bit-field definition, element by element, and torch's
+    float8_e8m0fnu for the scales."""
+    p = np.asarray(packed)
+    rows, nb = p.shape
+    vals = np.zeros((rows, nb * 2))
+    for r in range(rows):
+        for i in range(nb):
+            vals[r, 2 * i] = formats.e2m1_value(int(p[r, i]) & 15)
+            vals[r, 2 * i + 1] = formats.e2m1_value(int(p[r, i]) >> 4)
+    s = torch.from_numpy(np.ascontiguousarray(scale_bytes, dtype=np.uint8)).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    return vals * np.repeat(s, 32, axis=1)
+
+
+def test_fp4_single_expert_top1_is_dense_silu_mlp():
+    """FP4 experts (README bullet "FP4 recovery - used surgically"), E = 1, top-1: the dense gated
+    MLP with torch's silu and matmul in float64 on independently dequantized e2m1 weights."""
+    rng = np.random.default_rng(13)
+    T, K, I = 5, 64, 64
+    planes = workloads.draw_planes_fp4(rng, 1, K, I)
+    x = formats.bf16_bits_to_f64(workloads.draw_x(rng, T, K))
+    y = forward.moe_forward(x, np.zeros((T, 1), np.int32), np.ones((T, 1), np.float32), **planes, fp4=True)
+    wgu = torch.from_numpy(_dense_fp4_independent(planes["gu_codes"][0], planes["gu_scales"][0]))
+    wdn = torch.from_numpy(_dense_fp4_independent(planes["dn_codes"][0], planes["dn_scales"][0]))
+    xt = torch.from_numpy(x)
+    ref = torch.matmul(torch.nn.functional.silu(torch.matmul(xt, wgu[:I].T)) * torch.matmul(xt, wgu[I:].T), wdn.T)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12 * np.abs(ref.numpy()).max())
+
+
+def test_fp4_sign_and_scale_invariants_are_exact():
+    """Flipping the sign bit of every down code negates y; one more down scale step doubles it;
+    both exactly (power-of-two and sign changes are exact in f64)."""
+    rng = np.random.default_rng(14)
+    T, K, I, E = 7, 64, 64, 3
+    planes = workloads.draw_planes_fp4(rng, E, K, I)
+    x = formats.bf16_bits_to_f64(workloads.draw_x(rng, T, K))
+    ids, w = workloads.uniform_routing(rng, T, E, 2)
+    y = forward.moe_forward(x, ids, w, **planes, fp4=True)
+    neg = dict(planes, dn_codes=planes["dn_codes"] ^ np.uint8(0x88))
+    assert np.array_equal(forward.moe_forward(x, ids, w, **neg, fp4=True), -y)
+    dbl = dict(planes, dn_scales=planes["dn_scales"] + np.uint8(1))
+    assert np.array_equal(forward.moe_forward(x, ids, w, **dbl, fp4=True), 2 * y)

@@ -39,6 +39,17 @@ def draw_planes(rng, E, K, I):
     return dict(gu_codes=gu_codes, gu_scales=gu_scales, dn_codes=dn_codes, dn_scales=dn_scales)
 
 
+def draw_planes_fp4(rng, E, K, I):
+    """Canonical FP4 (MXFP4) planes of one layer, drawn in this order: gate_up codes [E, 2I, K/2]
+    (uniform bytes = two independent uniform e2m1 nibbles), gate_up scale bytes [E, 2I, K/32] =
+    127 + U{-10..-6}, down codes [E, K, I/2], down scale bytes [E, K, I/32] = 127 + U{-10..-6}."""
+    gu_codes = rng.integers(0, 256, size=(E, 2 * I, K // 2), dtype=np.uint8)
+    gu_scales = (127 + rng.integers(-10, -5, size=(E, 2 * I, K // 32))).astype(np.uint8)
+    dn_codes = rng.integers(0, 256, size=(E, K, I // 2), dtype=np.uint8)
+    dn_scales = (127 + rng.integers(-10, -5, size=(E, K, I // 32))).astype(np.uint8)
+    return dict(gu_codes=gu_codes, gu_scales=gu_scales, dn_codes=dn_codes, dn_scales=dn_scales)
+
+
 def _softmax_f32(logits):
     z = logits.astype(np.float64)
     z = z - z.max(axis=-1, keepdims=True)
