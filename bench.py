@@ -517,12 +517,55 @@ def bench_requant(args, moe, workloads, torch, dev):
     ms = float(np.median(times))
     nbytes = n * R * (C // 2 + C // 16 + C // 4 + C // 32) + 4 * n
     blocks = n * R * (C // 32)
-    del e2m1, e4m3, codes, scales
+    del e2m1, e4m3, s2d
     torch.cuda.empty_cache()
-    return dict(workload="nvfp4_to_w2: 256 tensors of [2048, 6144] (e2m1 x e4m3/16 x fp32 scale_2 -> 2-bit + UE8M0/32)",
-                ms=round(ms, 4), hbm_GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
-                hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                blocks_per_s=round(blocks / (ms * 1e-3), 1), algorithmic_bytes=nbytes, iters=args.requant_iters)
+    out = dict(workload="nvfp4_to_w2: 256 tensors of [2048, 6144] (e2m1 x e4m3/16 x fp32 scale_2 -> 2-bit + UE8M0/32)",
+               ms=round(ms, 4), hbm_GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
+               hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+               blocks_per_s=round(blocks / (ms * 1e-3), 1), algorithmic_bytes=nbytes, iters=args.requant_iters)
+
+    def timed(call):
+        call()
+        ts = []
+        for _ in range(args.requant_iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    # FP8 block-quant: e4m3 [n, R, C] + fp32 [n, R/128, C/128]
+    e4 = torch.empty((n, R, C), dtype=torch.uint8, device="cuda")
+    bs = torch.empty((n, R // 128, C // 128), dtype=torch.float32, device="cuda")
+    for i in range(n):
+        a, b = workloads.fp8_block_tensor(i, R, C)
+        e4[i].copy_(torch.from_numpy(a))
+        bs[i].copy_(torch.from_numpy(b))
+    ms = timed(lambda: moe.fp8_block128_to_w2(e4, bs, codes, scales))
+    nb8 = n * R * (C + C // 4 + C // 32) + 4 * n * (R // 128) * (C // 128)
+    out["fp8_block128"] = dict(workload="fp8_block128_to_w2: 256 tensors of [2048, 6144] (e4m3 x fp32 per 128x128 -> "
+                                        "2-bit + UE8M0/32)", ms=round(ms, 4),
+                               hbm_GBps=round(nb8 / (ms * 1e-3) / 1e9, 1), blocks_per_s=round(blocks / (ms * 1e-3), 1),
+                               algorithmic_bytes=nb8)
+    del e4, bs
+    torch.cuda.empty_cache()
+    # MXFP4: e2m1 [n, R, C/2] + UE8M0 [n, R, C/32]
+    e2 = torch.empty((n, R, C // 2), dtype=torch.uint8, device="cuda")
+    ue = torch.empty((n, R, C // 32), dtype=torch.uint8, device="cuda")
+    for i in range(n):
+        a, b = workloads.mxfp4_tensor(i, R, C)
+        e2[i].copy_(torch.from_numpy(a))
+        ue[i].copy_(torch.from_numpy(b))
+    ms = timed(lambda: moe.mxfp4_to_w2(e2, ue, codes, scales))
+    nb4 = n * R * (C // 2 + C // 32 + C // 4 + C // 32)
+    out["mxfp4"] = dict(workload="mxfp4_to_w2: 256 tensors of [2048, 6144] (e2m1 x UE8M0/32 -> 2-bit + UE8M0/32)",
+                        ms=round(ms, 4), hbm_GBps=round(nb4 / (ms * 1e-3) / 1e9, 1),
+                        blocks_per_s=round(blocks / (ms * 1e-3), 1), algorithmic_bytes=nb4)
+    del e2, ue, codes, scales
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(canon, inst):

@@ -20,7 +20,7 @@ PATH_AUTO, PATH_DECODE, PATH_GEMM = 0, 1, 2
 STAGE_ROUTE, STAGE_GATE_UP, STAGE_DOWN, STAGE_COMBINE = 0, 1, 2, 3
 
 STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ESCALE", -4: "ENOMEM", -5: "EHIP",
-          -6: "EWORKSPACE", -7: "ENVFP4"}
+          -6: "EWORKSPACE", -7: "ENVFP4", -8: "ENAN"}
 
 
 class MoeW2Error(RuntimeError):
@@ -56,6 +56,8 @@ def _lib():
             "nvfp4_to_w2": ([I32, I32, I32, P, P, P, P, P, P], I32),
             "moe_w2_planes_create": ([I32, I32, I32, P, ctypes.POINTER(P)], I32),
             "moe_w4_pack": ([I32, I32, I32, P, P, P, P, P, ctypes.POINTER(P)], I32),
+            "fp8_block128_to_w2": ([I32, I32, I32, P, P, P, P, P], I32),
+            "mxfp4_to_w2": ([I32, I32, I32, P, P, P, P, P], I32),
             "moe_w4_unpack": ([P, P, P, P, P, P], I32),
             "moe_w4_forward": ([P, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
             "moe_w2_pack_slot": ([P, I32, P, P, P, P, P], I32),
@@ -300,4 +302,31 @@ def nvfp4_to_w2(e2m1, e4m3, scale_2, codes=None, scales=None):
     _check(_lib().nvfp4_to_w2(n, R, C, _dev(e2m1, torch.uint8, "e2m1"), _dev(e4m3, torch.uint8, "e4m3"),
                               _dev(scale_2, torch.float32, "scale_2"), _dev(codes, torch.uint8, "codes"),
                               _dev(scales, torch.uint8, "scales"), _stream()), "nvfp4_to_w2")
+    return codes, scales
+
+
+def fp8_block128_to_w2(e4m3, bscale, codes=None, scales=None):
+    """e4m3 [n, R, C] uint8, bscale [n, R/128, C/128] fp32 (device) -> (codes [n, R, C/4], scales [n, R, C/32])."""
+    n, R, C = e4m3.shape
+    if codes is None:
+        codes = torch.empty((n, R, C // 4), dtype=torch.uint8, device="cuda")
+    if scales is None:
+        scales = torch.empty((n, R, C // 32), dtype=torch.uint8, device="cuda")
+    _check(_lib().fp8_block128_to_w2(n, R, C, _dev(e4m3, torch.uint8, "e4m3"), _dev(bscale, torch.float32, "bscale"),
+                                     _dev(codes, torch.uint8, "codes"), _dev(scales, torch.uint8, "scales"), _stream()),
+           "fp8_block128_to_w2")
+    return codes, scales
+
+
+def mxfp4_to_w2(e2m1, ue8m0, codes=None, scales=None):
+    """e2m1 [n, R, C/2] uint8, ue8m0 [n, R, C/32] uint8 (device) -> (codes [n, R, C/4], scales [n, R, C/32])."""
+    n, R, half_c = e2m1.shape
+    C = half_c * 2
+    if codes is None:
+        codes = torch.empty((n, R, C // 4), dtype=torch.uint8, device="cuda")
+    if scales is None:
+        scales = torch.empty((n, R, C // 32), dtype=torch.uint8, device="cuda")
+    _check(_lib().mxfp4_to_w2(n, R, C, _dev(e2m1, torch.uint8, "e2m1"), _dev(ue8m0, torch.uint8, "ue8m0"),
+                              _dev(codes, torch.uint8, "codes"), _dev(scales, torch.uint8, "scales"), _stream()),
+           "mxfp4_to_w2")
     return codes, scales

@@ -118,6 +118,7 @@ const char* moe_w2_status_string(int status) {
     case MOE_W2_EHIP: return "HIP runtime error";
     case MOE_W2_EWORKSPACE: return "workspace missing or too small";
     case MOE_W2_ENVFP4: return "NaN e4m3 scale or non-finite scale_2 in NVFP4 input";
+    case MOE_W2_ENAN: return "NaN element or scale, or non-finite scale, in FP8 / MXFP4 input";
     default: return "unknown status";
   }
 }
@@ -363,6 +364,48 @@ int nvfp4_to_w2(int n, int R, int C, const uint8_t* e2m1, const uint8_t* e4m3, c
   (void)hipFree(dflag);
   if (err != hipSuccess) return MOE_W2_EHIP;
   return flag ? MOE_W2_ENVFP4 : MOE_W2_OK;
+}
+
+// Runs a re-quantizer launch with a device flag for invalid input (synchronous).
+static int requant_call(hipStream_t s, int bad_status, hipError_t (*launch)(int32_t*, const void*), const void* ctx) {
+  int32_t* dflag = nullptr;
+  if (hipMalloc(&dflag, sizeof(int32_t)) != hipSuccess) { (void)hipGetLastError(); return MOE_W2_ENOMEM; }
+  int32_t flag = 0;
+  hipError_t err = hipMemsetAsync(dflag, 0, sizeof(int32_t), s);
+  if (err == hipSuccess) err = launch(dflag, ctx);
+  if (err == hipSuccess) err = hipMemcpyAsync(&flag, dflag, 4, hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  (void)hipFree(dflag);
+  if (err != hipSuccess) return MOE_W2_EHIP;
+  return flag ? bad_status : MOE_W2_OK;
+}
+
+int fp8_block128_to_w2(int n, int R, int C, const uint8_t* e4m3, const float* bscale, uint8_t* codes,
+                       uint8_t* scales, void* stream) {
+  if (n < 0 || R < 0 || C < 0) return MOE_W2_EINVAL;
+  if (R % 128 || C % 128) return MOE_W2_EUNSUPPORTED;
+  if ((long long)n * R * C == 0) return MOE_W2_OK;
+  if (!e4m3 || !bscale || !codes || !scales) return MOE_W2_EINVAL;
+  struct Ctx { int n, R, C; const uint8_t* e; const float* b; uint8_t *c, *s; hipStream_t st; } ctx{
+      n, R, C, e4m3, bscale, codes, scales, (hipStream_t)stream};
+  return requant_call((hipStream_t)stream, MOE_W2_ENAN, [](int32_t* f, const void* p) {
+    const Ctx& c = *static_cast<const Ctx*>(p);
+    return launch_fp8_block128_to_w2(c.n, c.R, c.C, c.e, c.b, c.c, c.s, f, c.st);
+  }, &ctx);
+}
+
+int mxfp4_to_w2(int n, int R, int C, const uint8_t* e2m1, const uint8_t* ue8m0, uint8_t* codes, uint8_t* scales,
+                void* stream) {
+  if (n < 0 || R < 0 || C < 0) return MOE_W2_EINVAL;
+  if (C % 32) return MOE_W2_EUNSUPPORTED;
+  if ((long long)n * R * C == 0) return MOE_W2_OK;
+  if (!e2m1 || !ue8m0 || !codes || !scales) return MOE_W2_EINVAL;
+  struct Ctx { int n, R, C; const uint8_t *e, *u; uint8_t *c, *s; hipStream_t st; } ctx{
+      n, R, C, e2m1, ue8m0, codes, scales, (hipStream_t)stream};
+  return requant_call((hipStream_t)stream, MOE_W2_ENAN, [](int32_t* f, const void* p) {
+    const Ctx& c = *static_cast<const Ctx*>(p);
+    return launch_mxfp4_to_w2(c.n, c.R, c.C, c.e, c.u, c.c, c.s, f, c.st);
+  }, &ctx);
 }
 
 }  // extern "C"

@@ -107,7 +107,11 @@ hipError_t launch_gemm_down(const moe_w2_planes* p, int T, int top_k, const Work
 hipError_t launch_combine(int T, int top_k, int E, int K, const int32_t* ids, const float* w,
                           const float* pair_out, void* y, int out_dtype, hipStream_t s);
 
-// Re-quantizer
+// Re-quantizers
+hipError_t launch_fp8_block128_to_w2(int n, int R, int C, const uint8_t* e4m3, const float* bscale,
+                                     uint8_t* codes, uint8_t* scales, int32_t* flag, hipStream_t s);
+hipError_t launch_mxfp4_to_w2(int n, int R, int C, const uint8_t* e2m1, const uint8_t* ue8m0, uint8_t* codes,
+                              uint8_t* scales, int32_t* flag, hipStream_t s);
 hipError_t launch_nvfp4_to_w2(int n, int R, int C, const uint8_t* e2m1, const uint8_t* e4m3,
                               const float* scale_2, uint8_t* codes, uint8_t* scales, int32_t* flag,
                               hipStream_t s);

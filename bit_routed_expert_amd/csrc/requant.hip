@@ -117,7 +117,160 @@ nvfp4_to_w2_kernel(long long nblocks, long long blocks_per_tensor,
   scales[b] = (uint8_t)(best + 127);
 }
 
+// ------------------------------------------------------------------------------------------------
+// FP8 block-quant and MXFP4 inputs ("The v0.24.0 port", section "Our hooks", fp8.py bullet: fp8
+// weights with fp32 scales per 128 x 128 block re-quantized to the sign-symmetric codebook in
+// float64 math; README: the FP8 block-quant and FP4 checkpoint flavours load). The same exact
+// search, with every element's own exponent: |x_k| = N_k * 2^P_k (N_k < 2^28), each element
+// aligned to the block's smallest exponent Pm in 64 bits (a_k = N_k << (P_k - Pm), the exponents
+// of one block differ by at most 14 for fp8 and not at all for MXFP4, so a_k < 2^42):
+//   D(e) 2^-Z = Q(e) 2^(2e - Z) - A(e) 2^(e + 1 + Pm - Z),  Q = 32 + 15 n4(e),
+//   A(e) = sum a_k + 3 * sum over {t_k > e} a_k,
+// with the same thresholds t_k and window [top-6, top] as above.
+// ------------------------------------------------------------------------------------------------
+__device__ void search_block(const uint32_t (&N)[32], const int (&P)[32], uint32_t neg, uint32_t& c0, uint32_t& c1,
+                             int& best) {
+  constexpr int kNone = -100000;
+  int t[32];
+  int top = kNone, Pm = 1 << 30;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    t[k] = kNone;
+    if (N[k]) {
+      const int L = ilog2_u32(N[k]);
+      t[k] = P[k] + L - 1 + (4ull * N[k] > (5ull << L) ? 1 : 0);
+      const int c = P[k] + L + ((N[k] & (N[k] - 1)) ? 1 : 0);
+      top = c > top ? c : top;
+      Pm = P[k] < Pm ? P[k] : Pm;
+    }
+  }
+  best = -127;
+  if (top != kNone) {
+    const int lo = max(-127, min(127, top - 6));
+    const int hi = max(-127, min(127, top));
+    const int Z = min(2 * lo, lo + 1 + Pm);
+    uint64_t a[32], tot = 0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      a[k] = N[k] ? (uint64_t)N[k] << (P[k] - Pm) : 0ull;
+      tot += a[k];
+    }
+    __int128 best_v = 0;
+    for (int e = lo; e <= hi; ++e) {
+      uint64_t a4 = 0;
+      int n4 = 0;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const bool q4 = t[k] > e;
+        a4 += q4 ? a[k] : 0ull;
+        n4 += q4 ? 1 : 0;
+      }
+      const __int128 A = (__int128)(tot + 3ull * a4);
+      const __int128 Q = 32 + 15 * n4;
+      const __int128 v = (Q << (2 * e - Z)) - (A << (e + 1 + Pm - Z));
+      if (e == lo || v < best_v) { best_v = v; best = e; }
+    }
+  }
+  c0 = c1 = 0;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const bool q4 = t[k] > best;
+    const bool ng = (neg >> k) & 1u;
+    const uint32_t c = ng ? (q4 ? 0u : 1u) : (q4 ? 3u : 2u);
+    if (k < 16) c0 |= c << (2 * k); else c1 |= c << (2 * (k - 16));
+  }
+}
+
+// fp8 e4m3 [n][R][C] with fp32 scales [n][R/128][C/128]: one thread per 32-element block.
+__global__ void __launch_bounds__(256)
+fp8_block128_to_w2_kernel(long long nblocks, int R, int C, const uint8_t* __restrict__ e4m3,
+                          const float* __restrict__ bscale, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                          int32_t* __restrict__ flag) {
+  const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const int nb_row = C / 32;
+  const long long row = b / nb_row;           // row over all tensors
+  const int c32 = (int)(b - row * nb_row);
+  const long long tensor = row / R;
+  const int r = (int)(row - tensor * R);
+  const float sc = bscale[(tensor * (R / 128) + r / 128) * (C / 128) + c32 / 4];
+  const uint32_t su = __builtin_bit_cast(uint32_t, sc);
+  const int sexp = (su >> 23) & 255;
+  if (sexp == 255) { atomicOr(flag, 1); *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{0, 0}; scales[b] = 0; return; }
+  const uint32_t F = sexp ? ((su & 0x7fffffu) | 0x800000u) : (su & 0x7fffffu);
+  const int G = sexp ? sexp - 150 : -149;
+  const uint32_t sneg = su >> 31;
+  const u32x4_t w0 = *reinterpret_cast<const u32x4_t*>(e4m3 + 32 * b);
+  const u32x4_t w1 = *reinterpret_cast<const u32x4_t*>(e4m3 + 32 * b + 16);
+  uint32_t N[32];
+  int P[32];
+  uint32_t neg = 0;
+  bool nan = false;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t word = k < 16 ? w0[k >> 2] : w1[(k - 16) >> 2];
+    const uint32_t byte = (word >> (8 * (k & 3))) & 0xffu;
+    const int ex = (byte >> 3) & 15, mt = byte & 7;
+    nan |= ex == 15 && mt == 7;
+    const uint32_t S = ex ? 8u + mt : (uint32_t)mt;
+    N[k] = S * F;                            // < 2^28
+    P[k] = (ex ? ex - 10 : -9) + G;
+    neg |= (((byte >> 7) ^ sneg) & 1u) << k;
+  }
+  if (nan) { atomicOr(flag, 1); *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{0, 0}; scales[b] = 0; return; }
+  uint32_t c0, c1;
+  int best;
+  search_block(N, P, neg, c0, c1, best);
+  *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{c0, c1};
+  scales[b] = (uint8_t)(best + 127);
+}
+
+// MXFP4 e2m1 [n][R][C/2] with UE8M0 bytes [n][R][C/32]: one thread per 32-element block.
+__global__ void __launch_bounds__(256)
+mxfp4_to_w2_kernel(long long nblocks, const uint8_t* __restrict__ e2m1, const uint8_t* __restrict__ ue8m0,
+                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int32_t* __restrict__ flag) {
+  const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const int sb = ue8m0[b];
+  if (sb == 255) { atomicOr(flag, 1); *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{0, 0}; scales[b] = 0; return; }
+  const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(e2m1 + 16 * b);
+  constexpr uint64_t kTwiceMag = 0x0C08060403020100ull;
+  uint32_t N[32];
+  int P[32];
+  uint32_t neg = 0;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t nib = (raw[k >> 3] >> (4 * (k & 7))) & 15u;
+    N[k] = (uint32_t)((kTwiceMag >> (8 * (nib & 7))) & 0xff);   // twice the e2m1 magnitude
+    P[k] = sb - 128;                                              // 2^(b-127), halved
+    neg |= ((nib >> 3) & 1u) << k;
+  }
+  uint32_t c0, c1;
+  int best;
+  search_block(N, P, neg, c0, c1, best);
+  *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{c0, c1};
+  scales[b] = (uint8_t)(best + 127);
+}
+
 }  // namespace
+
+hipError_t launch_fp8_block128_to_w2(int n, int R, int C, const uint8_t* e4m3, const float* bscale,
+                                     uint8_t* codes, uint8_t* scales, int32_t* flag, hipStream_t s) {
+  const long long nb = (long long)n * R * (C / 32);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(fp8_block128_to_w2_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, nb, R, C, e4m3,
+                     bscale, codes, scales, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_to_w2(int n, int R, int C, const uint8_t* e2m1, const uint8_t* ue8m0, uint8_t* codes,
+                              uint8_t* scales, int32_t* flag, hipStream_t s) {
+  const long long nb = (long long)n * R * (C / 32);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp4_to_w2_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, nb, e2m1, ue8m0, codes,
+                     scales, flag);
+  return hipGetLastError();
+}
 
 hipError_t launch_nvfp4_to_w2(int n, int R, int C, const uint8_t* e2m1, const uint8_t* e4m3,
                               const float* scale_2, uint8_t* codes, uint8_t* scales, int32_t* flag,

@@ -52,7 +52,9 @@ enum moe_w2_status {
   MOE_W2_ENOMEM = -4,        /* device allocation failed */
   MOE_W2_EHIP = -5,          /* a HIP runtime call failed */
   MOE_W2_EWORKSPACE = -6,    /* workspace null or smaller than moe_w2_workspace_bytes() */
-  MOE_W2_ENVFP4 = -7         /* NaN e4m3 byte or NaN / infinite scale_2 in nvfp4_to_w2 input */
+  MOE_W2_ENVFP4 = -7,        /* NaN e4m3 byte or NaN / infinite scale_2 in nvfp4_to_w2 input */
+  MOE_W2_ENAN = -8           /* NaN element or scale, or non-finite scale, in fp8_block128_to_w2 /
+                                mxfp4_to_w2 input */
 };
 
 enum moe_w2_out_dtype { MOE_W2_OUT_BF16 = 0, MOE_W2_OUT_F32 = 1 };
@@ -270,6 +272,35 @@ int moe_w2_read_miss_counter(const void* workspace, int64_t* miss_pairs, void* s
  */
 int nvfp4_to_w2(int n, int R, int C,
                 const uint8_t* e2m1, const uint8_t* e4m3, const float* scale_2,
+                uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * fp8_block128_to_w2 - load-time re-quantizer FP8 block-quant -> canonical 2-bit planes.
+ * Source: "The v0.24.0 port", section "Our hooks", fp8.py bullet (FP8 block-quant checkpoints:
+ * fp8 weights with fp32 block-128 scales re-quantized to the sign-symmetric codebook at load in
+ * float64 math); README: the three checkpoint flavours that load.
+ *   e4m3   [n][R][C]          E4M3FN weights
+ *   bscale [n][R/128][C/128]  fp32 scale of each 128 x 128 block (reading: the usual block-quant
+ *                             layout; the pages name "block-128" only)
+ *   codes  [n][R][C/4], scales [n][R][C/32]  as nvfp4_to_w2
+ * x = e4m3 * bscale (exact: 4 + 24 significant bits); then exactly nvfp4_to_w2's choice per
+ * 32-element block (exponent minimising the exact squared error over [-127, 127], ties to the
+ * lower exponent, |x| = 2.5 * 2^e -> magnitude 1, sign from the sign bit of x).
+ * R and C multiples of 128. Synchronous; MOE_W2_ENAN for a NaN e4m3 byte or a non-finite scale
+ * (the affected blocks' outputs are then unspecified).
+ */
+int fp8_block128_to_w2(int n, int R, int C, const uint8_t* e4m3, const float* bscale,
+                       uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * mxfp4_to_w2 - load-time re-quantizer MXFP4 (e2m1 with UE8M0 block-32 scales, the FP4
+ * checkpoints' experts; README: "FP4 experts ... codes remap") -> canonical 2-bit planes.
+ *   e2m1 [n][R][C/2] (low nibble = even element), ue8m0 [n][R][C/32]; outputs as nvfp4_to_w2.
+ * x = e2m1 * 2^(b-127) exactly, then nvfp4_to_w2's choice per block (reading: the "codes remap"
+ * of the FP4 flavour is this exact re-quantization; an e2m1 code has 16 values, the 2-bit code 4,
+ * so no plain remap exists). C a multiple of 32. Synchronous; MOE_W2_ENAN for a scale byte 255.
+ */
+int mxfp4_to_w2(int n, int R, int C, const uint8_t* e2m1, const uint8_t* ue8m0,
                 uint8_t* codes, uint8_t* scales, void* stream);
 
 #ifdef __cplusplus

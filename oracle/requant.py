@@ -55,6 +55,12 @@ def _load():
         lib.oracle_requant_rows.argtypes = [ctypes.c_int64, ctypes.c_int64, u8p, u8p, ctypes.c_float,
                                             u8p, u8p, ctypes.c_int, ctypes.c_int]
         lib.oracle_requant_rows.restype = ctypes.c_int
+        f32p = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_fp8_block128_rows.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, u8p, f32p, u8p, u8p,
+                                                 ctypes.c_int, ctypes.c_int]
+        lib.oracle_fp8_block128_rows.restype = ctypes.c_int
+        lib.oracle_mxfp4_rows.argtypes = [ctypes.c_int64, ctypes.c_int64, u8p, u8p, u8p, u8p, ctypes.c_int, ctypes.c_int]
+        lib.oracle_mxfp4_rows.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -81,6 +87,32 @@ def nvfp4_block_values(e2m1_bytes, e4m3_bytes, scale2):
         v = e2m1_value(nib) * e4m3_value(int(e4m3_bytes[k // 16])) * s2
         negs.append(math.copysign(1.0, v) < 0)
         mags.append(Fraction(abs(v)))
+    return negs, mags
+
+
+def fp8_block_values(e4m3_bytes, scale):
+    """One 32-element block of FP8 block-quant weights ("The v0.24.0 port", section "Our hooks",
+    fp8.py bullet: fp8 + fp32 block-128 scales re-quantized in float64 math): x = e4m3 * scale,
+    formed in f64 (exact: at most 4 + 24 significant bits). Returns (negative flags, exact
+    magnitudes as Fractions)."""
+    s = float(np.float32(scale))
+    negs, mags = [], []
+    for b in e4m3_bytes:
+        v = e4m3_value(int(b)) * s
+        negs.append(math.copysign(1.0, v) < 0)
+        mags.append(Fraction(abs(v)))
+    return negs, mags
+
+
+def mxfp4_block_values(e2m1_bytes, scale_byte):
+    """One 32-element MXFP4 block (README: the FP4 checkpoints' experts): x = e2m1 * 2^(b-127),
+    exact. Returns (negative flags, exact magnitudes)."""
+    t = Fraction(2) ** (int(scale_byte) - 127)
+    negs, mags = [], []
+    for k in range(32):
+        v = e2m1_value((int(e2m1_bytes[k // 2]) >> (4 * (k & 1))) & 15)
+        negs.append(math.copysign(1.0, v) < 0)
+        mags.append(Fraction(abs(v)) * t)
     return negs, mags
 
 
@@ -153,3 +185,57 @@ def nvfp4_to_w2(e2m1, e4m3, scale2, window=True, nthreads=None):
     for i in range(n):
         codes[i], scales[i] = requant_rows(e2m1[i], e4m3[i], scale2[i], window, nthreads)
     return codes, scales
+
+
+def fp8_block128_to_w2(e4m3, scales, window=True, nthreads=None):
+    """FP8 block-quant tensors: e4m3 [n, R, C] bytes, scales [n, R/128, C/128] fp32 ->
+    codes [n, R, C/4], scale bytes [n, R, C/32] (the exact search of this module per 32-block)."""
+    lib = _load()
+    e4m3 = np.ascontiguousarray(e4m3, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    n, R, C = e4m3.shape
+    if R % 128 or C % 128 or scales.shape != (n, R // 128, C // 128):
+        raise ValueError("shape mismatch")
+    codes = np.zeros((n, R, C // 4), dtype=np.uint8)
+    out = np.zeros((n, R, C // 32), dtype=np.uint8)
+    nt = nthreads or os.cpu_count() or 1
+    f32p = ctypes.POINTER(ctypes.c_float)
+    for i in range(n):
+        rc = lib.oracle_fp8_block128_rows(R, C, 0, _ptr(e4m3[i]), scales[i].ctypes.data_as(f32p), _ptr(codes[i]),
+                                          _ptr(out[i]), int(bool(window)), int(nt))
+        if rc:
+            raise ValueError("invalid FP8 input (NaN e4m3 byte or non-finite scale)")
+    return codes, out
+
+
+def mxfp4_to_w2(e2m1, ue8m0, window=True, nthreads=None):
+    """MXFP4 tensors: e2m1 [n, R, C/2], ue8m0 [n, R, C/32] -> codes [n, R, C/4], scale bytes [n, R, C/32]."""
+    lib = _load()
+    e2m1 = np.ascontiguousarray(e2m1, dtype=np.uint8)
+    ue8m0 = np.ascontiguousarray(ue8m0, dtype=np.uint8)
+    n, R, half_c = e2m1.shape
+    C = half_c * 2
+    if ue8m0.shape != (n, R, C // 32):
+        raise ValueError("shape mismatch")
+    codes = np.zeros((n, R, C // 4), dtype=np.uint8)
+    out = np.zeros((n, R, C // 32), dtype=np.uint8)
+    nt = nthreads or os.cpu_count() or 1
+    for i in range(n):
+        if lib.oracle_mxfp4_rows(R, C, _ptr(e2m1[i]), _ptr(ue8m0[i]), _ptr(codes[i]), _ptr(out[i]),
+                                 int(bool(window)), int(nt)):
+            raise ValueError("invalid MXFP4 input (scale byte 255)")
+    return codes, out
+
+
+def requant_block_c_fp8(e4m3_bytes, scale, window=False):
+    """One FP8 block through the C implementation (a [128, 128] tile holding the block in row 0)."""
+    e = np.zeros((1, 128, 128), np.uint8)
+    e[0, 0, :32] = np.asarray(e4m3_bytes, np.uint8)
+    codes, sc = fp8_block128_to_w2(e, np.full((1, 1, 1), scale, np.float32), window, 1)
+    return [(int(codes[0, 0, k // 4]) >> (2 * (k % 4))) & 3 for k in range(32)], int(sc[0, 0, 0])
+
+
+def requant_block_c_mxfp4(e2m1_bytes, scale_byte, window=False):
+    codes, sc = mxfp4_to_w2(np.asarray(e2m1_bytes, np.uint8).reshape(1, 1, 16), np.full((1, 1, 1), scale_byte, np.uint8),
+                            window, 1)
+    return [(int(codes[0, 0, k // 4]) >> (2 * (k % 4))) & 3 for k in range(32)], int(sc[0, 0, 0])

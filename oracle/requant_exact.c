@@ -109,25 +109,12 @@ static int gt_five(uint64_t N, int d) {
 static int ilog2(uint64_t v) { int r = -1; while (v) { v >>= 1; ++r; } return r; }
 
 /*
- * One 32-element block. e2m1: 16 bytes (low nibble = even element), e4m3: 2 bytes (one per 16
- * elements), scale2 decoded as F * 2^G with sign neg2. Writes 8 canonical code bytes and the
- * scale byte.
+ * The exact search of one 32-element block whose elements are |x_k| = N[k] * 2^P[k] (N < 2^32)
+ * with sign flags neg[k]. Writes 8 canonical code bytes and the scale byte. Shared by every input
+ * format: the format only decides how N, P and the sign come out of its bytes.
  */
-static int requant_block(const uint8_t* e2m1, const uint8_t* e4m3, uint64_t F, int G, int neg2,
-                         int window, uint8_t* codes_out, uint8_t* scale_out) {
-  uint64_t N[32];
-  int P[32], neg[32];
-  for (int j = 0; j < 2; ++j) {
-    uint64_t S; int Pe, negs;
-    if (decode_e4m3(e4m3[j], &S, &Pe, &negs)) return -1;
-    for (int i = 0; i < 16; ++i) {
-      int k = 16 * j + i;
-      int nib = (e2m1[k / 2] >> (4 * (k & 1))) & 15;
-      N[k] = (uint64_t)E2M1_TWICE_MAG[nib & 7] * S * F;   /* < 12*15*2^24 < 2^32 */
-      P[k] = Pe + G - 1;                                    /* the -1 undoes the doubling */
-      neg[k] = ((nib >> 3) & 1) ^ negs ^ neg2;
-    }
-  }
+static void requant_elems(const uint64_t* N, const int* P, const int* neg, int window, uint8_t* codes_out,
+                          uint8_t* scale_out) {
   /* max |x| and top = ceil(log2 max|x|) */
   int any = 0, top = 0;
   for (int k = 0; k < 32; ++k) {
@@ -193,7 +180,97 @@ static int requant_block(const uint8_t* e2m1, const uint8_t* e4m3, uint64_t F, i
     codes_out[k / 4] |= (uint8_t)(c << (2 * (k % 4)));
   }
   *scale_out = (uint8_t)(best_e + 127);
+}
+
+/*
+ * One NVFP4 block. e2m1: 16 bytes (low nibble = even element), e4m3: 2 bytes (one per 16
+ * elements), scale2 decoded as F * 2^G with sign neg2.
+ */
+static int requant_block(const uint8_t* e2m1, const uint8_t* e4m3, uint64_t F, int G, int neg2,
+                         int window, uint8_t* codes_out, uint8_t* scale_out) {
+  uint64_t N[32];
+  int P[32], neg[32];
+  for (int j = 0; j < 2; ++j) {
+    uint64_t S; int Pe, negs;
+    if (decode_e4m3(e4m3[j], &S, &Pe, &negs)) return -1;
+    for (int i = 0; i < 16; ++i) {
+      int k = 16 * j + i;
+      int nib = (e2m1[k / 2] >> (4 * (k & 1))) & 15;
+      N[k] = (uint64_t)E2M1_TWICE_MAG[nib & 7] * S * F;   /* < 12*15*2^24 < 2^32 */
+      P[k] = Pe + G - 1;                                    /* the -1 undoes the doubling */
+      neg[k] = ((nib >> 3) & 1) ^ negs ^ neg2;
+    }
+  }
+  requant_elems(N, P, neg, window, codes_out, scale_out);
   return 0;
+}
+
+/*
+ * FP8 block-quant input ("The v0.24.0 port", section "Our hooks", fp8.py bullet: fp8 weights
+ * with fp32 scales per 128 x 128 block, re-quantized in float64 math): x = e4m3 * scale, exact
+ * (4 + 24 significant bits). One 32-element block of a row: 32 e4m3 bytes and the fp32 scale of
+ * its 128 x 128 block.
+ */
+static int requant_block_fp8(const uint8_t* e4m3, float scale, int window, uint8_t* codes_out, uint8_t* scale_out) {
+  uint64_t F; int G, negs;
+  if (decode_f32(scale, &F, &G, &negs)) return -1;
+  uint64_t N[32];
+  int P[32], neg[32];
+  for (int k = 0; k < 32; ++k) {
+    uint64_t S; int Pe, ne;
+    if (decode_e4m3(e4m3[k], &S, &Pe, &ne)) return -1;
+    N[k] = S * F;            /* < 15 * 2^24 */
+    P[k] = Pe + G;
+    neg[k] = ne ^ negs;
+  }
+  requant_elems(N, P, neg, window, codes_out, scale_out);
+  return 0;
+}
+
+/*
+ * MXFP4 input (the FP4 checkpoints' experts; README: "FP4 experts ... codes remap"): x = e2m1 *
+ * 2^(b-127) with one UE8M0 byte b per 32 elements, exact. Byte 255 (NaN) is rejected.
+ */
+static int requant_block_mxfp4(const uint8_t* e2m1, uint8_t b, int window, uint8_t* codes_out, uint8_t* scale_out) {
+  if (b == 255) return -1;
+  uint64_t N[32];
+  int P[32], neg[32];
+  for (int k = 0; k < 32; ++k) {
+    int nib = (e2m1[k / 2] >> (4 * (k & 1))) & 15;
+    N[k] = (uint64_t)E2M1_TWICE_MAG[nib & 7];
+    P[k] = (int)b - 127 - 1;
+    neg[k] = (nib >> 3) & 1;
+  }
+  requant_elems(N, P, neg, window, codes_out, scale_out);
+  return 0;
+}
+
+/* fp8 block-quant rows of one tensor: e4m3 [nrows][C], scales [nrows/128][C/128] (fp32) ->
+   codes [nrows][C/4], scales_out [nrows][C/32] */
+int oracle_fp8_block128_rows(int64_t nrows, int64_t C, int64_t row0, const uint8_t* e4m3, const float* scales,
+                             uint8_t* codes, uint8_t* scales_out, int window, int nthreads) {
+  if (C % 128) return -2;
+  int64_t nb = nrows * (C / 32);
+  int err = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(|:err)
+  for (int64_t b = 0; b < nb; ++b) {
+    int64_t r = b / (C / 32), c32 = b % (C / 32);
+    float sc = scales[((row0 + r) / 128) * (C / 128) + (32 * c32) / 128];
+    err |= requant_block_fp8(e4m3 + 32 * b, sc, window, codes + 8 * b, scales_out + b) ? 1 : 0;
+  }
+  return err ? -1 : 0;
+}
+
+/* MXFP4 rows: e2m1 [nrows][C/2], ue8m0 [nrows][C/32] -> codes [nrows][C/4], scales_out [nrows][C/32] */
+int oracle_mxfp4_rows(int64_t nrows, int64_t C, const uint8_t* e2m1, const uint8_t* ue8m0, uint8_t* codes,
+                      uint8_t* scales_out, int window, int nthreads) {
+  if (C % 32) return -2;
+  int64_t nb = nrows * (C / 32);
+  int err = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(|:err)
+  for (int64_t b = 0; b < nb; ++b)
+    err |= requant_block_mxfp4(e2m1 + 16 * b, ue8m0[b], window, codes + 8 * b, scales_out + b) ? 1 : 0;
+  return err ? -1 : 0;
 }
 
 int oracle_requant_block(const uint8_t* e2m1_16, const uint8_t* e4m3_2, float scale2,

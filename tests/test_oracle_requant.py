@@ -200,3 +200,80 @@ def test_optimality_certificate_on_workload_blocks():
                 # nearest of the four codebook values with the same sign convention
                 assert abs(abs(Fraction(val)) - m) <= abs((5 - abs(Fraction(val)) / t) * t - m)
                 assert (val < 0) == negs[k]
+
+
+# ------------------------------------------------------------------------------------------------
+# FP8 block-quant and MXFP4 inputs ("The v0.24.0 port", section "Our hooks", fp8.py bullet: fp8 +
+# fp32 block-128 re-quantized in float64 math; README: FP8 block-quant and FP4 checkpoints load):
+# the same exact search, other element decoders.
+# ------------------------------------------------------------------------------------------------
+
+def _random_fp8_block(rng):
+    b = rng.integers(0, 256, 32).astype(np.uint8)
+    b[(b & 0x7F) == 0x7F] = 0x00                          # no NaN encodings
+    b[rng.random(32) < 0.1] = rng.choice([0x00, 0x80, 0x01, 0x81])   # zeros (signed) and subnormals
+    return b
+
+
+def test_fp8_and_mxfp4_c_match_rational_reference():
+    rng = np.random.default_rng(31)
+    for i in range(60):
+        b = _random_fp8_block(rng)
+        s = np.float32(rng.choice([1.0, -1.0]) * 2.0 ** rng.uniform(-20, 10)) if i % 10 else np.float32(1.5e-40)
+        assert requant.requant_block_c_fp8(b, s, window=False) == requant.requant_block_fraction(
+            *requant.fp8_block_values(b, s)), i
+        e = rng.integers(0, 256, 16).astype(np.uint8)
+        sb = int(rng.integers(0, 255))
+        assert requant.requant_block_c_mxfp4(e, sb, window=False) == requant.requant_block_fraction(
+            *requant.mxfp4_block_values(e, sb)), i
+
+
+def test_fp8_and_mxfp4_window_equals_full_scan():
+    rng = np.random.default_rng(32)
+    for i in range(400):
+        b = _random_fp8_block(rng)
+        s = np.float32(2.0 ** rng.uniform(-30, 20))
+        assert requant.requant_block_c_fp8(b, s, window=True) == requant.requant_block_c_fp8(b, s, window=False), i
+        e = rng.integers(0, 256, 16).astype(np.uint8)
+        sb = int(rng.integers(0, 255))
+        assert requant.requant_block_c_mxfp4(e, sb, True) == requant.requant_block_c_mxfp4(e, sb, False), i
+
+
+def test_w2_roundtrip_through_fp8_and_mxfp4():
+    """2-bit planes written as FP8 (+-1, +-4 are e4m3 values 0x38/0xB8, 0x48/0xC8; the block scale
+    2^e as the fp32 scale) or as MXFP4 (e2m1 +-1, +-4; scale byte 127 + e) re-quantize to
+    themselves, except single-magnitude blocks: (+-1, e) -> (+-4, e-2) (lower-exponent tie rule)."""
+    rng = np.random.default_rng(33)
+    n = 128
+    codes = rng.integers(0, 4, size=(n, 128), dtype=np.uint8)
+    codes[0, :32] = rng.choice([1, 2], size=32)                        # one single-magnitude block
+    e = int(rng.integers(-40, 40))
+    fp8_of = np.array([0xC8, 0xB8, 0x38, 0x48], np.uint8)
+    got_c, got_s = requant.fp8_block128_to_w2(fp8_of[codes][None], np.full((1, 1, 1), 2.0 ** e, np.float32))
+    got = formats.unpack_codes(got_c[0])
+    nib_of = np.array([0xE, 0xA, 0x2, 0x6], np.uint8)
+    nib = nib_of[codes]
+    m_c, m_s = requant.mxfp4_to_w2((nib[:, 0::2] | (nib[:, 1::2] << 4))[None], np.full((1, n, 4), 127 + e, np.uint8))
+    for g, s in ((got, got_s[0]), (formats.unpack_codes(m_c[0]), m_s[0])):
+        assert s[0, 0] == 127 + e - 2 and np.array_equal(g[0, :32], np.where(codes[0, :32] == 2, 3, 0))
+        assert np.all(s.reshape(-1)[1:] == 127 + e)
+        assert np.array_equal(g.reshape(-1)[32:], codes.reshape(-1)[32:])   # every other block
+
+
+def test_mxfp4_scale_equivariance_and_fp8_odd_symmetry():
+    """MXFP4: raising every scale byte by k raises every chosen exponent by k and keeps the codes
+    (within range). FP8: flipping every e4m3 sign bit maps codes c -> 3 - c, same exponents."""
+    rng = np.random.default_rng(34)
+    e2m1 = rng.integers(0, 256, size=(1, 64, 64), dtype=np.uint8)
+    sb = rng.integers(100, 140, size=(1, 64, 4)).astype(np.uint8)
+    c0, s0 = requant.mxfp4_to_w2(e2m1, sb)
+    for k in (-7, 1, 9):
+        ck, sk = requant.mxfp4_to_w2(e2m1, (sb.astype(int) + k).astype(np.uint8))
+        assert np.array_equal(ck, c0) and np.array_equal(sk.astype(int), s0.astype(int) + k)
+    b = rng.integers(0, 256, size=(1, 128, 128)).astype(np.uint8)
+    b[(b & 0x7F) == 0x7F] = 0x7E
+    sc = np.float32(2.0 ** rng.uniform(-10, 0, size=(1, 1, 1))).astype(np.float32)
+    fc, fs = requant.fp8_block128_to_w2(b, sc)
+    nc, ns = requant.fp8_block128_to_w2(b ^ np.uint8(0x80), sc)
+    assert np.array_equal(ns, fs)
+    assert np.array_equal(formats.unpack_codes(nc), 3 - formats.unpack_codes(fc))

@@ -143,3 +143,23 @@ def nvfp4_tensor(i, seed=REQUANT["seed"], R=REQUANT["R"], C=REQUANT["C"]):
     e4m3 = rng.integers(0x18, 0x59, size=(R, C // 16), dtype=np.uint8)
     scale2 = np.float32(rng.uniform(1e-3, 1e-2))
     return e2m1, e4m3, scale2
+
+
+def fp8_block_tensor(i, R=2048, C=6144, seed=REQUANT["seed"]):
+    """FP8 block-quant tensor i: E4M3FN bytes uniform over the 254 finite encodings [R, C] (so
+    zeros, subnormals, both signs and the whole exponent range occur), then fp32 scales per
+    128 x 128 block, 2^U(-12, -2) [R/128, C/128]; seeded by (seed, 1000 + i)."""
+    rng = np.random.default_rng([seed, 1000 + i])
+    b = rng.integers(0, 254, size=(R, C), dtype=np.uint16).astype(np.uint8)
+    b = np.where(b >= 0x7F, b + 1, b).astype(np.uint8)          # skip 0x7F; 0xFF is never drawn
+    scales = np.exp2(rng.uniform(-12.0, -2.0, size=(R // 128, C // 128))).astype(np.float32)
+    return b, scales
+
+
+def mxfp4_tensor(i, R=2048, C=6144, seed=REQUANT["seed"]):
+    """MXFP4 tensor i: e2m1 nibbles uniform over all 16 values, packed low nibble first [R, C/2],
+    UE8M0 scale bytes 127 + U{-12..2} [R, C/32]; seeded by (seed, 2000 + i)."""
+    rng = np.random.default_rng([seed, 2000 + i])
+    e2m1 = rng.integers(0, 256, size=(R, C // 2), dtype=np.uint8)
+    ue8m0 = (127 + rng.integers(-12, 3, size=(R, C // 32))).astype(np.uint8)
+    return e2m1, ue8m0
