@@ -262,7 +262,7 @@ def main():
     achieved = gu_bytes_all / (gu_ms_all * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     traffic = traffic_from_profiles("decode_gate_up", src_hash)
-    roofline = dict(bound="hbm", kernel="decode_gate_up_kernel<4,false> (T=8 and T=32 calls)",
+    roofline = dict(bound="hbm", kernel="decode_gate_up_kernel<4,false,0> (2-bit planes; T=8 and T=32 calls)",
                     achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
                     traffic=traffic, launches=n_gu, avg_launch_us=round(gu_ms_all / n_gu * 1e3, 3),
