@@ -22,6 +22,9 @@ The JSON line also carries:
                   core rate of the two grouped GEMMs against the dense bf16/fp16 peak;
   slots         - the expert-slot forward against the plain forward at T=8 and 32;
   w4            - the FP4 (MXFP4) expert planes: decode at T=1, 8, 32 and the prefill GEMMs;
+  requant       - the three load-time re-quantizers (NVFP4, FP8 block-128, MXFP4) over 256 tensors;
+  sweep         - the sign-bias diagnostic: 8 synthetic expert tensors of [2048, 6144] against all
+                  1239 candidate codebooks, with the symmetric / asymmetric statistics it finds;
   cpu_baseline  - the f64 CPU oracle on a bounded sample of the same workload.
 """
 import argparse
@@ -41,6 +44,12 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
 DECODE_TS = (1, 8, 32)
 DIRECT_MAX_PAIRS = 8            # pairs up to which the forward takes the two-kernel direct path
+# VALU issue peak: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 instruction per SIMD every 4 cycles
+VALU_PEAK_LANE_OPS = 256 * 4 * 2.4e9 / 4 * 64
+# VALU instructions per element per candidate exponent in the codebook sweep's main loop (the
+# high-word-select, no-zero variant taken by e2m1 codebooks): 335 per 32 elements in the gfx950
+# assembly hipcc -O3 emits for sweep.hip
+SWEEP_VALU_PER_EVAL = 335 / 32
 
 
 def parse():
@@ -56,6 +65,9 @@ def parse():
     ap.add_argument("--no-slots", action="store_true")
     ap.add_argument("--no-w4", action="store_true")
     ap.add_argument("--requant-iters", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--sweep-tensors", type=int, default=8)
+    ap.add_argument("--sweep-iters", type=int, default=2)
     ap.add_argument("--eager", action="store_true",
                     help="launch every timed call from Python instead of replaying HIP graphs (for profilers)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -303,6 +315,8 @@ def main():
         out["prefill"] = bench_prefill(args, moe, workloads, torch, dev)
     if not args.no_requant:
         out["requant"] = bench_requant(args, moe, workloads, torch, dev)
+    if not args.no_sweep:
+        out["sweep"] = bench_sweep(args, moe, workloads, torch, dev)
 
     # free GPU memory before the CPU baseline
     if not args.no_cpu_baseline:
@@ -588,5 +602,54 @@ def cpu_baseline(canon, inst):
                        f"host has {os.cpu_count()} logical CPUs")
 
 
+def bench_sweep(args, moe, workloads, torch, dev):
+    """moe_w2_codebook_sweep over --sweep-tensors synthetic tensors of [2048, 6144] (the sign-bias
+    diagnostic's own workload) and all 1239 candidate codebooks: time per call (synchronous, so
+    wall time between event records that bracket it), candidate-block evaluations per second, and
+    what the sweep finds: per tensor the least-error symmetric and asymmetric codebooks with their
+    relative RMS error and bias, and the bias of {-4,-1,1,4}."""
+    c = workloads.SWEEP
+    n, R, C = args.sweep_tensors, c["R"], c["C"]
+    fam = workloads.codebook_family()
+    x = torch.empty((n, R, C), dtype=torch.float32, device="cuda")
+    for i in range(n):
+        x[i].copy_(torch.from_numpy(workloads.sweep_tensor(i)))
+    moe.moe_w2_codebook_sweep(x, fam)        # warm-up (module load, first allocation)
+    ts = []
+    for _ in range(args.sweep_iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        st, mo, best = moe.moe_w2_codebook_sweep(x, fam)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    st, best = st.cpu().numpy(), best.cpu().numpy()
+    M = len(fam)
+    i_sym = int(np.where((fam == np.array([-4, -1, 1, 4], np.float32)).all(1))[0][0])
+    per = []
+    for t in range(n):
+        bs, ba = int(best[t, 0]), int(best[t, 1])
+        per.append(dict(best_sym=fam[bs].tolist(), sym_rel_rms=round(float(st[t, bs, 2]), 5),
+                        sym_bias=float(f"{st[t, bs, 3]:.3e}"), best_asym=fam[ba].tolist(),
+                        asym_rel_rms=round(float(st[t, ba, 2]), 5), asym_bias=float(f"{st[t, ba, 3]:.3e}"),
+                        w2_rel_rms=round(float(st[t, i_sym, 2]), 5), w2_bias=float(f"{st[t, i_sym, 3]:.3e}")))
+    ab = np.array([abs(p["asym_bias"]) for p in per])
+    sb = np.array([abs(p["sym_bias"]) for p in per])
+    blocks = n * R * C // 32
+    del x
+    torch.cuda.empty_cache()
+    return dict(workload=f"moe_w2_codebook_sweep: {n} synthetic tensors of [{R}, {C}] x {M} codebooks "
+                         "(4 distinct e2m1 values, max magnitude 3/4/6)",
+                ms=round(ms, 2), candidate_blocks_per_s=round(blocks * M / (ms * 1e-3), 1),
+                element_exponent_evals_per_s=round(blocks * M * 320 / (ms * 1e-3), 1),
+                roofline=dict(bound="alu", achieved=round(blocks * M * 320 * SWEEP_VALU_PER_EVAL / (ms * 1e-3) / 1e12, 2),
+                              peak=round(VALU_PEAK_LANE_OPS / 1e12, 2), unit="T VALU lane-ops/s",
+                              frac=round(blocks * M * 320 * SWEEP_VALU_PER_EVAL / (ms * 1e-3) / VALU_PEAK_LANE_OPS, 4)),
+                median_abs_bias_asym_over_sym=round(float(np.median(ab / np.maximum(sb, 1e-300))), 2),
+                asym_bias_negative=int(np.sum([p["asym_bias"] < 0 for p in per])),
+                tensors=per, iters=args.sweep_iters)
+
 if __name__ == "__main__":
     main()
+

@@ -63,6 +63,7 @@ def _lib():
             "moe_w2_pack_slot": ([P, I32, P, P, P, P, P], I32),
             "moe_w2_forward_slots": ([P, I32, P, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
             "moe_w2_read_miss_counter": ([P, ctypes.POINTER(ctypes.c_int64), P], I32),
+            "moe_w2_codebook_sweep": ([I32, I32, I32, P, I32, P, P, P, P, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -330,3 +331,25 @@ def mxfp4_to_w2(e2m1, ue8m0, codes=None, scales=None):
                               _dev(codes, torch.uint8, "codes"), _dev(scales, torch.uint8, "scales"), _stream()),
            "mxfp4_to_w2")
     return codes, scales
+
+
+def moe_w2_codebook_sweep(x, codebooks):
+    """Sign-bias diagnostic. x [n, R, C] float32 (device); codebooks [M, 4] float32 (host, numpy or
+    CPU tensor, each row strictly ascending). Returns (stats [n, M, 4] float64 = sse, err, rel_rms,
+    bias; moments [n, 2] float64 = sum x^2, sum x; best [n, 2] int32 = least-sse symmetric and
+    asymmetric codebook, -1 if none), all on the device."""
+    import numpy as np
+    n, R, C = x.shape
+    cb = np.ascontiguousarray(codebooks.cpu().numpy() if isinstance(codebooks, torch.Tensor) else codebooks,
+                              dtype=np.float32)
+    if cb.ndim != 2 or cb.shape[1] != 4:
+        raise ValueError("codebooks must be [M, 4]")
+    M = cb.shape[0]
+    stats = torch.empty((n, M, 4), dtype=torch.float64, device="cuda")
+    moments = torch.empty((n, 2), dtype=torch.float64, device="cuda")
+    best = torch.empty((n, 2), dtype=torch.int32, device="cuda")
+    _check(_lib().moe_w2_codebook_sweep(n, R, C, _dev(x, torch.float32, "x"), M,
+                                        cb.ctypes.data_as(ctypes.c_void_p), _dev(stats, torch.float64, "stats"),
+                                        _dev(moments, torch.float64, "moments"), _dev(best, torch.int32, "best"),
+                                        _stream()), "moe_w2_codebook_sweep")
+    return stats, moments, best

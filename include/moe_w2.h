@@ -303,6 +303,33 @@ int fp8_block128_to_w2(int n, int R, int C, const uint8_t* e4m3, const float* bs
 int mxfp4_to_w2(int n, int R, int C, const uint8_t* e2m1, const uint8_t* ue8m0,
                 uint8_t* codes, uint8_t* scales, void* stream);
 
+/*
+ * moe_w2_codebook_sweep - sign-bias diagnostic of 2-bit codebooks. README, bullet "2-bit expert
+ * planes - the sign-bias finding", and the vLLM-Moet article, section "Sign symmetry, not error
+ * size, is what collapses naive 2-bit experts": the L2-optimal 2-bit codebook is sign-asymmetric
+ * and leaves a per-tensor bias, the symmetric {-4,-1,1,4} reaches the same relative RMS error
+ * with a far smaller bias; a codebook sweep over expert tensors measures both.
+ *   x          [n][R][C] fp32, device, 16-byte aligned; blocks of 32 along C (C % 32 == 0)
+ *   codebooks  [M][4] fp32, HOST, each strictly ascending and finite; 1 <= M <= 4096
+ *   stats      [n][M][4] float64, device: {sse, err, rel_rms, bias} of tensor t under codebook m
+ *   moments    [n][2] float64, device: {sum x^2, sum x}
+ *   best       [n][2] int32, device: least-sse codebook with q0 = -q3 and q1 = -q2, and least-sse
+ *              other codebook (ties to the lower index; -1 if there is none of that kind)
+ * Quantization per codebook (readings where the pages are silent): scale 2^e per block, e in
+ * [-127, 127] (the planes' UE8M0 block-32 scale); nearest code, halfway -> the code of smaller
+ * magnitude, x = +-0 between q and -q -> the side of its sign bit; e minimises the block's
+ * squared error over the ten exponents from 7 below to 2 above e_c, the least e with
+ * max(|q0|,|q3|) 2^e >= max|x| (e_c = -127 for an all-zero block), equal errors to the lower e;
+ * a block's squared error is summed in float64 in element order without fused operations.
+ * sse = sum of (v - x)^2, err = sum of (v - x), rel_rms = sqrt(sse / sum x^2), bias =
+ * err / sqrt(N sum x^2) (mean error over the rms of x; 0 when sum x^2 = 0), N = R * C.
+ * Synchronous; allocates and frees its own scratch. MOE_W2_EINVAL for a bad codebook, pointer or
+ * size, MOE_W2_EUNSUPPORTED for C % 32 != 0, MOE_W2_ENAN if x holds a NaN or an infinity (the
+ * outputs are then unspecified).
+ */
+int moe_w2_codebook_sweep(int n, int R, int C, const float* x, int M, const float* codebooks,
+                          double* stats, double* moments, int32_t* best, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

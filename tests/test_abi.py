@@ -67,3 +67,22 @@ def test_host_side_validation(lib):
 def test_binding_imports_without_gpu():
     import bit_routed_expert_amd as m
     assert m.moe_w2_abi_version() == 1
+
+
+def test_codebook_sweep_host_validation(lib):
+    """Argument checks of moe_w2_codebook_sweep happen on the host, before any device call."""
+    P = ctypes.c_void_p
+    f = lib.moe_w2_codebook_sweep
+    f.argtypes = [ctypes.c_int] * 3 + [P, ctypes.c_int, P, P, P, P, P]
+    f.restype = ctypes.c_int
+    fake = ctypes.c_void_p(256)
+    good = (ctypes.c_float * 4)(-4, -1, 1, 4)
+    flat = (ctypes.c_float * 4)(-4, -1, -1, 4)
+    nan = (ctypes.c_float * 4)(-4, -1, 1, float("nan"))
+    assert f(1, 2, 64, fake, 1, flat, fake, fake, fake, None) == -1
+    assert f(1, 2, 64, fake, 1, nan, fake, fake, fake, None) == -1
+    assert f(1, 2, 48, fake, 1, good, fake, fake, fake, None) == -2
+    assert f(1, 2, 64, fake, 0, good, fake, fake, fake, None) == -1
+    assert f(1, 2, 64, fake, 1, None, fake, fake, fake, None) == -1
+    assert f(-1, 2, 64, fake, 1, good, fake, fake, fake, None) == -1
+    assert f(0, 2, 64, None, 1, good, None, None, None, None) == 0

@@ -163,3 +163,30 @@ def mxfp4_tensor(i, R=2048, C=6144, seed=REQUANT["seed"]):
     e2m1 = rng.integers(0, 256, size=(R, C // 2), dtype=np.uint8)
     ue8m0 = (127 + rng.integers(-12, 3, size=(R, C // 32))).astype(np.uint8)
     return e2m1, ue8m0
+
+
+SWEEP = dict(n=180, R=2048, C=6144, seed=5)
+
+
+def codebook_family():
+    """Candidate 2-bit codebooks for the sign-bias sweep: every set of 4 distinct values from the
+    15 e2m1 values {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6} whose largest magnitude is 3, 4 or 6
+    (one representative per power-of-two scaling, which the block exponent absorbs), ascending,
+    in lexicographic order: float32 [1239, 4]. Holds {-4,-1,1,4} and the other symmetric sets."""
+    import itertools
+    mags = [0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    vals = sorted([-m for m in mags] + [0.0] + mags)
+    out = [c for c in itertools.combinations(vals, 4) if max(abs(c[0]), abs(c[3])) in (3.0, 4.0, 6.0)]
+    return np.array(out, dtype=np.float32)
+
+
+def sweep_tensor(i, R=SWEEP["R"], C=SWEEP["C"], seed=SWEEP["seed"]):
+    """Synthetic expert weight tensor i for the sign-bias sweep, float32 [R, C], stream seed
+    (seed, i): standard normal values, 5% of them (uniform draw < 0.05) widened x3 for heavier
+    tails, then each row scaled by 2^U(-9, -5) (per-output-channel spread). Symmetric in sign."""
+    rng = np.random.default_rng([seed, i])
+    z = rng.standard_normal((R, C), dtype=np.float32)
+    wide = rng.random((R, C), dtype=np.float32) < 0.05
+    np.multiply(z, np.float32(3.0), out=z, where=wide)
+    z *= np.exp2(rng.uniform(-9.0, -5.0, size=(R, 1))).astype(np.float32)
+    return z
