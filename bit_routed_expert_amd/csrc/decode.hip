@@ -224,6 +224,29 @@ MOEW2_DEV void stream_k(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt, i
   }
 }
 
+// R row pairs of one wave as one continuous stream (KS = 1, nkt a multiple of kRing): the slot
+// that held k-tile kt of row pair r is refilled with step r * nkt + kt + kRing of the sequence,
+// which past the pair's last k-tile is the next pair's first, so the ring never drains between
+// pairs. Row pair r accumulates into acc[r]; rows of pair r + 1 start at tile 2 * nkt further.
+template <int NP, int NB, int FMT, int R>
+MOEW2_DEV void stream_rows(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt, int nkt, const uint8_t* arow,
+                           int KR, int g, f32x4_t (&acc)[R][NB], int lane) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    for (int k0 = 0; k0 < nkt; k0 += kRing) {
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) {
+        const int kt = k0 + i;
+        mma_tile<NP, NB, FMT>(ring[i], arow, KR, kt, g, acc[r]);
+        const int kn = kt + kRing;
+        const bool wrap = kn >= nkt;
+        const int rn = wrap ? r + 1 : r;
+        load_tile<NB, FMT>(ring[i], wt, 2 * rn * nkt + (wrap ? kn - nkt : kn), rn < R, lane);
+      }
+    }
+  }
+}
+
 // Stage n rows (split into NP parts) while the weight ring is primed. Batches beyond the first
 // go first, one round trip each; the first batch is issued just before the prime and committed
 // after it, so every path reaches the streaming loop with the same loads outstanding (the
@@ -426,18 +449,23 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------------------------
-// routed down: grid (K / (32*NP), P). The group is that of the gate_up stage (pair_group); wave w handles row groups 2*rq and 2*rq + 1, rq = blockIdx.x*NP + w/KS, over the
-// reduction slice w%KS. Per-pair rows go to pair_out at the pair index (bijective);
+// routed down: grid (K / (32*NPW*R), P). The group is that of the gate_up stage (pair_group);
+// wave w handles the R row pairs rq .. rq + R - 1, rq = (blockIdx.x*NPW + w/KS) * R (row groups
+// 2*rq and 2*rq + 1 of each), over the reduction slice w%KS; with R = 2 (whole reduction per
+// wave) the two pairs are one continuous weight stream, which halves the workgroups and the
+// per-workgroup costs (group scan, staging, ring start) per byte. Per-pair rows go to pair_out at
+// the pair index (bijective);
 // combine_kernel then sums them per token in j order. The blockIdx.x == 0 workgroups count the
 // gated intermediates that overflowed fp16 (each pair belongs to one group).
 // ---------------------------------------------------------------------------------------------
-template <int NPW, int FMT>
+template <int NPW, int FMT, int R>
 __global__ void __launch_bounds__(kThreads)
 decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                    const _Float16* __restrict__ act, const int32_t* __restrict__ ids,
                    float* __restrict__ pair_out, long long* __restrict__ counters, int P, int E, int K,
                    int I) {
   constexpr int KS = kWaves / NPW;
+  static_assert(R == 1 || KS == 1, "row pairs per wave need the whole reduction in each wave");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ ScanLds sh;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -446,7 +474,7 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
   if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, nullptr, e, n_e)) return;
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int pw = w / KS, ks = w % KS;
-  const int rq = blockIdx.x * NPW + pw;
+  const int rq = (blockIdx.x * NPW + pw) * R;   // the wave's first row pair
   WaveTiles wt = wave_tiles<FMT>(codes, scales, e, (uint32_t)(nrg * nkt));
   wt.tile[0] = (uint32_t)(2 * rq * nkt);
   wt.tile[1] = (uint32_t)((2 * rq + 1) * nkt);
@@ -470,21 +498,29 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
     if (ninf) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)ninf);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
-    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    stream_k<3, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, I, lane >> 4, acc, lane);
-    reduce_split_k<KS>(acc, red, w, ks, lane);
+    f32x4_t acc[R][2];
+#pragma unroll
+    for (int q = 0; q < R; ++q) acc[q][0] = acc[q][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (R == 1) {
+      stream_k<3, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, I, lane >> 4, acc[0], lane);
+      reduce_split_k<KS>(acc[0], red, w, ks, lane);
+    } else {
+      stream_rows<3, 2, FMT, R>(ring, wt, nkt, lds + (size_t)ma * stride, I, lane >> 4, acc, lane);
+    }
     if (ks == 0 && lane < 16) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int col = 16 * (2 * rq + b) + lane;
+      for (int q = 0; q < R; ++q)
 #pragma unroll
-        for (int r = 0; r < kChunk; ++r) {
-          if (r < n) {
-            const int pp = r == 0 ? pr[0] : r == 1 ? pr[1] : r == 2 ? pr[2] : pr[3];
-            pair_out[(size_t)pp * K + col] = acc[b][r];
+        for (int b = 0; b < 2; ++b) {
+          const int col = 16 * (2 * (rq + q) + b) + lane;
+#pragma unroll
+          for (int r = 0; r < kChunk; ++r) {
+            if (r < n) {
+              const int pp = r == 0 ? pr[0] : r == 1 ? pr[1] : r == 2 ? pr[2] : pr[3];
+              pair_out[(size_t)pp * K + col] = acc[q][b][r];
+            }
           }
         }
-      }
     }
     __syncthreads();
   }
@@ -669,11 +705,15 @@ static hipError_t decode_down_fmt(const moe_w2_planes* p, int T, int top_k, cons
   const int groups = min(p->E, P);
   const size_t lds = (size_t)kChunk * MxRow<3>::stride(p->I) + (size_t)kWaves * 2 * 4 * 16 * 4;
   float* po = (float*)(wsb + ws.pair_out);
-  if (pick_np(groups) == 4)
-    hipLaunchKernelGGL((decode_down_kernel<4, FMT>), dim3(p->K / 128, P), dim3(kThreads), lds, s,
+  const bool two_pairs = FMT == kFmtW2 && (p->I / kTileK) % kRing == 0 && p->K % 256 == 0;
+  if (pick_np(groups) == 4 && two_pairs)
+    hipLaunchKernelGGL((decode_down_kernel<4, FMT, 2>), dim3(p->K / 256, P), dim3(kThreads), lds, s,
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I);
+  else if (pick_np(groups) == 4)
+    hipLaunchKernelGGL((decode_down_kernel<4, FMT, 1>), dim3(p->K / 128, P), dim3(kThreads), lds, s,
                        p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I);
   else
-    hipLaunchKernelGGL((decode_down_kernel<1, FMT>), dim3(p->K / 32, P), dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((decode_down_kernel<1, FMT, 1>), dim3(p->K / 32, P), dim3(kThreads), lds, s,
                        p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I);
   return hipGetLastError();
 }
