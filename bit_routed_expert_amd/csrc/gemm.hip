@@ -392,12 +392,16 @@ gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the tile's pair indices, fetched now so that the epilogue's stores do not wait on them
+  __shared__ int tile_pairs[BM];
+  if (tid < BM) tile_pairs[tid] = perm[rs + min(tid, rows_valid - 1)];
 
   const Fp4Masks fm = fp4_masks();
   const KLoads<A6Tile, FMT> ld{aq, aoff, codes, scales, tb0, nkt, w, lane};
   k_loop(lds, ld, nkt, wave_active, [&](const uint8_t* abuf, const BRegs<FMT>& br, auto part, bool mma) {
     a6_ktile(acc, abuf, br, part, mma, rows_valid, lane, fm);
   });
+  __syncthreads();   // tile_pairs visible to every wave
   if (!wave_active) return;
 
   // ---- epilogue: per-pair rows at the pair index ----
@@ -407,7 +411,7 @@ gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict
     for (int r = 0; r < 4; ++r) {
       const int row = m * 16 + 4 * (lane >> 4) + r;
       if (row >= rows_valid) continue;
-      const int p = perm[rs + row];
+      const int p = tile_pairs[row];
 #pragma unroll
       for (int t = 0; t < 4; ++t) pair_out[(size_t)p * K + 16 * (rg0 + t) + (lane & 15)] = acc[m][t][r];
     }
