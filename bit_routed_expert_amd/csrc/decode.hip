@@ -631,7 +631,9 @@ __global__ void combine_kernel(const int32_t* __restrict__ ids, const float* __r
         const int p = t * top_k + j0 + i;
         id[i] = ids[p];
         w[i] = wts[p];
-        o[i] = *reinterpret_cast<const float4*>(pair_out + (size_t)p * K + c);
+        // each per-pair row is read once: nontemporal keeps it from evicting L2 lines
+        const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pair_out + (size_t)p * K + c));
+        o[i] = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
 #pragma unroll
