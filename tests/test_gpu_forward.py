@@ -67,6 +67,7 @@ CASES = [
     (128, 512, 256, 4, 4, 26, True),    # 512 pairs: the most the decode kernels take
     (20, 512, 1024, 64, 8, 27, False),  # >= 32 groups, I/256 a multiple of 4: two row pairs per wave in down
     (24, 768, 768, 48, 6, 28, True),    # >= 32 groups, I/256 = 3: one row pair per wave, 4 per workgroup
+    (40, 256, 256, 1024, 8, 29, True),  # E = 1024, the most experts a layer may have
 ]
 
 
