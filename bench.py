@@ -20,6 +20,7 @@ The JSON line also carries:
   per_batch     - per-T forward time and whole-forward algorithmic HBM rate;
   prefill       - the 8192-token prefill workload (K=6144, Zipf(1.1) routing): tokens/s and matrix
                   core rate of the two grouped GEMMs against the dense bf16/fp16 peak;
+  zipf_decode   - the 64-token Zipf-routed decode batch at K=6144: time, active experts, HBM rate;
   slots         - the expert-slot forward against the plain forward at T=8 and 32;
   w4            - the FP4 (MXFP4) expert planes: decode at T=1, 8, 32 and the prefill GEMMs;
   requant       - the three load-time re-quantizers (NVFP4, FP8 block-128, MXFP4) over 256 tensors;
@@ -312,7 +313,7 @@ def main():
     if not args.no_w4:
         out["w4"] = bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I)
     if not args.no_prefill:
-        out["prefill"] = bench_prefill(args, moe, workloads, torch, dev)
+        out["prefill"], out["zipf_decode"] = bench_prefill(args, moe, workloads, torch, dev)
     if not args.no_requant:
         out["requant"] = bench_requant(args, moe, workloads, torch, dev)
     if not args.no_sweep:
@@ -456,7 +457,8 @@ def bench_prefill(args, moe, workloads, torch, dev, fp4=False):
         planes = moe.moe_w4_pack(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")])
     else:
         canon = workloads.zipf_layer(c["seed"], K, I, E)
-        planes = moe.moe_w2_pack(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")])
+        dcanon = [dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")]
+        planes = moe.moe_w2_pack(*dcanon)
     del canon
     d = workloads.zipf_instances(T, 1, c["seed"], K, E, top_k)[0]
     x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).cuda()
@@ -489,9 +491,14 @@ def bench_prefill(args, moe, workloads, torch, dev, fp4=False):
     f_dn = 2.0 * P * K * I
     gemm_tflops = (f_gu + f_dn) / ((gu + dn) * 1e-3) / 1e12
     fwd_tflops = (f_gu + f_dn) / (fwd * 1e-3) / 1e12
-    del planes, ws
+    del ws, y
+    zipf_decode = None
+    if not fp4:
+        zipf_decode = bench_zipf_decode(args, moe, workloads, torch, dev, [planes, moe.moe_w2_pack(*dcanon)])
+        del dcanon
+    del planes
     torch.cuda.empty_cache()
-    return dict(
+    res = dict(
         workload=("moe_w4 (FP4)" if fp4 else "moe_w2") + " prefill: T=8192 K=6144 I=2048 E=256 top-8 Zipf(1.1)",
         tokens_per_s=round(T / (fwd * 1e-3), 1), fwd_ms=round(float(fwd), 4),
         route_ms=round(float(rt), 4), gate_up_ms=round(float(gu), 4), down_ms=round(float(dn), 4),
@@ -500,6 +507,53 @@ def bench_prefill(args, moe, workloads, torch, dev, fp4=False):
         gemm_tflops=round(gemm_tflops, 1), gemm_mfma_frac=round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         fwd_tflops=round(fwd_tflops, 1), fwd_mfma_frac=round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         peak_tflops=MFMA_BF16_PEAK_TFLOPS, iters=args.prefill_iters)
+    return (res, zipf_decode) if not fp4 else res
+
+
+def bench_zipf_decode(args, moe, workloads, torch, dev, layers, R=16, n_rep=32):
+    """The Zipf-routed decode batch: T=64 tokens, K=6144 I=2048 E=256 top-8 with Zipf(1.1) expert
+    popularity (R seeded routing instances). The planes are the prefill layer's (same shape; the
+    weight values do not change the time), packed twice at distinct addresses and alternated so that
+    no call finds its weights in the 256 MB last-level cache. n_rep forwards captured in one HIP
+    graph; algorithmic bytes = each instance's active experts' planes + x + y + ids + w."""
+    c = workloads.DECODE_ZIPF
+    T, K, I, E, top_k = c["T"], c["K"], c["I"], c["E"], c["top_k"]
+    insts = workloads.zipf_instances(T, R, c["seed"], K, E, top_k)
+    xs = [torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).cuda() for d in insts]
+    ids = [dev(d["topk_ids"]) for d in insts]
+    ws_ = [dev(d["topk_w"]) for d in insts]
+    wss = [moe.alloc_workspace(layers[0], T, top_k) for _ in range(R)]
+    y = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    gu_b, dn_b = expert_bytes(K, I)
+    nact = [len(np.unique(d["topk_ids"][(d["topk_ids"] >= 0) & (d["topk_ids"] < E)])) for d in insts]
+
+    def loop():
+        nbytes = 0
+        for k in range(n_rep):
+            r = k % R
+            moe.moe_w2_forward(layers[k % 2], xs[r], ids[r], ws_[r], workspace=wss[r], y=y)
+            nbytes += nact[r] * (gu_b + dn_b) + 2 * T * K * 2 + T * top_k * 8
+        return nbytes
+    loop()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nbytes = loop()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n_rep * 1e3
+    gbps = nbytes / n_rep / (us * 1e-6) / 1e9
+    return dict(workload="moe_w2 decode: T=64 K=6144 I=2048 E=256 top-8 Zipf(1.1) routing",
+                fwd_us=round(us, 2), tokens_per_s=round(T / (us * 1e-6), 1),
+                mean_active_experts=round(float(np.mean(nact)), 1), hbm_GBps=round(gbps, 1),
+                hbm_frac=round(gbps / HBM_PEAK_GBPS, 4), us_at_70pct_hbm=round(nbytes / n_rep / (0.7 * HBM_PEAK_GBPS * 1e3), 1),
+                routing_instances=R, calls=n_rep)
 
 
 def bench_requant(args, moe, workloads, torch, dev):

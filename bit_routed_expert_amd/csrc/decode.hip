@@ -22,9 +22,9 @@
 //
 // Two organisations ("The v0.24.0 port", bullet "Deterministic unpermute": per-pair outputs are
 // placed bijectively and summed in a fixed order, no atomics on values):
-//  * routed (8 < P <= kDecodeMaxPairs): one group per active expert holding all its pairs, found
-//    by each workgroup from the ids (no routing pass, see pair_group); the down kernel writes per-pair rows o[p]
-//    and combine_kernel sums them in j order per token.
+//  * routed (8 < P <= kDecodeMaxPairs): one group per kChunk pairs of an active expert, found
+//    by each workgroup from the ids (no routing pass, see pair_group); the down kernel writes
+//    per-pair rows o[p] and combine_kernel sums them in j order per token.
 //  * direct (tiny batches, P = T*top_k <= kDirectMaxPairs): no routing pass; gate_up runs one
 //    group per pair, and one down kernel covers every pair of a column block and combines in LDS.
 #include "common.h"
@@ -302,11 +302,11 @@ MOEW2_DEV void reduce_split_k(f32x4_t* acc, float* red, int w, int ks, int lane)
 
 // ---------------------------------------------------------------------------------------------
 // Routing inside the decode kernels (8 < P <= kDecodeMaxPairs, no routing pass): workgroup row p
-// (blockIdx.y) takes expert e = ids[p] when p is the first pair routed to e, and finds all of
-// e's pairs in ascending pair order with wave ballots over the ids - the order of the routing
-// pass's stable sort ("The v0.24.0 port", bullet "Deterministic unpermute"). Rows whose pair is
-// not the first of its expert, or whose id is outside [0, E), exit at once. Pair p's gated row is
-// act[p].
+// (blockIdx.y) finds all pairs of expert e = ids[p] in ascending pair order with wave ballots over
+// the ids - the order of the routing pass's stable sort ("The v0.24.0 port", bullet
+// "Deterministic unpermute") - and takes the kChunk of them that start at p when p's rank among
+// them is a multiple of kChunk. Other rows, and rows whose id is outside [0, E), exit at once.
+// Pair p's gated row is act[p].
 // ---------------------------------------------------------------------------------------------
 constexpr int kScanBallots = kDecodeMaxPairs / 64;   // 64 pairs per ballot
 static_assert(kDecodeMaxPairs == 2 * kThreads, "two ids per thread");
@@ -327,11 +327,13 @@ MOEW2_DEV int select_bit64(uint64_t v, int k) {
   return pos;
 }
 
-// Selects the group of workgroup row p: its expert e and pair count n; false (for the whole
-// workgroup) when p does not start a group. With `counters` non-null the workgroup also records
+// Selects the chunk of workgroup row p: its expert e, the expert's pair count n and the rank c0
+// of pair p among them; true (for the whole workgroup) when p starts a chunk, i.e. c0 is a
+// multiple of kChunk - so the kChunk-pair chunks of a popular expert run on separate rows in
+// parallel instead of one after another. With `counters` non-null the workgroup also records
 // the invalid pair count and clears the overflow count.
 MOEW2_DEV bool pair_group(const int32_t* ids, int P, int E, int p, ScanLds& sh, int tid, int lane, int w,
-                          long long* counters, int& e, int& n) {
+                          long long* counters, int& e, int& n, int& c0) {
   e = ids[p];
   const int id0 = tid < P ? ids[tid] : -1;
   const int id1 = tid + kThreads < P ? ids[tid + kThreads] : -1;
@@ -355,13 +357,14 @@ MOEW2_DEV bool pair_group(const int32_t* ids, int P, int E, int p, ScanLds& sh, 
   }
   if (e < 0 || e >= E) return false;
   const int word = p >> 6;
-  for (int i = 0; i < word; ++i)
-    if (sh.ball[i]) return false;
-  if (sh.ball[word] & ((1ull << (p & 63)) - 1ull)) return false;
+  c0 = __popcll(sh.ball[word] & ((1ull << (p & 63)) - 1ull));
   n = 0;
 #pragma unroll
-  for (int i = 0; i < kScanBallots; ++i) n += __popcll(sh.ball[i]);
-  return true;
+  for (int i = 0; i < kScanBallots; ++i) {
+    if (i < word) c0 += __popcll(sh.ball[i]);
+    n += __popcll(sh.ball[i]);
+  }
+  return c0 % kChunk == 0;
 }
 
 // Pair index of the m-th pair (from 0) of the selected group.
@@ -378,9 +381,9 @@ MOEW2_DEV int pair_at(const ScanLds& sh, int m) {
 // ---------------------------------------------------------------------------------------------
 // gate_up: grid (I / (16*NP), groups). Wave w handles row-pair q = blockIdx.x*NP + w/KS (gate row
 // group 2q, up row group 2q+1) over the reduction slice w%KS of KS = 4/NP.
-// DIRECT: group = pair blockIdx.y (expert ids[p]). Otherwise group = all pairs of expert
-// ids[blockIdx.y] when blockIdx.y is the first of them (pair_group). The gated row of pair p is
-// act[p] in both.
+// DIRECT: group = pair blockIdx.y (expert ids[p]). Otherwise group = the kChunk pairs of expert
+// ids[blockIdx.y] from blockIdx.y on, when blockIdx.y starts such a chunk (pair_group). The gated
+// row of pair p is act[p] in both.
 // ---------------------------------------------------------------------------------------------
 template <int NPW, bool DIRECT, int FMT>
 __global__ void __launch_bounds__(kThreads)
@@ -393,7 +396,7 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
   __shared__ ScanLds sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
-  int e, n_total;
+  int e, n_total, first = 0;
   bool valid = true;
   if (DIRECT) {
     // no early exit: the x row is requested together with the id (an invalid pair streams no
@@ -404,7 +407,7 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
     n_total = 1;
   } else {
     long long* cnt = blockIdx.x == 0 && blockIdx.y == 0 ? counters : nullptr;
-    if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, cnt, e, n_total)) return;
+    if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, cnt, e, n_total, first)) return;
   }
   const int nkt = K / kTileK, nrg = 2 * I / kTileRows;
   const int pw = w / KS, ks = w % KS;
@@ -416,8 +419,8 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
   const int stride = MxRow<2>::stride(K);
   float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][2][4][16]
   TileRegs<2, FMT> ring[kRing];
-  for (int c0 = 0; c0 < n_total; c0 += kChunk) {
-    const int n = min(kChunk, n_total - c0);
+  {
+    const int c0 = first, n = min(kChunk, n_total - c0);
     // pair and token of each staged row (the same in every lane)
     int pr[kChunk];
 #pragma unroll
@@ -444,7 +447,6 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
         }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -470,8 +472,8 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
   __shared__ ScanLds sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
-  int e, n_e;
-  if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, nullptr, e, n_e)) return;
+  int e, n_e, first;
+  if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, nullptr, e, n_e, first)) return;
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int pw = w / KS, ks = w % KS;
   const int rq = (blockIdx.x * NPW + pw) * R;   // the wave's first row pair
@@ -483,8 +485,8 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
   float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][2][4][16]
   const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
   TileRegs<2, FMT> ring[kRing];
-  for (int c0 = 0; c0 < n_e; c0 += kChunk) {
-    const int n = min(kChunk, n_e - c0);
+  {
+    const int c0 = first, n = min(kChunk, n_e - c0);
     int pr[kChunk];
 #pragma unroll
     for (int m = 0; m < kChunk; ++m) pr[m] = pair_at(sh, c0 + min(m, n - 1));
@@ -522,7 +524,6 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
           }
         }
     }
-    __syncthreads();
   }
 }
 
