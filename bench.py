@@ -527,33 +527,36 @@ def bench_zipf_decode(args, moe, workloads, torch, dev, layers, R=16, n_rep=32):
     gu_b, dn_b = expert_bytes(K, I)
     nact = [len(np.unique(d["topk_ids"][(d["topk_ids"] >= 0) & (d["topk_ids"] < E)])) for d in insts]
 
-    def loop():
-        nbytes = 0
-        for k in range(n_rep):
-            r = k % R
-            moe.moe_w2_forward(layers[k % 2], xs[r], ids[r], ws_[r], workspace=wss[r], y=y)
-            nbytes += nact[r] * (gu_b + dn_b) + 2 * T * K * 2 + T * top_k * 8
-        return nbytes
-    loop()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        nbytes = loop()
-    g.replay()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / n_rep * 1e3
+    def timed(path):
+        def loop():
+            nbytes = 0
+            for k in range(n_rep):
+                r = k % R
+                moe.moe_w2_forward(layers[k % 2], xs[r], ids[r], ws_[r], workspace=wss[r], y=y, path=path)
+                nbytes += nact[r] * (gu_b + dn_b) + 2 * T * K * 2 + T * top_k * 8
+            return nbytes
+        loop()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            nbytes = loop()
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n_rep * 1e3, nbytes
+    us, nbytes = timed(moe.PATH_AUTO)            # P = 512: the decode kernels
+    us_gemm, _ = timed(moe.PATH_GEMM)
     gbps = nbytes / n_rep / (us * 1e-6) / 1e9
     return dict(workload="moe_w2 decode: T=64 K=6144 I=2048 E=256 top-8 Zipf(1.1) routing",
                 fwd_us=round(us, 2), tokens_per_s=round(T / (us * 1e-6), 1),
                 mean_active_experts=round(float(np.mean(nact)), 1), hbm_GBps=round(gbps, 1),
                 hbm_frac=round(gbps / HBM_PEAK_GBPS, 4), us_at_70pct_hbm=round(nbytes / n_rep / (0.7 * HBM_PEAK_GBPS * 1e3), 1),
-                routing_instances=R, calls=n_rep)
+                gemm_path_fwd_us=round(us_gemm, 2), routing_instances=R, calls=n_rep)
 
 
 def bench_requant(args, moe, workloads, torch, dev):
