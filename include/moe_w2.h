@@ -60,7 +60,9 @@ enum moe_w2_status {
 enum moe_w2_out_dtype { MOE_W2_OUT_BF16 = 0, MOE_W2_OUT_F32 = 1 };
 
 /* Which kernels moe_w2_forward uses. AUTO picks DECODE for T*top_k <= 512, else GEMM. DECODE
- * supports T*top_k <= 512 only (MOE_W2_EUNSUPPORTED above). */
+ * supports T*top_k <= 512 only (MOE_W2_EUNSUPPORTED above). DECODE streams an expert's weights
+ * once per 4 of its pairs, so for batches whose routing concentrates dozens of pairs on a few
+ * experts GEMM can be the faster choice; both give results within the same tolerance. */
 enum moe_w2_path { MOE_W2_PATH_AUTO = 0, MOE_W2_PATH_DECODE = 1, MOE_W2_PATH_GEMM = 2 };
 
 /* The four stages of moe_w2_forward, in order (see moe_w2_forward_stage). */
