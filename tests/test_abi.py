@@ -83,6 +83,7 @@ def test_codebook_sweep_host_validation(lib):
     assert f(1, 2, 64, fake, 1, nan, fake, fake, fake, None) == -1
     assert f(1, 2, 48, fake, 1, good, fake, fake, fake, None) == -2
     assert f(1, 2, 64, fake, 0, good, fake, fake, fake, None) == -1
+    assert f(1, 2, 64, fake, 4097, good, fake, fake, fake, None) == -1     # more codebooks than allowed
     assert f(1, 2, 64, fake, 1, None, fake, fake, fake, None) == -1
     assert f(-1, 2, 64, fake, 1, good, fake, fake, fake, None) == -1
     assert f(0, 2, 64, None, 1, good, None, None, None, None) == 0

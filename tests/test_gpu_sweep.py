@@ -136,3 +136,18 @@ def test_errors_and_empty(gpu):
     assert ei.value.status == -2
     st, mo, best = _gpu(np.zeros((2, 0, 64), np.float32), np.array([SYM, [-2, -1, 0, 1]], np.float32))
     assert np.all(st == 0) and np.all(mo == 0) and best.tolist() == [[0, 1], [0, 1]]
+
+
+def test_most_codebooks_allowed(gpu):
+    """4096 candidate codebooks (the maximum) on a small tensor: every statistic against the oracle."""
+    rng = np.random.default_rng(17)
+    cbs = np.sort(rng.uniform(-8, 8, size=(4096, 4)), axis=1).astype(np.float32)
+    cbs[:, 1] += np.float32(1e-3)          # keep each row strictly ascending after rounding
+    cbs[:, 2] += np.float32(2e-3)
+    cbs[:, 3] += np.float32(3e-3)
+    cbs = np.sort(cbs, axis=1)
+    assert np.all(np.diff(cbs, axis=1) > 0)
+    x = np.stack([workloads.sweep_tensor(i, R=4, C=64) for i in range(2)])
+    st, mo, best = _gpu(x, cbs)
+    st_o, mo_o, best_o = sweep.codebook_sweep(x, cbs)
+    _check_close(st, mo, best, st_o, mo_o, best_o, 4 * 64)
