@@ -258,7 +258,10 @@ MOEW2_DEV void stream_rows(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt
 // whose every workgroup starts at once and reads the same few rows (the tiny-batch organisation),
 // priming the whole ring first puts the entire weight volume in the memory queues ahead of those
 // row loads; committing first leaves the memory idle while every workgroup waits for the same
-// rows. Half and half keeps half the weights streaming while the rows arrive.
+// rows. Priming part of the ring first keeps weights streaming while the rows arrive: measured
+// best at one slot of four for the tiny-batch gate_up (T=1 gate_up 9.7 -> 9.3 us against two;
+// all four: 10.2; none: 10.8) and two for the tiny-batch down (one: within noise; four: 9.1 us
+// against 8.4).
 template <int NT, int NP, int NB, int FMT, int SPLIT = kRing, class RowOff>
 MOEW2_DEV void stage_and_prime(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt, int kb, int ke, int lane,
                                uint8_t* lds, int stride, const uint16_t* src, int KR, int n, RowOff row_off,
@@ -430,7 +433,7 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
       return (size_t)(pp / top_k) * K;
     };
     int ninf = 0;
-    stage_and_prime<kThreads, 2, 2, FMT, DIRECT ? kRing / 2 : kRing>(ring, wt, kb, ke, lane, lds, stride, x, K, n,
+    stage_and_prime<kThreads, 2, 2, FMT, DIRECT ? 1 : kRing>(ring, wt, kb, ke, lane, lds, stride, x, K, n,
                                                                 row_off, tid, false, ninf);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
