@@ -258,3 +258,33 @@ def test_act_overflow_is_counted(gpu, T, path):
     inv, ovf = moe.moe_w2_read_counters(ws)
     print(f"T={T} path={path}: act_overflow {ovf}, oracle {lo}..{hi} of {a.size}")
     assert lo > 0 and inv == 0 and lo <= ovf <= hi
+
+
+def _random_cases(n=14, seed=2024):
+    """Shapes drawn once from a fixed seed: T in [1, 160], K and I multiples of 256 up to 1280 (so
+    I/256 takes values that do and do not divide the decode ring), E in [1, 96], top_k up to
+    min(8, E), uniform or Zipf routing - a spread of group counts, chunk splits and ragged tiles."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 97))
+        top_k = int(rng.integers(1, min(8, E) + 1))
+        out.append((int(rng.integers(1, 161)), 256 * int(rng.integers(1, 6)), 256 * int(rng.integers(1, 6)), E, top_k,
+                    1000 + i, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"T{c[0]}K{c[1]}I{c[2]}E{c[3]}k{c[4]}{'z' if c[6] else 'u'}")
+def test_random_shapes_parity(gpu, case):
+    """Both kernel families (decode only where T*top_k <= 512) against the oracle."""
+    T, K, I, E, top_k, seed, zipf = case
+    c = _case(T, K, I, E, top_k, seed, zipf)
+    h = pack(c)
+    y_ref = _oracle(c)
+    for path in PATHS:
+        if path == moe.PATH_DECODE and T * top_k > 512:
+            continue
+        y = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path).cpu().numpy()
+        err = rel_max_err(y, y_ref)
+        print(f"{case} path={path} rel max err {err:.2e}")
+        assert err <= TOL, (case, path, err)
