@@ -125,3 +125,30 @@ def test_w4_decode_full_shape_sampled_tokens(gpu, T):
     assert err <= TOL
     yg = _fwd(h, c, moe.PATH_GEMM)
     assert np.max(np.abs(y - yg)) <= 5e-3 * np.sqrt(np.mean(y.astype(np.float64) ** 2))
+
+
+def _random_cases(n=8, seed=4048):
+    """Seeded random shapes as for the 2-bit planes: T in [1, 160], K and I multiples of 256 up to
+    1280, E in [1, 96], top_k up to min(8, E), uniform or Zipf routing."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 97))
+        top_k = int(rng.integers(1, min(8, E) + 1))
+        out.append((int(rng.integers(1, 161)), 256 * int(rng.integers(1, 6)), 256 * int(rng.integers(1, 6)), E, top_k,
+                    2000 + i, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"T{c[0]}K{c[1]}I{c[2]}E{c[3]}k{c[4]}{'z' if c[6] else 'u'}")
+def test_w4_random_shapes_parity(gpu, case):
+    T, K, I, E, top_k, seed, zipf = case
+    c = _case(T, K, I, E, top_k, seed, zipf)
+    h = pack4(c)
+    y_ref = _oracle(c)
+    for path in (moe.PATH_DECODE, moe.PATH_GEMM):
+        if path == moe.PATH_DECODE and T * top_k > 512:
+            continue
+        err = rel_max_err(_fwd(h, c, path), y_ref)
+        print(f"{case} path={path} rel max err {err:.2e}")
+        assert err <= TOL, (case, path, err)
