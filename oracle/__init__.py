@@ -22,8 +22,12 @@ Modules:
   formats  - the number formats (codebook, UE8M0, e2m1, e4m3) and the canonical code packing.
   forward  - routing and the f64 forward (definition written out; numpy matmul as the only
              library step).
-  requant  - the re-quantizer: an exact Fraction reference for small inputs and a ctypes wrapper
-             around ``requant_exact.c`` (exact integer arithmetic) for large ones.
+  requant  - the re-quantizers (NVFP4, FP8 block-128 and MXFP4 inputs): an exact Fraction
+             reference for small inputs and a ctypes wrapper around ``requant_exact.c`` (exact
+             integer arithmetic) for large ones.
+  sweep    - the sign-bias codebook sweep (README bullet "2-bit expert planes - the sign-bias
+             finding"): an exact Fraction reference for single blocks and a ctypes wrapper around
+             ``codebook_sweep.c`` (float64 in element order) for whole tensors.
 
 Parity status of each function is stated in its docstring; every function here is pinned by a
 ``-m "not gpu"`` test except where a docstring says "parity unpinned".
