@@ -5,8 +5,10 @@ torch device tensors' pointers and the current HIP stream to the C ABI and turns
 exceptions. There is no fallback: if the library is missing or no GPU is present, calls fail.
 
 Functions keep the C names: moe_w2_pack, moe_w2_unpack, moe_w2_workspace_bytes, moe_w2_route,
-moe_w2_forward, moe_w2_read_counters, nvfp4_to_w2, and the expert-slot entry points
-moe_w2_planes_create, moe_w2_pack_slot, moe_w2_forward_slots, moe_w2_read_miss_counter.
+moe_w2_forward, moe_w2_forward_stage, moe_w2_read_counters; the re-quantizers nvfp4_to_w2,
+fp8_block128_to_w2, mxfp4_to_w2; the FP4 planes moe_w4_pack, moe_w4_unpack, moe_w4_forward; the
+expert-slot entry points moe_w2_planes_create, moe_w2_pack_slot, moe_w2_forward_slots,
+moe_w2_read_miss_counter; and the sign-bias diagnostic moe_w2_codebook_sweep.
 """
 import ctypes
 import os

@@ -9,7 +9,9 @@
  * 32 elements along each GEMM's reduction axis; the forward routes pairs (token, expert) to a
  * grouped gate/up GEMM, a SiLU-gated product, a grouped down GEMM and a router-weighted,
  * deterministic combine; NVFP4 experts (e2m1 x e4m3 block-16 x fp32 per-tensor scale_2) are
- * re-quantized to those planes at load time.
+ * re-quantized to those planes at load time. Beside these: FP8 block-128 and MXFP4 re-quantizers,
+ * FP4 (MXFP4) expert planes with the same forward, a slot-indexed forward for partially resident
+ * experts, and the codebook sweep behind the sign-symmetric codebook choice.
  *
  * Conventions (all entry points):
  *  - Pointers are HIP device pointers unless a parameter says "host". The caller owns every
