@@ -10,8 +10,10 @@
 //
 // Both GEMMs run on the block-scaled instruction with A = fp6 (e2m3) and B = fp4 (e2m1): the
 // weights' codes become e2m1 operands with two bit operations per 8 values and their UE8M0 bytes
-// are the instruction's B scales; the activations (x for gate_up, the fp16 gated intermediate
-// for down) are first expanded into three block-scaled e2m3 parts by quant_a6_kernel (one pass).
+// are the instruction's B scales; the activations are expanded into three block-scaled e2m3
+// parts: x by quant_x6_kernel (one pass before gate_up), the fp16 gated intermediate by the
+// gate_up epilogue itself (each gate_up workgroup holds whole 32-value blocks of its rows, so it
+// writes the down GEMM's split records directly and the intermediate never goes to HBM).
 // fp6 x fp4 runs at twice the rate of fp8 x fp4, so three fp6 parts cost less than two fp8 ones.
 #include <type_traits>
 
@@ -202,13 +204,12 @@ MOEW2_DEV void k_loop(uint8_t* lds, const KLoads<AT, FMT>& ld, int nkt, bool act
 }
 
 // ------------------------------------------------------------------------------------------------
-// Activation splits: one thread per 32-value block, three e2m3 parts into the 608-byte record of
-// its (row, k-tile) (layout at kA6Bytes in common.h). x: bf16 [T][K], one record per (token,
-// k-tile); gated intermediate: fp16 [P][I] in sorted order, one record per (sorted row, k-tile).
+// x split: one thread per 32-value block of x (bf16 [T][K]), three e2m3 parts into the 608-byte
+// record of its (token, k-tile) (layout at kA6Bytes in common.h). The gated intermediate's
+// records are written by the gate_up epilogue with the same arithmetic.
 // ------------------------------------------------------------------------------------------------
-template <bool kBf16>
 __global__ void __launch_bounds__(256)
-quant_a6_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst, int rows, int n) {
+quant_x6_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst, int rows, int n) {
   const int nb = n / 32, nkt = n / kTileK;
   const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= (long long)rows * nb) return;
@@ -220,8 +221,8 @@ quant_a6_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst, int
     const u32x4_t w = ld16(sp + 8 * q);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[8 * q + 2 * j] = kBf16 ? bf16_lo(w[j]) : f16_lo(w[j]);
-      v[8 * q + 2 * j + 1] = kBf16 ? bf16_hi(w[j]) : f16_hi(w[j]);
+      v[8 * q + 2 * j] = bf16_lo(w[j]);
+      v[8 * q + 2 * j + 1] = bf16_hi(w[j]);
     }
   }
   float a = 0.f;
@@ -298,13 +299,26 @@ MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][4], const uint8_t* abuf, const BRegs<F
 
 // ------------------------------------------------------------------------------------------------
 // gate_up: rows of the split x gathered through the sort permutation (token = pair / top_k).
+// Wave w of N-block nb holds gated columns 32 * (8 nb + w) .. +31 of its BM rows: block w of the
+// down GEMM's k-tile nb (2I is a multiple of BN, so every wave has its block). The epilogue
+// rounds a = silu(g) * u to fp16, passes the BM x 32 block through the wave's own LDS region (row
+// stride 36 floats, 4 mod 8 dwords, for the row-per-lane reads), lane r splits row r's block into
+// its three e2m3 parts (the arithmetic of quant_x6_kernel, on the fp16-rounded values) and puts
+// them in row r's split record, assembled in LDS; the workgroup then writes the BM whole records
+// (sorted row, k-tile nb) with 16-byte stores of consecutive chunks.
 // ------------------------------------------------------------------------------------------------
+constexpr int kTpStride = 36;                           // floats per row of the epilogue's block
+constexpr int kTpBytes = BM * kTpStride * 4;            // one wave's region
+constexpr int kRecOff = kWaves * kTpBytes;              // the assembled records
+constexpr int kGateUpLds = kRecOff + BM * kA6Bytes > kAStages * A6Tile::kBytes ? kRecOff + BM * kA6Bytes
+                                                                                 : kAStages * A6Tile::kBytes;
+static_assert(kWaves * 32 == kTileK, "a gate_up workgroup covers one down k-tile of gated columns");
 template <int FMT>
 __global__ void __launch_bounds__(kThreads, kWgPerCu)
 gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                        const uint8_t* __restrict__ xq, const int32_t* __restrict__ offsets,
                        const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
-                       const int32_t* __restrict__ meta, _Float16* __restrict__ act,
+                       const int32_t* __restrict__ meta, uint8_t* __restrict__ aq,
                        long long* __restrict__ counters, int T, int K, int I, int top_k, int n_blocks) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const TileMap tm = map_tile(tiles, meta, offsets, n_blocks);
@@ -336,29 +350,53 @@ gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restr
   k_loop(lds, ld, nkt, wave_active, [&](const uint8_t* abuf, const BRegs<FMT>& br, auto part, bool mma) {
     a6_ktile(acc, abuf, br, part, mma, rows_valid, lane, fm);
   });
-  if (!wave_active) return;
+  __syncthreads();   // every wave is done with the A stages, which the epilogue reuses
 
-  // ---- epilogue: a = silu(g) * u in fp16 at the sorted row ----
-  unsigned n_inf = 0;
+  // ---- epilogue: a = silu(g) * u in fp16, block w of each sorted row's split record ----
+  if (wave_active) {
+    float* tp = reinterpret_cast<float*>(lds + w * kTpBytes);
+    unsigned n_inf = 0;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 4; ++m) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = m * 16 + 4 * (lane >> 4) + r;
-      if (row >= rows_valid) continue;
-      const int sr = rs + row;
+      for (int r = 0; r < 4; ++r) {
+        const int row = m * 16 + 4 * (lane >> 4) + r;
 #pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const float a = silu_mul(acc[m][2 * pr][r], acc[m][2 * pr + 1][r]);
-        const _Float16 h = (_Float16)a;
-        n_inf += __builtin_isinf((float)h) ? 1u : 0u;
-        const int col = 16 * (rg0 / 2 + pr) + (lane & 15);
-        act[(size_t)sr * I + col] = h;
+        for (int pr = 0; pr < 2; ++pr) {
+          const float a = silu_mul(acc[m][2 * pr][r], acc[m][2 * pr + 1][r]);
+          const float h = (float)(_Float16)a;
+          n_inf += row < rows_valid && __builtin_isinf(h) ? 1u : 0u;
+          tp[row * kTpStride + 16 * pr + (lane & 15)] = h;
+        }
       }
     }
+    // one counter update per lane that saw an overflow (none on finite workloads)
+    if (n_inf) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)n_inf);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the region is this wave's alone
+    if (lane < rows_valid) {
+      float v[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x4_t f = *reinterpret_cast<const f32x4_t*>(tp + lane * kTpStride + 4 * q);
+        v[4 * q] = f[0], v[4 * q + 1] = f[1], v[4 * q + 2] = f[2], v[4 * q + 3] = f[3];
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[q]));
+      const uint32_t sb = a6_scale_byte(amax);
+      u32x6_t part[3];
+      a6_split(v, sb, part);
+      a6_store(lds + kRecOff + lane * kA6Bytes, w, part, sb);
+    }
   }
-  // one counter update per lane that saw an overflow (none on finite workloads)
-  if (n_inf) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)n_inf);
+  __syncthreads();   // every block of every record is in LDS
+  const size_t rec_stride = (size_t)(I / kTileK) * kA6Bytes;
+  uint8_t* rec0 = aq + ((size_t)rs * (I / kTileK) + tm.nb) * kA6Bytes;
+  for (int c = tid; c < rows_valid * kA6Chunks; c += kThreads) {
+    const int row = c / kA6Chunks, j = c - row * kA6Chunks;
+    *reinterpret_cast<u32x4_t*>(rec0 + row * rec_stride + 16 * j) =
+        *reinterpret_cast<const u32x4_t*>(lds + kRecOff + row * kA6Bytes + 16 * j);
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -429,16 +467,15 @@ hipError_t launch_gemm_gate_up(const moe_w2_planes* p, int T, int top_k, const v
                                const Workspace& ws, uint8_t* wsb, hipStream_t s) {
   if (ws.max_tiles == 0) return hipSuccess;
   const long long nblk32 = (long long)T * (p->K / 32);
-  hipLaunchKernelGGL(quant_a6_kernel<true>, dim3((unsigned)((nblk32 + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(quant_x6_kernel, dim3((unsigned)((nblk32 + 255) / 256)), dim3(256), 0, s,
                      (const uint16_t*)x, wsb + ws.xq, T, p->K);
   const int nblk = (2 * p->I + BN - 1) / BN;
   auto kern = p->fmt == kFmtW4 ? gemm_gate_up_mx_kernel<kFmtW4> : gemm_gate_up_mx_kernel<kFmtW2>;
-  hipLaunchKernelGGL(kern, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads),
-                     kAStages * A6Tile::kBytes, s,
+  hipLaunchKernelGGL(kern, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads), kGateUpLds, s,
                      p->gu_codes, p->gu_scales, (const uint8_t*)(wsb + ws.xq),
                      (const int32_t*)(wsb + ws.offsets), (const int32_t*)(wsb + ws.perm),
                      (const int32_t*)(wsb + ws.tiles), (const int32_t*)(wsb + ws.meta),
-                     (_Float16*)(wsb + ws.act), (long long*)(wsb + ws.counters), T, p->K, p->I, top_k, nblk);
+                     wsb + ws.aq, (long long*)(wsb + ws.counters), T, p->K, p->I, top_k, nblk);
   return hipGetLastError();
 }
 
@@ -446,9 +483,6 @@ hipError_t launch_gemm_down(const moe_w2_planes* p, int T, int top_k, const Work
                             uint8_t* wsb, hipStream_t s) {
   if (ws.max_tiles == 0) return hipSuccess;
   const int P = T * top_k;
-  const long long nblk32 = (long long)P * (p->I / 32);
-  hipLaunchKernelGGL(quant_a6_kernel<false>, dim3((unsigned)((nblk32 + 255) / 256)), dim3(256), 0, s,
-                     (const uint16_t*)(wsb + ws.act), wsb + ws.aq, P, p->I);
   const int nblk = (p->K + BN - 1) / BN;
   auto kern = p->fmt == kFmtW4 ? gemm_down_mx_kernel<kFmtW4> : gemm_down_mx_kernel<kFmtW2>;
   hipLaunchKernelGGL(kern, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads),

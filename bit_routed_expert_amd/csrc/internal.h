@@ -45,9 +45,9 @@ struct Workspace {
   size_t rank;        // int32 [P] rank of a pair within its chunk and expert
   size_t xq;          // x split for the block-scaled instruction (GEMM path): one 608-byte
                       // three-part e2m3 record per (token, k-tile), layout at kA6Bytes
-  size_t act;         // fp16 [P][I] gated intermediate: sorted order (GEMM), pair order (decode)
-  size_t aq;          // gated intermediate split (GEMM path): one 608-byte three-part e2m3
-                      // record per (sorted row, k-tile)
+  size_t act;         // fp16 [P][I] gated intermediate in pair order (decode path)
+  size_t aq;          // gated intermediate split (GEMM path, written by the gate_up epilogue):
+                      // one 608-byte three-part e2m3 record per (sorted row, k-tile)
   size_t pair_out;    // fp32 [P][K] per-pair down outputs, indexed by pair id
   size_t slot_ids;    // int32 [P] the ids mapped to slots (slot forward)
   size_t total;
