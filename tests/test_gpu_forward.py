@@ -9,7 +9,7 @@ import bit_routed_expert_amd as moe
 from oracle import formats, forward as oracle_fwd
 import workloads
 
-from gpu_helpers import bf16_rne_bits, dev, forward, pack, rel_max_err
+from gpu_helpers import bf16_rne_bits, dev, dev_bf16, forward, pack, rel_max_err
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -288,3 +288,41 @@ def test_random_shapes_parity(gpu, case):
         err = rel_max_err(y, y_ref)
         print(f"{case} path={path} rel max err {err:.2e}")
         assert err <= TOL, (case, path, err)
+
+
+@pytest.mark.parametrize("out_dtype", [moe.OUT_F32, moe.OUT_BF16], ids=["f32", "bf16"])
+def test_decode_routed_edge_tokens(gpu, out_dtype):
+    """The routed decode organisation with two row pairs per wave in down (2-bit planes, >= 32
+    active groups, I/256 a multiple of 4): tokens with invalid ids, one with a duplicate id and one
+    with no valid id (a zero row). Three forwards on one workspace are bit-identical, fp32 matches
+    the oracle and bf16 is its round-to-nearest-even, and a stage sequence that runs the down stage
+    twice gives the same y."""
+    T, K, I, E, top_k = 24, 512, 1024, 64, 8
+    c = _case(T, K, I, E, top_k, 71)
+    ids = c["topk_ids"].copy()
+    ids[::4, 2] = -1
+    ids[1::6, 5] = E
+    ids[3, 1] = ids[3, 0]
+    ids[7, :] = -1
+    h = pack(c)
+    ws = moe.alloc_workspace(h, T, top_k)
+    ys = [forward(h, c["x"], ids, c["topk_w"], out_dtype, moe.PATH_DECODE, ws) for _ in range(3)]
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+    y32 = forward(h, c["x"], ids, c["topk_w"], moe.OUT_F32, moe.PATH_DECODE, ws).cpu().numpy()
+    assert np.all(y32[7] == 0)
+    y_ref = oracle_fwd.moe_forward(formats.bf16_bits_to_f64(c["x"]), ids, c["topk_w"], c["gu_codes"], c["gu_scales"],
+                                   c["dn_codes"], c["dn_scales"])
+    assert rel_max_err(y32, y_ref) <= TOL
+    if out_dtype == moe.OUT_BF16:   # bf16 output = RNE of the same path's fp32 result
+        bits = ys[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(bits, bf16_rne_bits(y32))
+    inv, _ = moe.moe_w2_read_counters(ws)
+    assert inv == int(((ids < 0) | (ids >= E)).sum())
+    # stages one at a time, the down stage twice
+    x_d, ids_d, w_d = dev_bf16(c["x"]), dev(ids), dev(np.asarray(c["topk_w"], np.float32))
+    y2 = torch.full_like(ys[0], 7.0)
+    for st in (moe.STAGE_ROUTE, moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_DOWN, moe.STAGE_COMBINE):
+        moe.moe_w2_forward_stage(st, h, x_d, ids_d, w_d, y2, ws, out_dtype, moe.PATH_DECODE)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, ys[0])
