@@ -326,3 +326,27 @@ def test_decode_routed_edge_tokens(gpu, out_dtype):
         moe.moe_w2_forward_stage(st, h, x_d, ids_d, w_d, y2, ws, out_dtype, moe.PATH_DECODE)
     torch.cuda.synchronize()
     assert torch.equal(y2, ys[0])
+
+
+@pytest.mark.parametrize("T,path,zipf", [(1, moe.PATH_DECODE, False), (40, moe.PATH_DECODE, False),
+                                         (12, moe.PATH_GEMM, False), (300, moe.PATH_GEMM, True)],
+                         ids=["direct", "routed-decode", "gemm-single-row-tiles", "gemm-zipf"])
+def test_stages_in_order_equal_forward(gpu, T, path, zipf):
+    """ROUTE, GATE_UP, DOWN, COMBINE called one at a time on one workspace give moe_w2_forward's y
+    bit for bit, for each organisation; at T=12 on the GEMM kernels nearly every M-tile holds a
+    single valid row (the gate_up epilogue writes only that row's split records)."""
+    K, I, E, top_k = 512, 1024, 64, 8
+    c = _case(T, K, I, E, top_k, 81 + T, zipf=zipf)
+    h = pack(c)
+    ws = moe.alloc_workspace(h, T, top_k)
+    y = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path, ws)
+    x_d, ids_d = dev_bf16(c["x"]), dev(np.asarray(c["topk_ids"], np.int32))
+    w_d = dev(np.asarray(c["topk_w"], np.float32))
+    y2 = torch.full_like(y, 7.0)
+    for st in (moe.STAGE_ROUTE, moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE):
+        moe.moe_w2_forward_stage(st, h, x_d, ids_d, w_d, y2, ws, moe.OUT_F32, path)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y)
+    y_ref = oracle_fwd.moe_forward(formats.bf16_bits_to_f64(c["x"]), c["topk_ids"], c["topk_w"], c["gu_codes"],
+                                   c["gu_scales"], c["dn_codes"], c["dn_scales"])
+    assert rel_max_err(y.cpu().numpy(), y_ref) <= TOL
