@@ -40,6 +40,9 @@ static bool shape_ok(int E, int K, int I) {
          (long long)I * K / 2 < (1LL << 31);
 }
 
+// Pair counts above 2^30 are not supported by any entry point (the kernels index pairs in 32 bits).
+static bool pairs_ok(int T, int top_k) { return (long long)T * top_k <= (1LL << 30); }
+
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_W2_OK : MOE_W2_EHIP; }
 
 // One device allocation holding E experts' (or slots') native planes and the validation flag.
@@ -86,7 +89,7 @@ static int forward_check(const moe_w2_planes* p, int T, int top_k, const void* x
   if (out_dtype != MOE_W2_OUT_BF16 && out_dtype != MOE_W2_OUT_F32) return MOE_W2_EINVAL;
   if (path != MOE_W2_PATH_AUTO && path != MOE_W2_PATH_DECODE && path != MOE_W2_PATH_GEMM) return MOE_W2_EINVAL;
   if (T > 0 && (!x || !topk_ids || !topk_w || !y)) return MOE_W2_EINVAL;
-  if ((long long)T * top_k > (1LL << 30)) return MOE_W2_EUNSUPPORTED;
+  if (!pairs_ok(T, top_k)) return MOE_W2_EUNSUPPORTED;
   if ((long long)T * p->K >= (1LL << 31) || (long long)T * top_k * p->I >= (1LL << 31))
     return MOE_W2_EUNSUPPORTED;  // the GEMM kernels index x and the intermediate in 32 bits
   if ((long long)T * (p->K / kTileK) * kA6Bytes >= (1LL << 32) ||
@@ -202,12 +205,12 @@ int moe_w2_planes_info(const moe_w2_planes* p, int* E, int* K, int* I, size_t* b
 }
 
 size_t moe_w2_workspace_bytes(const moe_w2_planes* p, int T, int top_k) {
-  if (!p || T < 0 || top_k < 1 || top_k > 32) return 0;
+  if (!p || T < 0 || top_k < 1 || top_k > 32 || !pairs_ok(T, top_k)) return 0;
   return workspace_layout(p->E, p->K, p->I, T, top_k).total;
 }
 
 size_t moe_w2_route_workspace_bytes(int E, int T, int top_k) {
-  if (E < 1 || E > 1024 || T < 0 || top_k < 1 || top_k > 32) return 0;
+  if (E < 1 || E > 1024 || T < 0 || top_k < 1 || top_k > 32 || !pairs_ok(T, top_k)) return 0;
   const int P = T * top_k;
   const int max_tiles = P / kGemmBM + (E < P ? E : P) + 1;
   return align_up((size_t)E * 4) + align_up(8 * 4) + align_up((size_t)max_tiles * 2 * 4) +
@@ -217,7 +220,7 @@ size_t moe_w2_route_workspace_bytes(int E, int T, int top_k) {
 int moe_w2_route(int E, int T, int top_k, const int32_t* topk_ids, int32_t* offsets, int32_t* perm,
                  void* workspace, size_t workspace_bytes, void* stream) {
   if (E < 1 || T < 0 || top_k < 1) return MOE_W2_EINVAL;
-  if (E > 1024 || top_k > 32) return MOE_W2_EUNSUPPORTED;
+  if (E > 1024 || top_k > 32 || !pairs_ok(T, top_k)) return MOE_W2_EUNSUPPORTED;
   if (!offsets || (T > 0 && (!topk_ids || !perm))) return MOE_W2_EINVAL;
   const size_t need = moe_w2_route_workspace_bytes(E, T, top_k);
   if (!workspace || workspace_bytes < need) return MOE_W2_EWORKSPACE;

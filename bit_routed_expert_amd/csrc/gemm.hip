@@ -82,6 +82,14 @@ MOEW2_DEV void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier for the k-loop, as an asm statement with a memory clobber: the compiler may
+// move no memory access across it in either direction (no LDS read of the k-tile it releases, no
+// direct-to-LDS load into the stage it frees), and it adds no wait of its own. A workgroup-scope
+// fence would order the same accesses but makes the compiler drain every outstanding load
+// (vmcnt(0)) at each barrier, since it counts the direct-to-LDS loads as LDS stores; the k-loop's
+// explicit vmcnt(N) waits already say which of those loads have landed.
+MOEW2_DEV void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <int CH, int SRC>
 struct ATile {
   static constexpr int kChunks = BM * CH;
@@ -181,7 +189,7 @@ MOEW2_DEV void k_loop(uint8_t* lds, const KLoads<AT, FMT>& ld, int nkt, bool act
   auto step = [&](int kt, BRegs<FMT>& cur, BRegs<FMT>& ahead) {
     // k-tile kt has landed: its A was issued in the previous step before that step's B loads
     wait_vm<kBLoads<FMT>>();
-    __builtin_amdgcn_s_barrier();      // ... in every wave; and every wave is done with kt - 1
+    lds_barrier();                     // ... in every wave; and every wave is done with kt - 1
     const int ka = max(0, min(kt + 1, nkt - 1));
     const int kb = min(kt + 2, nkt - 1);
     uint8_t* a_stage = lds + ((kt + 1) & 1) * AT::kBytes;    // the stage kt - 1 used

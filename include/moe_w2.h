@@ -24,7 +24,9 @@
  *    is enqueued. No call prints, aborts or throws.
  *  - Shapes: K (hidden size) and I (expert intermediate size) must be multiples of 256 with
  *    I*K < 2^32;
- *    1 <= E <= 1024; 1 <= top_k <= 32; T >= 0 (T = 0 is a no-op). A forward also needs
+ *    1 <= E <= 1024; 1 <= top_k <= 32; T >= 0 (T = 0 is a no-op); T*top_k <= 2^30 in every
+ *    entry point that takes T (moe_w2_workspace_bytes and moe_w2_route_workspace_bytes return 0
+ *    above it, the others MOE_W2_EUNSUPPORTED). A forward also needs
  *    T*K < 2^31 and T*top_k*I < 2^31 (element counts of x and of the gated intermediate),
  *    T*(K/256)*608 < 2^32 and T*top_k*(I/256)*608 < 2^32 (bytes of their split copies).
  *

@@ -75,13 +75,14 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None, fp4=False):
+def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None, fp4=False, workers=1):
     """Per-pair down-projection outputs o[(t, j)] in f64.
 
     x: [T, K] f64 (the bf16 activations' exact values). Returns an array [len(tokens), top_k, K];
     rows of invalid pairs are zero. ``tokens`` restricts the computation to a subset of tokens
     (for spot checks of large workloads); default all tokens. fp4: the planes hold e2m1 codes
-    (two per byte) instead of 2-bit codes.
+    (two per byte) instead of 2-bit codes. ``workers`` > 1 computes that many experts at a time
+    in threads; every pair's arithmetic is the same either way (each pair belongs to one expert).
     """
     dq = _dequant(fp4)
     x = np.asarray(x, dtype=np.float64)
@@ -93,9 +94,8 @@ def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=N
     tokens = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     out = np.zeros((len(tokens), top_k, K), dtype=np.float64)
     sel = ids[tokens]  # [n_tok, top_k]
-    for e in np.unique(sel):
-        if e < 0 or e >= E:
-            continue
+
+    def expert(e):
         rows, js = np.nonzero(sel == e)
         w_gu = dq(gu_codes[e], gu_scales[e])  # [2I, K]
         w_dn = dq(dn_codes[e], dn_scales[e])  # [K, I]
@@ -104,12 +104,21 @@ def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=N
         u = xe @ w_gu[I:].T
         a = silu(g) * u
         out[rows, js] = a @ w_dn.T                        # [n_e, K]
+
+    experts = [int(e) for e in np.unique(sel) if 0 <= e < E]
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(expert, experts))
+    else:
+        for e in experts:
+            expert(e)
     return out
 
 
-def moe_forward(x, topk_ids, topk_w, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None, fp4=False):
+def moe_forward(x, topk_ids, topk_w, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None, fp4=False, workers=1):
     """y[t] = sum_j (ascending) w[t, j] * o_(t, j); f64 [len(tokens), K]."""
-    o = pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens, fp4)
+    o = pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens, fp4, workers)
     w = np.asarray(topk_w, dtype=np.float64)
     tokens = np.arange(o.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
     w = w[tokens]

@@ -137,6 +137,37 @@ def requant_block_fraction(negs, mags):
     return codes, best_e + 127
 
 
+def requant_block_int(negs, mags):
+    """The same full scan as requant_block_fraction, in Python integers (about twenty times
+    faster, for pinning the C version on many blocks). Every magnitude is a dyadic rational, so
+    with L the largest of 127 and the magnitudes' denominator exponents, X_i = |x_i| * 2^L and the
+    step T = 2^(e+L) of every candidate e >= -127 are integers; SSE(e) * 4^L is then the integer
+    sum of (X_i - q_i T)^2, compared exactly across all 255 exponents (equal -> lower e)."""
+    L = 127
+    for m in mags:
+        d = m.denominator
+        if d & (d - 1):
+            raise ValueError("magnitude is not a dyadic rational")
+        L = max(L, d.bit_length() - 1)
+    X = [m.numerator << (L - (m.denominator.bit_length() - 1)) for m in mags]
+    best_e, best_sse = None, None
+    for e in range(-127, 128):
+        T = 1 << (e + L)
+        sse = 0
+        for x in X:
+            q = 4 if 2 * x > 5 * T else 1
+            d = x - q * T
+            sse += d * d
+        if best_sse is None or sse < best_sse:
+            best_e, best_sse = e, sse
+    T = 1 << (best_e + L)
+    codes = []
+    for neg, x in zip(negs, X):
+        q4 = 2 * x > 5 * T
+        codes.append((0 if q4 else 1) if neg else (3 if q4 else 2))
+    return codes, best_e + 127
+
+
 # ---------------------------------------------------------------------------------------------
 # exact integer implementation (C)
 # ---------------------------------------------------------------------------------------------

@@ -64,6 +64,24 @@ def test_host_side_validation(lib):
     assert lib.moe_w2_route(256, 4, 8, fake, fake, fake, None, 0, None) == -6
 
 
+def test_pair_count_bound(lib):
+    """T * top_k above 2^30 pairs is refused on the host: the size queries return 0 and the route
+    call MOE_W2_EUNSUPPORTED (no signed overflow into a wrong size or a negative pair count)."""
+    P = ctypes.c_void_p
+    fake = P(16)
+    lib.moe_w2_route_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_w2_route_workspace_bytes.argtypes = [ctypes.c_int] * 3
+    lib.moe_w2_route.argtypes = [ctypes.c_int] * 3 + [P] * 4 + [ctypes.c_size_t, P]
+    lib.moe_w2_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_w2_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
+    at_bound = (1 << 30) // 8
+    assert lib.moe_w2_route_workspace_bytes(256, at_bound, 8) > 0
+    for T, k in ((at_bound + 1, 8), (1 << 28, 32), (2**31 - 1, 2), (2**31 - 1, 32)):
+        assert lib.moe_w2_route_workspace_bytes(256, T, k) == 0
+        assert lib.moe_w2_route(256, T, k, fake, fake, fake, fake, 1 << 40, None) == -2
+    assert lib.moe_w2_workspace_bytes(None, 1 << 28, 32) == 0
+
+
 def test_binding_imports_without_gpu():
     import bit_routed_expert_amd as m
     assert m.moe_w2_abi_version() == 1

@@ -245,3 +245,55 @@ def test_fp4_sign_and_scale_invariants_are_exact():
     assert np.array_equal(forward.moe_forward(x, ids, w, **neg, fp4=True), -y)
     dbl = dict(planes, dn_scales=planes["dn_scales"] + np.uint8(1))
     assert np.array_equal(forward.moe_forward(x, ids, w, **dbl, fp4=True), 2 * y)
+
+
+def test_brute_force_tiny_multi_expert():
+    """E=3 experts, top-2, T=3 tokens, K=I=32, by scalar loops per pair and per output element:
+    each weight read straight from its packed byte and scale byte (codebook printed on the pages,
+    tests/golden/codebook.txt; UE8M0 value 2^(b-127)), no matrix routine and no grouping by
+    expert. Token 1 routes twice to one expert (summed like any pair), token 2 has an invalid id
+    (contributes nothing). The oracle's grouped f64 forward must agree to rounding."""
+    import math
+    book = {}
+    with open(os.path.join(GOLDEN, "codebook.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                c, v = line.split()
+                book[int(c)] = float(v)
+    rng = np.random.default_rng(21)
+    E, T, K, I, top_k = 3, 3, 32, 32, 2
+    gu_codes = rng.integers(0, 256, size=(E, 2 * I, K // 4), dtype=np.uint8)
+    gu_scales = (127 + rng.integers(-4, 2, size=(E, 2 * I, K // 32))).astype(np.uint8)
+    dn_codes = rng.integers(0, 256, size=(E, K, I // 4), dtype=np.uint8)
+    dn_scales = (127 + rng.integers(-4, 2, size=(E, K, I // 32))).astype(np.uint8)
+    x_bits = workloads.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    x = formats.bf16_bits_to_f64(x_bits)
+    ids = np.array([[2, 0], [1, 1], [0, 7]], np.int32)
+    w = np.array([[0.625, 0.375], [0.5, 0.25], [0.75, 0.125]], np.float32)
+
+    def weight(codes, scales, e, r, k):
+        code = (int(codes[e, r, k // 4]) >> (2 * (k % 4))) & 3
+        return book[code] * 2.0 ** (int(scales[e, r, k // 32]) - 127)
+
+    y = [[0.0] * K for _ in range(T)]
+    for t in range(T):
+        for j in range(top_k):
+            e = int(ids[t, j])
+            if not 0 <= e < E:
+                continue
+            a = []
+            for i in range(I):
+                g = sum(weight(gu_codes, gu_scales, e, i, k) * float(x[t, k]) for k in range(K))
+                u = sum(weight(gu_codes, gu_scales, e, I + i, k) * float(x[t, k]) for k in range(K))
+                a.append(g / (1.0 + math.exp(-g)) * u)
+            for n in range(K):
+                o = sum(weight(dn_codes, dn_scales, e, n, i) * a[i] for i in range(I))
+                y[t][n] += float(w[t, j]) * o
+    want = np.array(y)
+    got = forward.moe_forward(x, ids, w, gu_codes, gu_scales, dn_codes, dn_scales)
+    rms = np.sqrt(np.mean(want ** 2))
+    assert rms > 0
+    assert np.max(np.abs(got - want)) <= 1e-12 * rms
+    # a dropped term, a gate/up swap or a wrong expert would be off by orders of magnitude more
+    assert np.max(np.abs(got[2] - float(w[2, 0]) * forward.pair_outputs(x, ids, gu_codes, gu_scales, dn_codes,
+                                                                        dn_scales)[2, 0])) <= 1e-12 * rms

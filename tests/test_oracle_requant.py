@@ -2,6 +2,7 @@
 invariants; the C implementation is also pinned against the exact rational reference."""
 from fractions import Fraction
 import math
+import os
 
 import numpy as np
 import pytest
@@ -277,3 +278,103 @@ def test_mxfp4_scale_equivariance_and_fp8_odd_symmetry():
     nc, ns = requant.fp8_block128_to_w2(b ^ np.uint8(0x80), sc)
     assert np.array_equal(ns, fs)
     assert np.array_equal(formats.unpack_codes(nc), 3 - formats.unpack_codes(fc))
+
+
+# ---------------------------------------------------------------------------------------------
+# the C re-quantizer against the plain full-scan definition on 10^4 blocks per input format
+# ---------------------------------------------------------------------------------------------
+
+def test_int_scan_equals_rational_scan():
+    """requant_block_int (integer full scan) == requant_block_fraction (rational full scan) on
+    workload, full-range, FP8 and MXFP4 blocks and the constructed edge blocks."""
+    rng = np.random.default_rng(12)
+    blocks = []
+    for full in (False, True):
+        a, b, s = _random_blocks(rng, 40, full)
+        blocks += [requant.nvfp4_block_values(a[i], b[i], s[i]) for i in range(40)]
+    for _ in range(40):
+        sc = np.float32(rng.choice([1.0, -1.0]) * 2.0 ** rng.uniform(-20, 10))
+        blocks.append(requant.fp8_block_values(_random_fp8_block(rng), sc))
+    for _ in range(40):
+        blocks.append(requant.mxfp4_block_values(rng.integers(0, 256, 16, dtype=np.uint8), int(rng.integers(0, 255))))
+    z = np.zeros(16, np.uint8)
+    blocks.append(requant.nvfp4_block_values(z, np.array([0x38, 0x38], np.uint8), np.float32(1.0)))
+    blocks.append(requant.mxfp4_block_values(np.full(16, 0x22, np.uint8), 0))       # all 2^-127
+    blocks.append(requant.mxfp4_block_values(np.full(16, 0x77, np.uint8), 254))     # all 6 * 2^127
+    for negs, mags in blocks:
+        assert requant.requant_block_int(negs, mags) == requant.requant_block_fraction(negs, mags)
+
+
+def _plain_scan_chunk(job):
+    """Worker: (format, arrays) -> [(codes, scale byte)] per block by the integer full scan."""
+    kind, arrs = job
+    out = []
+    if kind == "nvfp4":
+        a, b, s2 = arrs
+        for i in range(len(a)):
+            out.append(requant.requant_block_int(*requant.nvfp4_block_values(a[i], b[i], s2)))
+    elif kind == "fp8":
+        e4, sc = arrs           # e4m3 bytes [n, 32], one scale
+        for i in range(len(e4)):
+            out.append(requant.requant_block_int(*requant.fp8_block_values(e4[i], sc)))
+    else:
+        a, ue = arrs            # e2m1 bytes [n, 16], scale bytes [n]
+        for i in range(len(a)):
+            out.append(requant.requant_block_int(*requant.mxfp4_block_values(a[i], int(ue[i]))))
+    return out
+
+
+def _c_blocks(codes, scales):
+    """Canonical codes [n, 8] + scale bytes [n] -> [(codes list, byte)] per 32-block."""
+    c = formats.unpack_codes(codes)
+    return [(c[i].tolist(), int(scales[i])) for i in range(len(c))]
+
+
+@pytest.mark.slow
+def test_c_matches_plain_scan_many_blocks():
+    """The C re-quantizer (7-exponent window, integer D(e) algebra) equals the plain full scan over
+    all 255 exponents on 10,000 random blocks of each input format: NVFP4 with workload-range
+    scales, NVFP4 over the whole e4m3 / fp32 range, FP8 block-128 (any finite e4m3 byte, signed zeros and subnormals, scales
+    2^U(-40, 40)) and MXFP4 (any scale byte 0..254)."""
+    from concurrent.futures import ProcessPoolExecutor
+    rng = np.random.default_rng(13)
+    jobs, want_c = [], []
+    chunk = 500
+    for full in (False, True):
+        for _ in range(10000 // chunk):
+            a, b, s = _random_blocks(rng, chunk, full)
+            s2 = s[0]
+            jobs.append(("nvfp4", (a, b, s2)))
+            want_c.append(("nvfp4", a, b, s2))
+    for _ in range(10000 // chunk):
+        e4 = np.stack([_random_fp8_block(rng) for _ in range(chunk)])   # signed zeros, subnormals
+        sc = np.float32(rng.choice([1.0, -1.0]) * 2.0 ** rng.uniform(-40, 40))
+        jobs.append(("fp8", (e4, sc)))
+        want_c.append(("fp8", e4, sc))
+    for _ in range(10000 // chunk):
+        a = rng.integers(0, 256, size=(chunk, 16), dtype=np.uint8)
+        ue = rng.integers(0, 255, size=chunk, dtype=np.uint8)
+        jobs.append(("mxfp4", (a, ue)))
+        want_c.append(("mxfp4", a, ue))
+    with ProcessPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        plain = list(ex.map(_plain_scan_chunk, jobs))
+    n = 0
+    for ref, (kind, *arrs) in zip(plain, want_c):
+        if kind == "nvfp4":
+            a, b, s2 = arrs
+            codes, scales = requant.requant_rows(a, b, s2)
+            got = _c_blocks(codes, scales[:, 0])
+        elif kind == "fp8":
+            e4, sc = arrs
+            # 500 blocks as 125 rows x 4 blocks of one 128 x 128 tile (padded rows are zero)
+            tile = np.zeros((1, 128, 128), np.uint8)
+            tile[0, :chunk // 4] = e4.reshape(chunk // 4, 128)
+            codes, scales = requant.fp8_block128_to_w2(tile, np.full((1, 1, 1), sc, np.float32))
+            got = _c_blocks(codes[0, :chunk // 4].reshape(chunk, 8), scales[0, :chunk // 4].reshape(chunk))
+        else:
+            a, ue = arrs
+            codes, scales = requant.mxfp4_to_w2(a.reshape(1, chunk, 16), ue.reshape(1, chunk, 1))
+            got = _c_blocks(codes[0], scales[0, :, 0])
+        assert got == ref, kind
+        n += len(ref)
+    assert n == 40000
