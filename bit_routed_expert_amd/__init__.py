@@ -5,7 +5,7 @@ torch device tensors' pointers and the current HIP stream to the C ABI and turns
 exceptions. There is no fallback: if the library is missing or no GPU is present, calls fail.
 
 Functions keep the C names: moe_w2_pack, moe_w2_unpack, moe_w2_workspace_bytes, moe_w2_route,
-moe_w2_forward, moe_w2_forward_stage, moe_w2_read_counters; the re-quantizers nvfp4_to_w2,
+moe_w2_forward, moe_w2_forward_stage, moe_w2_forward_noalloc, moe_w2_read_counters; the re-quantizers nvfp4_to_w2,
 fp8_block128_to_w2, mxfp4_to_w2; the FP4 planes moe_w4_pack, moe_w4_unpack, moe_w4_forward; the
 expert-slot entry points moe_w2_planes_create, moe_w2_pack_slot, moe_w2_forward_slots,
 moe_w2_read_miss_counter; and the sign-bias diagnostic moe_w2_codebook_sweep.
@@ -54,6 +54,7 @@ def _lib():
             "moe_w2_route": ([I32, I32, I32, P, P, P, P, SZ, P], I32),
             "moe_w2_forward": ([P, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
             "moe_w2_forward_stage": ([P, I32, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
+            "moe_w2_forward_noalloc": ([P, I32, I32, P, P, P, P, I32, I32, P], I32),
             "moe_w2_read_counters": ([P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), P], I32),
             "nvfp4_to_w2": ([I32, I32, I32, P, P, P, P, P, P], I32),
             "moe_w2_planes_create": ([I32, I32, I32, P, ctypes.POINTER(P)], I32),
@@ -228,6 +229,20 @@ def moe_w2_forward(planes, x, topk_ids, topk_w, out_dtype=OUT_BF16, workspace=No
                                  _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_w, torch.float32, "topk_w"),
                                  ctypes.c_void_p(y.data_ptr()), int(out_dtype), _dev(workspace, torch.uint8, "workspace"),
                                  workspace.numel(), int(path), _stream()), "moe_w2_forward")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_W2_NOALLOC_SCRATCH_BYTES
+
+
+def moe_w2_forward_noalloc(planes, x, topk_ids, topk_w, y, out_dtype=OUT_BF16, path=PATH_AUTO):
+    """moe_w2_forward with the library's own per-GPU scratch as workspace: allocates nothing (y is
+    the caller's, preallocated). Calls that may overlap on one GPU race on that scratch."""
+    T, _ = x.shape
+    _check(_lib().moe_w2_forward_noalloc(planes.handle, T, topk_ids.shape[1], _dev(x, torch.bfloat16, "x"),
+                                         _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_w, torch.float32, "topk_w"),
+                                         ctypes.c_void_p(y.data_ptr()), int(out_dtype), int(path), _stream()),
+           "moe_w2_forward_noalloc")
     return y
 
 

@@ -2,6 +2,8 @@
 // sequence of kernel launches for each entry point.
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
@@ -298,6 +300,51 @@ int moe_w2_forward(const moe_w2_planes* p, int T, int top_k, const void* x, cons
     if (st != MOE_W2_OK) return st;
   }
   return MOE_W2_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+// moe_w2_forward_noalloc: moe_w2_forward with its workspace in library-owned device memory, for
+// callers that cannot allocate. `scratch` is a file-scope device array; each GPU the library runs
+// on holds its own copy, at its own address, until the process ends. On the host the array's name
+// is only a stand-in: its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and that pointer, never the name, is what host code passes to kernels.
+// ------------------------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MOE_W2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, null until looked up
+
+// Address of this device's scratch array (looked up on the device's first call), or null.
+void* scratch_ptr(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[device]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[device] = ptr;
+  }
+  return g_scratch_ptr[device];
+}
+}  // namespace
+
+int moe_w2_forward_noalloc(const moe_w2_planes* p, int T, int top_k, const void* x, const int32_t* topk_ids,
+                           const float* topk_w, void* y, int out_dtype, int path, void* stream) {
+  if (!p || T < 0 || top_k < 1) return MOE_W2_EINVAL;
+  if (top_k > 32 || !pairs_ok(T, top_k)) return MOE_W2_EUNSUPPORTED;
+  const size_t need = workspace_layout(p->E, p->K, p->I, T, top_k).total;
+  if (need > (size_t)MOE_W2_NOALLOC_SCRATCH_BYTES) return MOE_W2_EUNSUPPORTED;
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) return MOE_W2_EHIP;
+  if (device != p->device) return MOE_W2_EINVAL;   // the planes live on another device
+  void* ws = scratch_ptr(device);
+  if (!ws) return MOE_W2_EHIP;
+  return moe_w2_forward(p, T, top_k, x, topk_ids, topk_w, y, out_dtype, ws, (size_t)MOE_W2_NOALLOC_SCRATCH_BYTES,
+                        path, stream);
 }
 
 int moe_w2_forward_slots(const moe_w2_planes* p, int E, const int32_t* slot_of_expert, int T, int top_k,
