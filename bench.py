@@ -17,7 +17,10 @@ The JSON line also carries:
                   the activated experts, x read, gated intermediate written) / its average launch
                   duration, from HIP events around a graph of back-to-back launches of that stage
                   (same inputs, same launch configuration) on the stream it runs on;
-  per_batch     - per-T forward time and whole-forward algorithmic HBM rate;
+  per_batch     - per-T forward time, whole-forward algorithmic HBM rate and its fraction of peak;
+  cold_calls    - per-call forward times (p10 / median / p90 over 100 calls per T) with a 1 GiB
+                  scratch copy before every call, so no call finds weights in the 256 MB last-level
+                  cache, timed with an event pair each (the pair's own cost is reported beside);
   prefill       - the 8192-token prefill workload (K=6144, Zipf(1.1) routing): tokens/s and matrix
                   core rate of the two grouped GEMMs against the dense bf16/fp16 peak;
   zipf_decode   - the 64-token Zipf-routed decode batch at K=6144: time, active experts, HBM rate;
@@ -26,7 +29,8 @@ The JSON line also carries:
   requant       - the three load-time re-quantizers (NVFP4, FP8 block-128, MXFP4) over 256 tensors;
   sweep         - the sign-bias diagnostic: 8 synthetic expert tensors of [2048, 6144] against all
                   1239 candidate codebooks, with the symmetric / asymmetric statistics it finds;
-  cpu_baseline  - the f64 CPU oracle on a bounded sample of the same workload.
+  cpu_baseline  - the f64 CPU oracle on a bounded sample of the same workload (the prefill, Zipf
+                  decode and re-quantizer legs carry their own oracle timing).
 """
 import argparse
 import hashlib
@@ -43,6 +47,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
+MFMA_FP6_PEAK_TFLOPS = 10100.0  # MI355X dense fp6 / fp4 matrix peak (the instruction the GEMMs issue)
+A_PARTS = 3                     # the GEMMs' activations enter as three e2m3 parts: 3 instructions per product
+COLD_CALLS = 100                # per-call timing: calls per batch shape, each after a 1 GiB scratch copy
+REQUANT_THREADS = max(1, min(16, os.cpu_count() or 1))   # OpenMP threads of the C re-quantizer oracle
+CPU_WORKERS = 1                 # CPU oracle legs: the oracle as it stands (one expert at a time, BLAS threads inside)
 DECODE_TS = (1, 8, 32)
 DIRECT_MAX_PAIRS = 8            # pairs up to which the forward takes the two-kernel direct path
 # VALU issue peak: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 instruction per SIMD every 4 cycles
@@ -271,15 +280,19 @@ def main():
         per_batch[f"T{T}"] = dict(
             fwd_us=round(res["forward"] * 1e3, 2), gate_up_us=round(res["gate_up"] * 1e3, 2),
             down_us=round(res["down"] * 1e3, 2), fwd_hbm_GBps=round(res["fwd_GBps"], 1),
+            fwd_hbm_frac=round(res["fwd_GBps"] / HBM_PEAK_GBPS, 4),
+            fwd_us_at_70pct_hbm=round(nbytes_full / n_rep / (0.7 * HBM_PEAK_GBPS * 1e3), 2),
             gate_up_hbm_GBps=round(res["gu_GBps"], 1), tokens_per_s=round(T / (res["forward"] * 1e-3), 1))
     achieved = gu_bytes_all / (gu_ms_all * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     traffic = traffic_from_profiles("decode_gate_up", src_hash)
     roofline = dict(bound="hbm", kernel="decode_gate_up_kernel<4,false,0> (2-bit planes; T=8 and T=32 calls)",
+                    scope="the dominant kernel alone; whole_forward_frac has each decode shape's whole forward",
                     achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
                     traffic=traffic, launches=n_gu, avg_launch_us=round(gu_ms_all / n_gu * 1e3, 3),
-                    algorithmic_bytes_per_launch=int(gu_bytes_all / n_gu))
+                    algorithmic_bytes_per_launch=int(gu_bytes_all / n_gu),
+                    whole_forward_frac={k: v["fwd_hbm_frac"] for k, v in per_batch.items()})
     del kws
 
     out = {
@@ -298,7 +311,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3(split x2/x3)*e2m1->f32",
+        "dtype_note": ("bf16 x and fp16 gated intermediate enter the block-scaled matrix instruction as exact "
+                       "e4m3 parts (two for x, three for the intermediate) times the e2m1 weights with their UE8M0 "
+                       "scales; fp32 accumulation; bf16 output = RNE of the fp32 result"),
         "data": "synthetic",
         "config": {"workload": "moe_w2 decode: K=4096 I=2048 E=256 top-8 uniform routing, "
                                "one forward each at T=1,8,32 per step (41 tokens)",
@@ -308,21 +324,84 @@ def main():
         "source_hash": src_hash,
     }
 
+    out["cold_calls"] = bench_cold_calls(torch, moe, layers, inst, ws, ys, per_batch)
     if not args.no_slots:
         out["slots"] = bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K)
     if not args.no_w4:
         out["w4"] = bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I)
+    zipf_host = None
     if not args.no_prefill:
-        out["prefill"], out["zipf_decode"] = bench_prefill(args, moe, workloads, torch, dev)
+        out["prefill"], out["zipf_decode"], zipf_host = bench_prefill(args, moe, workloads, torch, dev)
     if not args.no_requant:
         out["requant"] = bench_requant(args, moe, workloads, torch, dev)
     if not args.no_sweep:
         out["sweep"] = bench_sweep(args, moe, workloads, torch, dev)
 
-    # free GPU memory before the CPU baseline
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(canon, inst)
+        if not args.no_prefill and zipf_host is not None:
+            out["prefill"]["cpu_baseline"] = cpu_baseline_prefill(zipf_host, out["prefill"])
+            out["zipf_decode"]["cpu_baseline"] = cpu_baseline_zipf(zipf_host["planes"], workloads)
+        if not args.no_requant:
+            out["requant"]["cpu_baseline"] = cpu_baseline_requant(workloads)
     print(json.dumps(out), flush=True)
+
+
+def cold_call_times(torch, call, n, flush_bytes=1 << 30):
+    """n calls of call(k), each after a copy of a flush_bytes scratch buffer (which displaces the
+    last-level cache) and between its own event pair on the current stream; also n empty event
+    pairs after the same copy. Returns (per-call us, empty-pair us) as numpy arrays."""
+    src = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    pairs, empty = [], []
+    for k in range(n):
+        dst.copy_(src)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call(k)
+        b.record(stream)
+        pairs.append((a, b))
+    for k in range(n):
+        dst.copy_(src)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b.record(stream)
+        empty.append((a, b))
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    e = np.array([a.elapsed_time(b) * 1e3 for a, b in empty])
+    del src, dst
+    torch.cuda.empty_cache()
+    return t, e
+
+
+def pct(a):
+    p10, p50, p90 = np.percentile(a, [10, 50, 90])
+    return dict(p10=round(float(p10), 2), median=round(float(p50), 2), p90=round(float(p90), 2))
+
+
+def bench_cold_calls(torch, moe, layers, inst, ws, ys, per_batch):
+    """Per-call forward times at T = 1, 8, 32 (COLD_CALLS calls each, cycling the routing instances
+    and the two plane copies), every call after a 1 GiB scratch copy: the distribution behind the
+    graph-replay figures, and the check that those figures do not come from weights left in the
+    256 MB last-level cache (graph_vs_cold = back-to-back graph time / cold median, the latter
+    minus the event pair's own cost)."""
+    out = {}
+    for T in DECODE_TS:
+        R = len(inst[T])
+
+        def call(k):
+            d = inst[T][k % R]
+            moe.moe_w2_forward(layers[k % 2], d["x"], d["ids"], d["w"], workspace=ws[T], y=ys[T])
+        call(0)
+        t, e = cold_call_times(torch, call, COLD_CALLS)
+        pe = float(np.median(e))
+        out[f"T{T}"] = dict(**pct(t), event_pair_us=round(pe, 2), calls=COLD_CALLS,
+                            graph_vs_cold=round(per_batch[f"T{T}"]["fwd_us"] / (float(np.median(t)) - pe), 4))
+    out["note"] = ("each call between its own event pair after a 1 GiB device copy; the pair alone (event_pair_us, "
+                   "after the same copy) costs a few us, so medians minus event_pair_us compare with per_batch")
+    return out
 
 
 def w4_expert_bytes(K, I):
@@ -452,6 +531,7 @@ def bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K):
 def bench_prefill(args, moe, workloads, torch, dev, fp4=False):
     c = workloads.PREFILL
     T, K, I, E, top_k = c["T"], c["K"], c["I"], c["E"], c["top_k"]
+    host = None
     if fp4:
         canon = workloads.draw_planes_fp4(np.random.default_rng(13), E, K, I)
         planes = moe.moe_w4_pack(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")])
@@ -459,8 +539,12 @@ def bench_prefill(args, moe, workloads, torch, dev, fp4=False):
         canon = workloads.zipf_layer(c["seed"], K, I, E)
         dcanon = [dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")]
         planes = moe.moe_w2_pack(*dcanon)
+        if not args.no_cpu_baseline:
+            host = canon          # kept for the CPU oracle legs at the end of the run
     del canon
     d = workloads.zipf_instances(T, 1, c["seed"], K, E, top_k)[0]
+    if host is not None:
+        host = dict(planes=host, inst=d)
     x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).cuda()
     ids, w = dev(d["topk_ids"]), dev(d["topk_w"])
     ws = moe.alloc_workspace(planes, T, top_k)
@@ -506,8 +590,16 @@ def bench_prefill(args, moe, workloads, torch, dev, fp4=False):
         gate_up_tflops=round(f_gu / (gu * 1e-3) / 1e12, 1), down_tflops=round(f_dn / (dn * 1e-3) / 1e12, 1),
         gemm_tflops=round(gemm_tflops, 1), gemm_mfma_frac=round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         fwd_tflops=round(fwd_tflops, 1), fwd_mfma_frac=round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-        peak_tflops=MFMA_BF16_PEAK_TFLOPS, iters=args.prefill_iters)
-    return (res, zipf_decode) if not fp4 else res
+        peak_tflops=MFMA_BF16_PEAK_TFLOPS,
+        # the instructions actually issued: fp6 (e2m3) activations x fp4 weights, three activation
+        # parts per product, against the dense fp6 / fp4 matrix peak
+        gemm_instr_tflops=round(A_PARTS * gemm_tflops, 1),
+        gemm_instr_frac=round(A_PARTS * gemm_tflops / MFMA_FP6_PEAK_TFLOPS, 4),
+        instr_peak_tflops=MFMA_FP6_PEAK_TFLOPS,
+        frac_note=("mfma_frac: algorithmic flops (2*P*3*I*K) per second against the dense bf16 peak; "
+                   "instr_frac: the fp6 x fp4 instruction flops issued (3 parts) against the dense fp6/fp4 peak"),
+        iters=args.prefill_iters)
+    return (res, zipf_decode, host) if not fp4 else res
 
 
 def bench_zipf_decode(args, moe, workloads, torch, dev, layers, R=16, n_rep=32):
@@ -552,11 +644,17 @@ def bench_zipf_decode(args, moe, workloads, torch, dev, layers, R=16, n_rep=32):
     us, nbytes = timed(moe.PATH_AUTO)            # P = 512: the decode kernels
     us_gemm, _ = timed(moe.PATH_GEMM)
     gbps = nbytes / n_rep / (us * 1e-6) / 1e9
+
+    def call(k):
+        r = k % R
+        moe.moe_w2_forward(layers[k % 2], xs[r], ids[r], ws_[r], workspace=wss[r], y=y)
+    ct, ce = cold_call_times(torch, call, COLD_CALLS)
+    cold = dict(**pct(ct), event_pair_us=round(float(np.median(ce)), 2), calls=COLD_CALLS)
     return dict(workload="moe_w2 decode: T=64 K=6144 I=2048 E=256 top-8 Zipf(1.1) routing",
                 fwd_us=round(us, 2), tokens_per_s=round(T / (us * 1e-6), 1),
                 mean_active_experts=round(float(np.mean(nact)), 1), hbm_GBps=round(gbps, 1),
                 hbm_frac=round(gbps / HBM_PEAK_GBPS, 4), us_at_70pct_hbm=round(nbytes / n_rep / (0.7 * HBM_PEAK_GBPS * 1e3), 1),
-                gemm_path_fwd_us=round(us_gemm, 2), routing_instances=R, calls=n_rep)
+                gemm_path_fwd_us=round(us_gemm, 2), routing_instances=R, calls=n_rep, cold_calls=cold)
 
 
 def bench_requant(args, moe, workloads, torch, dev):
@@ -639,24 +737,90 @@ def bench_requant(args, moe, workloads, torch, dev):
     return out
 
 
-def cpu_baseline(canon, inst):
-    """The f64 oracle on one bench step: routing instance 0 at T = 1, 8 and 32 of the decode workload."""
+def _threads():
     from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] + [CPU_WORKERS])
+
+
+def cpu_baseline(canon, inst, steps=1):
+    """The f64 oracle on `steps` bench steps: routing instances 0.. at T = 1, 8 and 32 of the decode
+    workload."""
     from oracle import formats, forward
 
     t0 = time.perf_counter()
     tokens = 0
-    for T in DECODE_TS:
-        h = inst[T][0]["host"]
-        forward.moe_forward(formats.bf16_bits_to_f64(h["x"]), h["topk_ids"], h["topk_w"], canon["gu_codes"],
-                            canon["gu_scales"], canon["dn_codes"], canon["dn_scales"])
-        tokens += T
+    for s in range(steps):
+        for T in DECODE_TS:
+            h = inst[T][s]["host"]
+            forward.moe_forward(formats.bf16_bits_to_f64(h["x"]), h["topk_ids"], h["topk_w"], canon["gu_codes"],
+                                canon["gu_scales"], canon["dn_codes"], canon["dn_scales"], workers=CPU_WORKERS)
+            tokens += T
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return dict(value=round(tokens / dt, 3), unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"one bench step: routing instance 0 at T=1, 8 and 32 of the decode workload "
+    return dict(value=round(tokens / dt, 3), unit="tokens/s", cores=int(_threads()), kind="oracle",
+                sample=f"{steps} bench steps: routing instances 0..{steps - 1} at T=1, 8 and 32 of the decode workload "
                        f"({tokens} tokens, every activated expert dequantized in f64), {dt:.1f} s wall; "
                        f"host has {os.cpu_count()} logical CPUs")
+
+
+def cpu_baseline_prefill(host, gpu_res, stride=4):
+    """The f64 oracle on the 8192-token prefill, restricted to whole expert groups: every
+    `stride`-th expert in descending group size (so large and small groups alike), all of their
+    pairs. Rate = sampled pairs / wall time, reported per token (top_k pairs)."""
+    from oracle import formats, forward
+
+    d, pl = host["inst"], host["planes"]
+    ids = d["topk_ids"]
+    E, top_k = pl["gu_codes"].shape[0], ids.shape[1]
+    counts = np.bincount(ids.ravel(), minlength=E)
+    experts = np.argsort(-counts, kind="stable")[::stride]
+    sel = np.isin(ids, experts)
+    tokens = np.nonzero(sel.any(axis=1))[0]
+    x = formats.bf16_bits_to_f64(d["x"])
+    t0 = time.perf_counter()
+    forward.moe_forward(x, np.where(sel, ids, -1).astype(np.int32), d["topk_w"], pl["gu_codes"], pl["gu_scales"],
+                        pl["dn_codes"], pl["dn_scales"], tokens=tokens, workers=CPU_WORKERS)
+    dt = time.perf_counter() - t0
+    pairs = int(sel.sum())
+    tps = pairs / top_k / dt
+    return dict(value=round(tps, 2), unit="tokens/s", cores=int(_threads()), kind="oracle",
+                gpu_over_cpu=round(gpu_res["tokens_per_s"] / tps, 1),
+                sample=f"{len(experts)} of {E} experts (every {stride}th by group size), all {pairs} of their pairs "
+                       f"({pairs / ids.size:.1%} of the 65,536), {dt:.1f} s wall; tokens/s = pairs/s / top_k")
+
+
+def cpu_baseline_zipf(planes, workloads, n_inst=1):
+    """The f64 oracle on whole Zipf-routed decode batches (T=64, K=6144), routing instances 0.."""
+    from oracle import formats, forward
+
+    c = workloads.DECODE_ZIPF
+    insts = workloads.zipf_instances(c["T"], n_inst, c["seed"], c["K"], c["E"], c["top_k"])
+    t0 = time.perf_counter()
+    for d in insts:
+        forward.moe_forward(formats.bf16_bits_to_f64(d["x"]), d["topk_ids"], d["topk_w"], planes["gu_codes"],
+                            planes["gu_scales"], planes["dn_codes"], planes["dn_scales"], workers=CPU_WORKERS)
+    dt = time.perf_counter() - t0
+    return dict(value=round(n_inst * c["T"] / dt, 3), unit="tokens/s", cores=int(_threads()), kind="oracle",
+                sample=f"routing instances 0..{n_inst - 1} (whole batches of {c['T']} tokens), {dt:.1f} s wall")
+
+
+def cpu_baseline_requant(workloads, n=32):
+    """The exact C re-quantizer oracle (integer SSE, OpenMP over REQUANT_THREADS threads) on the first
+    n of the 256 NVFP4 tensors; input generation is outside the timed region."""
+    from oracle import requant
+
+    c = workloads.REQUANT
+    R, C = c["R"], c["C"]
+    tensors = [workloads.nvfp4_tensor(i) for i in range(n)]
+    requant.requant_rows(tensors[0][0][:8], tensors[0][1][:8], tensors[0][2], nthreads=REQUANT_THREADS)   # load
+    t0 = time.perf_counter()
+    for a, b, s2 in tensors:
+        requant.requant_rows(a, b, s2, nthreads=REQUANT_THREADS)
+    dt = time.perf_counter() - t0
+    blocks = n * R * (C // 32)
+    nbytes = n * R * (C // 2 + C // 16 + C // 4 + C // 32) + 4 * n
+    return dict(value=round(blocks / dt, 1), unit="blocks/s", cores=REQUANT_THREADS, kind="oracle",
+                GBps=round(nbytes / dt / 1e9, 3), ms_for_256_tensors=round(dt / n * 256 * 1e3, 1),
+                sample=f"the first {n} of the 256 tensors of [{R}, {C}] ({blocks} blocks), {dt:.1f} s wall")
 
 
 def bench_sweep(args, moe, workloads, torch, dev):

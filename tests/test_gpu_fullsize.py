@@ -31,7 +31,7 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-2
 
 
-WORKERS = max(1, min(16, os.cpu_count() or 1))   # oracle experts computed at a time (CPU threads)
+WORKERS = max(1, min(4, os.cpu_count() or 1))   # oracle experts computed at a time (CPU threads)
 
 
 def _oracle(planes, inst, tokens, ids=None, w=None):
