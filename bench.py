@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--sweep-iters", type=int, default=2)
     ap.add_argument("--eager", action="store_true",
                     help="launch every timed call from Python instead of replaying HIP graphs (for profilers)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the 2-bit prefill leg (for counter profiles of the grouped GEMMs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run three 1 GiB device-to-device copies (a plain copy kernel of known size, "
                          "to scale the HBM byte counters of a profile)")
@@ -142,6 +144,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.prefill_only:
+        args.no_cpu_baseline = True
+        res, _, _ = bench_prefill(args, moe, workloads, torch, dev, zipf=False)
+        print(json.dumps(dict(prefill=res)), flush=True)
+        return
     c = workloads.DECODE
     K, I, E, top_k = c["K"], c["I"], c["E"], c["top_k"]
     canon = workloads.decode_layer()
@@ -528,7 +535,7 @@ def bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K):
                          "resident in permuted slots", **res)
 
 
-def bench_prefill(args, moe, workloads, torch, dev, fp4=False):
+def bench_prefill(args, moe, workloads, torch, dev, fp4=False, zipf=True):
     c = workloads.PREFILL
     T, K, I, E, top_k = c["T"], c["K"], c["I"], c["E"], c["top_k"]
     host = None
@@ -577,7 +584,7 @@ def bench_prefill(args, moe, workloads, torch, dev, fp4=False):
     fwd_tflops = (f_gu + f_dn) / (fwd * 1e-3) / 1e12
     del ws, y
     zipf_decode = None
-    if not fp4:
+    if not fp4 and zipf:
         zipf_decode = bench_zipf_decode(args, moe, workloads, torch, dev, [planes, moe.moe_w2_pack(*dcanon)])
         del dcanon
     del planes

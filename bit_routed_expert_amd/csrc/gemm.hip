@@ -24,16 +24,20 @@ namespace moew2 {
 namespace {
 
 constexpr int BM = kGemmBM;     // 64 sorted pair rows (4 MFMA row tiles)
-constexpr int kWaves = 8;       // each wave: all BM rows x 64 weight rows (4 row groups of 16)
-constexpr int BN = 64 * kWaves; // 512 weight rows per workgroup
+constexpr int kRGW = 4;         // weight row groups of 16 per wave: each wave is BM rows x 64 weight rows
+constexpr int kWaves = 8;       // two waves per SIMD
+constexpr int BN = 16 * kRGW * kWaves;   // 512 weight rows per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWgPerCu = 1;
 
-// Tile shape: the 2-bit weights cost 0.28 byte per element against 2 bytes for the activations,
-// so the workgroup tile is wide in N (512 weight rows) and short in M (64 rows): per k-tile a
-// workgroup moves 39 KB of split activations and 37 KB of weights into the CU. (Two workgroups
-// of 64 x 256 per CU moved 1.5x the bytes per flop and measured no faster, nor did 32 x 128 wave
-// tiles, which halve the LDS operand reads.)
+// Tile shape: the 2-bit weights cost 0.28 byte per element against 2.4 bytes for the split
+// activations, so the workgroup tile is wide in N (512 weight rows) and short in M (64 rows): per
+// k-tile a workgroup moves 39 KB of split activations and 37 KB of weights into the CU. Measured
+// alternatives, in alternating runs on one box (gate_up / down GEMM): this tiling 2.54 / 1.48 ms;
+// 4 waves of 64 x 128 (half the LDS operand reads per instruction, one wave per SIMD)
+// 2.63 / 1.52 ms; each with a third A stage (A two k-tiles ahead) 2.60 / 1.51 and 2.64 / 1.56 ms.
+// Earlier: two workgroups of 64 x 256 per CU moved 1.5x the bytes per flop, 32 x 128 wave tiles
+// doubled the B loads; neither was faster.
 //
 // The workgroup -> tile mapping is XCD-aware: consecutive workgroup ids are dispatched to the
 // 8 XCDs in turn, so workgroup b takes logical tile (b % 8) * per_xcd + b / 8. Each XCD then walks
@@ -66,12 +70,13 @@ MOEW2_DEV TileMap map_tile(const int32_t* tiles, const int32_t* meta, const int3
 // k-tile) as SRC contiguous chunks, so a stage is filled by direct global -> LDS loads: wave
 // instruction j writes chunks 64j .. 64j+63, lane i chunk 64j+i, from the source chunk of that
 // (row, chunk) (chunks past SRC repeat the last one; they pad the stride only).
-// Two A stages alternate (k-tile kt + 1 is requested while kt is computed); the B registers of
-// each wave rotate through three sets (k-tile kt + 2 is requested while kt is computed), since B
-// comes from HBM and A mostly from L2. In each step the A loads are issued before the B loads,
-// so "k-tile kt has landed" is "at most the kBLoads B loads of kt + 2 are outstanding". Every wave
-// issues the same loads every step (the tail repeats the last k-tile into a free stage), so the
-// counted waits below are exact.
+// kAStages A stages rotate (k-tile kt + kAStages - 1 is requested into the stage kt - 1 used
+// while kt is computed); the B registers of each wave rotate through three sets (k-tile kt + 2 is
+// requested while kt is computed), since B comes from HBM and A mostly from L2. In each step the A
+// loads are issued before the B loads, so with two stages "k-tile kt has landed" is "at most the
+// kBLoads B loads of kt + 2 are outstanding" (with three, at most the previous step's loads).
+// Every wave issues the same loads every step (the tail repeats the last k-tile into a free
+// stage), so the counted waits below are exact.
 // ------------------------------------------------------------------------------------------------
 constexpr int kAStages = 2;
 
@@ -115,15 +120,15 @@ MOEW2_DEV void a_sources(uint32_t (&off)[AT::kPerWave], int w, int lane, RowOff 
   }
 }
 
-// B: the 4 row groups of a wave, one native k-tile (code loads per row group: 1 for 2-bit codes,
-// 2 for fp4 codes)
+// B: the kRGW row groups of a wave, one native k-tile (code loads per row group: 1 for 2-bit
+// codes, 2 for fp4 codes)
 template <int FMT>
 struct BRegs {
-  u32x4_t c[4][WFmt<FMT>::kLoads];
-  uint32_t s[4];
+  u32x4_t c[kRGW][WFmt<FMT>::kLoads];
+  uint32_t s[kRGW];
 };
 template <int FMT>
-constexpr int kBLoads = 4 * (WFmt<FMT>::kLoads + 1);   // vector memory instructions for one BRegs
+constexpr int kBLoads = kRGW * (WFmt<FMT>::kLoads + 1);   // vector memory instructions for one BRegs
 constexpr int kGroups = 8;   // instruction groups per k-tile: 2 columns C x 4 row tiles m
 
 template <int I, int N, class F>
@@ -156,6 +161,14 @@ struct KLoads {
       const int j = min(w + kWaves * N, AT::kInstr - 1);
       __builtin_amdgcn_global_load_lds((const void*)(abase + (aoff[N] + (uint32_t)ka * AT::kSrcBytes)),
                                        (__attribute__((address_space(3))) void*)(stage + 1024 * j), 16, 0, 0);
+      if constexpr (N == AT::kPerWave - 1) {
+        // The k-loop's wait for this stage counts on every DMA instruction of the step being
+        // issued before the step's B loads. Items of one group may otherwise be interleaved by
+        // the compiler (it placed B loads ahead of the last DMA instruction), which would leave
+        // that DMA uncounted by the wait and let its chunks be read before they land.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
     } else {
       constexpr int L = WFmt<FMT>::kLoads;
       constexpr int n = N - AT::kPerWave, t = n / (L + 1), q = n % (L + 1);
@@ -182,31 +195,37 @@ struct KLoads {
 // The k-loop: COMPUTE(stage, BRegs, part, mma) for every step, where part(integral_constant<I>)
 // issues load group I (COMPUTE calls it for I = 0..7 in order, always) and mma says whether the
 // step has a k-tile to multiply (not the first two steps, the tail of the last round or idle
-// waves). K-tile j uses A stage j % 2 and B register set j % 3.
+// waves). K-tile j uses A stage j % 3 and B register set j % 3.
 template <class AT, int FMT, class Compute>
 MOEW2_DEV void k_loop(uint8_t* lds, const KLoads<AT, FMT>& ld, int nkt, bool active, Compute compute) {
+  static_assert(kAStages == 2 || kAStages == 3, "A runs kAStages - 1 k-tiles ahead");
   BRegs<FMT> b0, b1, b2;
-  auto step = [&](int kt, BRegs<FMT>& cur, BRegs<FMT>& ahead) {
-    // k-tile kt has landed: its A was issued in the previous step before that step's B loads
-    wait_vm<kBLoads<FMT>>();
+  // POS = kt mod 3 (kt = -2 starts the first round, so the round positions are 1, 2, 0)
+  auto step = [&](int kt, auto pos, BRegs<FMT>& cur, BRegs<FMT>& ahead) {
+    constexpr int POS = decltype(pos)::value;
+    // k-tile kt has landed: its B was issued two steps ago, its A kAStages - 1 steps ago, each
+    // before the B loads of its step; what may still be outstanding is what came after
+    wait_vm<kAStages == 3 ? AT::kPerWave + kBLoads<FMT> : kBLoads<FMT>>();
     lds_barrier();                     // ... in every wave; and every wave is done with kt - 1
-    const int ka = max(0, min(kt + 1, nkt - 1));
-    const int kb = min(kt + 2, nkt - 1);
-    uint8_t* a_stage = lds + ((kt + 1) & 1) * AT::kBytes;    // the stage kt - 1 used
+    const int ka = max(0, min(kt + kAStages - 1, nkt - 1));
+    const int kb = max(0, min(kt + 2, nkt - 1));
+    // A: the stage kt - 1 used; computing from the stage of kt
+    const int a_next = kAStages == 3 ? (POS + 2) % 3 : ((kt + 1) & 1);
+    const int a_cur = kAStages == 3 ? POS : (kt & 1);
+    uint8_t* a_stage = lds + a_next * AT::kBytes;
     auto part = [&](auto ic) { ld.template group<decltype(ic)::value>(ka, a_stage, kb, ahead); };
     // Every step runs the same instruction stream except the matrix instructions themselves: the
     // loads and LDS reads are unconditional (a step without a k-tile reads a stale stage), so the
     // compiler's count of outstanding loads stays exact and no operand needs a merge copy.
     const bool mma = active && kt >= 0 && kt < nkt;
-    compute(lds + (kt & 1) * AT::kBytes, cur, part, mma);
+    compute(lds + a_cur * AT::kBytes, cur, part, mma);
   };
-  // Whole rounds of three steps (the B register sets rotate by three): the first round's first
-  // two steps only issue (A of k-tile 0 - twice - and B of k-tiles 0 and 1), steps past the last
-  // k-tile only load repeats of it.
+  // Whole rounds of three steps (B register sets, and three A stages, rotate by three): the first
+  // round's first two steps only issue, steps past the last k-tile only load repeats of it.
   for (int kt = -2; kt < nkt; kt += 3) {
-    step(kt, b1, b0);
-    step(kt + 1, b2, b1);
-    step(kt + 2, b0, b2);
+    step(kt, std::integral_constant<int, 1>(), b1, b0);
+    step(kt + 1, std::integral_constant<int, 2>(), b2, b1);
+    step(kt + 2, std::integral_constant<int, 0>(), b0, b2);
   }
   wait_vm<0>();                        // no DMA may still target this workgroup's LDS
 }
@@ -271,20 +290,21 @@ using A6Tile = ATile<kA6Chunks + 1, kA6Chunks>;
 static_assert(kA6Bytes % 16 == 0, "split record is whole chunks");
 
 // The k-loop body shared by both GEMMs: for each instruction column C of the k-tile, the B
-// operands of the wave's 4 row groups, then per row tile m the three parts x 4 row groups of
-// instructions. The next row tile's operand is read from LDS while this one's 12 instructions
-// run, the group's share of the loads two k-tiles ahead goes out with it, and the three parts of
-// one accumulator are 4 instructions apart (back-to-back dependent instructions stall).
+// operands of the wave's kRGW row groups, then per row tile m the three parts x kRGW row groups
+// of instructions. The next row tile's operand is read from LDS while this one's 3 * kRGW
+// instructions run, the group's share of the loads two k-tiles ahead goes out with it, and the
+// three parts of one accumulator are kRGW instructions apart (back-to-back dependent instructions
+// stall).
 template <int FMT, class Part>
-MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][4], const uint8_t* abuf, const BRegs<FMT>& br, Part part, bool mma,
+MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][kRGW], const uint8_t* abuf, const BRegs<FMT>& br, Part part, bool mma,
                         int rows_valid, int lane, const Fp4Masks& fm) {
   const int g = lane >> 4;
   const uint8_t* arow = abuf + (lane & 15) * kA6Stride;
   static_for<0, 2>([&](auto cc) {
     constexpr int C = decltype(cc)::value;
-    i32x8_t bo[4];
+    i32x8_t bo[kRGW];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) bo[t] = b_operand<FMT, C>(br.c[t], fm);
+    for (int t = 0; t < kRGW; ++t) bo[t] = b_operand<FMT, C>(br.c[t], fm);
     A6Op cur = a6_load(arow, C, g), nxt;
     static_for<0, 4>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
@@ -294,11 +314,11 @@ MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][4], const uint8_t* abuf, const BRegs<F
       // a row tile with no valid row (the ragged end of an expert's group) skips its instructions
       if (mma && 16 * m < rows_valid) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[m][t] = mx6_mfma<0, C>(cur.p[0], bo[t], acc[m][t], cur.s, br.s[t]);
+        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<0, C>(cur.p[0], bo[t], acc[m][t], cur.s, br.s[t]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[m][t] = mx6_mfma<1, C>(cur.p[1], bo[t], acc[m][t], cur.s, br.s[t]);
+        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<1, C>(cur.p[1], bo[t], acc[m][t], cur.s, br.s[t]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[m][t] = mx6_mfma<2, C>(cur.p[2], bo[t], acc[m][t], cur.s, br.s[t]);
+        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<2, C>(cur.p[2], bo[t], acc[m][t], cur.s, br.s[t]);
       }
       if constexpr (m < 3) cur = nxt;
     });
@@ -307,20 +327,25 @@ MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][4], const uint8_t* abuf, const BRegs<F
 
 // ------------------------------------------------------------------------------------------------
 // gate_up: rows of the split x gathered through the sort permutation (token = pair / top_k).
-// Wave w of N-block nb holds gated columns 32 * (8 nb + w) .. +31 of its BM rows: block w of the
-// down GEMM's k-tile nb (2I is a multiple of BN, so every wave has its block). The epilogue
-// rounds a = silu(g) * u to fp16, passes the BM x 32 block through the wave's own LDS region (row
-// stride 36 floats, 4 mod 8 dwords, for the row-per-lane reads), lane r splits row r's block into
-// its three e2m3 parts (the arithmetic of quant_x6_kernel, on the fp16-rounded values) and puts
-// them in row r's split record, assembled in LDS; the workgroup then writes the BM whole records
-// (sorted row, k-tile nb) with 16-byte stores of consecutive chunks.
+// Wave w of N-block nb holds row groups kRGW * (kWaves nb + w) .. + kRGW - 1 (gate, up, gate, up,
+// ...), i.e. gated columns 8 kRGW (kWaves nb + w) .. + 8 kRGW - 1 of its BM rows: blocks
+// kBPW w .. kBPW w + kBPW - 1 (kBPW = kRGW / 4 blocks of 32) of the down GEMM's k-tile nb (2I is a
+// multiple of BN, so every wave has its blocks). The epilogue rounds a = silu(g) * u to fp16,
+// passes each BM x 32 block through the wave's own LDS region (row stride 36 floats, 4 mod 8
+// dwords, for the row-per-lane reads), lane r splits row r of each block into its three e2m3
+// parts (the arithmetic of quant_x6_kernel, on the fp16-rounded values) and puts them in row r's
+// split record, assembled in LDS; the workgroup then writes the BM whole records (sorted row,
+// k-tile nb) with 16-byte stores of consecutive chunks.
 // ------------------------------------------------------------------------------------------------
+constexpr int kBPW = kRGW / 4;                          // 32-value blocks of gated columns per wave
 constexpr int kTpStride = 36;                           // floats per row of the epilogue's block
-constexpr int kTpBytes = BM * kTpStride * 4;            // one wave's region
+constexpr int kTpBlock = BM * kTpStride;                // floats of one block in the wave's region
+constexpr int kTpBytes = kBPW * kTpBlock * 4;           // one wave's region
 constexpr int kRecOff = kWaves * kTpBytes;              // the assembled records
 constexpr int kGateUpLds = kRecOff + BM * kA6Bytes > kAStages * A6Tile::kBytes ? kRecOff + BM * kA6Bytes
                                                                                  : kAStages * A6Tile::kBytes;
-static_assert(kWaves * 32 == kTileK, "a gate_up workgroup covers one down k-tile of gated columns");
+static_assert(kRGW % 4 == 0, "a wave holds whole 32-value blocks of gated columns");
+static_assert(kWaves * kBPW * 32 == kTileK, "a gate_up workgroup covers one down k-tile of gated columns");
 template <int FMT>
 __global__ void __launch_bounds__(kThreads, kWgPerCu)
 gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -335,9 +360,10 @@ gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restr
   const int nkt = K / kTileK, nrg = 2 * I / kTileRows;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // row groups 4*(nb*kWaves + w) .. +3 of this wave (gate, up, gate, up); a matrix with fewer
-  // than BN rows leaves waves idle (they still load a valid row group to keep the waits exact)
-  const int rg0 = 4 * (tm.nb * kWaves + w);
+  // row groups kRGW*(nb*kWaves + w) .. + kRGW - 1 of this wave (gate, up, gate, up, ...); a matrix
+  // with fewer than BN rows leaves waves idle (they still load a valid row group to keep the waits
+  // exact)
+  const int rg0 = kRGW * (tm.nb * kWaves + w);
   const bool wave_active = rg0 < nrg;
   const size_t tb0 = (size_t)e * nrg * nkt + (size_t)(wave_active ? rg0 : 0) * nkt;
 
@@ -347,11 +373,11 @@ gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restr
     return (uint32_t)tok * (uint32_t)(nkt * A6Tile::kSrcBytes);
   });
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[4][kRGW];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < kRGW; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const Fp4Masks fm = fp4_masks();
   const KLoads<A6Tile, FMT> ld{xq, aoff, codes, scales, tb0, nkt, w, lane};
@@ -360,7 +386,7 @@ gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restr
   });
   __syncthreads();   // every wave is done with the A stages, which the epilogue reuses
 
-  // ---- epilogue: a = silu(g) * u in fp16, block w of each sorted row's split record ----
+  // ---- epilogue: a = silu(g) * u in fp16, blocks kBPW w .. of each sorted row's split record ----
   if (wave_active) {
     float* tp = reinterpret_cast<float*>(lds + w * kTpBytes);
     unsigned n_inf = 0;
@@ -369,12 +395,14 @@ gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restr
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m * 16 + 4 * (lane >> 4) + r;
+        // gate/up row-group pair pr: gated columns 16 pr .. 16 pr + 15 of the wave, i.e. block
+        // pr / 2, columns 16 (pr % 2) .. of it
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
+        for (int pr = 0; pr < kRGW / 2; ++pr) {
           const float a = silu_mul(acc[m][2 * pr][r], acc[m][2 * pr + 1][r]);
           const float h = (float)(_Float16)a;
           n_inf += row < rows_valid && __builtin_isinf(h) ? 1u : 0u;
-          tp[row * kTpStride + 16 * pr + (lane & 15)] = h;
+          tp[(pr / 2) * kTpBlock + row * kTpStride + 16 * (pr % 2) + (lane & 15)] = h;
         }
       }
     }
@@ -382,19 +410,22 @@ gemm_gate_up_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restr
     if (n_inf) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)n_inf);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the region is this wave's alone
     if (lane < rows_valid) {
-      float v[32];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const f32x4_t f = *reinterpret_cast<const f32x4_t*>(tp + lane * kTpStride + 4 * q);
-        v[4 * q] = f[0], v[4 * q + 1] = f[1], v[4 * q + 2] = f[2], v[4 * q + 3] = f[3];
+      for (int b = 0; b < kBPW; ++b) {
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const f32x4_t f = *reinterpret_cast<const f32x4_t*>(tp + b * kTpBlock + lane * kTpStride + 4 * q);
+          v[4 * q] = f[0], v[4 * q + 1] = f[1], v[4 * q + 2] = f[2], v[4 * q + 3] = f[3];
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[q]));
+        const uint32_t sb = a6_scale_byte(amax);
+        u32x6_t part[3];
+        a6_split(v, sb, part);
+        a6_store(lds + kRecOff + lane * kA6Bytes, kBPW * w + b, part, sb);
       }
-      float amax = 0.f;
-#pragma unroll
-      for (int q = 0; q < 32; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[q]));
-      const uint32_t sb = a6_scale_byte(amax);
-      u32x6_t part[3];
-      a6_split(v, sb, part);
-      a6_store(lds + kRecOff + lane * kA6Bytes, w, part, sb);
     }
   }
   __syncthreads();   // every block of every record is in LDS
@@ -424,7 +455,7 @@ gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg0 = 4 * (tm.nb * kWaves + w);
+  const int rg0 = kRGW * (tm.nb * kWaves + w);
   const bool wave_active = rg0 < nrg;
   const size_t tb0 = (size_t)e * nrg * nkt + (size_t)(wave_active ? rg0 : 0) * nkt;
 
@@ -433,11 +464,11 @@ gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict
     return (uint32_t)(rs + min(r, rows_valid - 1)) * (uint32_t)(nkt * A6Tile::kSrcBytes);
   });
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[4][kRGW];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < kRGW; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // the tile's pair indices, fetched now so that the epilogue's stores do not wait on them
   __shared__ int tile_pairs[BM];
   if (tid < BM) tile_pairs[tid] = perm[rs + min(tid, rows_valid - 1)];
@@ -459,7 +490,7 @@ gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict
       if (row >= rows_valid) continue;
       const int p = tile_pairs[row];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) pair_out[(size_t)p * K + 16 * (rg0 + t) + (lane & 15)] = acc[m][t][r];
+      for (int t = 0; t < kRGW; ++t) pair_out[(size_t)p * K + 16 * (rg0 + t) + (lane & 15)] = acc[m][t][r];
     }
   }
 }
