@@ -648,8 +648,9 @@ def bench_zipf_decode(args, moe, workloads, torch, dev, layers, R=16, n_rep=32):
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n_rep * 1e3, nbytes
-    us, nbytes = timed(moe.PATH_AUTO)            # P = 512: the decode kernels
+    us, nbytes = timed(moe.PATH_AUTO)            # P = 512: the sorted decode organisation
     us_gemm, _ = timed(moe.PATH_GEMM)
+    us_routed, _ = timed(moe.PATH_DECODE)
     gbps = nbytes / n_rep / (us * 1e-6) / 1e9
 
     def call(k):
@@ -661,7 +662,8 @@ def bench_zipf_decode(args, moe, workloads, torch, dev, layers, R=16, n_rep=32):
                 fwd_us=round(us, 2), tokens_per_s=round(T / (us * 1e-6), 1),
                 mean_active_experts=round(float(np.mean(nact)), 1), hbm_GBps=round(gbps, 1),
                 hbm_frac=round(gbps / HBM_PEAK_GBPS, 4), us_at_70pct_hbm=round(nbytes / n_rep / (0.7 * HBM_PEAK_GBPS * 1e3), 1),
-                gemm_path_fwd_us=round(us_gemm, 2), routing_instances=R, calls=n_rep, cold_calls=cold)
+                gemm_path_fwd_us=round(us_gemm, 2), routed_decode_fwd_us=round(us_routed, 2),
+                routing_instances=R, calls=n_rep, cold_calls=cold)
 
 
 def bench_requant(args, moe, workloads, torch, dev):

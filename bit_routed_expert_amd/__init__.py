@@ -18,7 +18,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoew2.so")
 
 OUT_BF16, OUT_F32 = 0, 1
-PATH_AUTO, PATH_DECODE, PATH_GEMM = 0, 1, 2
+PATH_AUTO, PATH_DECODE, PATH_GEMM, PATH_DECODE_SORTED = 0, 1, 2, 3
 STAGE_ROUTE, STAGE_GATE_UP, STAGE_DOWN, STAGE_COMBINE = 0, 1, 2, 3
 
 STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ESCALE", -4: "ENOMEM", -5: "EHIP",

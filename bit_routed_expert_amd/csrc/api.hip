@@ -15,13 +15,14 @@ Workspace workspace_layout(int E, int K, int I, int T, int top_k) {
   const int P = T * top_k;
   w.P = P;
   w.max_tiles = P > 0 ? P / kGemmBM + (E < P ? E : P) + 1 : 0;
+  w.max_chunks = P > 0 ? P / kDecodeChunk + (E < P ? E : P) + 1 : 0;
   size_t o = 0;
   w.counters = o;  o += align_up(3 * sizeof(long long));
   w.offsets = o;   o += align_up((size_t)(E + 1) * 4);
   w.perm = o;      o += align_up((size_t)P * 4);
   w.active = o;    o += align_up((size_t)E * 4);
   w.meta = o;      o += align_up(8 * 4);
-  w.tiles = o;     o += align_up((size_t)w.max_tiles * 2 * 4);
+  w.tiles = o;     o += align_up((size_t)w.max_chunks * 2 * 4);   // max_chunks >= max_tiles
   const size_t rs = route_scratch_bytes(E, P);
   w.chunk_cnt = o;
   w.rank = o + (rs - align_up((size_t)P * 4));
@@ -89,7 +90,9 @@ static int forward_check(const moe_w2_planes* p, int T, int top_k, const void* x
   if (!p || T < 0 || top_k < 1) return MOE_W2_EINVAL;
   if (top_k > 32) return MOE_W2_EUNSUPPORTED;
   if (out_dtype != MOE_W2_OUT_BF16 && out_dtype != MOE_W2_OUT_F32) return MOE_W2_EINVAL;
-  if (path != MOE_W2_PATH_AUTO && path != MOE_W2_PATH_DECODE && path != MOE_W2_PATH_GEMM) return MOE_W2_EINVAL;
+  if (path != MOE_W2_PATH_AUTO && path != MOE_W2_PATH_DECODE && path != MOE_W2_PATH_GEMM &&
+      path != MOE_W2_PATH_DECODE_SORTED)
+    return MOE_W2_EINVAL;
   if (T > 0 && (!x || !topk_ids || !topk_w || !y)) return MOE_W2_EINVAL;
   if (!pairs_ok(T, top_k)) return MOE_W2_EUNSUPPORTED;
   if ((long long)T * p->K >= (1LL << 31) || (long long)T * top_k * p->I >= (1LL << 31))
@@ -99,11 +102,21 @@ static int forward_check(const moe_w2_planes* p, int T, int top_k, const void* x
     return MOE_W2_EUNSUPPORTED;  // ... and their split copies with 32-bit byte offsets
   const Workspace ws = workspace_layout(p->E, p->K, p->I, T, top_k);
   if (!workspace || workspace_bytes < ws.total) return MOE_W2_EWORKSPACE;
-  const bool decode = path == MOE_W2_PATH_DECODE ||
+  const bool decode = path == MOE_W2_PATH_DECODE || path == MOE_W2_PATH_DECODE_SORTED ||
                       (path == MOE_W2_PATH_AUTO && (long long)T * top_k <= kDecodeMaxPairs);
-  // every decode workgroup scans all ids itself (two per thread)
+  // every decode workgroup of the routed organisation scans all ids itself (two per thread); the
+  // sorted one takes its chunks from a routing pass of at most kDecodeMaxPairs pairs
   if (decode && (long long)T * top_k > kDecodeMaxPairs) return MOE_W2_EUNSUPPORTED;
   return MOE_W2_OK;
+}
+
+// Kernel family of a forward: -1 = grouped GEMMs, else the decode organisation.
+static int decode_mode(int path, int P) {
+  if (path == MOE_W2_PATH_GEMM || (path == MOE_W2_PATH_AUTO && P > kDecodeMaxPairs)) return -1;
+  if (path == MOE_W2_PATH_DECODE_SORTED) return kDecodeSorted;
+  if (P <= kDirectMaxPairs) return kDecodeDirect;
+  if (path == MOE_W2_PATH_AUTO && P >= kSortedMinPairs) return kDecodeSorted;
+  return kDecodeRouted;
 }
 }  // namespace moew2
 
@@ -239,6 +252,7 @@ int moe_w2_route(int E, int T, int top_k, const int32_t* topk_ids, int32_t* offs
   o.rank = (int32_t*)(w + route_scratch_bytes(E, P) - align_up((size_t)P * 4));
   o.counters = nullptr;
   o.max_tiles = max_tiles;
+  o.tile_rows = kGemmBM;
   return hip_status(launch_route(E, T, top_k, topk_ids, o, (hipStream_t)stream));
 }
 
@@ -252,15 +266,15 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
   if (T == 0) return MOE_W2_OK;
   hipStream_t s = (hipStream_t)stream;
   uint8_t* wsb = (uint8_t*)workspace;
-  const bool decode = path == MOE_W2_PATH_DECODE ||
-                      (path == MOE_W2_PATH_AUTO && (long long)T * top_k <= kDecodeMaxPairs);
-  // the decode kernels find their pairs from the ids themselves (no routing pass); the direct
-  // organisation also combines inside the down stage
-  const bool direct = decode && (long long)T * top_k <= kDirectMaxPairs;
+  const int mode = decode_mode(path, T * top_k);
+  const bool decode = mode >= 0;
+  // the routed and direct decode organisations find their pairs from the ids themselves (no
+  // routing pass); the direct organisation also combines inside the down stage
+  const bool direct = mode == kDecodeDirect;
   hipError_t err = hipSuccess;
   switch (stage) {
     case MOE_W2_STAGE_ROUTE: {
-      if (decode) break;
+      if (mode == kDecodeRouted || mode == kDecodeDirect) break;
       RouteOut o;
       o.offsets = (int32_t*)(wsb + ws.offsets);
       o.perm = (int32_t*)(wsb + ws.perm);
@@ -270,16 +284,17 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
       o.counters = (long long*)(wsb + ws.counters);
       o.chunk_cnt = (int32_t*)(wsb + ws.chunk_cnt);
       o.rank = (int32_t*)(wsb + ws.rank);
-      o.max_tiles = ws.max_tiles;
+      o.max_tiles = mode == kDecodeSorted ? ws.max_chunks : ws.max_tiles;
+      o.tile_rows = mode == kDecodeSorted ? kDecodeChunk : kGemmBM;
       err = launch_route(p->E, T, top_k, topk_ids, o, s);
       break;
     }
     case MOE_W2_STAGE_GATE_UP:
-      err = decode ? launch_decode_gate_up(p, T, top_k, x, topk_ids, ws, wsb, direct, s)
+      err = decode ? launch_decode_gate_up(p, T, top_k, x, topk_ids, ws, wsb, mode, s)
                    : launch_gemm_gate_up(p, T, top_k, x, ws, wsb, s);
       break;
     case MOE_W2_STAGE_DOWN:
-      err = decode ? launch_decode_down(p, T, top_k, topk_ids, topk_w, y, out_dtype, ws, wsb, direct, s)
+      err = decode ? launch_decode_down(p, T, top_k, topk_ids, topk_w, y, out_dtype, ws, wsb, mode, s)
                    : launch_gemm_down(p, T, top_k, ws, wsb, s);
       break;
     default:

@@ -381,36 +381,66 @@ MOEW2_DEV int pair_at(const ScanLds& sh, int m) {
   return 0;
 }
 
+// Chunk of the sorted organisation: workgroup row ti takes the ti-th entry (expert, first sorted
+// row) of the routing pass's chunk list, in expert order; its pairs are perm[rs .. rs + n).
+struct SortedChunk {
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* tiles;
+  const int32_t* meta;
+};
+MOEW2_DEV bool sorted_chunk(const SortedChunk& sc, int ti, int& e, int& n, int (&pr)[kChunk]) {
+  if (ti >= sc.meta[1]) return false;
+  e = sc.tiles[2 * ti];
+  const int rs = sc.tiles[2 * ti + 1];
+  n = min(kChunk, sc.offsets[e + 1] - rs);
+#pragma unroll
+  for (int m = 0; m < kChunk; ++m) pr[m] = sc.perm[rs + min(m, n - 1)];
+  return true;
+}
+static_assert(kChunk == kDecodeChunk, "the routing pass cuts chunks of the decode kernels' size");
+
 // ---------------------------------------------------------------------------------------------
 // gate_up: grid (I / (16*NP), groups). Wave w handles row-pair q = blockIdx.x*NP + w/KS (gate row
 // group 2q, up row group 2q+1) over the reduction slice w%KS of KS = 4/NP.
-// DIRECT: group = pair blockIdx.y (expert ids[p]). Otherwise group = the kChunk pairs of expert
-// ids[blockIdx.y] from blockIdx.y on, when blockIdx.y starts such a chunk (pair_group). The gated
-// row of pair p is act[p] in both.
+// kDecodeDirect: group = pair blockIdx.y (expert ids[p]). kDecodeRouted: group = the kChunk pairs
+// of expert ids[blockIdx.y] from blockIdx.y on, when blockIdx.y starts such a chunk (pair_group).
+// kDecodeSorted: group = chunk blockIdx.y of the routing pass. The gated row of pair p is act[p]
+// in all three.
 // ---------------------------------------------------------------------------------------------
-template <int NPW, bool DIRECT, int FMT>
+template <int NPW, int MODE, int FMT>
 __global__ void __launch_bounds__(kThreads)
 decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                       const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
                       _Float16* __restrict__ act, long long* __restrict__ counters,
-                      int P, int E, int K, int I, int top_k) {
+                      int P, int E, int K, int I, int top_k, SortedChunk sc) {
   constexpr int KS = kWaves / NPW;
+  constexpr bool DIRECT = MODE == kDecodeDirect;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ ScanLds sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
-  int e, n_total, first = 0;
+  int e, n;
+  int pr[kChunk];   // pair and token of each staged row (the same in every lane)
   bool valid = true;
-  if (DIRECT) {
+  if constexpr (MODE == kDecodeDirect) {
     // no early exit: the x row is requested together with the id (an invalid pair streams no
     // weights and gets a row of zeros, which the down stage stages like any other)
     const int id = ids[blockIdx.y];
     valid = id >= 0 && id < E;
     e = valid ? id : 0;
-    n_total = 1;
+    n = 1;
+#pragma unroll
+    for (int m = 0; m < kChunk; ++m) pr[m] = (int)blockIdx.y;
+  } else if constexpr (MODE == kDecodeSorted) {
+    if (!sorted_chunk(sc, blockIdx.y, e, n, pr)) return;
   } else {
     long long* cnt = blockIdx.x == 0 && blockIdx.y == 0 ? counters : nullptr;
+    int n_total, first;
     if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, cnt, e, n_total, first)) return;
+    n = min(kChunk, n_total - first);
+#pragma unroll
+    for (int m = 0; m < kChunk; ++m) pr[m] = pair_at(sh, first + min(m, n - 1));
   }
   const int nkt = K / kTileK, nrg = 2 * I / kTileRows;
   const int pw = w / KS, ks = w % KS;
@@ -423,11 +453,6 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
   float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][2][4][16]
   TileRegs<2, FMT> ring[kRing];
   {
-    const int c0 = first, n = min(kChunk, n_total - c0);
-    // pair and token of each staged row (the same in every lane)
-    int pr[kChunk];
-#pragma unroll
-    for (int m = 0; m < kChunk; ++m) pr[m] = DIRECT ? (int)blockIdx.y : pair_at(sh, c0 + min(m, n - 1));
     auto row_off = [&](int m) -> size_t {
       const int pp = m == 0 ? pr[0] : m == 1 ? pr[1] : m == 2 ? pr[2] : pr[3];
       return (size_t)(pp / top_k) * K;
@@ -463,20 +488,30 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
 // combine_kernel then sums them per token in j order. The blockIdx.x == 0 workgroups count the
 // gated intermediates that overflowed fp16 (each pair belongs to one group).
 // ---------------------------------------------------------------------------------------------
-template <int NPW, int FMT, int R>
+template <int NPW, int FMT, int R, int MODE>
 __global__ void __launch_bounds__(kThreads)
 decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                    const _Float16* __restrict__ act, const int32_t* __restrict__ ids,
                    float* __restrict__ pair_out, long long* __restrict__ counters, int P, int E, int K,
-                   int I) {
+                   int I, SortedChunk sc) {
   constexpr int KS = kWaves / NPW;
   static_assert(R == 1 || KS == 1, "row pairs per wave need the whole reduction in each wave");
+  static_assert(MODE == kDecodeRouted || MODE == kDecodeSorted, "the direct organisation has its own down kernel");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ ScanLds sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
-  int e, n_e, first;
-  if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, nullptr, e, n_e, first)) return;
+  int e, n;
+  int pr[kChunk];
+  if constexpr (MODE == kDecodeSorted) {
+    if (!sorted_chunk(sc, blockIdx.y, e, n, pr)) return;
+  } else {
+    int n_e, first;
+    if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, nullptr, e, n_e, first)) return;
+    n = min(kChunk, n_e - first);
+#pragma unroll
+    for (int m = 0; m < kChunk; ++m) pr[m] = pair_at(sh, first + min(m, n - 1));
+  }
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int pw = w / KS, ks = w % KS;
   const int rq = (blockIdx.x * NPW + pw) * R;   // the wave's first row pair
@@ -489,10 +524,6 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
   const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
   TileRegs<2, FMT> ring[kRing];
   {
-    const int c0 = first, n = min(kChunk, n_e - c0);
-    int pr[kChunk];
-#pragma unroll
-    for (int m = 0; m < kChunk; ++m) pr[m] = pair_at(sh, c0 + min(m, n - 1));
     auto row_off = [&](int m) -> size_t {
       const int pp = m == 0 ? pr[0] : m == 1 ? pr[1] : m == 2 ? pr[2] : pr[3];
       return (size_t)pp * I;
@@ -665,71 +696,98 @@ size_t decode_direct_lds(int I) {
   return (size_t)kDirectMaxPairs * MxRow<3>::stride(I) + (size_t)kDirectMaxPairs * 2 * 16 * 4;
 }
 
+static SortedChunk sorted_chunks(const Workspace& ws, const uint8_t* wsb) {
+  return SortedChunk{(const int32_t*)(wsb + ws.offsets), (const int32_t*)(wsb + ws.perm),
+                     (const int32_t*)(wsb + ws.tiles), (const int32_t*)(wsb + ws.meta)};
+}
+
 template <int FMT>
 static hipError_t decode_gate_up_fmt(const moe_w2_planes* p, int T, int top_k, const void* x,
-                                     const int32_t* ids, const Workspace& ws, uint8_t* wsb, bool direct,
+                                     const int32_t* ids, const Workspace& ws, uint8_t* wsb, int mode,
                                      hipStream_t s) {
   const int P = T * top_k;
-  const int groups = direct ? P : min(p->E, P);   // at most this many workgroup rows do work
   const size_t lds = (size_t)kChunk * MxRow<2>::stride(p->K) + (size_t)kWaves * 2 * 4 * 16 * 4;
   const uint16_t* xb = (const uint16_t*)x;
   _Float16* act = (_Float16*)(wsb + ws.act);
   long long* cnt = (long long*)(wsb + ws.counters);
-  if (direct) {
-    hipLaunchKernelGGL((decode_gate_up_kernel<1, true, FMT>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k);
-  } else if (pick_np(groups) == 4) {
-    hipLaunchKernelGGL((decode_gate_up_kernel<4, false, FMT>), dim3(p->I / 64, P), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k);
+  const SortedChunk sc = sorted_chunks(ws, wsb);
+  if (mode == kDecodeDirect) {
+    hipLaunchKernelGGL((decode_gate_up_kernel<1, kDecodeDirect, FMT>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc);
+  } else if (mode == kDecodeSorted) {
+    // one workgroup row per chunk of the routing pass (at most max_chunks; rows past meta[1] exit);
+    // the same split of the reduction over waves as the routed organisation, so that both give
+    // bit-identical results
+    if (pick_np(min(p->E, P)) == 4)
+      hipLaunchKernelGGL((decode_gate_up_kernel<4, kDecodeSorted, FMT>), dim3(p->I / 64, ws.max_chunks),
+                         dim3(kThreads), lds, s, p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I,
+                         top_k, sc);
+    else
+      hipLaunchKernelGGL((decode_gate_up_kernel<1, kDecodeSorted, FMT>), dim3(p->I / 16, ws.max_chunks),
+                         dim3(kThreads), lds, s, p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I,
+                         top_k, sc);
+  } else if (pick_np(min(p->E, P)) == 4) {   // at most this many workgroup rows do work
+    hipLaunchKernelGGL((decode_gate_up_kernel<4, kDecodeRouted, FMT>), dim3(p->I / 64, P), dim3(kThreads), lds, s,
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc);
   } else {
-    hipLaunchKernelGGL((decode_gate_up_kernel<1, false, FMT>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k);
+    hipLaunchKernelGGL((decode_gate_up_kernel<1, kDecodeRouted, FMT>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_gate_up(const moe_w2_planes* p, int T, int top_k, const void* x,
-                                 const int32_t* ids, const Workspace& ws, uint8_t* wsb, bool direct,
+                                 const int32_t* ids, const Workspace& ws, uint8_t* wsb, int mode,
                                  hipStream_t s) {
   if (T * top_k == 0) return hipSuccess;
-  return p->fmt == kFmtW4 ? decode_gate_up_fmt<kFmtW4>(p, T, top_k, x, ids, ws, wsb, direct, s)
-                          : decode_gate_up_fmt<kFmtW2>(p, T, top_k, x, ids, ws, wsb, direct, s);
+  return p->fmt == kFmtW4 ? decode_gate_up_fmt<kFmtW4>(p, T, top_k, x, ids, ws, wsb, mode, s)
+                          : decode_gate_up_fmt<kFmtW2>(p, T, top_k, x, ids, ws, wsb, mode, s);
+}
+
+template <int FMT, int MODE>
+static hipError_t decode_down_routed(const moe_w2_planes* p, int rows, int P, const int32_t* ids, const Workspace& ws,
+                                     uint8_t* wsb, hipStream_t s) {
+  const int groups = min(p->E, P);   // both organisations split the reduction alike (bit-identical results)
+  const size_t lds = (size_t)kChunk * MxRow<3>::stride(p->I) + (size_t)kWaves * 2 * 4 * 16 * 4;
+  const _Float16* act = (const _Float16*)(wsb + ws.act);
+  long long* cnt = (long long*)(wsb + ws.counters);
+  float* po = (float*)(wsb + ws.pair_out);
+  const SortedChunk sc = sorted_chunks(ws, wsb);
+  const bool two_pairs = FMT == kFmtW2 && (p->I / kTileK) % kRing == 0 && p->K % 256 == 0;
+  if (pick_np(groups) == 4 && two_pairs)
+    hipLaunchKernelGGL((decode_down_kernel<4, FMT, 2, MODE>), dim3(p->K / 256, rows), dim3(kThreads), lds, s,
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc);
+  else if (pick_np(groups) == 4)
+    hipLaunchKernelGGL((decode_down_kernel<4, FMT, 1, MODE>), dim3(p->K / 128, rows), dim3(kThreads), lds, s,
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc);
+  else
+    hipLaunchKernelGGL((decode_down_kernel<1, FMT, 1, MODE>), dim3(p->K / 32, rows), dim3(kThreads), lds, s,
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc);
+  return hipGetLastError();
 }
 
 template <int FMT>
 static hipError_t decode_down_fmt(const moe_w2_planes* p, int T, int top_k, const int32_t* ids, const float* w,
-                                  void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, bool direct,
+                                  void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, int mode,
                                   hipStream_t s) {
   const int P = T * top_k;
-  const _Float16* act = (const _Float16*)(wsb + ws.act);
-  long long* cnt = (long long*)(wsb + ws.counters);
-  if (direct) {
+  if (mode == kDecodeDirect) {
+    const _Float16* act = (const _Float16*)(wsb + ws.act);
+    long long* cnt = (long long*)(wsb + ws.counters);
     hipLaunchKernelGGL(decode_down_direct_kernel<FMT>, dim3(p->K / 16), dim3(kDirectThreads), decode_direct_lds(p->I),
                        s, p->dn_codes, p->dn_scales, act, ids, w, y, cnt, out_dtype, T, p->E, p->K, p->I, top_k);
     return hipGetLastError();
   }
-  const int groups = min(p->E, P);
-  const size_t lds = (size_t)kChunk * MxRow<3>::stride(p->I) + (size_t)kWaves * 2 * 4 * 16 * 4;
-  float* po = (float*)(wsb + ws.pair_out);
-  const bool two_pairs = FMT == kFmtW2 && (p->I / kTileK) % kRing == 0 && p->K % 256 == 0;
-  if (pick_np(groups) == 4 && two_pairs)
-    hipLaunchKernelGGL((decode_down_kernel<4, FMT, 2>), dim3(p->K / 256, P), dim3(kThreads), lds, s,
-                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I);
-  else if (pick_np(groups) == 4)
-    hipLaunchKernelGGL((decode_down_kernel<4, FMT, 1>), dim3(p->K / 128, P), dim3(kThreads), lds, s,
-                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I);
-  else
-    hipLaunchKernelGGL((decode_down_kernel<1, FMT, 1>), dim3(p->K / 32, P), dim3(kThreads), lds, s,
-                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I);
-  return hipGetLastError();
+  return mode == kDecodeSorted ? decode_down_routed<FMT, kDecodeSorted>(p, ws.max_chunks, P, ids, ws, wsb, s)
+                               : decode_down_routed<FMT, kDecodeRouted>(p, P, P, ids, ws, wsb, s);
 }
 
 hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const int32_t* ids, const float* w,
-                              void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, bool direct,
+                              void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, int mode,
                               hipStream_t s) {
   if (T * top_k == 0) return hipSuccess;
-  return p->fmt == kFmtW4 ? decode_down_fmt<kFmtW4>(p, T, top_k, ids, w, y, out_dtype, ws, wsb, direct, s)
-                          : decode_down_fmt<kFmtW2>(p, T, top_k, ids, w, y, out_dtype, ws, wsb, direct, s);
+  return p->fmt == kFmtW4 ? decode_down_fmt<kFmtW4>(p, T, top_k, ids, w, y, out_dtype, ws, wsb, mode, s)
+                          : decode_down_fmt<kFmtW2>(p, T, top_k, ids, w, y, out_dtype, ws, wsb, mode, s);
 }
 
 hipError_t launch_combine(int T, int top_k, int E, int K, const int32_t* ids, const float* w,

@@ -40,7 +40,8 @@ struct Workspace {
   size_t perm;        // int32 [P]
   size_t active;      // int32 [E]   expert of each active slot
   size_t meta;        // int32 [8]   [0] = number of active experts, [1] = number of GEMM M-tiles
-  size_t tiles;       // int32 [max_tiles][2] (expert, first sorted row) GEMM M-tiles
+  size_t tiles;       // int32 [max(max_tiles, max_chunks)][2] (expert, first sorted row): the GEMM
+                      // M-tiles, or the sorted decode organisation's chunks
   size_t chunk_cnt;   // int32 [nchunks][E+1] per-chunk counts (large routing)
   size_t rank;        // int32 [P] rank of a pair within its chunk and expert
   size_t xq;          // x split for the block-scaled instruction (GEMM path): one 608-byte
@@ -51,12 +52,14 @@ struct Workspace {
   size_t pair_out;    // fp32 [P][K] per-pair down outputs, indexed by pair id
   size_t slot_ids;    // int32 [P] the ids mapped to slots (slot forward)
   size_t total;
-  int P, nchunks, max_tiles;
+  int P, nchunks, max_tiles, max_chunks;
 };
 
 constexpr int kRouteChunk = 256;       // pairs per routing chunk
 constexpr int kRouteSmallMax = 1024;   // single-workgroup routing up to this many pairs
 constexpr int kGemmBM = 64;            // GEMM M-tile (sorted pair rows)
+constexpr int kDecodeChunk = 4;        // decode kernels: token rows per weight pass
+constexpr int kSortedMinPairs = 384;   // AUTO path: the sorted decode organisation from this many pairs
 constexpr int kDecodeMaxPairs = 512;   // AUTO path: decode kernels up to this many pairs
 constexpr int kDirectMaxPairs = 8;     // decode without a routing pass up to this many pairs
 
@@ -87,16 +90,21 @@ struct RouteOut {
   int32_t* chunk_cnt; // scratch for P > kRouteSmallMax
   int32_t* rank;      // scratch for P > kRouteSmallMax
   int max_tiles;
+  int tile_rows;      // rows per tile of the tile list (kGemmBM or kDecodeChunk)
 };
 hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const RouteOut& o, hipStream_t s);
 
-// Decode path (small groups): gate_up + SiLU, down, combine.
-// direct = no routing pass (P <= kDirectMaxPairs); the direct down launch also writes y.
+// Decode path (small groups): gate_up + SiLU, down, combine. Organisations:
+//  kDecodeRouted - each workgroup row finds its expert's pairs from the ids (no routing pass);
+//  kDecodeDirect - P <= kDirectMaxPairs, one group per pair; the down launch also writes y;
+//  kDecodeSorted - workgroup rows walk the chunk list of a routing pass (kDecodeChunk rows per
+//                  chunk, in expert order), so one expert's chunks run together.
+enum { kDecodeRouted = 0, kDecodeDirect = 1, kDecodeSorted = 2 };
 hipError_t launch_decode_gate_up(const moe_w2_planes* p, int T, int top_k, const void* x,
-                                 const int32_t* ids, const Workspace& ws, uint8_t* wsb, bool direct,
+                                 const int32_t* ids, const Workspace& ws, uint8_t* wsb, int mode,
                                  hipStream_t s);
 hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const int32_t* ids, const float* w,
-                              void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, bool direct,
+                              void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, int mode,
                               hipStream_t s);
 size_t decode_direct_lds(int I);
 // GEMM path (large groups)

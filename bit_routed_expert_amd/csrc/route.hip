@@ -48,7 +48,7 @@ __device__ int block_exclusive_scan(int* data, int n, int* scratch /* blockDim i
 // (`cnt` has E+1 entries and is overwritten by its exclusive scan). Shared by both paths.
 __device__ void finish_routing(int* cnt, int E, int P, int* scratch, int* tmp,
                                int32_t* offsets, int32_t* active, int32_t* meta, int32_t* tiles,
-                               long long* counters, int max_tiles) {
+                               long long* counters, int max_tiles, int bm) {
   const int tid = threadIdx.x, nt = blockDim.x;
   // per-expert activity and tile counts
   for (int b = tid; b < E; b += nt) tmp[b] = cnt[b] > 0 ? 1 : 0;
@@ -59,7 +59,7 @@ __device__ void finish_routing(int* cnt, int E, int P, int* scratch, int* tmp,
     if (n > 0) active[tmp[b]] = b;  // tmp[b] = slot
   }
   __syncthreads();
-  for (int b = tid; b < E; b += nt) tmp[b] = (cnt[b] + kGemmBM - 1) / kGemmBM;
+  for (int b = tid; b < E; b += nt) tmp[b] = (cnt[b] + bm - 1) / bm;
   __syncthreads();
   int n_tiles = block_exclusive_scan(tmp, E, scratch);
   // offsets: exclusive scan of the E+1 bins (the last bin holds the invalid pairs)
@@ -70,8 +70,8 @@ __device__ void finish_routing(int* cnt, int E, int P, int* scratch, int* tmp,
   for (int b = tid; b < E; b += nt) {
     int n = cnt[b + 1] - cnt[b];
     int t0 = tmp[b];
-    for (int m = 0; m * kGemmBM < n; ++m) {
-      if (t0 + m < max_tiles) { tiles[2 * (t0 + m)] = b; tiles[2 * (t0 + m) + 1] = cnt[b] + m * kGemmBM; }
+    for (int m = 0; m * bm < n; ++m) {
+      if (t0 + m < max_tiles) { tiles[2 * (t0 + m)] = b; tiles[2 * (t0 + m) + 1] = cnt[b] + m * bm; }
     }
   }
   if (tid == 0) {
@@ -88,7 +88,7 @@ __device__ void finish_routing(int* cnt, int E, int P, int* scratch, int* tmp,
 __global__ void __launch_bounds__(kRoundThreads)
 route_small_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __restrict__ offsets,
                    int32_t* __restrict__ perm, int32_t* active, int32_t* meta, int32_t* tiles,
-                   long long* counters, int max_tiles) {
+                   long long* counters, int max_tiles, int bm) {
   extern __shared__ int lds[];
   const int nb = E + 1;
   uint32_t* masks = reinterpret_cast<uint32_t*>(lds);
@@ -127,7 +127,7 @@ route_small_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __res
   }
   for (int b = tid; b < nb; b += kRoundThreads) cnt[b] = running[b];
   __syncthreads();
-  finish_routing(cnt, E, P, scratch, tmp, offsets, active, meta, tiles, counters, max_tiles);
+  finish_routing(cnt, E, P, scratch, tmp, offsets, active, meta, tiles, counters, max_tiles, bm);
   __syncthreads();
   // cnt now holds the exclusive scan over bins (bin start positions)
   for (int p = tid; p < P; p += kRoundThreads) {
@@ -147,7 +147,7 @@ constexpr int kFastWords = kFastThreads / 32;
 __global__ void __launch_bounds__(kFastThreads)
 route_fast_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __restrict__ offsets,
                   int32_t* __restrict__ perm, int32_t* active, int32_t* meta, int32_t* tiles,
-                  long long* counters, int max_tiles) {
+                  long long* counters, int max_tiles, int bm) {
   extern __shared__ int lds[];
   const int nb = E + 1;
   uint32_t* masks = reinterpret_cast<uint32_t*>(lds);     // [nb][32]
@@ -170,7 +170,7 @@ route_fast_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __rest
   if (tid < nb) {
     for (int w = 0; w < kFastWords; ++w) c += __popc(masks[tid * kFastWords + w]);
     v = (uint32_t)c << 20;
-    if (tid < E && c > 0) v |= ((uint32_t)((c + kGemmBM - 1) / kGemmBM) << 10) | 1u;
+    if (tid < E && c > 0) v |= ((uint32_t)((c + bm - 1) / bm) << 10) | 1u;
   }
   // block exclusive scan of the packed values (fields never carry into each other)
   uint32_t incl = v;
@@ -192,8 +192,8 @@ route_fast_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __rest
     offsets[tid] = s0;
     if (tid < E && c > 0) {
       active[a0] = tid;
-      for (int m = 0; m * kGemmBM < c; ++m)
-        if (t0 + m < max_tiles) { tiles[2 * (t0 + m)] = tid; tiles[2 * (t0 + m) + 1] = s0 + m * kGemmBM; }
+      for (int m = 0; m * bm < c; ++m)
+        if (t0 + m < max_tiles) { tiles[2 * (t0 + m)] = tid; tiles[2 * (t0 + m) + 1] = s0 + m * bm; }
     }
     if (tid == E) {
       meta[0] = a0;
@@ -249,7 +249,7 @@ route_chunk_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __res
 __global__ void __launch_bounds__(1024)
 route_scan_kernel(int E, int P, int nchunks, int32_t* __restrict__ chunk_cnt,
                   int32_t* __restrict__ offsets, int32_t* active, int32_t* meta, int32_t* tiles,
-                  long long* counters, int max_tiles) {
+                  long long* counters, int max_tiles, int bm) {
   extern __shared__ int lds[];
   const int nb = E + 1;
   int* cnt = lds;
@@ -274,7 +274,7 @@ route_scan_kernel(int E, int P, int nchunks, int32_t* __restrict__ chunk_cnt,
     cnt[b] = run;
   }
   __syncthreads();
-  finish_routing(cnt, E, P, scratch, tmp, offsets, active, meta, tiles, counters, max_tiles);
+  finish_routing(cnt, E, P, scratch, tmp, offsets, active, meta, tiles, counters, max_tiles, bm);
   __syncthreads();
   // keep the bin start positions for the scatter in offsets' spare copy: chunk_cnt row nchunks
   for (int b = tid; b < nb; b += blockDim.x) chunk_cnt[(long long)nchunks * nb + b] = cnt[b];
@@ -309,14 +309,14 @@ hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const Route
   if (P <= kFastThreads && E <= 256) {
     size_t lds = (size_t)nb * kFastWords * 4 + (size_t)nb * 4 + 16 * 4;
     hipLaunchKernelGGL(route_fast_kernel, dim3(1), dim3(kFastThreads), lds, s, ids, E, P, o.offsets, o.perm,
-                       o.active, o.meta, o.tiles, o.counters, o.max_tiles);
+                       o.active, o.meta, o.tiles, o.counters, o.max_tiles, o.tile_rows);
     return hipGetLastError();
   }
   if (P <= kSmallMaxPairs) {
     size_t lds = (size_t)nb * kMaskWords * 4 + (size_t)3 * nb * 4 + (size_t)kSmallMaxPairs * 4 +
                  kRoundThreads * 4;
     hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kRoundThreads), lds, s, ids, E, P,
-                       o.offsets, o.perm, o.active, o.meta, o.tiles, o.counters, o.max_tiles);
+                       o.offsets, o.perm, o.active, o.meta, o.tiles, o.counters, o.max_tiles, o.tile_rows);
     return hipGetLastError();
   }
   const int nchunks = (P + kChunkPairs - 1) / kChunkPairs;
@@ -325,7 +325,7 @@ hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const Route
                      o.chunk_cnt, o.rank);
   size_t lds2 = (size_t)2 * nb * 4 + 1024 * 4;
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), lds2, s, E, P, nchunks, o.chunk_cnt,
-                     o.offsets, o.active, o.meta, o.tiles, o.counters, o.max_tiles);
+                     o.offsets, o.active, o.meta, o.tiles, o.counters, o.max_tiles, o.tile_rows);
   hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(kRoundThreads), 0, s, ids, E, P,
                      nchunks, o.chunk_cnt, o.rank, o.perm);
   return hipGetLastError();

@@ -63,11 +63,20 @@ enum moe_w2_status {
 
 enum moe_w2_out_dtype { MOE_W2_OUT_BF16 = 0, MOE_W2_OUT_F32 = 1 };
 
-/* Which kernels moe_w2_forward uses. AUTO picks DECODE for T*top_k <= 512, else GEMM. DECODE
- * supports T*top_k <= 512 only (MOE_W2_EUNSUPPORTED above). DECODE streams an expert's weights
- * once per 4 of its pairs, so for batches whose routing concentrates dozens of pairs on a few
- * experts GEMM can be the faster choice; both give results within the same tolerance. */
-enum moe_w2_path { MOE_W2_PATH_AUTO = 0, MOE_W2_PATH_DECODE = 1, MOE_W2_PATH_GEMM = 2 };
+/* Which kernels moe_w2_forward uses. AUTO picks the decode kernels for T*top_k <= 512, else
+ * GEMM; among the decode organisations, DECODE_SORTED from 384 pairs up, DECODE below. The decode
+ * kernels (both organisations) support T*top_k <= 512 only (MOE_W2_EUNSUPPORTED above); they
+ * stream an expert's weights once per 4 of its pairs. DECODE finds each expert's pairs from the
+ * ids inside the kernels (no routing pass); DECODE_SORTED runs a routing pass first and walks its
+ * chunks in expert order, so the chunks of a popular expert run together and re-read its weights
+ * from L2 rather than HBM. All paths give results within the same tolerance, and the two decode
+ * organisations give bit-identical results (same per-pair arithmetic). */
+enum moe_w2_path {
+  MOE_W2_PATH_AUTO = 0,
+  MOE_W2_PATH_DECODE = 1,
+  MOE_W2_PATH_GEMM = 2,
+  MOE_W2_PATH_DECODE_SORTED = 3
+};
 
 /* The four stages of moe_w2_forward, in order (see moe_w2_forward_stage). */
 enum moe_w2_stage {

@@ -13,7 +13,8 @@ from gpu_helpers import bf16_rne_bits, dev, dev_bf16, forward, pack, rel_max_err
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
-PATHS = [moe.PATH_DECODE, moe.PATH_GEMM]
+PATHS = [moe.PATH_DECODE, moe.PATH_GEMM, moe.PATH_DECODE_SORTED]
+DECODE_PATHS = (moe.PATH_DECODE, moe.PATH_DECODE_SORTED)
 
 
 def _oracle(case, tokens=None):
@@ -77,8 +78,8 @@ def test_mid_size_parity(gpu, case, path):
     T, K, I, E, top_k, seed, zipf = case
     c = _case(T, K, I, E, top_k, seed, zipf)
     h = pack(c)
-    if path == moe.PATH_DECODE and T * top_k > 512:
-        # the decode kernels scan all ids in every workgroup and stop at 512 pairs
+    if path in DECODE_PATHS and T * top_k > 512:
+        # the decode kernels stop at 512 pairs
         with pytest.raises(moe.MoeW2Error) as exc:
             forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path)
         assert exc.value.status == -2
@@ -282,7 +283,7 @@ def test_random_shapes_parity(gpu, case):
     h = pack(c)
     y_ref = _oracle(c)
     for path in PATHS:
-        if path == moe.PATH_DECODE and T * top_k > 512:
+        if path in DECODE_PATHS and T * top_k > 512:
             continue
         y = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, path).cpu().numpy()
         err = rel_max_err(y, y_ref)
@@ -290,13 +291,14 @@ def test_random_shapes_parity(gpu, case):
         assert err <= TOL, (case, path, err)
 
 
+@pytest.mark.parametrize("path", DECODE_PATHS, ids=["routed", "sorted"])
 @pytest.mark.parametrize("out_dtype", [moe.OUT_F32, moe.OUT_BF16], ids=["f32", "bf16"])
-def test_decode_routed_edge_tokens(gpu, out_dtype):
-    """The routed decode organisation with two row pairs per wave in down (2-bit planes, >= 32
-    active groups, I/256 a multiple of 4): tokens with invalid ids, one with a duplicate id and one
-    with no valid id (a zero row). Three forwards on one workspace are bit-identical, fp32 matches
-    the oracle and bf16 is its round-to-nearest-even, and a stage sequence that runs the down stage
-    twice gives the same y."""
+def test_decode_routed_edge_tokens(gpu, out_dtype, path):
+    """The routed and sorted decode organisations with two row pairs per wave in down (2-bit
+    planes, >= 32 active groups, I/256 a multiple of 4): tokens with invalid ids, one with a
+    duplicate id and one with no valid id (a zero row). Three forwards on one workspace are
+    bit-identical, fp32 matches the oracle and bf16 is its round-to-nearest-even, and a stage
+    sequence that runs the down stage twice gives the same y."""
     T, K, I, E, top_k = 24, 512, 1024, 64, 8
     c = _case(T, K, I, E, top_k, 71)
     ids = c["topk_ids"].copy()
@@ -306,10 +308,10 @@ def test_decode_routed_edge_tokens(gpu, out_dtype):
     ids[7, :] = -1
     h = pack(c)
     ws = moe.alloc_workspace(h, T, top_k)
-    ys = [forward(h, c["x"], ids, c["topk_w"], out_dtype, moe.PATH_DECODE, ws) for _ in range(3)]
+    ys = [forward(h, c["x"], ids, c["topk_w"], out_dtype, path, ws) for _ in range(3)]
     for y in ys[1:]:
         assert torch.equal(y, ys[0])
-    y32 = forward(h, c["x"], ids, c["topk_w"], moe.OUT_F32, moe.PATH_DECODE, ws).cpu().numpy()
+    y32 = forward(h, c["x"], ids, c["topk_w"], moe.OUT_F32, path, ws).cpu().numpy()
     assert np.all(y32[7] == 0)
     y_ref = oracle_fwd.moe_forward(formats.bf16_bits_to_f64(c["x"]), ids, c["topk_w"], c["gu_codes"], c["gu_scales"],
                                    c["dn_codes"], c["dn_scales"])
@@ -323,14 +325,15 @@ def test_decode_routed_edge_tokens(gpu, out_dtype):
     x_d, ids_d, w_d = dev_bf16(c["x"]), dev(ids), dev(np.asarray(c["topk_w"], np.float32))
     y2 = torch.full_like(ys[0], 7.0)
     for st in (moe.STAGE_ROUTE, moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_DOWN, moe.STAGE_COMBINE):
-        moe.moe_w2_forward_stage(st, h, x_d, ids_d, w_d, y2, ws, out_dtype, moe.PATH_DECODE)
+        moe.moe_w2_forward_stage(st, h, x_d, ids_d, w_d, y2, ws, out_dtype, path)
     torch.cuda.synchronize()
     assert torch.equal(y2, ys[0])
 
 
 @pytest.mark.parametrize("T,path,zipf", [(1, moe.PATH_DECODE, False), (40, moe.PATH_DECODE, False),
+                                         (40, moe.PATH_DECODE_SORTED, True),
                                          (12, moe.PATH_GEMM, False), (300, moe.PATH_GEMM, True)],
-                         ids=["direct", "routed-decode", "gemm-single-row-tiles", "gemm-zipf"])
+                         ids=["direct", "routed-decode", "sorted-decode-zipf", "gemm-single-row-tiles", "gemm-zipf"])
 def test_stages_in_order_equal_forward(gpu, T, path, zipf):
     """ROUTE, GATE_UP, DOWN, COMBINE called one at a time on one workspace give moe_w2_forward's y
     bit for bit, for each organisation; at T=12 on the GEMM kernels nearly every M-tile holds a
@@ -350,3 +353,16 @@ def test_stages_in_order_equal_forward(gpu, T, path, zipf):
     y_ref = oracle_fwd.moe_forward(formats.bf16_bits_to_f64(c["x"]), c["topk_ids"], c["topk_w"], c["gu_codes"],
                                    c["gu_scales"], c["dn_codes"], c["dn_scales"])
     assert rel_max_err(y.cpu().numpy(), y_ref) <= TOL
+
+
+@pytest.mark.parametrize("T,zipf", [(2, False), (5, True), (24, False), (48, True), (64, True), (64, False)])
+def test_sorted_and_routed_decode_are_bit_identical(gpu, T, zipf):
+    """The two decode organisations process the same chunks of each expert's pairs with the same
+    per-row arithmetic (only the workgroup order differs), so their outputs agree bit for bit, on
+    uniform and skewed routing up to the 512-pair limit (K=1024, I=512, E=64, top-8)."""
+    K, I, E, top_k = 1024, 512, 64, 8
+    c = _case(T, K, I, E, top_k, 300 + T, zipf=zipf)
+    h = pack(c)
+    a = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, moe.PATH_DECODE)
+    b = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, moe.PATH_DECODE_SORTED)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))

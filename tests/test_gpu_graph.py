@@ -12,7 +12,7 @@ from gpu_helpers import dev, dev_bf16, pack
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T,path", [(8, moe.PATH_DECODE), (200, moe.PATH_GEMM)])
+@pytest.mark.parametrize("T,path", [(8, moe.PATH_DECODE), (100, moe.PATH_DECODE_SORTED), (200, moe.PATH_GEMM)])
 def test_graph_replays_match_eager(gpu, T, path):
     rng = np.random.default_rng(5 + T)
     K, I, E, top_k = 512, 512, 16, 4

@@ -59,6 +59,7 @@ CASES = [
     (3, 512, 512, 8, 2, 41, False, moe.PATH_DECODE),        # direct tiny-batch kernels
     (37, 512, 768, 16, 4, 42, False, moe.PATH_DECODE),
     (128, 512, 256, 4, 4, 43, True, moe.PATH_DECODE),
+    (60, 512, 512, 32, 8, 46, True, moe.PATH_DECODE_SORTED),
     (4, 256, 512, 8, 2, 40, False, moe.PATH_GEMM),
     (300, 768, 512, 8, 2, 44, False, moe.PATH_GEMM),
     (200, 1024, 256, 32, 8, 45, True, moe.PATH_GEMM),
