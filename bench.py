@@ -76,6 +76,7 @@ def parse():
     ap.add_argument("--no-w4", action="store_true")
     ap.add_argument("--requant-iters", type=int, default=5)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-shards", action="store_true")
     ap.add_argument("--sweep-tensors", type=int, default=8)
     ap.add_argument("--sweep-iters", type=int, default=2)
     ap.add_argument("--eager", action="store_true",
@@ -293,7 +294,7 @@ def main():
     achieved = gu_bytes_all / (gu_ms_all * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     traffic = traffic_from_profiles("decode_gate_up", src_hash)
-    roofline = dict(bound="hbm", kernel="decode_gate_up_kernel<4,false,0> (2-bit planes; T=8 and T=32 calls)",
+    roofline = dict(bound="hbm", kernel="decode_gate_up_kernel<4,0,0> (routed decode, 2-bit planes; T=8 and T=32 calls)",
                     scope="the dominant kernel alone; whole_forward_frac has each decode shape's whole forward",
                     achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
@@ -332,6 +333,8 @@ def main():
     }
 
     out["cold_calls"] = bench_cold_calls(torch, moe, layers, inst, ws, ys, per_batch)
+    if not args.no_shards:
+        out["tp_shards"] = bench_shards(args, moe, workloads, torch, dev, inst)
     if not args.no_slots:
         out["slots"] = bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K)
     if not args.no_w4:
@@ -408,6 +411,75 @@ def bench_cold_calls(torch, moe, layers, inst, ws, ys, per_batch):
                             graph_vs_cold=round(per_batch[f"T{T}"]["fwd_us"] / (float(np.median(t)) - pe), 4))
     out["note"] = ("each call between its own event pair after a 1 GiB device copy; the pair alone (event_pair_us, "
                    "after the same copy) costs a few us, so medians minus event_pair_us compare with per_batch")
+    return out
+
+
+def bench_shards(args, moe, workloads, torch, dev, inst):
+    """One GPU's share of the layer under tensor parallelism over the expert intermediate size
+    (G = 2, 4 ranks: I = 1024, 512; the pages ship kernels for these shard widths): each rank holds
+    gate_up rows I/G and the down reduction I/G of every expert, sees every token and produces a
+    partial y (the cross-rank sum is out of scope). Decode at K=4096 T = 1, 8, 32 with the decode
+    workload's routing instances and x, and the Zipf T=64 batch at K=6144; each shape timed as a
+    graph of back-to-back forwards over two plane copies; algorithmic bytes per call = the
+    instance's active experts' shard planes + x + y + ids + w."""
+    E, top_k = 256, 8
+    stream = torch.cuda.current_stream()
+    n_rep = max(2, args.steps)
+
+    def timed(layers, insts, K, I):
+        R = len(insts)
+        T = insts[0]["x"].shape[0]
+        ws = [moe.alloc_workspace(layers[0], T, top_k) for _ in range(R)]
+        y = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+        gu_b, dn_b = expert_bytes(K, I)
+        nb = 0
+        def loop():
+            nb = 0
+            for k in range(n_rep):
+                d = insts[k % R]
+                moe.moe_w2_forward(layers[k % 2], d["x"], d["ids"], d["w"], workspace=ws[k % R], y=y)
+                ids = d["ids_np"]
+                nb += len(np.unique(ids[(ids >= 0) & (ids < E)])) * (gu_b + dn_b) + 2 * T * K * 2 + T * top_k * 8
+            return nb
+        loop()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            nb = loop()
+        g.replay()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        g.replay()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        us = a0.elapsed_time(a1) / n_rep * 1e3
+        gbps = nb / n_rep / (us * 1e-6) / 1e9
+        return dict(fwd_us=round(us, 2), hbm_GBps=round(gbps, 1), hbm_frac=round(gbps / HBM_PEAK_GBPS, 4),
+                    tokens_per_s=round(T / (us * 1e-6), 1))
+
+    out = {}
+    cz = workloads.DECODE_ZIPF
+    zi = workloads.zipf_instances(cz["T"], 16, cz["seed"], cz["K"], E, top_k)
+    zinst = [dict(x=torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).cuda(), ids=dev(d["topk_ids"]),
+                  w=dev(d["topk_w"]), ids_np=d["topk_ids"]) for d in zi]
+    for G in (2, 4):
+        res = {}
+        for K, insts_by_T in ((4096, {T: inst[T] for T in DECODE_TS}), (cz["K"], {cz["T"]: zinst})):
+            I = 2048 // G
+            canon = workloads.draw_planes(np.random.default_rng([20, G, K]), E, K, I)
+            d_canon = [dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")]
+            layers = [moe.moe_w2_pack(*d_canon), moe.moe_w2_pack(*d_canon)]
+            del canon, d_canon
+            for T, insts in insts_by_T.items():
+                key = f"T{T}" if K == 4096 else f"zipf_T{T}_K{K}"
+                res[key] = timed(layers, insts, K, I)
+            for h in layers:
+                h.free()
+            torch.cuda.empty_cache()
+        out[f"tp{G}_I{2048 // G}"] = res
+    out["workload"] = ("one rank's share under tensor parallelism over I: moe_w2 decode K=4096 E=256 top-8 uniform "
+                       "routing at T=1,8,32 and the Zipf(1.1) T=64 batch at K=6144, I = 2048/G")
     return out
 
 
