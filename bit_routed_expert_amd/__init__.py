@@ -62,6 +62,8 @@ def _lib():
             "fp8_block128_to_w2": ([I32, I32, I32, P, P, P, P, P], I32),
             "mxfp4_to_w2": ([I32, I32, I32, P, P, P, P, P], I32),
             "moe_w4_unpack": ([P, P, P, P, P, P], I32),
+            "moe_w4_pack_nvfp4": ([I32, I32, I32, P, P, P, P, P, P, P, ctypes.POINTER(P)], I32),
+            "moe_w4_unpack_nvfp4": ([P, P, P, P, P, P, P, P], I32),
             "moe_w4_forward": ([P, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
             "moe_w2_pack_slot": ([P, I32, P, P, P, P, P], I32),
             "moe_w2_forward_slots": ([P, I32, P, I32, I32, P, P, P, P, I32, P, SZ, I32, P], I32),
@@ -167,8 +169,42 @@ def moe_w4_unpack(planes):
     return out
 
 
+def moe_w4_pack_nvfp4(gu_codes, gu_scales, gu_scale2, dn_codes, dn_scales, dn_scale2):
+    """Canonical NVFP4 device planes -> Planes. Shapes: gu_codes [E, 2I, K/2] uint8 (two e2m1
+    codes per byte, low nibble = even element), gu_scales [E, 2I, K/16] uint8 (E4M3FN),
+    gu_scale2 [E, 2] float32 (gate, up), dn_codes [E, K, I/2], dn_scales [E, K, I/16],
+    dn_scale2 [E] float32."""
+    E, two_i, k2 = gu_codes.shape
+    K, I = k2 * 2, two_i // 2
+    if tuple(gu_scales.shape) != (E, 2 * I, K // 16) or tuple(dn_codes.shape) != (E, K, I // 2) \
+            or tuple(dn_scales.shape) != (E, K, I // 16) or tuple(gu_scale2.shape) != (E, 2) \
+            or tuple(dn_scale2.shape) != (E,):
+        raise ValueError("inconsistent plane shapes")
+    h = ctypes.c_void_p()
+    _check(_lib().moe_w4_pack_nvfp4(
+        E, K, I, _dev(gu_codes, torch.uint8, "gu_codes"), _dev(gu_scales, torch.uint8, "gu_scales"),
+        _dev(gu_scale2, torch.float32, "gu_scale2"), _dev(dn_codes, torch.uint8, "dn_codes"),
+        _dev(dn_scales, torch.uint8, "dn_scales"), _dev(dn_scale2, torch.float32, "dn_scale2"),
+        _stream(), ctypes.byref(h)), "moe_w4_pack_nvfp4")
+    return Planes(h, E, K, I)
+
+
+def moe_w4_unpack_nvfp4(planes):
+    E, K, I = planes.E, planes.K, planes.I
+    d = torch.device("cuda")
+    out = (torch.empty((E, 2 * I, K // 2), dtype=torch.uint8, device=d),
+           torch.empty((E, 2 * I, K // 16), dtype=torch.uint8, device=d),
+           torch.empty((E, 2), dtype=torch.float32, device=d),
+           torch.empty((E, K, I // 2), dtype=torch.uint8, device=d),
+           torch.empty((E, K, I // 16), dtype=torch.uint8, device=d),
+           torch.empty((E,), dtype=torch.float32, device=d))
+    _check(_lib().moe_w4_unpack_nvfp4(planes.handle, *[ctypes.c_void_p(t.data_ptr()) for t in out], _stream()),
+           "moe_w4_unpack_nvfp4")
+    return out
+
+
 def moe_w4_forward(planes, x, topk_ids, topk_w, out_dtype=OUT_BF16, workspace=None, path=PATH_AUTO, y=None):
-    """moe_w2_forward on FP4 planes (moe_w4_pack)."""
+    """moe_w2_forward on FP4 planes (moe_w4_pack or moe_w4_pack_nvfp4)."""
     T, K = x.shape
     top_k = topk_ids.shape[1]
     if workspace is None:

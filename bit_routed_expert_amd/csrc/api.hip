@@ -52,12 +52,13 @@ static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_W2_OK : MOE_W
 static int planes_alloc(int E, int K, int I, int fmt, moe_w2_planes** out) {
   const size_t n_gu = (size_t)E * 2 * I * K;
   const size_t n_dn = (size_t)E * K * I;
-  const int cb = code_bits(fmt);
+  const int cb = code_bits(fmt), sg = scale_group(fmt);
   size_t o = 0;
   const size_t o_guc = o; o += align_up(n_gu * cb / 8);
-  const size_t o_gus = o; o += align_up(n_gu / 32);
+  const size_t o_gus = o; o += align_up(n_gu / sg);
   const size_t o_dnc = o; o += align_up(n_dn * cb / 8);
-  const size_t o_dns = o; o += align_up(n_dn / 32);
+  const size_t o_dns = o; o += align_up(n_dn / sg);
+  const size_t o_s2 = o;  o += align_up((size_t)E * 3 * sizeof(float));
   const size_t o_flag = o; o += align_up(4);
   moe_w2_planes* p = new (std::nothrow) moe_w2_planes;
   if (!p) return MOE_W2_ENOMEM;
@@ -69,6 +70,7 @@ static int planes_alloc(int E, int K, int I, int fmt, moe_w2_planes** out) {
   uint8_t* b = (uint8_t*)p->base;
   p->gu_codes = b + o_guc; p->gu_scales = b + o_gus;
   p->dn_codes = b + o_dnc; p->dn_scales = b + o_dns;
+  p->scale2 = (float*)(b + o_s2);
   p->flag = (int32_t*)(b + o_flag);
   *out = p;
   return MOE_W2_OK;
@@ -80,6 +82,7 @@ static int pack_status(const moe_w2_planes* p, hipError_t err, hipStream_t s) {
   if (err == hipSuccess) err = hipMemcpyAsync(&flag, p->flag, 4, hipMemcpyDeviceToHost, s);
   if (err == hipSuccess) err = hipStreamSynchronize(s);
   if (err != hipSuccess) return MOE_W2_EHIP;
+  if (flag & kFlagNaN) return MOE_W2_ENVFP4;
   return (flag & kFlagScale) ? MOE_W2_ESCALE : MOE_W2_OK;
 }
 
@@ -93,6 +96,7 @@ static int forward_check(const moe_w2_planes* p, int T, int top_k, const void* x
   if (path != MOE_W2_PATH_AUTO && path != MOE_W2_PATH_DECODE && path != MOE_W2_PATH_GEMM &&
       path != MOE_W2_PATH_DECODE_SORTED)
     return MOE_W2_EINVAL;
+  if (p->fmt == kFmtNV4 && path == MOE_W2_PATH_GEMM) return MOE_W2_EUNSUPPORTED;   // decode kernels only
   if (T > 0 && (!x || !topk_ids || !topk_w || !y)) return MOE_W2_EINVAL;
   if (!pairs_ok(T, top_k)) return MOE_W2_EUNSUPPORTED;
   if ((long long)T * p->K >= (1LL << 31) || (long long)T * top_k * p->I >= (1LL << 31))
@@ -102,17 +106,20 @@ static int forward_check(const moe_w2_planes* p, int T, int top_k, const void* x
     return MOE_W2_EUNSUPPORTED;  // ... and their split copies with 32-bit byte offsets
   const Workspace ws = workspace_layout(p->E, p->K, p->I, T, top_k);
   if (!workspace || workspace_bytes < ws.total) return MOE_W2_EWORKSPACE;
-  const bool decode = path == MOE_W2_PATH_DECODE || path == MOE_W2_PATH_DECODE_SORTED ||
-                      (path == MOE_W2_PATH_AUTO && (long long)T * top_k <= kDecodeMaxPairs);
-  // every decode workgroup of the routed organisation scans all ids itself (two per thread); the
-  // sorted one takes its chunks from a routing pass of at most kDecodeMaxPairs pairs
-  if (decode && (long long)T * top_k > kDecodeMaxPairs) return MOE_W2_EUNSUPPORTED;
+  // every decode workgroup of the routed organisation scans all ids itself (two per thread)
+  if (path == MOE_W2_PATH_DECODE && (long long)T * top_k > kDecodeMaxPairs) return MOE_W2_EUNSUPPORTED;
+  // the sorted organisation launches one workgroup row per chunk (grid rows are 16-bit)
+  if (ws.max_chunks > 65535 &&
+      (path == MOE_W2_PATH_DECODE_SORTED || (p->fmt == kFmtNV4 && (long long)T * top_k > kDecodeMaxPairs)))
+    return MOE_W2_EUNSUPPORTED;
   return MOE_W2_OK;
 }
 
-// Kernel family of a forward: -1 = grouped GEMMs, else the decode organisation.
-static int decode_mode(int path, int P) {
-  if (path == MOE_W2_PATH_GEMM || (path == MOE_W2_PATH_AUTO && P > kDecodeMaxPairs)) return -1;
+// Kernel family of a forward: -1 = grouped GEMMs, else the decode organisation. NVFP4 planes
+// run on the decode kernels at every size (the sorted organisation above kDecodeMaxPairs).
+static int decode_mode(int path, int P, int fmt) {
+  if (path == MOE_W2_PATH_GEMM) return -1;
+  if (path == MOE_W2_PATH_AUTO && P > kDecodeMaxPairs) return fmt == kFmtNV4 ? kDecodeSorted : -1;
   if (path == MOE_W2_PATH_DECODE_SORTED) return kDecodeSorted;
   if (P <= kDirectMaxPairs) return kDecodeDirect;
   if (path == MOE_W2_PATH_AUTO && P >= kSortedMinPairs) return kDecodeSorted;
@@ -170,6 +177,32 @@ int moe_w4_pack(int E, int K, int I, const uint8_t* gu_codes, const uint8_t* gu_
                 const uint8_t* dn_codes, const uint8_t* dn_scales, void* stream,
                 moe_w2_planes** out) {
   return pack_fmt(kFmtW4, E, K, I, gu_codes, gu_scales, dn_codes, dn_scales, stream, out);
+}
+
+int moe_w4_pack_nvfp4(int E, int K, int I, const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_scale2,
+                      const uint8_t* dn_codes, const uint8_t* dn_scales, const float* dn_scale2, void* stream,
+                      moe_w2_planes** out) {
+  if (!out) return MOE_W2_EINVAL;
+  *out = nullptr;
+  if (!gu_codes || !gu_scales || !gu_scale2 || !dn_codes || !dn_scales || !dn_scale2) return MOE_W2_EINVAL;
+  if (E < 0 || K < 0 || I < 0) return MOE_W2_EINVAL;
+  if (!shape_ok(E, K, I) || (long long)I * K >= (1LL << 31)) return MOE_W2_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  moe_w2_planes* p = nullptr;
+  int st = planes_alloc(E, K, I, kFmtNV4, &p);
+  if (st != MOE_W2_OK) return st;
+  st = pack_status(p, launch_pack_nv4(p, gu_codes, gu_scales, gu_scale2, dn_codes, dn_scales, dn_scale2, 0, s), s);
+  if (st != MOE_W2_OK) { (void)hipFree(p->base); delete p; return st; }
+  *out = p;
+  return MOE_W2_OK;
+}
+
+int moe_w4_unpack_nvfp4(const moe_w2_planes* p, uint8_t* gu_codes, uint8_t* gu_scales, float* gu_scale2,
+                        uint8_t* dn_codes, uint8_t* dn_scales, float* dn_scale2, void* stream) {
+  if (!p || !gu_codes || !gu_scales || !gu_scale2 || !dn_codes || !dn_scales || !dn_scale2) return MOE_W2_EINVAL;
+  if (p->fmt != kFmtNV4) return MOE_W2_EINVAL;
+  return hip_status(launch_pack_nv4(p, gu_codes, gu_scales, gu_scale2, dn_codes, dn_scales, dn_scale2, 1,
+                                    (hipStream_t)stream));
 }
 
 int moe_w2_planes_create(int S, int K, int I, void* stream, moe_w2_planes** out) {
@@ -266,7 +299,7 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
   if (T == 0) return MOE_W2_OK;
   hipStream_t s = (hipStream_t)stream;
   uint8_t* wsb = (uint8_t*)workspace;
-  const int mode = decode_mode(path, T * top_k);
+  const int mode = decode_mode(path, T * top_k, p->fmt);
   const bool decode = mode >= 0;
   // the routed and direct decode organisations find their pairs from the ids themselves (no
   // routing pass); the direct organisation also combines inside the down stage
@@ -383,7 +416,7 @@ int moe_w2_forward_slots(const moe_w2_planes* p, int E, const int32_t* slot_of_e
 int moe_w4_forward(const moe_w2_planes* p, int T, int top_k, const void* x, const int32_t* topk_ids,
                    const float* topk_w, void* y, int out_dtype, void* workspace, size_t workspace_bytes,
                    int path, void* stream) {
-  if (!p || p->fmt != kFmtW4) return MOE_W2_EINVAL;
+  if (!p || (p->fmt != kFmtW4 && p->fmt != kFmtNV4)) return MOE_W2_EINVAL;
   return moe_w2_forward(p, T, top_k, x, topk_ids, topk_w, y, out_dtype, workspace, workspace_bytes, path, stream);
 }
 

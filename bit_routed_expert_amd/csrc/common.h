@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
@@ -37,11 +39,34 @@ constexpr int kTileScaleBytes = 128;
 // order (value i in nibble i, low nibble first) - one fully coalesced 1 KiB wave load per
 // instruction. Scale tiles are the 2-bit planes' (byte 2l + c).
 constexpr int kTileCodeBytesW4 = 2048;
+
+// NVFP4 planes (e2m1 codes, one E4M3FN scale per 16 values along the reduction axis and one fp32
+// scale_2 per tensor: W = e2m1 x e4m3 x scale_2) feed the 16 x 16 x 32 bf16 / fp16 matrix
+// instructions, with W's e2m1 x e4m3 part formed exactly in registers (at most 2 + 4 significant
+// bits) and scale_2 applied to the fp32 result. Tiles of 16 rows x 256 values hold 2048 code
+// bytes: half c (values 128c .. 128c + 127 of the tile) at [1024c, 1024c + 1024), lane l's 16
+// bytes at 1024c + 16l; with n = l % 16 (row) and g = l / 16, dword j of them holds values
+// 128c + 32j + 8g .. + 7 of row n (value i in nibble i, low nibble first): the B operand of
+// instruction j of half c, whose 32 reduction values are exactly one 32-block. Scale tiles are
+// 256 bytes: byte 128h + 8n + 4c + j is the e4m3 scale of 16-block 16kt + 8c + 2j + h of row n,
+// so lane l reads its two scale words (c = 0, 1; byte j = instruction j) at 128 (g / 2) + 8n.
+constexpr int kTileScaleBytesNV4 = 256;
+
 template <int FMT>
 struct WFmt {
   static constexpr int kCodeBytes = FMT ? kTileCodeBytesW4 : kTileCodeBytes;
   static constexpr int kLoads = FMT ? 2 : 1;   // 16-byte code loads per lane per tile
+  static constexpr int kScaleBytes = FMT == 2 ? kTileScaleBytesNV4 : 128;   // per tile
+  static constexpr int kScaleWords = FMT == 2 ? 2 : 1;                      // per lane per tile
 };
+
+template <int I, int N, class F>
+MOEW2_DEV void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>());
+    static_for<I + 1, N>(f);
+  }
+}
 
 // Two e2m1 words (values 0..7 and 8..15 of a native dword, 8 codes each).
 MOEW2_DEV void native_to_fp4(uint32_t dw, uint32_t& blk0, uint32_t& blk1) {
@@ -301,6 +326,68 @@ MOEW2_DEV u32x4_t buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t 
 }
 MOEW2_DEV uint32_t buf_ld2_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, kPolicyNT);
+}
+
+// ------------------------------------------------------------------------------------------
+// NVFP4 B operands and the 16 x 16 x 32 instructions. Operand layout (both A and B): lane l
+// supplies row / column l % 16 and reduction values 8(l/16) .. 8(l/16) + 7 of the instruction;
+// accumulator register r of lane l holds row 4(l/16) + r, column l % 16 (as for the block-scaled
+// instruction above).
+// ------------------------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2e_t __attribute__((ext_vector_type(2)));
+
+// 8 e2m1 codes (value i in nibble i) times e4m3 byte J of `sw`, as 8 bf16 values. Exact: the
+// e2m1 value (from the conversion with scale 1) times the e4m3 value is exact in fp32 and has at
+// most 6 significant bits, so its bf16 rounding changes nothing.
+template <int J>
+MOEW2_DEV bf16x8_t nv4_b_bf16(uint32_t codes, uint32_t sw) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)sw, J);
+  bf16x8_t r;
+  static_for<0, 4>([&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    const f32x2e_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, q);
+    r[2 * q] = (__bf16)(f[0] * s);
+    r[2 * q + 1] = (__bf16)(f[1] * s);
+  });
+  return r;
+}
+
+// The same as 8 fp16 values: the conversion applies the power-of-two part 2^E of |s| for the
+// e4m3 value s (it uses only its scale operand's exponent), a packed fp16 multiply the signed
+// mantissa factor f = s / 2^E, |f| in [1, 2) (3 fraction bits at most). Both steps are exact:
+// |e2m1 x 2^E| lies in [2^-10, 1536] and the product in [2^-10, 2688], inside fp16's normal
+// range, with at most 6 significant bits. A zero scale gives zeros.
+template <int J>
+MOEW2_DEV f16x8_t nv4_b_f16(uint32_t codes, uint32_t sw) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)sw, J);
+  const bool zero = s == 0.f;
+  const float p2 = zero ? 1.f : __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, s) & 0x7F800000u);
+  const _Float16 m = zero ? (_Float16)0.f : (_Float16)(s / p2);
+  const f16x2_t mm = {m, m};
+  f16x8_t r;
+  static_for<0, 4>([&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    const f16x2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, p2, q) * mm;
+    r[2 * q] = h[0];
+    r[2 * q + 1] = h[1];
+  });
+  return r;
+}
+
+MOEW2_DEV f32x4_t mfma32_bf16(const u32x4_t& a, const bf16x8_t& b, f32x4_t c) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), b,
+                                                                             __builtin_bit_cast(f32x4e_t, c), 0, 0, 0));
+}
+MOEW2_DEV f32x4_t mfma32_f16(const u32x4_t& a, const f16x8_t& b, f32x4_t c) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), b,
+                                                                            __builtin_bit_cast(f32x4e_t, c), 0, 0, 0));
+}
+
+MOEW2_DEV u32x2_t buf_ld8_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kPolicyNT));
 }
 
 // Round-to-nearest-even fp32 -> bf16 bits (finite and infinite inputs; NaN stays NaN).

@@ -51,17 +51,19 @@ MOEW2_DEV WaveTiles wave_tiles(const uint8_t* codes, const uint8_t* scales, int 
   constexpr uint32_t cb = WFmt<FMT>::kCodeBytes;
   WaveTiles wt;
   wt.codes = buffer_view(codes + (size_t)e * tiles_per_expert * cb, tiles_per_expert * cb);
-  wt.scales = buffer_view(scales + (size_t)e * tiles_per_expert * kTileScaleBytes, tiles_per_expert * kTileScaleBytes);
+  constexpr uint32_t sb = WFmt<FMT>::kScaleBytes;
+  wt.scales = buffer_view(scales + (size_t)e * tiles_per_expert * sb, tiles_per_expert * sb);
   return wt;
 }
 
 // Weight tile registers of one k-tile: per row group (NB of them), the lane's code bytes (16 for
-// 2-bit codes, 2 x 16 for fp4 codes; block layout) and its two scale bytes (instructions 0 and 1
-// of the k-tile).
+// 2-bit codes, 2 x 16 for fp4 codes; tile layouts in common.h) and its scales: two UE8M0 bytes
+// (instructions 0 and 1 of the k-tile), or for NVFP4 planes two words of four e4m3 bytes (half c,
+// instruction j).
 template <int NB, int FMT>
 struct TileRegs {
   u32x4_t c[NB][WFmt<FMT>::kLoads];
-  uint32_t s[NB];
+  uint32_t s[NB][WFmt<FMT>::kScaleWords];
 };
 
 // The tile's byte offset goes in the scalar offset; the lane's offset (shifted out of range when
@@ -75,7 +77,14 @@ MOEW2_DEV void load_tile(TileRegs<NB, FMT>& r, const WaveTiles& wt, int kt, bool
 #pragma unroll
     for (int q = 0; q < WFmt<FMT>::kLoads; ++q)
       r.c[b][q] = buf_ld16_nt(wt.codes, (16u * (uint32_t)lane) | oob, t * WFmt<FMT>::kCodeBytes + 1024u * q);
-    r.s[b] = buf_ld2_nt(wt.scales, (2u * (uint32_t)lane) | oob, t * kTileScaleBytes);
+    if constexpr (FMT == kFmtNV4) {
+      const u32x2_t sv = buf_ld8_nt(wt.scales, (128u * (uint32_t)(lane >> 5) + 8u * (uint32_t)(lane & 15)) | oob,
+                                    t * kTileScaleBytesNV4);
+      r.s[b][0] = sv[0];
+      r.s[b][1] = sv[1];
+    } else {
+      r.s[b][0] = buf_ld2_nt(wt.scales, (2u * (uint32_t)lane) | oob, t * kTileScaleBytes);
+    }
   }
 }
 
@@ -84,12 +93,18 @@ MOEW2_DEV void load_tile(TileRegs<NB, FMT>& r, const WaveTiles& wt, int kt, bool
 //   part 0 [KR] bytes | ... | part NP-1 [KR] | scale words [KR/256][4 lane groups][SW bytes] | pad
 // with SW = 4 for two parts (part 0 c0, c1, part 1 c0, c1) and 8 for three parts (the same,
 // then part 2 c0, c1, 0, 0); c = instruction 0 or 1 of the k-tile.
+// NP = 0 (bf16) and 1 (fp16): the row's 16-bit values unchanged, for the NVFP4 planes' 16 x 16 x 32
+// instructions; a 16-byte pad per row puts the 16 rows of an operand read on distinct banks.
 // ---------------------------------------------------------------------------------------------
 template <int NP>
 struct MxRow {
+  static constexpr bool kRaw = NP < 2;
   static constexpr int kSW = NP == 2 ? 4 : 8;
-  __host__ __device__ static int stride(int KR) { return NP * KR + KR / kTileK * 4 * kSW + 64; }
+  __host__ __device__ static int stride(int KR) { return kRaw ? 2 * KR + 16 : NP * KR + KR / kTileK * 4 * kSW + 64; }
 };
+// activation row formats: x (bf16) and the gated intermediate (fp16) for each weight format
+template <int FMT> constexpr int kXRow = FMT == kFmtNV4 ? 0 : 2;
+template <int FMT> constexpr int kARow = FMT == kFmtNV4 ? 1 : 3;
 
 // Pieces of 16 bytes (8 values) of n rows; piece idx of the flat [n][len/8] range goes to thread
 // idx % NT; a batch covers kStage pieces per thread, issued together and committed together.
@@ -117,6 +132,24 @@ template <int NT, int NP>
 MOEW2_DEV void stage_commit_split(const Stage& st, uint8_t* lds, int stride, int KR, int n, int base, int tid,
                                   bool count_inf, int& ninf) {
   const int per_row = KR / 8, total = n * per_row;
+  if constexpr (MxRow<NP>::kRaw) {
+    // 16-bit rows stored as they come (NP = 1: fp16, whose infinities are counted)
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const int idx = base + i * NT + tid;
+      if (idx < total) {
+        const u32x4_t v = st.v[i];
+        if (NP == 1 && count_inf) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            ninf += (__builtin_isinf(f16_lo(v[q])) ? 1 : 0) + (__builtin_isinf(f16_hi(v[q])) ? 1 : 0);
+        }
+        const int m = idx / per_row, c8 = idx - m * per_row;
+        *reinterpret_cast<u32x4_t*>(lds + (size_t)m * stride + 16 * c8) = v;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kStage; ++i) {
     const int idx = base + i * NT + tid;
@@ -185,21 +218,47 @@ MOEW2_DEV void mma_chunk(const TileRegs<NB, FMT>& r, const uint8_t* kbase, int K
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const i32x8_t bo = b_operand<FMT, C>(r.c[b]);
-    acc[b] = mx_mfma<C, C>(a0, bo, acc[b], w0, r.s[b]);
-    acc[b] = mx_mfma<2 + C, C>(a1, bo, acc[b], w0, r.s[b]);
-    if (NP == 3) acc[b] = mx_mfma<C, C>(a2, bo, acc[b], w1, r.s[b]);
+    acc[b] = mx_mfma<C, C>(a0, bo, acc[b], w0, r.s[b][0]);
+    acc[b] = mx_mfma<2 + C, C>(a1, bo, acc[b], w0, r.s[b][0]);
+    if (NP == 3) acc[b] = mx_mfma<C, C>(a2, bo, acc[b], w1, r.s[b][0]);
   }
+}
+
+// One k-tile of NVFP4 planes from a 16-bit staged row: per half c and instruction j, lane group g
+// supplies row values 256kt + 128c + 32j + 8g .. + 7 (one 16-byte LDS read) and the B values at
+// the same reduction positions (NV4 tile layout in common.h); NP = 0: bf16 rows, 1: fp16.
+template <int NP, int NB>
+MOEW2_DEV void mma_tile_nv4(const TileRegs<NB, kFmtNV4>& r, const uint8_t* arow, int kt, int g, f32x4_t* acc) {
+  const uint8_t* kb = arow + 2 * (kt * kTileK + 8 * g);
+  static_for<0, 2>([&](auto cc) {
+    constexpr int C = decltype(cc)::value;
+    static_for<0, 4>([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kb + 2 * (128 * C + 32 * J));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if constexpr (NP == 0) acc[b] = mfma32_bf16(a, nv4_b_bf16<J>(r.c[b][C][J], r.s[b][C]), acc[b]);
+        else acc[b] = mfma32_f16(a, nv4_b_f16<J>(r.c[b][C][J], r.s[b][C]), acc[b]);
+      }
+    });
+  });
 }
 
 // One k-tile from the lane's staged row `arow`.
 template <int NP, int NB, int FMT>
 MOEW2_DEV void mma_tile(const TileRegs<NB, FMT>& r, const uint8_t* arow, int KR, int kt, int g, f32x4_t* acc) {
+  if constexpr (FMT == kFmtNV4) {
+    static_assert(MxRow<NP>::kRaw, "NVFP4 planes take 16-bit activation rows");
+    mma_tile_nv4<NP, NB>(r, arow, kt, g, acc);
+    return;
+  } else {
   const uint8_t* kbase = arow + kt * kTileK;
   const uint8_t* sw = arow + NP * KR + (kt * 4 + g) * MxRow<NP>::kSW;
   const uint32_t w0 = *reinterpret_cast<const uint32_t*>(sw);
   const uint32_t w1 = NP == 3 ? *reinterpret_cast<const uint32_t*>(sw + 4) : 0u;
   mma_chunk<0, NP, NB, FMT>(r, kbase, KR, w0, w1, g, acc);
   mma_chunk<1, NP, NB, FMT>(r, kbase, KR, w0, w1, g, acc);
+  }
 }
 
 // ring[i] <- k-tile kb + i for i in [I0, I1) (out-of-range requests past ke)
@@ -413,7 +472,7 @@ __global__ void __launch_bounds__(kThreads)
 decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                       const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
                       _Float16* __restrict__ act, long long* __restrict__ counters,
-                      int P, int E, int K, int I, int top_k, SortedChunk sc) {
+                      int P, int E, int K, int I, int top_k, SortedChunk sc, const float* __restrict__ scale2) {
   constexpr int KS = kWaves / NPW;
   constexpr bool DIRECT = MODE == kDecodeDirect;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -449,7 +508,10 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
   wt.tile[0] = (uint32_t)(2 * q * nkt);
   wt.tile[1] = (uint32_t)((2 * q + 1) * nkt);
   const int kb = ks * nkt / KS, ke = valid ? (ks + 1) * nkt / KS : kb;
-  const int stride = MxRow<2>::stride(K);
+  // NVFP4: scale_2 of the expert's gate and up tensors, applied to the fp32 results
+  const float sg = FMT == kFmtNV4 ? scale2[3 * e] : 1.f, su = FMT == kFmtNV4 ? scale2[3 * e + 1] : 1.f;
+  constexpr int XR = kXRow<FMT>;
+  const int stride = MxRow<XR>::stride(K);
   float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][2][4][16]
   TileRegs<2, FMT> ring[kRing];
   {
@@ -458,12 +520,12 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
       return (size_t)(pp / top_k) * K;
     };
     int ninf = 0;
-    stage_and_prime<kThreads, 2, 2, FMT, DIRECT ? 1 : kRing>(ring, wt, kb, ke, lane, lds, stride, x, K, n,
+    stage_and_prime<kThreads, XR, 2, FMT, DIRECT ? 1 : kRing>(ring, wt, kb, ke, lane, lds, stride, x, K, n,
                                                                 row_off, tid, false, ninf);
     __syncthreads();
     const int ma = min(lane & 15, n - 1);
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    stream_k<2, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, K, lane >> 4, acc, lane);
+    stream_k<XR, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, K, lane >> 4, acc, lane);
     reduce_split_k<KS>(acc, red, w, ks, lane);
     if (ks == 0 && lane < 16) {
       // accumulator register r of lanes 0..15 holds token row r, column lane
@@ -471,7 +533,7 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
       for (int r = 0; r < kChunk; ++r) {
         if (r < n) {
           const int pp = r == 0 ? pr[0] : r == 1 ? pr[1] : r == 2 ? pr[2] : pr[3];
-          act[(size_t)pp * I + 16 * q + lane] = valid ? (_Float16)silu_mul(acc[0][r], acc[1][r]) : (_Float16)0.f;
+          act[(size_t)pp * I + 16 * q + lane] = valid ? (_Float16)silu_mul(acc[0][r] * sg, acc[1][r] * su) : (_Float16)0.f;
         }
       }
     }
@@ -493,7 +555,7 @@ __global__ void __launch_bounds__(kThreads)
 decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                    const _Float16* __restrict__ act, const int32_t* __restrict__ ids,
                    float* __restrict__ pair_out, long long* __restrict__ counters, int P, int E, int K,
-                   int I, SortedChunk sc) {
+                   int I, SortedChunk sc, const float* __restrict__ scale2) {
   constexpr int KS = kWaves / NPW;
   static_assert(R == 1 || KS == 1, "row pairs per wave need the whole reduction in each wave");
   static_assert(MODE == kDecodeRouted || MODE == kDecodeSorted, "the direct organisation has its own down kernel");
@@ -519,9 +581,11 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
   wt.tile[0] = (uint32_t)(2 * rq * nkt);
   wt.tile[1] = (uint32_t)((2 * rq + 1) * nkt);
   const int kb = ks * nkt / KS, ke = (ks + 1) * nkt / KS;
-  const int stride = MxRow<3>::stride(I);
+  constexpr int AR = kARow<FMT>;
+  const int stride = MxRow<AR>::stride(I);
   float* red = reinterpret_cast<float*>(lds + (size_t)kChunk * stride);  // [kWaves][2][4][16]
   const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
+  const float sd = FMT == kFmtNV4 ? scale2[3 * e + 2] : 1.f;   // NVFP4: the down tensor's scale_2
   TileRegs<2, FMT> ring[kRing];
   {
     auto row_off = [&](int m) -> size_t {
@@ -529,7 +593,7 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
       return (size_t)pp * I;
     };
     int ninf = 0;
-    stage_and_prime<kThreads, 3, 2, FMT>(ring, wt, kb, ke, lane, lds, stride, act16, I, n, row_off, tid,
+    stage_and_prime<kThreads, AR, 2, FMT>(ring, wt, kb, ke, lane, lds, stride, act16, I, n, row_off, tid,
                                     blockIdx.x == 0, ninf);
     if (ninf) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)ninf);
     __syncthreads();
@@ -538,10 +602,10 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
 #pragma unroll
     for (int q = 0; q < R; ++q) acc[q][0] = acc[q][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (R == 1) {
-      stream_k<3, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, I, lane >> 4, acc[0], lane);
+      stream_k<AR, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, I, lane >> 4, acc[0], lane);
       reduce_split_k<KS>(acc[0], red, w, ks, lane);
     } else {
-      stream_rows<3, 2, FMT, R>(ring, wt, nkt, lds + (size_t)ma * stride, I, lane >> 4, acc, lane);
+      stream_rows<AR, 2, FMT, R>(ring, wt, nkt, lds + (size_t)ma * stride, I, lane >> 4, acc, lane);
     }
     if (ks == 0 && lane < 16) {
 #pragma unroll
@@ -553,7 +617,7 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
           for (int r = 0; r < kChunk; ++r) {
             if (r < n) {
               const int pp = r == 0 ? pr[0] : r == 1 ? pr[1] : r == 2 ? pr[2] : pr[3];
-              pair_out[(size_t)pp * K + col] = acc[q][b][r];
+              pair_out[(size_t)pp * K + col] = acc[q][b][r] * sd;
             }
           }
         }
@@ -575,14 +639,15 @@ __global__ void __launch_bounds__(kDirectThreads)
 decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                           const _Float16* __restrict__ act, const int32_t* __restrict__ ids,
                           const float* __restrict__ wts, void* __restrict__ y, long long* __restrict__ counters,
-                          int out_dtype, int T, int E, int K, int I, int top_k) {
+                          int out_dtype, int T, int E, int K, int I, int top_k, const float* __restrict__ scale2) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int P = T * top_k;                         // <= kDirectMaxPairs
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int rg = blockIdx.x;
-  const int stride = MxRow<3>::stride(I);
+  constexpr int AR = kARow<FMT>;
+  const int stride = MxRow<AR>::stride(I);
   float* o = reinterpret_cast<float*>(lds + (size_t)kDirectMaxPairs * stride);  // [P][16]
   float* red = o + kDirectMaxPairs * 16;                                        // [P][16]
   // wave w: pair p = w / 2, reduction half w % 2
@@ -608,7 +673,7 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
   auto row_off = [&](int m) -> size_t { return (size_t)m * I; };
   TileRegs<1, FMT> ring[kRing];
   int ninf = 0;
-  stage_and_prime<kDirectThreads, 3, 1, FMT, kRing / 2>(ring, wt, kb, ke, lane, lds, stride, act16, I, P, row_off,
+  stage_and_prime<kDirectThreads, AR, 1, FMT, kRing / 2>(ring, wt, kb, ke, lane, lds, stride, act16, I, P, row_off,
                                                    tid, blockIdx.x == 0, ninf);
   __syncthreads();
   if (blockIdx.x == 0) {
@@ -618,14 +683,15 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
     if (tid < P && (cid[tid] < 0 || cid[tid] >= E)) atomicAdd(&cnt[0], 1);
   }
   f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  stream_k<3, 1, FMT>(ring, wt, kb, ke, lds + (size_t)(p < P ? p : 0) * stride, I, lane >> 4, acc, lane);
+  stream_k<AR, 1, FMT>(ring, wt, kb, ke, lds + (size_t)(p < P ? p : 0) * stride, I, lane >> 4, acc, lane);
   if (valid && hk == 1 && lane < 16) red[p * 16 + lane] = acc[0][0];
   __syncthreads();
   if (blockIdx.x == 0 && tid == 0) {
     counters[0] = cnt[0];
     counters[1] = cnt[1];
   }
-  if (valid && hk == 0 && lane < 16) o[p * 16 + lane] = acc[0][0] + red[p * 16 + lane];
+  if (valid && hk == 0 && lane < 16)
+    o[p * 16 + lane] = (acc[0][0] + red[p * 16 + lane]) * (FMT == kFmtNV4 ? scale2[3 * id + 2] : 1.f);
   __syncthreads();
   // combine: y[t][16*rg + c] = sum_j w[t,j] * o[t*top_k+j][c]
   for (int idx = tid; idx < T * 16; idx += kDirectThreads) {
@@ -713,7 +779,7 @@ static hipError_t decode_gate_up_fmt(const moe_w2_planes* p, int T, int top_k, c
   const SortedChunk sc = sorted_chunks(ws, wsb);
   if (mode == kDecodeDirect) {
     hipLaunchKernelGGL((decode_gate_up_kernel<1, kDecodeDirect, FMT>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc);
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc, p->scale2);
   } else if (mode == kDecodeSorted) {
     // one workgroup row per chunk of the routing pass (at most max_chunks; rows past meta[1] exit);
     // the same split of the reduction over waves as the routed organisation, so that both give
@@ -721,17 +787,17 @@ static hipError_t decode_gate_up_fmt(const moe_w2_planes* p, int T, int top_k, c
     if (pick_np(min(p->E, P)) == 4)
       hipLaunchKernelGGL((decode_gate_up_kernel<4, kDecodeSorted, FMT>), dim3(p->I / 64, ws.max_chunks),
                          dim3(kThreads), lds, s, p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I,
-                         top_k, sc);
+                         top_k, sc, p->scale2);
     else
       hipLaunchKernelGGL((decode_gate_up_kernel<1, kDecodeSorted, FMT>), dim3(p->I / 16, ws.max_chunks),
                          dim3(kThreads), lds, s, p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I,
-                         top_k, sc);
+                         top_k, sc, p->scale2);
   } else if (pick_np(min(p->E, P)) == 4) {   // at most this many workgroup rows do work
     hipLaunchKernelGGL((decode_gate_up_kernel<4, kDecodeRouted, FMT>), dim3(p->I / 64, P), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc);
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc, p->scale2);
   } else {
     hipLaunchKernelGGL((decode_gate_up_kernel<1, kDecodeRouted, FMT>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc);
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc, p->scale2);
   }
   return hipGetLastError();
 }
@@ -740,6 +806,7 @@ hipError_t launch_decode_gate_up(const moe_w2_planes* p, int T, int top_k, const
                                  const int32_t* ids, const Workspace& ws, uint8_t* wsb, int mode,
                                  hipStream_t s) {
   if (T * top_k == 0) return hipSuccess;
+  if (p->fmt == kFmtNV4) return decode_gate_up_fmt<kFmtNV4>(p, T, top_k, x, ids, ws, wsb, mode, s);
   return p->fmt == kFmtW4 ? decode_gate_up_fmt<kFmtW4>(p, T, top_k, x, ids, ws, wsb, mode, s)
                           : decode_gate_up_fmt<kFmtW2>(p, T, top_k, x, ids, ws, wsb, mode, s);
 }
@@ -756,13 +823,13 @@ static hipError_t decode_down_routed(const moe_w2_planes* p, int rows, int P, co
   const bool two_pairs = FMT == kFmtW2 && (p->I / kTileK) % kRing == 0 && p->K % 256 == 0;
   if (pick_np(groups) == 4 && two_pairs)
     hipLaunchKernelGGL((decode_down_kernel<4, FMT, 2, MODE>), dim3(p->K / 256, rows), dim3(kThreads), lds, s,
-                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc);
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc, p->scale2);
   else if (pick_np(groups) == 4)
     hipLaunchKernelGGL((decode_down_kernel<4, FMT, 1, MODE>), dim3(p->K / 128, rows), dim3(kThreads), lds, s,
-                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc);
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc, p->scale2);
   else
     hipLaunchKernelGGL((decode_down_kernel<1, FMT, 1, MODE>), dim3(p->K / 32, rows), dim3(kThreads), lds, s,
-                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc);
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc, p->scale2);
   return hipGetLastError();
 }
 
@@ -775,7 +842,7 @@ static hipError_t decode_down_fmt(const moe_w2_planes* p, int T, int top_k, cons
     const _Float16* act = (const _Float16*)(wsb + ws.act);
     long long* cnt = (long long*)(wsb + ws.counters);
     hipLaunchKernelGGL(decode_down_direct_kernel<FMT>, dim3(p->K / 16), dim3(kDirectThreads), decode_direct_lds(p->I),
-                       s, p->dn_codes, p->dn_scales, act, ids, w, y, cnt, out_dtype, T, p->E, p->K, p->I, top_k);
+                       s, p->dn_codes, p->dn_scales, act, ids, w, y, cnt, out_dtype, T, p->E, p->K, p->I, top_k, p->scale2);
     return hipGetLastError();
   }
   return mode == kDecodeSorted ? decode_down_routed<FMT, kDecodeSorted>(p, ws.max_chunks, P, ids, ws, wsb, s)
@@ -786,6 +853,7 @@ hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const in
                               void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, int mode,
                               hipStream_t s) {
   if (T * top_k == 0) return hipSuccess;
+  if (p->fmt == kFmtNV4) return decode_down_fmt<kFmtNV4>(p, T, top_k, ids, w, y, out_dtype, ws, wsb, mode, s);
   return p->fmt == kFmtW4 ? decode_down_fmt<kFmtW4>(p, T, top_k, ids, w, y, out_dtype, ws, wsb, mode, s)
                           : decode_down_fmt<kFmtW2>(p, T, top_k, ids, w, y, out_dtype, ws, wsb, mode, s);
 }

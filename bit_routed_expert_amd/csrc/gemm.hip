@@ -131,14 +131,6 @@ template <int FMT>
 constexpr int kBLoads = kRGW * (WFmt<FMT>::kLoads + 1);   // vector memory instructions for one BRegs
 constexpr int kGroups = 8;   // instruction groups per k-tile: 2 columns C x 4 row tiles m
 
-template <int I, int N, class F>
-MOEW2_DEV void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>());
-    static_for<I + 1, N>(f);
-  }
-}
-
 // The loads of one step for one wave, as kItems single instructions: the stage's DMA instructions
 // for k-tile ka (waves whose last instruction index lies past the stage repeat the stage's last
 // instruction - the same bytes to the same chunks - so every wave issues kPerWave), then the B
@@ -504,6 +496,7 @@ inline unsigned gemm_grid(int max_tiles, int n_blocks) {
 
 hipError_t launch_gemm_gate_up(const moe_w2_planes* p, int T, int top_k, const void* x,
                                const Workspace& ws, uint8_t* wsb, hipStream_t s) {
+  if (p->fmt == kFmtNV4) return hipErrorInvalidValue;   // NVFP4 planes run on the decode kernels
   if (ws.max_tiles == 0) return hipSuccess;
   const long long nblk32 = (long long)T * (p->K / 32);
   hipLaunchKernelGGL(quant_x6_kernel, dim3((unsigned)((nblk32 + 255) / 256)), dim3(256), 0, s,
@@ -520,6 +513,7 @@ hipError_t launch_gemm_gate_up(const moe_w2_planes* p, int T, int top_k, const v
 
 hipError_t launch_gemm_down(const moe_w2_planes* p, int T, int top_k, const Workspace& ws,
                             uint8_t* wsb, hipStream_t s) {
+  if (p->fmt == kFmtNV4) return hipErrorInvalidValue;
   if (ws.max_tiles == 0) return hipSuccess;
   const int P = T * top_k;
   const int nblk = (p->K + BN - 1) / BN;

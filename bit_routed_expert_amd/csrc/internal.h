@@ -9,28 +9,33 @@
 
 struct moe_w2_planes {
   int E, K, I;
-  int fmt;             // weight format: kFmtW2 (2-bit codes) or kFmtW4 (e2m1 codes), both UE8M0 / 32
+  int fmt;             // weight format: kFmtW2 (2-bit codes) or kFmtW4 (e2m1 codes), both UE8M0 / 32;
+                       // kFmtNV4 (e2m1 codes, E4M3FN / 16, fp32 scale_2 per tensor)
   int device;
   void* base;          // single device allocation
   size_t bytes;
   uint8_t* gu_codes;   // [E][2I/16][K/256][tile code bytes: 1024 (w2) or 2048 (w4)]
   uint8_t* gu_scales;  // [E][2I/16][K/256][128]
   uint8_t* dn_codes;   // [E][K/16][I/256][tile code bytes]
-  uint8_t* dn_scales;  // [E][K/16][I/256][128]
+  uint8_t* dn_scales;  // [E][K/16][I/256][128]   (NVFP4: 256-byte scale tiles)
+  float* scale2;       // NVFP4: [E][3] fp32 scale_2 of the gate rows, the up rows and the down matrix
   int32_t* flag;       // pack-time validation flags (device)
 };
 
 namespace moew2 {
 
-// Weight formats of the planes. W2: 2-bit sign-symmetric codes; W4: e2m1 (fp4) codes (MXFP4).
-enum { kFmtW2 = 0, kFmtW4 = 1 };
-inline int code_bits(int fmt) { return fmt == kFmtW4 ? 4 : 2; }
+// Weight formats of the planes. W2: 2-bit sign-symmetric codes; W4: e2m1 (fp4) codes (MXFP4);
+// NV4: e2m1 codes with E4M3FN scales per 16 and an fp32 scale_2 per tensor (NVFP4).
+enum { kFmtW2 = 0, kFmtW4 = 1, kFmtNV4 = 2 };
+inline int code_bits(int fmt) { return fmt == kFmtW2 ? 2 : 4; }
+inline int scale_group(int fmt) { return fmt == kFmtNV4 ? 16 : 32; }   // values per scale byte
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Pack-time validation flags
-enum { kFlagScale = 1 };   // pack: a scale byte above 252
+enum { kFlagScale = 1,      // pack: a UE8M0 scale byte above 252
+       kFlagNaN = 2 };     // pack (NVFP4): a NaN e4m3 scale byte or a non-finite scale_2
 
 // Workspace layout of one forward.
 struct Workspace {
@@ -67,6 +72,9 @@ Workspace workspace_layout(int E, int K, int I, int T, int top_k);
 size_t route_scratch_bytes(int E, int P);
 
 // Launchers (return hipError_t of the launch)
+hipError_t launch_pack_nv4(const moe_w2_planes* p, const uint8_t* gu_codes, const uint8_t* gu_scales,
+                           const float* gu_scale2, const uint8_t* dn_codes, const uint8_t* dn_scales,
+                           const float* dn_scale2, int unpack, hipStream_t s);
 hipError_t launch_pack(const moe_w2_planes* p, const uint8_t* gu_codes, const uint8_t* gu_scales,
                        const uint8_t* dn_codes, const uint8_t* dn_scales, hipStream_t s);
 hipError_t launch_pack_experts(const moe_w2_planes* p, int e0, int n, const uint8_t* gu_codes,

@@ -166,6 +166,85 @@ __global__ void unpack_scales_kernel(const uint8_t* __restrict__ native, uint8_t
   for (int d = 0; d < 8; ++d) dst[d] = tile[2 * (16 * (d & 3) + j) + (d >> 2)];
 }
 
+// NVFP4 codes (canonical: two e2m1 codes per byte, low nibble = even element; NV4 tile layout in
+// common.h): one thread per (matrix, tile, half c, lane); dword j of the lane's 16 bytes holds the
+// 8 codes of values 128c + 32j + 8g .. + 7 of its row, i.e. 4 consecutive canonical bytes.
+__global__ void pack_codes_nv4_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ native,
+                                      int nmat, int NR, int KR, int I, int gate_up, int unpack) {
+  const int nkt = KR / kTileK, nrg = NR / kTileRows;
+  const long long total = (long long)nmat * nrg * nkt * 128;
+  long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int lane = (int)(gid & 63), c = (int)((gid >> 6) & 1);
+  long long t = gid >> 7;
+  const int kt = (int)(t % nkt); t /= nkt;
+  const int rg = (int)(t % nrg);
+  const int e = (int)(t / nrg);
+  const int cr = canonical_row(rg * kTileRows + (lane & 15), I, gate_up != 0);
+  uint8_t* row = const_cast<uint8_t*>(canon) + ((long long)e * NR + cr) * (KR / 2) + 128 * kt + 64 * c + 4 * (lane >> 4);
+  uint32_t* tile = reinterpret_cast<uint32_t*>(native + ((long long)e * nrg * nkt + (long long)rg * nkt + kt) *
+                                               kTileCodeBytesW4 + 1024 * c + 16 * lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t* src = reinterpret_cast<uint32_t*>(row + 16 * j);
+    if (unpack) *src = tile[j];
+    else tile[j] = *src;
+  }
+}
+
+// NVFP4 scales (canonical: one E4M3FN byte per 16 values along the reduction axis): one thread
+// per (matrix, tile, 16-block parity h, row n); byte 128h + 8n + 4c + j of the tile is the scale
+// of 16-block 16kt + 8c + 2j + h of row n. A NaN encoding (0x7F, 0xFF) is flagged.
+__global__ void pack_scales_nv4_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ native,
+                                       int nmat, int NR, int KR, int I, int gate_up, int32_t* __restrict__ flag,
+                                       int unpack) {
+  const int nkt = KR / kTileK, nrg = NR / kTileRows, nsc = KR / 16;
+  const long long total = (long long)nmat * nrg * nkt * 32;
+  long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int n = (int)(gid & 15), h = (int)((gid >> 4) & 1);
+  long long t = gid >> 5;
+  const int kt = (int)(t % nkt); t /= nkt;
+  const int rg = (int)(t % nrg);
+  const int e = (int)(t / nrg);
+  const int cr = canonical_row(rg * kTileRows + n, I, gate_up != 0);
+  uint8_t* row = const_cast<uint8_t*>(canon) + ((long long)e * NR + cr) * nsc + 16 * kt + h;
+  uint8_t* tile = native + ((long long)e * nrg * nkt + (long long)rg * nkt + kt) * kTileScaleBytesNV4 + 128 * h + 8 * n;
+  int bad = 0;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (unpack) {
+        row[8 * c + 2 * j] = tile[4 * c + j];
+      } else {
+        const uint8_t b = row[8 * c + 2 * j];
+        bad |= (b & 0x7F) == 0x7F;
+        tile[4 * c + j] = b;
+      }
+    }
+  if (bad) atomicOr(flag, kFlagNaN);
+}
+
+// scale_2 of experts [e0, e0 + n): gate and up from gu [n][2], down from dn [n], into planes [E][3]
+// (or back, with unpack); a non-finite value is flagged.
+__global__ void copy_scale2_kernel(const float* __restrict__ gu, const float* __restrict__ dn, float* __restrict__ planes,
+                                   int n, int32_t* __restrict__ flag, int unpack) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  if (unpack) {
+    const_cast<float*>(gu)[2 * i] = planes[3 * i];
+    const_cast<float*>(gu)[2 * i + 1] = planes[3 * i + 1];
+    const_cast<float*>(dn)[i] = planes[3 * i + 2];
+    return;
+  }
+  const float a = gu[2 * i], b = gu[2 * i + 1], c = dn[i];
+  planes[3 * i] = a;
+  planes[3 * i + 1] = b;
+  planes[3 * i + 2] = c;
+  if (!__builtin_isfinite(a) || !__builtin_isfinite(b) || !__builtin_isfinite(c)) atomicOr(flag, kFlagNaN);
+}
+
 inline unsigned grid_for(long long n, int block) { return (unsigned)((n + block - 1) / block); }
 
 }  // namespace
@@ -203,6 +282,32 @@ hipError_t launch_pack_experts(const moe_w2_planes* p, int e0, int n, const uint
 hipError_t launch_pack(const moe_w2_planes* p, const uint8_t* gu_codes, const uint8_t* gu_scales,
                        const uint8_t* dn_codes, const uint8_t* dn_scales, hipStream_t s) {
   return launch_pack_experts(p, 0, p->E, gu_codes, gu_scales, dn_codes, dn_scales, s);
+}
+
+// NVFP4 planes, both directions (unpack = native -> canonical; the flag is cleared and set on
+// packing only).
+hipError_t launch_pack_nv4(const moe_w2_planes* p, const uint8_t* gu_codes, const uint8_t* gu_scales,
+                           const float* gu_scale2, const uint8_t* dn_codes, const uint8_t* dn_scales,
+                           const float* dn_scale2, int unpack, hipStream_t s) {
+  const int E = p->E, K = p->K, I = p->I;
+  const int B = 256;
+  if (!unpack) {
+    hipError_t err = hipMemsetAsync(p->flag, 0, sizeof(int32_t), s);
+    if (err != hipSuccess) return err;
+  }
+  const long long t_gu = (long long)E * (2 * I / kTileRows) * (K / kTileK);
+  const long long t_dn = (long long)E * (K / kTileRows) * (I / kTileK);
+  hipLaunchKernelGGL(pack_codes_nv4_kernel, dim3(grid_for(t_gu * 128, B)), dim3(B), 0, s, gu_codes, p->gu_codes, E,
+                     2 * I, K, I, 1, unpack);
+  hipLaunchKernelGGL(pack_codes_nv4_kernel, dim3(grid_for(t_dn * 128, B)), dim3(B), 0, s, dn_codes, p->dn_codes, E, K,
+                     I, I, 0, unpack);
+  hipLaunchKernelGGL(pack_scales_nv4_kernel, dim3(grid_for(t_gu * 32, B)), dim3(B), 0, s, gu_scales, p->gu_scales, E,
+                     2 * I, K, I, 1, p->flag, unpack);
+  hipLaunchKernelGGL(pack_scales_nv4_kernel, dim3(grid_for(t_dn * 32, B)), dim3(B), 0, s, dn_scales, p->dn_scales, E,
+                     K, I, I, 0, p->flag, unpack);
+  hipLaunchKernelGGL(copy_scale2_kernel, dim3(grid_for(E, B)), dim3(B), 0, s, gu_scale2, dn_scale2, p->scale2, E,
+                     p->flag, unpack);
+  return hipGetLastError();
 }
 
 hipError_t launch_unpack(const moe_w2_planes* p, uint8_t* gu_codes, uint8_t* gu_scales,

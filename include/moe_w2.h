@@ -64,9 +64,12 @@ enum moe_w2_status {
 enum moe_w2_out_dtype { MOE_W2_OUT_BF16 = 0, MOE_W2_OUT_F32 = 1 };
 
 /* Which kernels moe_w2_forward uses. AUTO picks the decode kernels for T*top_k <= 512, else
- * GEMM; among the decode organisations, DECODE_SORTED from 384 pairs up, DECODE below. The decode
- * kernels (both organisations) support T*top_k <= 512 only (MOE_W2_EUNSUPPORTED above); they
- * stream an expert's weights once per 4 of its pairs. DECODE finds each expert's pairs from the
+ * GEMM (NVFP4 planes: the sorted decode organisation); among the decode organisations,
+ * DECODE_SORTED from 384 pairs up, DECODE below. DECODE supports T*top_k <= 512 only
+ * (MOE_W2_EUNSUPPORTED above); DECODE_SORTED any number of pairs P = T*top_k with
+ * P/4 + min(E, P) + 1 <= 65535 (its launch has that many workgroup rows, one per chunk of up to 4
+ * pairs of one expert). Both stream an expert's weights once
+ * per 4 of its pairs. DECODE finds each expert's pairs from the
  * ids inside the kernels (no routing pass); DECODE_SORTED runs a routing pass first and walks its
  * chunks in expert order, so the chunks of a popular expert run together and re-read its weights
  * from L2 rather than HBM. All paths give results within the same tolerance, and the two decode
@@ -129,6 +132,35 @@ int moe_w4_pack(int E, int K, int I,
                 const uint8_t* gu_codes, const uint8_t* gu_scales,
                 const uint8_t* dn_codes, const uint8_t* dn_scales,
                 void* stream, moe_w2_planes** out);
+
+/*
+ * moe_w4_pack_nvfp4 - native planes of one MoE layer with NVFP4 experts: e2m1 codes, one
+ * E4M3FN scale per 16 elements along each GEMM's reduction axis and one fp32 scale_2 per tensor,
+ * weight = e2m1 x e4m3 x scale_2. Source: README opening paragraph and bullet "FP4 recovery - used
+ * surgically" (the NVFP4 checkpoint's experts kept at FP4 as a delta tier); "The v0.24.0 port",
+ * section "Our hooks", modelopt.py bullet (the NVFP4 format: e2m1 x e4m3 block-16 x per-tensor
+ * scale_2).
+ *   gu_codes  [E][2I][K/2]  two e2m1 codes per byte, low nibble = even element
+ *   gu_scales [E][2I][K/16] E4M3FN bytes        gu_scale2 [E][2] fp32: gate rows, up rows
+ *   dn_codes  [E][K][I/2]   dn_scales [E][K][I/16]   dn_scale2 [E] fp32
+ * A NaN scale byte (0x7F, 0xFF) or a non-finite scale_2 returns MOE_W2_ENVFP4; also needs
+ * I*K < 2^31. The planes work with moe_w4_forward / moe_w2_forward / moe_w2_forward_stage on the
+ * decode kernels at every batch size (PATH_AUTO takes the sorted decode organisation above 512
+ * pairs; PATH_GEMM returns MOE_W2_EUNSUPPORTED): the block-scaled matrix instruction takes only
+ * power-of-two block scales, so the weights enter the 16 x 16 x 32 bf16 (gate/up, with bf16 x) and
+ * fp16 (down, with the fp16 gated product) instructions, e2m1 x e4m3 formed exactly in registers
+ * and scale_2 applied to the fp32 results. Synchronous, like moe_w2_pack.
+ */
+int moe_w4_pack_nvfp4(int E, int K, int I,
+                      const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_scale2,
+                      const uint8_t* dn_codes, const uint8_t* dn_scales, const float* dn_scale2,
+                      void* stream, moe_w2_planes** out);
+
+/* Inverse of moe_w4_pack_nvfp4 into canonical buffers of its shapes (asynchronous; exact).
+ * MOE_W2_EINVAL for other planes. */
+int moe_w4_unpack_nvfp4(const moe_w2_planes* planes,
+                        uint8_t* gu_codes, uint8_t* gu_scales, float* gu_scale2,
+                        uint8_t* dn_codes, uint8_t* dn_scales, float* dn_scale2, void* stream);
 
 /* Inverse of moe_w2_pack into canonical buffers of its shapes (asynchronous; exact).
  * MOE_W2_EINVAL for planes made by moe_w4_pack. */
@@ -218,7 +250,8 @@ int moe_w2_forward_noalloc(const moe_w2_planes* planes, int T, int top_k,
                            const void* x, const int32_t* topk_ids, const float* topk_w,
                            void* y, int out_dtype, int path, void* stream);
 
-/* moe_w4_forward - moe_w2_forward on planes made by moe_w4_pack (MOE_W2_EINVAL for others). */
+/* moe_w4_forward - moe_w2_forward on planes made by moe_w4_pack or moe_w4_pack_nvfp4
+ * (MOE_W2_EINVAL for others). */
 int moe_w4_forward(const moe_w2_planes* planes, int T, int top_k,
                    const void* x, const int32_t* topk_ids, const float* topk_w,
                    void* y, int out_dtype,

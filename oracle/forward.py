@@ -6,6 +6,11 @@ Definition (reading of the pages; the plain reading is stated where they are sil
 * weights: W[r, k] = CODEBOOK[code[r, k]] * 2**(scale[r, k // 32] - 127)
   (README bullet "2-bit expert planes - the sign-bias finding" for the codebook; "The v0.24.0
   port", section "Our hooks", modelopt.py bullet for UE8M0 block-32 scales).
+* NVFP4 experts (README opening paragraph and bullet "FP4 recovery - used surgically"; "The
+  v0.24.0 port", section "Our hooks", modelopt.py bullet for the format):
+  W[r, k] = e2m1(code[r, k]) * e4m3(scale[r, k // 16]) * scale_2, with one fp32 scale_2 per
+  tensor: the gate rows, the up rows and the down matrix of an expert each have their own
+  (reading: the checkpoint quantizes gate and up as separate tensors; the pages do not say).
 * gate_up[e] holds 2I rows: rows 0..I-1 are the gate projection, rows I..2I-1 the up projection
   (the pages are silent on the order; this is the usual fused w13 layout).
 * per pair (t, j) with expert e = ids[t, j]:  g = G_e x_t,  u = U_e x_t,
@@ -21,7 +26,7 @@ Definition (reading of the pages; the plain reading is stated where they are sil
 """
 import numpy as np
 
-from .formats import CODEBOOK, E2M1_MAGNITUDE, unpack_codes, unpack_e2m1
+from .formats import CODEBOOK, E2M1_MAGNITUDE, e4m3_value, unpack_codes, unpack_e2m1
 
 _CODEBOOK = np.array(CODEBOOK, dtype=np.float64)
 _E2M1 = np.array([m for m in E2M1_MAGNITUDE] + [-m for m in E2M1_MAGNITUDE], dtype=np.float64)
@@ -47,6 +52,33 @@ def dequant_rows_fp4(packed, scale_bytes):
     if sb.size and (sb.max() > 254 or sb.min() < 0):
         raise ValueError("UE8M0 scale byte out of range")
     return vals * np.repeat(np.ldexp(1.0, sb - 127), 32, axis=-1)
+
+
+def _e4m3_table():
+    t = np.full(256, np.nan)
+    for b in range(256):
+        try:
+            t[b] = e4m3_value(b)
+        except ValueError:
+            pass
+    return t
+
+
+_E4M3 = _e4m3_table()
+
+
+def dequant_rows_nvfp4(packed, scale_bytes, scale2):
+    """NVFP4 rows: packed e2m1 codes [rows, n/2] + E4M3FN scale bytes [rows, n/16] + the fp32
+    scale_2 -> f64 weights [rows, n], W = e2m1(code) * e4m3(scale byte) * scale_2 (exact in f64:
+    at most 2 + 4 + 24 significant bits). NaN scale bytes or a non-finite scale_2 raise."""
+    vals = _E2M1[unpack_e2m1(packed)]
+    s = _E4M3[np.asarray(scale_bytes, dtype=np.uint8)]
+    if np.isnan(s).any():
+        raise ValueError("E4M3 NaN scale byte")
+    s2 = float(np.float32(scale2))
+    if not np.isfinite(s2):
+        raise ValueError("non-finite scale_2")
+    return vals * np.repeat(s, 16, axis=-1) * s2
 
 
 def _dequant(fp4):
@@ -75,7 +107,8 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None, fp4=False, workers=1):
+def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None, fp4=False, workers=1,
+                 nvfp4=None):
     """Per-pair down-projection outputs o[(t, j)] in f64.
 
     x: [T, K] f64 (the bf16 activations' exact values). Returns an array [len(tokens), top_k, K];
@@ -83,6 +116,7 @@ def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=N
     (for spot checks of large workloads); default all tokens. fp4: the planes hold e2m1 codes
     (two per byte) instead of 2-bit codes. ``workers`` > 1 computes that many experts at a time
     in threads; every pair's arithmetic is the same either way (each pair belongs to one expert).
+    nvfp4: (gu_scale2 [E, 2], dn_scale2 [E]) for NVFP4 planes (e2m1 codes, E4M3 block-16 scales).
     """
     dq = _dequant(fp4)
     x = np.asarray(x, dtype=np.float64)
@@ -95,10 +129,17 @@ def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=N
     out = np.zeros((len(tokens), top_k, K), dtype=np.float64)
     sel = ids[tokens]  # [n_tok, top_k]
 
+    def weights(e):
+        if nvfp4 is None:
+            return dq(gu_codes[e], gu_scales[e]), dq(dn_codes[e], dn_scales[e])
+        gs2, ds2 = np.asarray(nvfp4[0], np.float32), np.asarray(nvfp4[1], np.float32)
+        w_gu = np.concatenate([dequant_rows_nvfp4(gu_codes[e][:I], gu_scales[e][:I], gs2[e, 0]),
+                               dequant_rows_nvfp4(gu_codes[e][I:], gu_scales[e][I:], gs2[e, 1])])
+        return w_gu, dequant_rows_nvfp4(dn_codes[e], dn_scales[e], ds2[e])
+
     def expert(e):
         rows, js = np.nonzero(sel == e)
-        w_gu = dq(gu_codes[e], gu_scales[e])  # [2I, K]
-        w_dn = dq(dn_codes[e], dn_scales[e])  # [K, I]
+        w_gu, w_dn = weights(e)               # [2I, K], [K, I]
         xe = x[tokens[rows]]                              # [n_e, K]
         g = xe @ w_gu[:I].T                               # [n_e, I]
         u = xe @ w_gu[I:].T
@@ -116,9 +157,10 @@ def pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens=N
     return out
 
 
-def moe_forward(x, topk_ids, topk_w, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None, fp4=False, workers=1):
+def moe_forward(x, topk_ids, topk_w, gu_codes, gu_scales, dn_codes, dn_scales, tokens=None, fp4=False, workers=1,
+                nvfp4=None):
     """y[t] = sum_j (ascending) w[t, j] * o_(t, j); f64 [len(tokens), K]."""
-    o = pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens, fp4, workers)
+    o = pair_outputs(x, topk_ids, gu_codes, gu_scales, dn_codes, dn_scales, tokens, fp4, workers, nvfp4)
     w = np.asarray(topk_w, dtype=np.float64)
     tokens = np.arange(o.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
     w = w[tokens]

@@ -1,0 +1,191 @@
+"""NVFP4 expert planes (moe_w4_pack_nvfp4 / moe_w4_unpack_nvfp4 / moe_w4_forward) through the C
+ABI, against the f64 oracle with W = e2m1 x e4m3 x scale_2 (README opening paragraph and bullet
+"FP4 recovery - used surgically"; "The v0.24.0 port", section "Our hooks", modelopt.py bullet).
+
+Bar: max |y_gpu - y_oracle| <= 1e-2 * rms(y_oracle) on the fp32 output, the bar stated for every
+float output of the forward. The weights enter the bf16 / fp16 matrix instructions exactly and x
+is bf16, so the gate and up sums carry only fp32 rounding; the one coarse step is the fp16 gated
+intermediate (unit roundoff 2^-11), whose error in output n is at most 2^-11 * sum_i |D_ni a_i|.
+The block scales drawn here span 11 octaves, so a few products dominate each output (max|y| is
+about 13 rms) and that bound reaches about half the bar: an f64 forward with only the
+intermediate rounded to fp16 is off by 5.1e-3 rms on the worst random shape below, as is the
+kernel. Pack/unpack is exact; decode organisations (direct, routed, sorted) on every shape, the
+routed and sorted organisations bit-identical."""
+import numpy as np
+import pytest
+import torch
+
+import bit_routed_expert_amd as moe
+from oracle import formats, forward as oracle_fwd
+import workloads
+
+from gpu_helpers import dev, dev_bf16, rel_max_err
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+NAMES = ("gu_codes", "gu_scales", "gu_scale2", "dn_codes", "dn_scales", "dn_scale2")
+
+
+def pack_nv(planes):
+    return moe.moe_w4_pack_nvfp4(*[dev(planes[n]) for n in NAMES])
+
+
+def _case(T, K, I, E, top_k, seed, zipf=False):
+    rng = np.random.default_rng(seed)
+    planes = workloads.draw_planes_nvfp4(rng, E, K, I)
+    x = workloads.draw_x(rng, T, K)
+    if zipf:
+        ids, w = workloads.zipf_routing(rng, T, E, top_k, rank_perm=rng.permutation(E))
+    else:
+        ids, w = workloads.uniform_routing(rng, T, E, top_k)
+    return dict(planes, x=x, topk_ids=ids, topk_w=w)
+
+
+def _oracle(c, tokens=None, workers=1):
+    return oracle_fwd.moe_forward(formats.bf16_bits_to_f64(c["x"]), c["topk_ids"], c["topk_w"], c["gu_codes"],
+                                  c["gu_scales"], c["dn_codes"], c["dn_scales"], tokens=tokens, workers=workers,
+                                  nvfp4=(c["gu_scale2"], c["dn_scale2"]))
+
+
+def _fwd(h, c, path, ws=None):
+    y = moe.moe_w4_forward(h, dev_bf16(c["x"]), dev(c["topk_ids"]), dev(c["topk_w"]), out_dtype=moe.OUT_F32,
+                           path=path, workspace=ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape", [(8, 256, 512), (3, 512, 768), (16, 768, 256)])
+def test_nvfp4_pack_unpack_roundtrip_is_exact(gpu, shape):
+    E, K, I = shape
+    planes = workloads.draw_planes_nvfp4(np.random.default_rng(E + K), E, K, I)
+    back = moe.moe_w4_unpack_nvfp4(pack_nv(planes))
+    for name, t in zip(NAMES, back):
+        got = t.cpu().numpy()
+        assert np.array_equal(got.view(np.uint8), planes[name].view(np.uint8)), name
+
+
+CASES = [
+    (1, 256, 512, 8, 1, 50, False, moe.PATH_DECODE),          # one pair: direct kernels
+    (3, 512, 512, 8, 2, 51, False, moe.PATH_DECODE),          # direct, 6 pairs
+    (4, 256, 512, 8, 2, 52, False, moe.PATH_DECODE),          # routed
+    (37, 512, 768, 16, 4, 53, False, moe.PATH_DECODE),        # routed, ragged chunk tails
+    (128, 512, 256, 4, 4, 54, True, moe.PATH_DECODE),         # 512 pairs on 4 experts
+    (60, 512, 512, 32, 8, 55, True, moe.PATH_DECODE_SORTED),
+    (5, 768, 256, 8, 2, 56, False, moe.PATH_DECODE_SORTED),   # sorted below the AUTO threshold
+    (200, 1024, 256, 32, 8, 57, True, moe.PATH_AUTO),         # 1600 pairs: sorted
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"T{c[0]}K{c[1]}I{c[2]}E{c[3]}k{c[4]}-p{c[7]}" for c in CASES])
+def test_nvfp4_parity(gpu, case):
+    T, K, I, E, k, seed, zipf, path = case
+    c = _case(T, K, I, E, k, seed, zipf)
+    h = pack_nv(c)
+    y = _fwd(h, c, path)
+    err = rel_max_err(y, _oracle(c))
+    print(f"nvfp4 {case}: rel max err {err:.2e}")
+    assert err <= TOL
+
+
+def test_nvfp4_every_finite_scale_encoding(gpu):
+    """Scale bytes over all 254 finite E4M3FN encodings (negative, zero, subnormal, 448), the
+    gate/up/down scale_2 of each expert apart: the weights are still exact in the kernels."""
+    rng = np.random.default_rng(58)
+    T, K, I, E, k = 24, 512, 512, 4, 2
+    c = _case(T, K, I, E, k, 58)
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+    for name in ("gu_scales", "dn_scales"):
+        c[name] = finite[rng.integers(0, 254, size=c[name].shape)]
+    h = pack_nv(c)
+    y_ref = _oracle(c)
+    for path in (moe.PATH_DECODE, moe.PATH_DECODE_SORTED):
+        err = rel_max_err(_fwd(h, c, path), y_ref)
+        print(f"all encodings path={path}: rel max err {err:.2e}")
+        assert err <= TOL
+
+
+def test_nvfp4_routed_and_sorted_agree_bit_identically_and_repeat(gpu):
+    c = _case(64, 512, 512, 8, 4, 59, zipf=True)
+    h = pack_nv(c)
+    a = _fwd(h, c, moe.PATH_DECODE)
+    b = _fwd(h, c, moe.PATH_DECODE_SORTED)
+    assert np.array_equal(a.view(np.int32), b.view(np.int32))
+    assert np.array_equal(a.view(np.int32), _fwd(h, c, moe.PATH_DECODE).view(np.int32))
+    assert rel_max_err(a, _oracle(c)) <= TOL
+
+
+def test_nvfp4_errors_and_invalid_ids(gpu):
+    c = _case(16, 256, 256, 8, 4, 60)
+    c["topk_ids"] = c["topk_ids"].copy()
+    c["topk_ids"][3, 2] = -1
+    c["topk_ids"][7, 0] = 99
+    h = pack_nv(c)
+    ws = moe.alloc_workspace(h, 16, 4)
+    y = _fwd(h, c, moe.PATH_DECODE, ws)
+    assert rel_max_err(y, _oracle(c)) <= TOL
+    inv, _ = moe.moe_w2_read_counters(ws)
+    assert inv == 2
+    with pytest.raises(moe.MoeW2Error) as ex:              # the GEMM kernels take no NVFP4 planes
+        _fwd(h, c, moe.PATH_GEMM)
+    assert ex.value.status == -2
+    with pytest.raises(moe.MoeW2Error):                    # MXFP4 / 2-bit unpack of NVFP4 planes
+        moe.moe_w4_unpack(h)
+    with pytest.raises(moe.MoeW2Error):
+        moe.moe_w2_unpack(h)
+    with pytest.raises(moe.MoeW2Error):                    # NVFP4 unpack of MXFP4 planes
+        moe.moe_w4_unpack_nvfp4(moe.moe_w4_pack(*[dev(workloads.draw_planes_fp4(np.random.default_rng(1), 2, 256, 256)[n])
+                                                  for n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")]))
+    for name, idx, bad in (("gu_scales", (1, 5, 0), 0x7F), ("dn_scales", (2, 7, 3), 0xFF)):
+        s = c[name].copy()
+        s[idx] = bad
+        with pytest.raises(moe.MoeW2Error) as ex:
+            pack_nv(dict(c, **{name: s}))
+        assert ex.value.status == -7
+    for name, idx in (("gu_scale2", (3, 1)), ("dn_scale2", (5,))):
+        for bad in (np.inf, np.nan):
+            s = c[name].copy()
+            s[idx] = bad
+            with pytest.raises(moe.MoeW2Error) as ex:
+                pack_nv(dict(c, **{name: s}))
+            assert ex.value.status == -7
+
+
+@pytest.mark.parametrize("T", [1, 8, 32, 96])
+def test_nvfp4_decode_full_shape_sampled_tokens(gpu, T):
+    """K=4096, I=2048 (the decode shape) with E=64 experts and uniform top-8 routing, AUTO path
+    (T = 96 is 768 pairs: the sorted organisation); tokens sampled for the f64 oracle."""
+    rng = np.random.default_rng(70 + T)
+    K, I, E = 4096, 2048, 64
+    planes = workloads.draw_planes_nvfp4(rng, E, K, I)
+    x = workloads.draw_x(rng, T, K)
+    ids, w = workloads.uniform_routing(rng, T, E, 8)
+    c = dict(planes, x=x, topk_ids=ids, topk_w=w)
+    h = pack_nv(c)
+    y = _fwd(h, c, moe.PATH_AUTO)
+    toks = np.unique(np.array([0, T // 2, T - 1]))
+    err = rel_max_err(y[toks], _oracle(c, tokens=toks, workers=4))
+    print(f"nvfp4 decode T={T}: tokens {toks.tolist()} rel max err {err:.2e}")
+    assert err <= TOL
+
+
+def _random_cases(n=8, seed=4096):
+    """Seeded random shapes: T in [1, 160], K and I multiples of 256 up to 1280, E in [1, 96],
+    top_k up to min(8, E), uniform or Zipf routing; the AUTO path (direct, routed or sorted)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 97))
+        top_k = int(rng.integers(1, min(8, E) + 1))
+        out.append((int(rng.integers(1, 161)), 256 * int(rng.integers(1, 6)), 256 * int(rng.integers(1, 6)), E, top_k,
+                    3000 + i, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"T{c[0]}K{c[1]}I{c[2]}E{c[3]}k{c[4]}{'z' if c[6] else 'u'}")
+def test_nvfp4_random_shapes_parity(gpu, case):
+    T, K, I, E, top_k, seed, zipf = case
+    c = _case(T, K, I, E, top_k, seed, zipf)
+    h = pack_nv(c)
+    err = rel_max_err(_fwd(h, c, moe.PATH_AUTO), _oracle(c))
+    print(f"{case}: rel max err {err:.2e}")
+    assert err <= TOL, (case, err)

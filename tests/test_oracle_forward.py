@@ -4,6 +4,7 @@ exact invariants."""
 import os
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import formats, forward
@@ -297,3 +298,92 @@ def test_brute_force_tiny_multi_expert():
     # a dropped term, a gate/up swap or a wrong expert would be off by orders of magnitude more
     assert np.max(np.abs(got[2] - float(w[2, 0]) * forward.pair_outputs(x, ids, gu_codes, gu_scales, dn_codes,
                                                                         dn_scales)[2, 0])) <= 1e-12 * rms
+
+
+def _dense_nvfp4_independent(packed, scale_bytes, scale2):
+    """NVFP4 weights from the e2m1 bit-field definition element by element, torch's float8_e4m3fn
+    for the block-16 scales and an fp32 scale_2 (README opening paragraph; "The v0.24.0 port",
+    section "Our hooks", modelopt.py bullet)."""
+    p = np.asarray(packed)
+    rows, nb = p.shape
+    out = np.zeros((rows, nb * 2))
+    sb = torch.from_numpy(np.ascontiguousarray(scale_bytes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    s = sb.to(torch.float64).numpy()
+    for r in range(rows):
+        for k in range(nb * 2):
+            nib = (int(p[r, k // 2]) >> (4 * (k % 2))) & 15
+            out[r, k] = formats.e2m1_value(nib) * s[r, k // 16] * float(np.float32(scale2))
+    return out
+
+
+def test_nvfp4_dequant_covers_every_finite_scale_encoding():
+    """Every finite E4M3FN scale byte (both signs, zero, subnormals, 448) against torch's
+    float8_e4m3fn decode, and NaN scale bytes / a non-finite scale_2 are refused."""
+    rng = np.random.default_rng(31)
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+    scales = rng.permutation(np.concatenate([finite, finite])).reshape(4, 127)
+    codes = rng.integers(0, 256, size=(4, 127 * 8), dtype=np.uint8)
+    got = forward.dequant_rows_nvfp4(codes, scales, np.float32(3.0517578125e-05))
+    assert np.array_equal(got, _dense_nvfp4_independent(codes, scales, np.float32(3.0517578125e-05)))
+    for bad in (0x7F, 0xFF):
+        s = scales.copy()
+        s[3, 5] = bad
+        with pytest.raises(ValueError):
+            forward.dequant_rows_nvfp4(codes, s, 1.0)
+    with pytest.raises(ValueError):
+        forward.dequant_rows_nvfp4(codes, scales, np.inf)
+
+
+def test_nvfp4_single_expert_top1_is_dense_silu_mlp():
+    """NVFP4 experts, E = 1, top-1: the dense gated MLP with torch's silu and matmul in float64 on
+    independently dequantized weights; gate, up and down carry different scale_2 values, so a
+    swapped or shared scale_2 fails."""
+    rng = np.random.default_rng(32)
+    T, K, I = 5, 64, 64
+    planes = workloads.draw_planes_nvfp4(rng, 1, K, I)
+    planes["gu_scale2"] = np.array([[2.0 ** -14, 3.0 * 2.0 ** -13]], np.float32)
+    planes["dn_scale2"] = np.array([5.0 * 2.0 ** -15], np.float32)
+    x = formats.bf16_bits_to_f64(workloads.draw_x(rng, T, K))
+    y = forward.moe_forward(x, np.zeros((T, 1), np.int32), np.ones((T, 1), np.float32), planes["gu_codes"],
+                            planes["gu_scales"], planes["dn_codes"], planes["dn_scales"],
+                            nvfp4=(planes["gu_scale2"], planes["dn_scale2"]))
+    g = _dense_nvfp4_independent(planes["gu_codes"][0][:I], planes["gu_scales"][0][:I], planes["gu_scale2"][0, 0])
+    u = _dense_nvfp4_independent(planes["gu_codes"][0][I:], planes["gu_scales"][0][I:], planes["gu_scale2"][0, 1])
+    d = _dense_nvfp4_independent(planes["dn_codes"][0], planes["dn_scales"][0], planes["dn_scale2"][0])
+    xt = torch.from_numpy(x)
+    ref = torch.matmul(torch.nn.functional.silu(torch.matmul(xt, torch.from_numpy(g).T)) *
+                       torch.matmul(xt, torch.from_numpy(u).T), torch.from_numpy(d).T).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_nvfp4_with_power_of_two_pair_scales_is_mxfp4():
+    """Special case: when each 32-block's two E4M3 scales are the same power of two 2^(b-127)
+    (byte ((b - 120) << 3)) and every scale_2 is 1, the NVFP4 forward is the MXFP4 forward with
+    UE8M0 bytes b, exactly."""
+    rng = np.random.default_rng(33)
+    T, K, I, E = 6, 64, 96, 3
+    fp4 = workloads.draw_planes_fp4(rng, E, K, I)
+    for name in ("gu_scales", "dn_scales"):
+        fp4[name] = (127 + rng.integers(-6, 8, size=fp4[name].shape)).astype(np.uint8)
+    to_e4m3 = lambda b: np.repeat(((b.astype(np.int32) - 120) << 3).astype(np.uint8), 2, axis=-1)
+    x = formats.bf16_bits_to_f64(workloads.draw_x(rng, T, K))
+    ids, w = workloads.uniform_routing(rng, T, E, 2)
+    y4 = forward.moe_forward(x, ids, w, **fp4, fp4=True)
+    ynv = forward.moe_forward(x, ids, w, fp4["gu_codes"], to_e4m3(fp4["gu_scales"]), fp4["dn_codes"],
+                              to_e4m3(fp4["dn_scales"]), nvfp4=(np.ones((E, 2), np.float32), np.ones(E, np.float32)))
+    assert np.array_equal(y4, ynv)
+
+
+def test_nvfp4_down_scale2_and_scale_sign_invariants_are_exact():
+    """Doubling every down scale_2 doubles y; flipping the sign bit of every down E4M3 scale
+    negates y; both exactly."""
+    rng = np.random.default_rng(34)
+    T, K, I, E = 7, 64, 64, 3
+    p = workloads.draw_planes_nvfp4(rng, E, K, I)
+    x = formats.bf16_bits_to_f64(workloads.draw_x(rng, T, K))
+    ids, w = workloads.uniform_routing(rng, T, E, 2)
+    fwd = lambda dn_scales, dn_scale2: forward.moe_forward(x, ids, w, p["gu_codes"], p["gu_scales"], p["dn_codes"],
+                                                          dn_scales, nvfp4=(p["gu_scale2"], dn_scale2))
+    y = fwd(p["dn_scales"], p["dn_scale2"])
+    assert np.array_equal(fwd(p["dn_scales"], 2 * p["dn_scale2"]), 2 * y)
+    assert np.array_equal(fwd(p["dn_scales"] ^ np.uint8(0x80), p["dn_scale2"]), -y)

@@ -50,6 +50,22 @@ def draw_planes_fp4(rng, E, K, I):
     return dict(gu_codes=gu_codes, gu_scales=gu_scales, dn_codes=dn_codes, dn_scales=dn_scales)
 
 
+def draw_planes_nvfp4(rng, E, K, I):
+    """Canonical NVFP4 planes of one layer, drawn in this order: gate_up codes [E, 2I, K/2]
+    (uniform bytes = two independent uniform e2m1 nibbles), gate_up E4M3FN scale bytes
+    [E, 2I, K/16] uniform in 0x28..0x7E (the positive normal values 2^-2 .. 448, the range a
+    block scale amax/6/scale_2 takes), gate_up scale_2 [E, 2] = fp32(U[2e-5, 1e-4]) (gate, up),
+    down codes [E, K, I/2], down scale bytes [E, K, I/16] as above, down scale_2 [E] as above."""
+    gu_codes = rng.integers(0, 256, size=(E, 2 * I, K // 2), dtype=np.uint8)
+    gu_scales = rng.integers(0x28, 0x7F, size=(E, 2 * I, K // 16), dtype=np.uint8)
+    gu_scale2 = rng.uniform(2e-5, 1e-4, size=(E, 2)).astype(np.float32)
+    dn_codes = rng.integers(0, 256, size=(E, K, I // 2), dtype=np.uint8)
+    dn_scales = rng.integers(0x28, 0x7F, size=(E, K, I // 16), dtype=np.uint8)
+    dn_scale2 = rng.uniform(2e-5, 1e-4, size=(E,)).astype(np.float32)
+    return dict(gu_codes=gu_codes, gu_scales=gu_scales, gu_scale2=gu_scale2, dn_codes=dn_codes,
+                dn_scales=dn_scales, dn_scale2=dn_scale2)
+
+
 def _softmax_f32(logits):
     z = logits.astype(np.float64)
     z = z - z.max(axis=-1, keepdims=True)
