@@ -26,6 +26,7 @@ The JSON line also carries:
   zipf_decode   - the 64-token Zipf-routed decode batch at K=6144: time, active experts, HBM rate;
   slots         - the expert-slot forward against the plain forward at T=8 and 32;
   w4            - the FP4 (MXFP4) expert planes: decode at T=1, 8, 32 and the prefill GEMMs;
+  nvfp4         - the NVFP4 expert planes (e2m1, E4M3 per 16, fp32 scale_2): decode at T=1, 8, 32;
   requant       - the three load-time re-quantizers (NVFP4, FP8 block-128, MXFP4) over 256 tensors;
   sweep         - the sign-bias diagnostic: 8 synthetic expert tensors of [2048, 6144] against all
                   1239 candidate codebooks, with the symmetric / asymmetric statistics it finds;
@@ -339,6 +340,7 @@ def main():
         out["slots"] = bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K)
     if not args.no_w4:
         out["w4"] = bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I)
+        out["nvfp4"] = bench_nvfp4(args, moe, workloads, torch, dev, inst, E, top_k, K, I)
     zipf_host = None
     if not args.no_prefill:
         out["prefill"], out["zipf_decode"], zipf_host = bench_prefill(args, moe, workloads, torch, dev)
@@ -488,18 +490,15 @@ def w4_expert_bytes(K, I):
     return 2 * I * K // 2 + 2 * I * K // 32, K * I // 2 + K * I // 32
 
 
-def bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I):
-    """FP4 expert planes on the decode workload (same routing instances and x as the 2-bit decode
-    leg; two plane copies alternated), each T timed as a graph of back-to-back forwards; and the
-    prefill GEMM stages on the 8192-token Zipf workload."""
-    rng = np.random.default_rng(12)
-    layers = []
-    for _ in range(2):
-        canon = workloads.draw_planes_fp4(rng, E, K, I)
-        layers.append(moe.moe_w4_pack(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")]))
-        del canon
-    torch.cuda.empty_cache()
-    gu_b, dn_b = w4_expert_bytes(K, I)
+def nvfp4_expert_bytes(K, I):
+    """Bytes of one expert's NVFP4 planes: e2m1 codes (4 bits) + one E4M3 byte per 16 weights
+    (scale_2, 12 bytes per expert, is left out)."""
+    return 2 * I * K // 2 + 2 * I * K // 16, K * I // 2 + K * I // 16
+
+
+def time_decode_layers(args, moe, torch, layers, inst, E, top_k, K, gu_b, dn_b):
+    """Per decode T: back-to-back moe_w4_forward calls over the routing instances (two plane
+    copies alternated) captured in one graph; returns ({"T<n>": ...}, total microseconds)."""
     stream = torch.cuda.current_stream()
     n_rep = max(2, args.steps)
     res, total_us = {}, 0.0
@@ -507,7 +506,6 @@ def bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I):
         R = len(inst[T])
         ws = [moe.alloc_workspace(layers[0], T, top_k) for _ in range(R)]
         y = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
-        nbytes = 0
         def loop():
             nb = 0
             for k in range(n_rep):
@@ -529,9 +527,25 @@ def bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I):
         torch.cuda.synchronize()
         ms = a0.elapsed_time(a1) / n_rep
         total_us += ms * 1e3
-        res[f"T{T}"] = dict(fwd_us=round(ms * 1e3, 2), fwd_hbm_GBps=round(nbytes / n_rep / (ms * 1e-3) / 1e9, 1),
-                            tokens_per_s=round(T / (ms * 1e-3), 1))
+        gbps = nbytes / n_rep / (ms * 1e-3) / 1e9
+        res[f"T{T}"] = dict(fwd_us=round(ms * 1e3, 2), fwd_hbm_GBps=round(gbps, 1),
+                            fwd_hbm_frac=round(gbps / HBM_PEAK_GBPS, 3), tokens_per_s=round(T / (ms * 1e-3), 1))
         del ws
+    return res, total_us
+
+
+def bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I):
+    """FP4 expert planes on the decode workload (same routing instances and x as the 2-bit decode
+    leg; two plane copies alternated), each T timed as a graph of back-to-back forwards; and the
+    prefill GEMM stages on the 8192-token Zipf workload."""
+    rng = np.random.default_rng(12)
+    layers = []
+    for _ in range(2):
+        canon = workloads.draw_planes_fp4(rng, E, K, I)
+        layers.append(moe.moe_w4_pack(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")]))
+        del canon
+    torch.cuda.empty_cache()
+    res, total_us = time_decode_layers(args, moe, torch, layers, inst, E, top_k, K, *w4_expert_bytes(K, I))
     for h in layers:
         h.free()
     torch.cuda.empty_cache()
@@ -540,6 +554,25 @@ def bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I):
     if not args.no_prefill:
         out["prefill"] = bench_prefill(args, moe, workloads, torch, dev, fp4=True)
     return out
+
+
+def bench_nvfp4(args, moe, workloads, torch, dev, inst, E, top_k, K, I):
+    """NVFP4 expert planes (e2m1 + E4M3/16 + fp32 scale_2) on the decode workload, as bench_w4."""
+    rng = np.random.default_rng(13)
+    names = ("gu_codes", "gu_scales", "gu_scale2", "dn_codes", "dn_scales", "dn_scale2")
+    layers = []
+    for _ in range(2):
+        canon = workloads.draw_planes_nvfp4(rng, E, K, I)
+        layers.append(moe.moe_w4_pack_nvfp4(*[dev(canon[k]) for k in names]))
+        del canon
+    torch.cuda.empty_cache()
+    res, total_us = time_decode_layers(args, moe, torch, layers, inst, E, top_k, K, *nvfp4_expert_bytes(K, I))
+    for h in layers:
+        h.free()
+    torch.cuda.empty_cache()
+    return dict(workload="moe_w4 (NVFP4 e2m1 + E4M3/16 + fp32 scale_2 experts) decode: K=4096 I=2048 E=256 "
+                         "top-8 uniform routing, T=1,8,32",
+                decode_tokens_per_s=round(sum(DECODE_TS) / (total_us * 1e-6), 1), **res)
 
 
 def bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K):

@@ -359,13 +359,14 @@ MOEW2_DEV bf16x8_t nv4_b_bf16(uint32_t codes, uint32_t sw) {
 // e4m3 value s (it uses only its scale operand's exponent), a packed fp16 multiply the signed
 // mantissa factor f = s / 2^E, |f| in [1, 2) (3 fraction bits at most). Both steps are exact:
 // |e2m1 x 2^E| lies in [2^-10, 1536] and the product in [2^-10, 2688], inside fp16's normal
-// range, with at most 6 significant bits. A zero scale gives zeros.
+// range, with at most 6 significant bits. 2^E and 2^-E are formed from s's exponent field
+// (E in [-9, 8]); a zero scale takes 2^E = 2^-126 and f = 0, which gives zeros.
 template <int J>
 MOEW2_DEV f16x8_t nv4_b_f16(uint32_t codes, uint32_t sw) {
   const float s = __builtin_amdgcn_cvt_f32_fp8((int)sw, J);
-  const bool zero = s == 0.f;
-  const float p2 = zero ? 1.f : __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, s) & 0x7F800000u);
-  const _Float16 m = zero ? (_Float16)0.f : (_Float16)(s / p2);
+  const uint32_t eb = __builtin_bit_cast(uint32_t, s) & 0x7F800000u;
+  const float p2 = __builtin_bit_cast(float, eb > 0x00800000u ? eb : 0x00800000u);
+  const _Float16 m = (_Float16)(s * __builtin_bit_cast(float, 0x7F000000u - eb));
   const f16x2_t mm = {m, m};
   f16x8_t r;
   static_for<0, 4>([&](auto qc) {
