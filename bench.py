@@ -26,7 +26,8 @@ The JSON line also carries:
   zipf_decode   - the 64-token Zipf-routed decode batch at K=6144: time, active experts, HBM rate;
   slots         - the expert-slot forward against the plain forward at T=8 and 32;
   w4            - the FP4 (MXFP4) expert planes: decode at T=1, 8, 32 and the prefill GEMMs;
-  nvfp4         - the NVFP4 expert planes (e2m1, E4M3 per 16, fp32 scale_2): decode at T=1, 8, 32;
+  nvfp4         - the NVFP4 expert planes (e2m1, E4M3 per 16, fp32 scale_2): decode at T=1, 8, 32 and
+                  the prefill GEMMs;
   requant       - the three load-time re-quantizers (NVFP4, FP8 block-128, MXFP4) over 256 tensors;
   sweep         - the sign-bias diagnostic: 8 synthetic expert tensors of [2048, 6144] against all
                   1239 candidate codebooks, with the symmetric / asymmetric statistics it finds;
@@ -552,7 +553,7 @@ def bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I):
     out = dict(workload="moe_w4 (FP4 e2m1 + UE8M0/32 experts) decode: K=4096 I=2048 E=256 top-8 uniform "
                         "routing, T=1,8,32", decode_tokens_per_s=round(sum(DECODE_TS) / (total_us * 1e-6), 1), **res)
     if not args.no_prefill:
-        out["prefill"] = bench_prefill(args, moe, workloads, torch, dev, fp4=True)
+        out["prefill"] = bench_prefill(args, moe, workloads, torch, dev, fmt="w4")
     return out
 
 
@@ -570,9 +571,12 @@ def bench_nvfp4(args, moe, workloads, torch, dev, inst, E, top_k, K, I):
     for h in layers:
         h.free()
     torch.cuda.empty_cache()
-    return dict(workload="moe_w4 (NVFP4 e2m1 + E4M3/16 + fp32 scale_2 experts) decode: K=4096 I=2048 E=256 "
-                         "top-8 uniform routing, T=1,8,32",
-                decode_tokens_per_s=round(sum(DECODE_TS) / (total_us * 1e-6), 1), **res)
+    out = dict(workload="moe_w4 (NVFP4 e2m1 + E4M3/16 + fp32 scale_2 experts) decode: K=4096 I=2048 E=256 "
+                        "top-8 uniform routing, T=1,8,32",
+               decode_tokens_per_s=round(sum(DECODE_TS) / (total_us * 1e-6), 1), **res)
+    if not args.no_prefill:
+        out["prefill"] = bench_prefill(args, moe, workloads, torch, dev, fmt="nvfp4")
+    return out
 
 
 def bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K):
@@ -640,13 +644,20 @@ def bench_slots(args, moe, torch, dev, canon, inst, E, top_k, K):
                          "resident in permuted slots", **res)
 
 
-def bench_prefill(args, moe, workloads, torch, dev, fp4=False, zipf=True):
+def bench_prefill(args, moe, workloads, torch, dev, fmt="w2", zipf=True):
+    """The 8192-token prefill layer (Zipf(1.1) routing) on planes of the given format: "w2" (2-bit),
+    "w4" (MXFP4) or "nvfp4"; per-stage times and matrix-core rates."""
     c = workloads.PREFILL
     T, K, I, E, top_k = c["T"], c["K"], c["I"], c["E"], c["top_k"]
     host = None
-    if fp4:
+    fp4 = fmt != "w2"
+    if fmt == "w4":
         canon = workloads.draw_planes_fp4(np.random.default_rng(13), E, K, I)
         planes = moe.moe_w4_pack(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")])
+    elif fmt == "nvfp4":
+        canon = workloads.draw_planes_nvfp4(np.random.default_rng(14), E, K, I)
+        planes = moe.moe_w4_pack_nvfp4(*[dev(canon[k]) for k in ("gu_codes", "gu_scales", "gu_scale2", "dn_codes",
+                                                                  "dn_scales", "dn_scale2")])
     else:
         canon = workloads.zipf_layer(c["seed"], K, I, E)
         dcanon = [dev(canon[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")]
@@ -694,8 +705,9 @@ def bench_prefill(args, moe, workloads, torch, dev, fp4=False, zipf=True):
         del dcanon
     del planes
     torch.cuda.empty_cache()
+    label = {"w2": "moe_w2", "w4": "moe_w4 (FP4)", "nvfp4": "moe_w4 (NVFP4)"}[fmt]
     res = dict(
-        workload=("moe_w4 (FP4)" if fp4 else "moe_w2") + " prefill: T=8192 K=6144 I=2048 E=256 top-8 Zipf(1.1)",
+        workload=label + " prefill: T=8192 K=6144 I=2048 E=256 top-8 Zipf(1.1)",
         tokens_per_s=round(T / (fwd * 1e-3), 1), fwd_ms=round(float(fwd), 4),
         route_ms=round(float(rt), 4), gate_up_ms=round(float(gu), 4), down_ms=round(float(dn), 4),
         combine_ms=round(float(cb), 4),
@@ -703,14 +715,23 @@ def bench_prefill(args, moe, workloads, torch, dev, fp4=False, zipf=True):
         gemm_tflops=round(gemm_tflops, 1), gemm_mfma_frac=round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         fwd_tflops=round(fwd_tflops, 1), fwd_mfma_frac=round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         peak_tflops=MFMA_BF16_PEAK_TFLOPS,
+        iters=args.prefill_iters)
+    if fmt == "nvfp4":
+        # the 16 x 16 x 32 bf16 / fp16 instructions, one per product: instruction flops are the
+        # algorithmic ones, against the same dense bf16 / fp16 peak
+        res.update(gemm_instr_tflops=round(gemm_tflops, 1), gemm_instr_frac=round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                   instr_peak_tflops=MFMA_BF16_PEAK_TFLOPS,
+                   frac_note="bf16 (gate_up) and fp16 (down) instructions with the weights formed in registers: "
+                             "instruction flops = algorithmic flops (2*P*3*I*K), against the dense bf16/fp16 peak")
+    else:
         # the instructions actually issued: fp6 (e2m3) activations x fp4 weights, three activation
         # parts per product, against the dense fp6 / fp4 matrix peak
-        gemm_instr_tflops=round(A_PARTS * gemm_tflops, 1),
-        gemm_instr_frac=round(A_PARTS * gemm_tflops / MFMA_FP6_PEAK_TFLOPS, 4),
-        instr_peak_tflops=MFMA_FP6_PEAK_TFLOPS,
-        frac_note=("mfma_frac: algorithmic flops (2*P*3*I*K) per second against the dense bf16 peak; "
-                   "instr_frac: the fp6 x fp4 instruction flops issued (3 parts) against the dense fp6/fp4 peak"),
-        iters=args.prefill_iters)
+        res.update(gemm_instr_tflops=round(A_PARTS * gemm_tflops, 1),
+                   gemm_instr_frac=round(A_PARTS * gemm_tflops / MFMA_FP6_PEAK_TFLOPS, 4),
+                   instr_peak_tflops=MFMA_FP6_PEAK_TFLOPS,
+                   frac_note=("mfma_frac: algorithmic flops (2*P*3*I*K) per second against the dense bf16 peak; "
+                              "instr_frac: the fp6 x fp4 instruction flops issued (3 parts) against the dense "
+                              "fp6/fp4 peak"))
     return (res, zipf_decode, host) if not fp4 else res
 
 

@@ -96,7 +96,6 @@ static int forward_check(const moe_w2_planes* p, int T, int top_k, const void* x
   if (path != MOE_W2_PATH_AUTO && path != MOE_W2_PATH_DECODE && path != MOE_W2_PATH_GEMM &&
       path != MOE_W2_PATH_DECODE_SORTED)
     return MOE_W2_EINVAL;
-  if (p->fmt == kFmtNV4 && path == MOE_W2_PATH_GEMM) return MOE_W2_EUNSUPPORTED;   // decode kernels only
   if (T > 0 && (!x || !topk_ids || !topk_w || !y)) return MOE_W2_EINVAL;
   if (!pairs_ok(T, top_k)) return MOE_W2_EUNSUPPORTED;
   if ((long long)T * p->K >= (1LL << 31) || (long long)T * top_k * p->I >= (1LL << 31))
@@ -109,17 +108,13 @@ static int forward_check(const moe_w2_planes* p, int T, int top_k, const void* x
   // every decode workgroup of the routed organisation scans all ids itself (two per thread)
   if (path == MOE_W2_PATH_DECODE && (long long)T * top_k > kDecodeMaxPairs) return MOE_W2_EUNSUPPORTED;
   // the sorted organisation launches one workgroup row per chunk (grid rows are 16-bit)
-  if (ws.max_chunks > 65535 &&
-      (path == MOE_W2_PATH_DECODE_SORTED || (p->fmt == kFmtNV4 && (long long)T * top_k > kDecodeMaxPairs)))
-    return MOE_W2_EUNSUPPORTED;
+  if (ws.max_chunks > 65535 && path == MOE_W2_PATH_DECODE_SORTED) return MOE_W2_EUNSUPPORTED;
   return MOE_W2_OK;
 }
 
-// Kernel family of a forward: -1 = grouped GEMMs, else the decode organisation. NVFP4 planes
-// run on the decode kernels at every size (the sorted organisation above kDecodeMaxPairs).
-static int decode_mode(int path, int P, int fmt) {
-  if (path == MOE_W2_PATH_GEMM) return -1;
-  if (path == MOE_W2_PATH_AUTO && P > kDecodeMaxPairs) return fmt == kFmtNV4 ? kDecodeSorted : -1;
+// Kernel family of a forward: -1 = grouped GEMMs, else the decode organisation.
+static int decode_mode(int path, int P) {
+  if (path == MOE_W2_PATH_GEMM || (path == MOE_W2_PATH_AUTO && P > kDecodeMaxPairs)) return -1;
   if (path == MOE_W2_PATH_DECODE_SORTED) return kDecodeSorted;
   if (P <= kDirectMaxPairs) return kDecodeDirect;
   if (path == MOE_W2_PATH_AUTO && P >= kSortedMinPairs) return kDecodeSorted;
@@ -299,7 +294,7 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
   if (T == 0) return MOE_W2_OK;
   hipStream_t s = (hipStream_t)stream;
   uint8_t* wsb = (uint8_t*)workspace;
-  const int mode = decode_mode(path, T * top_k, p->fmt);
+  const int mode = decode_mode(path, T * top_k);
   const bool decode = mode >= 0;
   // the routed and direct decode organisations find their pairs from the ids themselves (no
   // routing pass); the direct organisation also combines inside the down stage

@@ -121,11 +121,12 @@ MOEW2_DEV void a_sources(uint32_t (&off)[AT::kPerWave], int w, int lane, RowOff 
 }
 
 // B: the kRGW row groups of a wave, one native k-tile (code loads per row group: 1 for 2-bit
-// codes, 2 for fp4 codes)
+// codes, 2 for fp4 codes; scale words per row group: one with the two UE8M0 bytes, or two of four
+// e4m3 bytes for NVFP4 planes)
 template <int FMT>
 struct BRegs {
   u32x4_t c[kRGW][WFmt<FMT>::kLoads];
-  uint32_t s[kRGW];
+  uint32_t s[kRGW][WFmt<FMT>::kScaleWords];
 };
 template <int FMT>
 constexpr int kBLoads = kRGW * (WFmt<FMT>::kLoads + 1);   // vector memory instructions for one BRegs
@@ -165,10 +166,16 @@ struct KLoads {
       constexpr int L = WFmt<FMT>::kLoads;
       constexpr int n = N - AT::kPerWave, t = n / (L + 1), q = n % (L + 1);
       const size_t ti = tb0 + (size_t)t * nkt + kb;
-      if constexpr (q < L)
+      if constexpr (q < L) {
         r.c[t][q] = ld16(codes + ti * WFmt<FMT>::kCodeBytes + 1024 * q + 16 * lane);
-      else
-        r.s[t] = *reinterpret_cast<const uint16_t*>(scales + ti * kTileScaleBytes + 2 * lane);
+      } else if constexpr (FMT == kFmtNV4) {
+        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(scales + ti * kTileScaleBytesNV4 +
+                                                              128 * (lane >> 5) + 8 * (lane & 15));
+        r.s[t][0] = v[0];
+        r.s[t][1] = v[1];
+      } else {
+        r.s[t][0] = *reinterpret_cast<const uint16_t*>(scales + ti * kTileScaleBytes + 2 * lane);
+      }
     }
   }
   template <int N0, int N1>
@@ -306,11 +313,11 @@ MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][kRGW], const uint8_t* abuf, const BReg
       // a row tile with no valid row (the ragged end of an expert's group) skips its instructions
       if (mma && 16 * m < rows_valid) {
 #pragma unroll
-        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<0, C>(cur.p[0], bo[t], acc[m][t], cur.s, br.s[t]);
+        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<0, C>(cur.p[0], bo[t], acc[m][t], cur.s, br.s[t][0]);
 #pragma unroll
-        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<1, C>(cur.p[1], bo[t], acc[m][t], cur.s, br.s[t]);
+        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<1, C>(cur.p[1], bo[t], acc[m][t], cur.s, br.s[t][0]);
 #pragma unroll
-        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<2, C>(cur.p[2], bo[t], acc[m][t], cur.s, br.s[t]);
+        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<2, C>(cur.p[2], bo[t], acc[m][t], cur.s, br.s[t][0]);
       }
       if constexpr (m < 3) cur = nxt;
     });
@@ -487,6 +494,168 @@ gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// NVFP4 planes (e2m1 codes, one E4M3 scale per 16 values, fp32 scale_2 per tensor; layout in
+// common.h). Their block-16 scales carry mantissa bits, which the block-scaled instruction's
+// UE8M0 scales cannot, so these GEMMs run on the 16 x 16 x 32 bf16 (gate_up: A = x as it is) and
+// fp16 (down: A = the fp16 gated intermediate) instructions, each B operand of 8 weights formed
+// exactly in registers from its codes and scale byte (nv4_b_bf16 / nv4_b_f16); scale_2 multiplies
+// the fp32 results. A needs no split pass: a stage holds BM rows of 256 16-bit values, filled by
+// direct global -> LDS loads straight from x (gathered through the sort permutation) or from the
+// gate_up epilogue's fp16 rows in sorted order. The k-loop, tile map, B register rotation and
+// counted waits are the ones above.
+// ------------------------------------------------------------------------------------------------
+constexpr int kN4Src = kTileK * 2 / 16;        // 32 chunks: one (row, k-tile) of 16-bit values
+constexpr int kN4Stride = 16 * (kN4Src + 1);   // LDS row stride 528 bytes (132 dwords, 4 mod 16)
+using N4Tile = ATile<kN4Src + 1, kN4Src>;
+
+// One k-tile: instruction J = 4C + j reduces values 32J .. 32J + 31; lane l's A operand is the
+// 16 bytes of values 32J + 8(l/16) .. + 7 of row l % 16 of each row tile, its B operand dword j of
+// half C of its code loads with scale byte j of scale word C. Per J: the wave's kRGW B operands,
+// then 4 row tiles x kRGW instructions (same accumulator 16 instructions apart); the step's load
+// group J goes out with it.
+template <int NP, class Part>
+MOEW2_DEV void nv4_ktile(f32x4_t (&acc)[4][kRGW], const uint8_t* abuf, const BRegs<kFmtNV4>& br, Part part,
+                         bool mma, int rows_valid, int lane) {
+  const uint8_t* arow = abuf + (lane & 15) * kN4Stride + 16 * (lane >> 4);
+  static_for<0, 8>([&](auto jc) {
+    constexpr int J = decltype(jc)::value, C = J / 4, j = J % 4;
+    typedef std::conditional_t<NP == 0, bf16x8_t, f16x8_t> BOp;
+    BOp bo[kRGW];
+#pragma unroll
+    for (int t = 0; t < kRGW; ++t) {
+      if constexpr (NP == 0) bo[t] = nv4_b_bf16<j>(br.c[t][C][j], br.s[t][C]);
+      else bo[t] = nv4_b_f16<j>(br.c[t][C][j], br.s[t][C]);
+    }
+    u32x4_t cur = *reinterpret_cast<const u32x4_t*>(arow + 64 * J), nxt;
+    part(std::integral_constant<int, J>());
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, 4>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < 3) nxt = *reinterpret_cast<const u32x4_t*>(arow + (m + 1) * 16 * kN4Stride + 64 * J);
+      if (mma && 16 * m < rows_valid) {
+#pragma unroll
+        for (int t = 0; t < kRGW; ++t) {
+          if constexpr (NP == 0) acc[m][t] = mfma32_bf16(cur, bo[t], acc[m][t]);
+          else acc[m][t] = mfma32_f16(cur, bo[t], acc[m][t]);
+        }
+      }
+      if constexpr (m < 3) cur = nxt;
+    });
+  });
+}
+
+// gate_up on NVFP4 planes: A = x rows gathered through the sort permutation; the epilogue writes
+// a = silu(sg g) (su u) in fp16 to the sorted rows of the intermediate ([sorted row][I]), which
+// the down GEMM reads as its A records.
+__global__ void __launch_bounds__(kThreads, kWgPerCu)
+gemm_gate_up_nv4_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                        const float* __restrict__ scale2, const uint16_t* __restrict__ x,
+                        const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+                        const int32_t* __restrict__ tiles, const int32_t* __restrict__ meta,
+                        _Float16* __restrict__ act, long long* __restrict__ counters, int K, int I, int top_k,
+                        int n_blocks) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const TileMap tm = map_tile(tiles, meta, offsets, n_blocks);
+  if (!tm.live) return;
+  const int e = tm.e, rs = tm.rs, rows_valid = tm.rows_valid;
+  const int nkt = K / kTileK, nrg = 2 * I / kTileRows;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg0 = kRGW * (tm.nb * kWaves + w);
+  const bool wave_active = rg0 < nrg;
+  const size_t tb0 = (size_t)e * nrg * nkt + (size_t)(wave_active ? rg0 : 0) * nkt;
+
+  uint32_t aoff[N4Tile::kPerWave];
+  a_sources<N4Tile>(aoff, w, lane, [&](int r) {
+    const int tok = perm[rs + min(r, rows_valid - 1)] / top_k;
+    return (uint32_t)tok * (uint32_t)(nkt * N4Tile::kSrcBytes);
+  });
+
+  f32x4_t acc[4][kRGW];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < kRGW; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const KLoads<N4Tile, kFmtNV4> ld{reinterpret_cast<const uint8_t*>(x), aoff, codes, scales, tb0, nkt, w, lane};
+  k_loop(lds, ld, nkt, wave_active, [&](const uint8_t* abuf, const BRegs<kFmtNV4>& br, auto part, bool mma) {
+    nv4_ktile<0>(acc, abuf, br, part, mma, rows_valid, lane);
+  });
+  if (!wave_active) return;
+
+  // ---- epilogue: gated columns 16 (rg0 / 2 + pr) + lane % 16 of rows 16 m + 4 (lane / 16) + r ----
+  const float sg = scale2[3 * e], su = scale2[3 * e + 1];
+  unsigned n_inf = 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m * 16 + 4 * (lane >> 4) + r;
+      if (row >= rows_valid) continue;
+#pragma unroll
+      for (int pr = 0; pr < kRGW / 2; ++pr) {
+        const _Float16 h = (_Float16)silu_mul(acc[m][2 * pr][r] * sg, acc[m][2 * pr + 1][r] * su);
+        n_inf += __builtin_isinf((float)h) ? 1u : 0u;
+        act[(size_t)(rs + row) * I + 16 * (rg0 / 2 + pr) + (lane & 15)] = h;
+      }
+    }
+  }
+  if (n_inf) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)n_inf);
+}
+
+// down on NVFP4 planes: A = the fp16 gated rows in sorted order; per-pair fp32 rows out, times the
+// down tensor's scale_2.
+__global__ void __launch_bounds__(kThreads, kWgPerCu)
+gemm_down_nv4_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                     const float* __restrict__ scale2, const _Float16* __restrict__ act,
+                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+                     const int32_t* __restrict__ tiles, const int32_t* __restrict__ meta,
+                     float* __restrict__ pair_out, int K, int I, int n_blocks) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const TileMap tm = map_tile(tiles, meta, offsets, n_blocks);
+  if (!tm.live) return;
+  const int e = tm.e, rs = tm.rs, rows_valid = tm.rows_valid;
+  const int nkt = I / kTileK, nrg = K / kTileRows;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg0 = kRGW * (tm.nb * kWaves + w);
+  const bool wave_active = rg0 < nrg;
+  const size_t tb0 = (size_t)e * nrg * nkt + (size_t)(wave_active ? rg0 : 0) * nkt;
+
+  uint32_t aoff[N4Tile::kPerWave];
+  a_sources<N4Tile>(aoff, w, lane, [&](int r) {
+    return (uint32_t)(rs + min(r, rows_valid - 1)) * (uint32_t)(nkt * N4Tile::kSrcBytes);
+  });
+
+  f32x4_t acc[4][kRGW];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < kRGW; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  __shared__ int tile_pairs[BM];
+  if (tid < BM) tile_pairs[tid] = perm[rs + min(tid, rows_valid - 1)];
+
+  const KLoads<N4Tile, kFmtNV4> ld{reinterpret_cast<const uint8_t*>(act), aoff, codes, scales, tb0, nkt, w, lane};
+  k_loop(lds, ld, nkt, wave_active, [&](const uint8_t* abuf, const BRegs<kFmtNV4>& br, auto part, bool mma) {
+    nv4_ktile<1>(acc, abuf, br, part, mma, rows_valid, lane);
+  });
+  __syncthreads();   // tile_pairs visible to every wave
+  if (!wave_active) return;
+  const float sd = scale2[3 * e + 2];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m * 16 + 4 * (lane >> 4) + r;
+      if (row >= rows_valid) continue;
+      const int p = tile_pairs[row];
+#pragma unroll
+      for (int t = 0; t < kRGW; ++t) pair_out[(size_t)p * K + 16 * (rg0 + t) + (lane & 15)] = acc[m][t][r] * sd;
+    }
+  }
+}
+
 }  // namespace
 
 inline unsigned gemm_grid(int max_tiles, int n_blocks) {
@@ -496,8 +665,16 @@ inline unsigned gemm_grid(int max_tiles, int n_blocks) {
 
 hipError_t launch_gemm_gate_up(const moe_w2_planes* p, int T, int top_k, const void* x,
                                const Workspace& ws, uint8_t* wsb, hipStream_t s) {
-  if (p->fmt == kFmtNV4) return hipErrorInvalidValue;   // NVFP4 planes run on the decode kernels
   if (ws.max_tiles == 0) return hipSuccess;
+  if (p->fmt == kFmtNV4) {
+    const int nblk = (2 * p->I + BN - 1) / BN;
+    hipLaunchKernelGGL(gemm_gate_up_nv4_kernel, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads),
+                       kAStages * N4Tile::kBytes, s, p->gu_codes, p->gu_scales, p->scale2, (const uint16_t*)x,
+                       (const int32_t*)(wsb + ws.offsets), (const int32_t*)(wsb + ws.perm),
+                       (const int32_t*)(wsb + ws.tiles), (const int32_t*)(wsb + ws.meta), (_Float16*)(wsb + ws.aq),
+                       (long long*)(wsb + ws.counters), p->K, p->I, top_k, nblk);
+    return hipGetLastError();
+  }
   const long long nblk32 = (long long)T * (p->K / 32);
   hipLaunchKernelGGL(quant_x6_kernel, dim3((unsigned)((nblk32 + 255) / 256)), dim3(256), 0, s,
                      (const uint16_t*)x, wsb + ws.xq, T, p->K);
@@ -513,10 +690,17 @@ hipError_t launch_gemm_gate_up(const moe_w2_planes* p, int T, int top_k, const v
 
 hipError_t launch_gemm_down(const moe_w2_planes* p, int T, int top_k, const Workspace& ws,
                             uint8_t* wsb, hipStream_t s) {
-  if (p->fmt == kFmtNV4) return hipErrorInvalidValue;
   if (ws.max_tiles == 0) return hipSuccess;
   const int P = T * top_k;
   const int nblk = (p->K + BN - 1) / BN;
+  if (p->fmt == kFmtNV4) {
+    hipLaunchKernelGGL(gemm_down_nv4_kernel, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads),
+                       kAStages * N4Tile::kBytes, s, p->dn_codes, p->dn_scales, p->scale2,
+                       (const _Float16*)(wsb + ws.aq), (const int32_t*)(wsb + ws.offsets),
+                       (const int32_t*)(wsb + ws.perm), (const int32_t*)(wsb + ws.tiles),
+                       (const int32_t*)(wsb + ws.meta), (float*)(wsb + ws.pair_out), p->K, p->I, nblk);
+    return hipGetLastError();
+  }
   auto kern = p->fmt == kFmtW4 ? gemm_down_mx_kernel<kFmtW4> : gemm_down_mx_kernel<kFmtW2>;
   hipLaunchKernelGGL(kern, dim3(gemm_grid(ws.max_tiles, nblk)), dim3(kThreads),
                      kAStages * A6Tile::kBytes, s,

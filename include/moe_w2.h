@@ -64,7 +64,7 @@ enum moe_w2_status {
 enum moe_w2_out_dtype { MOE_W2_OUT_BF16 = 0, MOE_W2_OUT_F32 = 1 };
 
 /* Which kernels moe_w2_forward uses. AUTO picks the decode kernels for T*top_k <= 512, else
- * GEMM (NVFP4 planes: the sorted decode organisation); among the decode organisations,
+ * GEMM; among the decode organisations,
  * DECODE_SORTED from 384 pairs up, DECODE below. DECODE supports T*top_k <= 512 only
  * (MOE_W2_EUNSUPPORTED above); DECODE_SORTED any number of pairs P = T*top_k with
  * P/4 + min(E, P) + 1 <= 65535 (its launch has that many workgroup rows, one per chunk of up to 4
@@ -144,12 +144,11 @@ int moe_w4_pack(int E, int K, int I,
  *   gu_scales [E][2I][K/16] E4M3FN bytes        gu_scale2 [E][2] fp32: gate rows, up rows
  *   dn_codes  [E][K][I/2]   dn_scales [E][K][I/16]   dn_scale2 [E] fp32
  * A NaN scale byte (0x7F, 0xFF) or a non-finite scale_2 returns MOE_W2_ENVFP4; also needs
- * I*K < 2^31. The planes work with moe_w4_forward / moe_w2_forward / moe_w2_forward_stage on the
- * decode kernels at every batch size (PATH_AUTO takes the sorted decode organisation above 512
- * pairs; PATH_GEMM returns MOE_W2_EUNSUPPORTED): the block-scaled matrix instruction takes only
- * power-of-two block scales, so the weights enter the 16 x 16 x 32 bf16 (gate/up, with bf16 x) and
- * fp16 (down, with the fp16 gated product) instructions, e2m1 x e4m3 formed exactly in registers
- * and scale_2 applied to the fp32 results. Synchronous, like moe_w2_pack.
+ * I*K < 2^31. The planes work with moe_w4_forward / moe_w2_forward / moe_w2_forward_stage on both
+ * kernel families and every path: the block-scaled matrix instruction takes only power-of-two
+ * block scales, so the weights enter the 16 x 16 x 32 bf16 (gate/up, with bf16 x) and fp16 (down,
+ * with the fp16 gated product) instructions, e2m1 x e4m3 formed exactly in registers and scale_2
+ * applied to the fp32 results. Synchronous, like moe_w2_pack.
  */
 int moe_w4_pack_nvfp4(int E, int K, int I,
                       const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_scale2,

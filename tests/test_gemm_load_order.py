@@ -48,10 +48,12 @@ def _steps(lines):
 
 def test_dma_before_b_loads_in_every_step(asm):
     steps = [(k, s) for k, s in _steps(asm) if "global_load_lds_dwordx4" in s and "global_load_dwordx4" in s]
-    assert len(steps) >= 8          # the k-loop steps of gate_up and down, both weight formats
+    assert len(steps) >= 12         # the k-loop steps of gate_up and down, all three weight formats
+    assert any("nv4" in k for k, _ in steps)
     for kern, s in steps:
         last_dma = max(i for i, op in enumerate(s) if op == "global_load_lds_dwordx4")
-        first_b = min(i for i, op in enumerate(s) if op in ("global_load_dwordx4", "global_load_ushort"))
+        first_b = min(i for i, op in enumerate(s)
+                      if op in ("global_load_dwordx4", "global_load_dwordx2", "global_load_ushort"))
         assert first_b > last_dma, kern
 
 

@@ -9,8 +9,9 @@ intermediate (unit roundoff 2^-11), whose error in output n is at most 2^-11 * s
 The block scales drawn here span 11 octaves, so a few products dominate each output (max|y| is
 about 13 rms) and that bound reaches about half the bar: an f64 forward with only the
 intermediate rounded to fp16 is off by 5.1e-3 rms on the worst random shape below, as is the
-kernel. Pack/unpack is exact; decode organisations (direct, routed, sorted) on every shape, the
-routed and sorted organisations bit-identical."""
+kernel. Pack/unpack is exact; both kernel families (the decode organisations - direct, routed,
+sorted - and the grouped GEMMs) on every shape, the routed and sorted organisations bit-identical,
+the two families within 5e-3 of rms of each other."""
 import numpy as np
 import pytest
 import torch
@@ -72,7 +73,11 @@ CASES = [
     (128, 512, 256, 4, 4, 54, True, moe.PATH_DECODE),         # 512 pairs on 4 experts
     (60, 512, 512, 32, 8, 55, True, moe.PATH_DECODE_SORTED),
     (5, 768, 256, 8, 2, 56, False, moe.PATH_DECODE_SORTED),   # sorted below the AUTO threshold
-    (200, 1024, 256, 32, 8, 57, True, moe.PATH_AUTO),         # 1600 pairs: sorted
+    (200, 1024, 256, 32, 8, 57, True, moe.PATH_AUTO),         # 1600 pairs: GEMM
+    (200, 1024, 256, 32, 8, 57, True, moe.PATH_DECODE_SORTED),
+    (4, 256, 512, 8, 2, 52, False, moe.PATH_GEMM),            # one ragged M-tile per expert
+    (300, 768, 512, 8, 2, 61, False, moe.PATH_GEMM),          # several M-tiles, ragged tails
+    (150, 512, 768, 64, 8, 62, True, moe.PATH_GEMM),          # 2I = 1536: a partial N-block
 ]
 
 
@@ -98,7 +103,7 @@ def test_nvfp4_every_finite_scale_encoding(gpu):
         c[name] = finite[rng.integers(0, 254, size=c[name].shape)]
     h = pack_nv(c)
     y_ref = _oracle(c)
-    for path in (moe.PATH_DECODE, moe.PATH_DECODE_SORTED):
+    for path in (moe.PATH_DECODE, moe.PATH_DECODE_SORTED, moe.PATH_GEMM):
         err = rel_max_err(_fwd(h, c, path), y_ref)
         print(f"all encodings path={path}: rel max err {err:.2e}")
         assert err <= TOL
@@ -112,6 +117,11 @@ def test_nvfp4_routed_and_sorted_agree_bit_identically_and_repeat(gpu):
     assert np.array_equal(a.view(np.int32), b.view(np.int32))
     assert np.array_equal(a.view(np.int32), _fwd(h, c, moe.PATH_DECODE).view(np.int32))
     assert rel_max_err(a, _oracle(c)) <= TOL
+    g = _fwd(h, c, moe.PATH_GEMM)
+    assert np.array_equal(g.view(np.int32), _fwd(h, c, moe.PATH_GEMM).view(np.int32))
+    d = rel_max_err(g, a.astype(np.float64))
+    print(f"decode vs GEMM rel max diff {d:.2e}")
+    assert d <= 5e-3
 
 
 def test_nvfp4_errors_and_invalid_ids(gpu):
@@ -125,9 +135,9 @@ def test_nvfp4_errors_and_invalid_ids(gpu):
     assert rel_max_err(y, _oracle(c)) <= TOL
     inv, _ = moe.moe_w2_read_counters(ws)
     assert inv == 2
-    with pytest.raises(moe.MoeW2Error) as ex:              # the GEMM kernels take no NVFP4 planes
-        _fwd(h, c, moe.PATH_GEMM)
-    assert ex.value.status == -2
+    y_g = _fwd(h, c, moe.PATH_GEMM, ws)                   # the GEMM family counts alike
+    assert rel_max_err(y_g, _oracle(c)) <= TOL
+    assert moe.moe_w2_read_counters(ws)[0] == 2
     with pytest.raises(moe.MoeW2Error):                    # MXFP4 / 2-bit unpack of NVFP4 planes
         moe.moe_w4_unpack(h)
     with pytest.raises(moe.MoeW2Error):
@@ -170,7 +180,8 @@ def test_nvfp4_decode_full_shape_sampled_tokens(gpu, T):
 
 def _random_cases(n=8, seed=4096):
     """Seeded random shapes: T in [1, 160], K and I multiples of 256 up to 1280, E in [1, 96],
-    top_k up to min(8, E), uniform or Zipf routing; the AUTO path (direct, routed or sorted)."""
+    top_k up to min(8, E), uniform or Zipf routing; the AUTO path (direct, routed or sorted decode
+    up to 512 pairs, else the GEMMs) and the GEMMs."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -186,6 +197,30 @@ def test_nvfp4_random_shapes_parity(gpu, case):
     T, K, I, E, top_k, seed, zipf = case
     c = _case(T, K, I, E, top_k, seed, zipf)
     h = pack_nv(c)
-    err = rel_max_err(_fwd(h, c, moe.PATH_AUTO), _oracle(c))
-    print(f"{case}: rel max err {err:.2e}")
-    assert err <= TOL, (case, err)
+    y_ref = _oracle(c)
+    for path in (moe.PATH_AUTO, moe.PATH_GEMM):
+        err = rel_max_err(_fwd(h, c, path), y_ref)
+        print(f"{case} path={path}: rel max err {err:.2e}")
+        assert err <= TOL, (case, path, err)
+
+
+def test_nvfp4_prefill_shape_sampled_tokens(gpu):
+    """The GEMM family at the prefill layer's K=6144, I=2048 with E=32 experts, 1024 tokens and
+    Zipf(1.1) top-8 routing (8,192 pairs, groups of a few to ~1,500 rows): 48 seeded tokens
+    against the f64 oracle, and every token's bf16 output equal to the RNE of its fp32 output."""
+    from gpu_helpers import bf16_rne_bits
+    rng = np.random.default_rng(80)
+    T, K, I, E = 1024, 6144, 2048, 32
+    planes = workloads.draw_planes_nvfp4(rng, E, K, I)
+    x = workloads.draw_x(rng, T, K)
+    ids, w = workloads.zipf_routing(rng, T, E, 8, rank_perm=rng.permutation(E))
+    c = dict(planes, x=x, topk_ids=ids, topk_w=w)
+    h = pack_nv(c)
+    y = _fwd(h, c, moe.PATH_AUTO)
+    toks = np.sort(rng.choice(T, 48, replace=False))
+    err = rel_max_err(y[toks], _oracle(c, tokens=toks, workers=4))
+    print(f"nvfp4 prefill shape: 48 tokens rel max err {err:.2e}")
+    assert err <= TOL
+    y16 = moe.moe_w4_forward(h, dev_bf16(x), dev(ids), dev(w), out_dtype=moe.OUT_BF16)
+    torch.cuda.synchronize()
+    assert np.array_equal(y16.view(torch.int16).cpu().numpy().view(np.uint16), bf16_rne_bits(y))
