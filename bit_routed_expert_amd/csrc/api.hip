@@ -31,6 +31,7 @@ Workspace workspace_layout(int E, int K, int I, int T, int top_k) {
   w.act = o;       o += align_up((size_t)P * I * 2);
   w.aq = o;        o += align_up((size_t)P * (I / kTileK) * kA6Bytes);
   w.pair_out = o;  o += align_up((size_t)P * K * 4);
+  w.gu_part = o;   o += P <= kWideMaxPairs ? align_up((size_t)kWideSlices * P * 2 * I * 4) : 0;
   w.slot_ids = o;  o += align_up((size_t)P * 4);
   w.total = o;
   return w;
@@ -314,6 +315,7 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
       o.rank = (int32_t*)(wsb + ws.rank);
       o.max_tiles = mode == kDecodeSorted ? ws.max_chunks : ws.max_tiles;
       o.tile_rows = mode == kDecodeSorted ? kDecodeChunk : kGemmBM;
+      o.wide = mode == kDecodeSorted && T * top_k <= kWideMaxPairs;
       err = launch_route(p->E, T, top_k, topk_ids, o, s);
       break;
     }

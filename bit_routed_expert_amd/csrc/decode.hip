@@ -27,6 +27,8 @@
 //    per-pair rows o[p] and combine_kernel sums them in j order per token.
 //  * direct (tiny batches, P = T*top_k <= kDirectMaxPairs): no routing pass; gate_up runs one
 //    group per pair, and one down kernel covers every pair of a column block and combines in LDS.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -269,15 +271,16 @@ MOEW2_DEV void prime_ring(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt,
 }
 
 // Consume k-tiles [kb, ke) from the primed ring; each consumed slot is refilled with the tile
-// kRing further on (or an out-of-range request), so every iteration issues the same loads.
+// kRing further on (or an out-of-range request), so every iteration issues the same loads. The
+// staged rows hold the reduction from k-tile koff on.
 template <int NP, int NB, int FMT>
 MOEW2_DEV void stream_k(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt, int kb, int ke, const uint8_t* arow,
-                        int KR, int g, f32x4_t* acc, int lane) {
+                        int KR, int g, f32x4_t* acc, int lane, int koff = 0) {
   for (int k0 = kb; k0 < ke; k0 += kRing) {
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       const int kt = k0 + i;
-      if (kt < ke) mma_tile<NP, NB, FMT>(ring[i], arow, KR, kt, g, acc);
+      if (kt < ke) mma_tile<NP, NB, FMT>(ring[i], arow, KR, kt - koff, g, acc);
       load_tile<NB, FMT>(ring[i], wt, kt + kRing, kt + kRing < ke, lane);
     }
   }
@@ -362,6 +365,31 @@ MOEW2_DEV void reduce_split_k(f32x4_t* acc, float* red, int w, int ks, int lane)
   }
 }
 
+// The same for accumulators of up to 16 token rows (all 64 lanes). `red` may alias the staged
+// rows: every wave is past its stream before any partial is written.
+template <int KS>
+MOEW2_DEV void reduce_split_k16(f32x4_t* acc, float* red, int w, int ks, int lane) {
+  if (KS == 1) return;
+  __syncthreads();
+  if (ks > 0) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[((w * 2 + b) * 4 + r) * 64 + lane] = acc[b][r];
+  }
+  __syncthreads();
+  if (ks == 0) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = acc[b][r];
+        for (int kk = 1; kk < KS; ++kk) v += red[(((w + kk) * 2 + b) * 4 + r) * 64 + lane];
+        acc[b][r] = v;
+      }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Routing inside the decode kernels (8 < P <= kDecodeMaxPairs, no routing pass): workgroup row p
 // (blockIdx.y) finds all pairs of expert e = ids[p] in ascending pair order with wave ballots over
@@ -440,18 +468,36 @@ MOEW2_DEV int pair_at(const ScanLds& sh, int m) {
   return 0;
 }
 
-// Chunk of the sorted organisation: workgroup row ti takes the ti-th entry (expert, first sorted
-// row) of the routing pass's chunk list, in expert order; its pairs are perm[rs .. rs + n).
+// Chunk of the sorted organisation: workgroup row ti takes the ti-th entry of the routing pass's
+// chunk list, in expert order: (expert, value). value = first sorted row rs of a group | slice cs
+// << 20 | (slices - 1) << 22. A group of at most kChunk rows is one entry (cs = 0, one slice);
+// with the wide list (forwards of at most kWideMaxPairs pairs) an expert's rows form groups of
+// kWideRows, each entry of a larger group one of its ceil(rows / kChunk) slices. The down stage
+// takes entry (rs, cs) as the kChunk rows rs + kChunk * cs .. of the group.
+constexpr int kWideRows = kWideSlices * kChunk;   // 16: one full MFMA row tile
 struct SortedChunk {
   const int32_t* offsets;
   const int32_t* perm;
   const int32_t* tiles;
   const int32_t* meta;
 };
-MOEW2_DEV bool sorted_chunk(const SortedChunk& sc, int ti, int& e, int& n, int (&pr)[kChunk]) {
+struct ChunkEntry {
+  int e, rs, cs, ncs;
+};
+MOEW2_DEV bool chunk_entry(const SortedChunk& sc, int ti, ChunkEntry& c) {
   if (ti >= sc.meta[1]) return false;
-  e = sc.tiles[2 * ti];
-  const int rs = sc.tiles[2 * ti + 1];
+  c.e = sc.tiles[2 * ti];
+  const int v = sc.tiles[2 * ti + 1];
+  c.rs = v & 0xFFFFF;
+  c.cs = (v >> 20) & 3;
+  c.ncs = ((v >> 22) & 3) + 1;
+  return true;
+}
+MOEW2_DEV bool sorted_chunk(const SortedChunk& sc, int ti, int& e, int& n, int (&pr)[kChunk]) {
+  ChunkEntry c;
+  if (!chunk_entry(sc, ti, c)) return false;
+  e = c.e;
+  const int rs = c.rs + kChunk * c.cs;
   n = min(kChunk, sc.offsets[e + 1] - rs);
 #pragma unroll
   for (int m = 0; m < kChunk; ++m) pr[m] = sc.perm[rs + min(m, n - 1)];
@@ -491,9 +537,8 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
     n = 1;
 #pragma unroll
     for (int m = 0; m < kChunk; ++m) pr[m] = (int)blockIdx.y;
-  } else if constexpr (MODE == kDecodeSorted) {
-    if (!sorted_chunk(sc, blockIdx.y, e, n, pr)) return;
   } else {
+    static_assert(MODE == kDecodeRouted, "the sorted organisation has its own gate_up kernel");
     long long* cnt = blockIdx.x == 0 && blockIdx.y == 0 ? counters : nullptr;
     int n_total, first;
     if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, cnt, e, n_total, first)) return;
@@ -537,6 +582,103 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// gate_up of the sorted organisation: grid (I / (16*NP), chunk entries). An entry of one slice
+// is the routed kernel's work for its <= kChunk rows (the same arithmetic, bit for bit). An entry
+// cs of a group of up to kWideRows rows split into ncs slices stages those rows over its share
+// [k0, k1) of the reduction only (the same LDS as kChunk whole rows), so one weight pass serves
+// up to 16 rows instead of 4, and writes the gate and up partial sums (times scale_2 for NVFP4
+// planes) to gu_part[cs][pair]; wide_finish_kernel sums the slices and forms the gated rows.
+// ---------------------------------------------------------------------------------------------
+template <int NPW, int FMT>
+__global__ void __launch_bounds__(kThreads)
+decode_gate_up_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                             const uint16_t* __restrict__ x, _Float16* __restrict__ act, float* __restrict__ gu_part,
+                             int P, int K, int I, int top_k, SortedChunk sc, const float* __restrict__ scale2) {
+  constexpr int KS = kWaves / NPW;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int row_pair[kWideRows];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
+  ChunkEntry c;
+  if (!chunk_entry(sc, blockIdx.y, c)) return;
+  const int e = c.e;
+  const bool wide = c.ncs > 1;
+  const int n = min(wide ? kWideRows : kChunk, sc.offsets[e + 1] - c.rs);
+  if (tid < kWideRows) row_pair[tid] = sc.perm[c.rs + min(tid, n - 1)];
+  const int nkt = K / kTileK, nrg = 2 * I / kTileRows;
+  const int k0 = c.cs * nkt / c.ncs, nk = (c.cs + 1) * nkt / c.ncs - k0;
+  const int pw = w / KS, ks = w % KS;
+  const int q = blockIdx.x * NPW + pw;
+  WaveTiles wt = wave_tiles<FMT>(codes, scales, e, (uint32_t)(nrg * nkt));
+  wt.tile[0] = (uint32_t)(2 * q * nkt);
+  wt.tile[1] = (uint32_t)((2 * q + 1) * nkt);
+  const int kb = k0 + ks * nk / KS, ke = k0 + (ks + 1) * nk / KS;
+  const float sg = FMT == kFmtNV4 ? scale2[3 * e] : 1.f, su = FMT == kFmtNV4 ? scale2[3 * e + 1] : 1.f;
+  constexpr int XR = kXRow<FMT>;
+  const int KR = nk * kTileK;
+  const int stride = MxRow<XR>::stride(KR);
+  __syncthreads();   // row_pair
+  TileRegs<2, FMT> ring[kRing];
+  auto row_off = [&](int m) -> size_t { return (size_t)(row_pair[m] / top_k) * K + (size_t)k0 * kTileK; };
+  int ninf = 0;
+  stage_and_prime<kThreads, XR, 2, FMT>(ring, wt, kb, ke, lane, lds, stride, x, KR, n, row_off, tid, false, ninf);
+  __syncthreads();
+  const int ma = min(lane & 15, n - 1);
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  stream_k<XR, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, KR, lane >> 4, acc, lane, k0);
+  reduce_split_k16<KS>(acc, reinterpret_cast<float*>(lds), w, ks, lane);
+  if (ks != 0) return;
+  // accumulator register r of lane l holds token row 4 (l / 16) + r, column l % 16
+  const int col = 16 * q + (lane & 15);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * (lane >> 4) + r;
+    if (row < n) {
+      const int pp = row_pair[row];
+      if (!wide) {
+        act[(size_t)pp * I + col] = (_Float16)silu_mul(acc[0][r] * sg, acc[1][r] * su);
+      } else {
+        float* gp = gu_part + ((size_t)c.cs * P + pp) * 2 * I;
+        gp[col] = acc[0][r] * sg;
+        gp[I + col] = acc[1][r] * su;
+      }
+    }
+  }
+}
+
+// Gated rows of the split groups: for sorted row blockIdx.x whose group has more than one slice,
+// a = silu(sum of the gate slices) * (sum of the up slices), slices added in order, rounded to
+// fp16 into act[pair]. Other rows return at once.
+__global__ void __launch_bounds__(256)
+wide_finish_kernel(const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+                   const int32_t* __restrict__ ids, const float* __restrict__ gu_part, _Float16* __restrict__ act,
+                   int P, int E, int I) {
+  const int r = blockIdx.x;
+  if (r >= offsets[E]) return;
+  const int p = perm[r];
+  const int e = ids[p];
+  const int base = offsets[e], ne = offsets[e + 1] - base;
+  const int g = (r - base) / kWideRows;
+  const int ng = min(kWideRows, ne - g * kWideRows);
+  const int ncs = (ng + kChunk - 1) / kChunk;
+  if (ncs < 2) return;
+  for (int i = 4 * (int)threadIdx.x; i < I; i += 4 * 256) {
+    f32x4_t gs = *reinterpret_cast<const f32x4_t*>(gu_part + (size_t)p * 2 * I + i);
+    f32x4_t us = *reinterpret_cast<const f32x4_t*>(gu_part + (size_t)p * 2 * I + I + i);
+    for (int cs = 1; cs < ncs; ++cs) {
+      const float* gp = gu_part + ((size_t)cs * P + p) * 2 * I;
+      gs += *reinterpret_cast<const f32x4_t*>(gp + i);
+      us += *reinterpret_cast<const f32x4_t*>(gp + I + i);
+    }
+    const _Float16 h0 = (_Float16)silu_mul(gs[0], us[0]), h1 = (_Float16)silu_mul(gs[1], us[1]);
+    const _Float16 h2 = (_Float16)silu_mul(gs[2], us[2]), h3 = (_Float16)silu_mul(gs[3], us[3]);
+    *reinterpret_cast<u32x2_t*>(act + (size_t)p * I + i) =
+        u32x2_t{(uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16),
+                (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16)};
   }
 }
 
@@ -781,17 +923,29 @@ static hipError_t decode_gate_up_fmt(const moe_w2_planes* p, int T, int top_k, c
     hipLaunchKernelGGL((decode_gate_up_kernel<1, kDecodeDirect, FMT>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
                        p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc, p->scale2);
   } else if (mode == kDecodeSorted) {
-    // one workgroup row per chunk of the routing pass (at most max_chunks; rows past meta[1] exit);
-    // the same split of the reduction over waves as the routed organisation, so that both give
-    // bit-identical results
+    // one workgroup row per chunk entry of the routing pass (at most max_chunks; rows past meta[1]
+    // exit); the same split of the reduction over waves as the routed organisation, so that
+    // entries of one slice give bit-identical results. LDS: the staged rows of the largest entry
+    // (kChunk whole rows, or 4 ncs rows of a 1/ncs share of the reduction) - the reduction of the
+    // waves' partial sums reuses it.
+    const bool wide = P <= kWideMaxPairs;
+    const int nkt = p->K / kTileK;
+    size_t lds_s = 0;
+    for (int ncs = 1; ncs <= (wide ? kWideSlices : 1); ++ncs) {
+      const size_t rows = ncs == 1 ? kChunk : (size_t)kChunk * ncs;
+      lds_s = std::max(lds_s, rows * MxRow<kXRow<FMT>>::stride((nkt + ncs - 1) / ncs * kTileK));
+    }
+    lds_s = std::max(lds_s, (size_t)kWaves * 2 * 4 * 64 * 4);
+    float* gu_part = (float*)(wsb + ws.gu_part);
     if (pick_np(min(p->E, P)) == 4)
-      hipLaunchKernelGGL((decode_gate_up_kernel<4, kDecodeSorted, FMT>), dim3(p->I / 64, ws.max_chunks),
-                         dim3(kThreads), lds, s, p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I,
-                         top_k, sc, p->scale2);
+      hipLaunchKernelGGL((decode_gate_up_sorted_kernel<4, FMT>), dim3(p->I / 64, ws.max_chunks), dim3(kThreads),
+                         lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, P, p->K, p->I, top_k, sc, p->scale2);
     else
-      hipLaunchKernelGGL((decode_gate_up_kernel<1, kDecodeSorted, FMT>), dim3(p->I / 16, ws.max_chunks),
-                         dim3(kThreads), lds, s, p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I,
-                         top_k, sc, p->scale2);
+      hipLaunchKernelGGL((decode_gate_up_sorted_kernel<1, FMT>), dim3(p->I / 16, ws.max_chunks), dim3(kThreads),
+                         lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, P, p->K, p->I, top_k, sc, p->scale2);
+    if (wide)
+      hipLaunchKernelGGL(wide_finish_kernel, dim3(P), dim3(256), 0, s, sc.offsets, sc.perm, ids, gu_part, act, P,
+                         p->E, p->I);
   } else if (pick_np(min(p->E, P)) == 4) {   // at most this many workgroup rows do work
     hipLaunchKernelGGL((decode_gate_up_kernel<4, kDecodeRouted, FMT>), dim3(p->I / 64, P), dim3(kThreads), lds, s,
                        p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc, p->scale2);

@@ -55,6 +55,8 @@ struct Workspace {
   size_t aq;          // gated intermediate split (GEMM path, written by the gate_up epilogue):
                       // one 608-byte three-part e2m3 record per (sorted row, k-tile)
   size_t pair_out;    // fp32 [P][K] per-pair down outputs, indexed by pair id
+  size_t gu_part;     // fp32 [kWideSlices][P][2I] gate (first I) and up partial sums of the sorted
+                      // decode organisation's reduction slices, by pair id (P <= kWideMaxPairs)
   size_t slot_ids;    // int32 [P] the ids mapped to slots (slot forward)
   size_t total;
   int P, nchunks, max_tiles, max_chunks;
@@ -67,6 +69,9 @@ constexpr int kDecodeChunk = 4;        // decode kernels: token rows per weight 
 constexpr int kSortedMinPairs = 384;   // AUTO path: the sorted decode organisation from this many pairs
 constexpr int kDecodeMaxPairs = 512;   // AUTO path: decode kernels up to this many pairs
 constexpr int kDirectMaxPairs = 8;     // decode without a routing pass up to this many pairs
+constexpr int kWideSlices = 4;         // sorted decode: a group of up to 4 chunks (16 rows) of one
+                                       // expert splits its gate_up reduction over this many workgroups
+constexpr int kWideMaxPairs = kDecodeMaxPairs;   // ... for forwards of at most this many pairs
 
 Workspace workspace_layout(int E, int K, int I, int T, int top_k);
 size_t route_scratch_bytes(int E, int P);
@@ -99,6 +104,7 @@ struct RouteOut {
   int32_t* rank;      // scratch for P > kRouteSmallMax
   int max_tiles;
   int tile_rows;      // rows per tile of the tile list (kGemmBM or kDecodeChunk)
+  int wide = 0;       // sorted decode organisation: groups of 4 tiles split along the reduction
 };
 hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const RouteOut& o, hipStream_t s);
 

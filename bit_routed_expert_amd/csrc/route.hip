@@ -20,6 +20,19 @@ constexpr int kSmallMaxPairs = 4096; // single-workgroup path
 
 __device__ __forceinline__ int bin_of(int id, int E) { return (id >= 0 && id < E) ? id : E; }
 
+// Entry m of the tile list of an expert with c pairs from sorted row s0: tiles of bm rows (value =
+// first row), or with `wide` (the sorted decode organisation) groups of 4*bm rows, each split into
+// ceil(rows / bm) reduction slices, entry m = slice m % 4 of group m / 4 (value = the group's first
+// row | slice << 20 | (slices - 1) << 22). The entry count is ceil(c / bm) either way, and a group
+// of at most bm rows is one entry with value = its first row.
+__device__ __forceinline__ int32_t tile_value(int s0, int c, int m, int bm, int wide) {
+  if (!wide) return s0 + m * bm;
+  const int g = m >> 2, ks = m & 3;
+  const int ng = min(4 * bm, c - 4 * bm * g);
+  const int nks = (ng + bm - 1) / bm;
+  return (s0 + 4 * bm * g) | (ks << 20) | ((nks - 1) << 22);
+}
+
 // In-place exclusive scan of n ints in LDS by the whole block; returns the total.
 __device__ int block_exclusive_scan(int* data, int n, int* scratch /* blockDim ints */) {
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -48,7 +61,7 @@ __device__ int block_exclusive_scan(int* data, int n, int* scratch /* blockDim i
 // (`cnt` has E+1 entries and is overwritten by its exclusive scan). Shared by both paths.
 __device__ void finish_routing(int* cnt, int E, int P, int* scratch, int* tmp,
                                int32_t* offsets, int32_t* active, int32_t* meta, int32_t* tiles,
-                               long long* counters, int max_tiles, int bm) {
+                               long long* counters, int max_tiles, int bm, int wide) {
   const int tid = threadIdx.x, nt = blockDim.x;
   // per-expert activity and tile counts
   for (int b = tid; b < E; b += nt) tmp[b] = cnt[b] > 0 ? 1 : 0;
@@ -71,7 +84,7 @@ __device__ void finish_routing(int* cnt, int E, int P, int* scratch, int* tmp,
     int n = cnt[b + 1] - cnt[b];
     int t0 = tmp[b];
     for (int m = 0; m * bm < n; ++m) {
-      if (t0 + m < max_tiles) { tiles[2 * (t0 + m)] = b; tiles[2 * (t0 + m) + 1] = cnt[b] + m * bm; }
+      if (t0 + m < max_tiles) { tiles[2 * (t0 + m)] = b; tiles[2 * (t0 + m) + 1] = tile_value(cnt[b], n, m, bm, wide); }
     }
   }
   if (tid == 0) {
@@ -88,7 +101,7 @@ __device__ void finish_routing(int* cnt, int E, int P, int* scratch, int* tmp,
 __global__ void __launch_bounds__(kRoundThreads)
 route_small_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __restrict__ offsets,
                    int32_t* __restrict__ perm, int32_t* active, int32_t* meta, int32_t* tiles,
-                   long long* counters, int max_tiles, int bm) {
+                   long long* counters, int max_tiles, int bm, int wide) {
   extern __shared__ int lds[];
   const int nb = E + 1;
   uint32_t* masks = reinterpret_cast<uint32_t*>(lds);
@@ -127,7 +140,7 @@ route_small_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __res
   }
   for (int b = tid; b < nb; b += kRoundThreads) cnt[b] = running[b];
   __syncthreads();
-  finish_routing(cnt, E, P, scratch, tmp, offsets, active, meta, tiles, counters, max_tiles, bm);
+  finish_routing(cnt, E, P, scratch, tmp, offsets, active, meta, tiles, counters, max_tiles, bm, wide);
   __syncthreads();
   // cnt now holds the exclusive scan over bins (bin start positions)
   for (int p = tid; p < P; p += kRoundThreads) {
@@ -147,7 +160,7 @@ constexpr int kFastWords = kFastThreads / 32;
 __global__ void __launch_bounds__(kFastThreads)
 route_fast_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __restrict__ offsets,
                   int32_t* __restrict__ perm, int32_t* active, int32_t* meta, int32_t* tiles,
-                  long long* counters, int max_tiles, int bm) {
+                  long long* counters, int max_tiles, int bm, int wide) {
   extern __shared__ int lds[];
   const int nb = E + 1;
   uint32_t* masks = reinterpret_cast<uint32_t*>(lds);     // [nb][32]
@@ -193,7 +206,7 @@ route_fast_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __rest
     if (tid < E && c > 0) {
       active[a0] = tid;
       for (int m = 0; m * bm < c; ++m)
-        if (t0 + m < max_tiles) { tiles[2 * (t0 + m)] = tid; tiles[2 * (t0 + m) + 1] = s0 + m * bm; }
+        if (t0 + m < max_tiles) { tiles[2 * (t0 + m)] = tid; tiles[2 * (t0 + m) + 1] = tile_value(s0, c, m, bm, wide); }
     }
     if (tid == E) {
       meta[0] = a0;
@@ -249,7 +262,7 @@ route_chunk_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __res
 __global__ void __launch_bounds__(1024)
 route_scan_kernel(int E, int P, int nchunks, int32_t* __restrict__ chunk_cnt,
                   int32_t* __restrict__ offsets, int32_t* active, int32_t* meta, int32_t* tiles,
-                  long long* counters, int max_tiles, int bm) {
+                  long long* counters, int max_tiles, int bm, int wide) {
   extern __shared__ int lds[];
   const int nb = E + 1;
   int* cnt = lds;
@@ -274,7 +287,7 @@ route_scan_kernel(int E, int P, int nchunks, int32_t* __restrict__ chunk_cnt,
     cnt[b] = run;
   }
   __syncthreads();
-  finish_routing(cnt, E, P, scratch, tmp, offsets, active, meta, tiles, counters, max_tiles, bm);
+  finish_routing(cnt, E, P, scratch, tmp, offsets, active, meta, tiles, counters, max_tiles, bm, wide);
   __syncthreads();
   // keep the bin start positions for the scatter in offsets' spare copy: chunk_cnt row nchunks
   for (int b = tid; b < nb; b += blockDim.x) chunk_cnt[(long long)nchunks * nb + b] = cnt[b];
@@ -309,14 +322,14 @@ hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const Route
   if (P <= kFastThreads && E <= 256) {
     size_t lds = (size_t)nb * kFastWords * 4 + (size_t)nb * 4 + 16 * 4;
     hipLaunchKernelGGL(route_fast_kernel, dim3(1), dim3(kFastThreads), lds, s, ids, E, P, o.offsets, o.perm,
-                       o.active, o.meta, o.tiles, o.counters, o.max_tiles, o.tile_rows);
+                       o.active, o.meta, o.tiles, o.counters, o.max_tiles, o.tile_rows, o.wide);
     return hipGetLastError();
   }
   if (P <= kSmallMaxPairs) {
     size_t lds = (size_t)nb * kMaskWords * 4 + (size_t)3 * nb * 4 + (size_t)kSmallMaxPairs * 4 +
                  kRoundThreads * 4;
     hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kRoundThreads), lds, s, ids, E, P,
-                       o.offsets, o.perm, o.active, o.meta, o.tiles, o.counters, o.max_tiles, o.tile_rows);
+                       o.offsets, o.perm, o.active, o.meta, o.tiles, o.counters, o.max_tiles, o.tile_rows, o.wide);
     return hipGetLastError();
   }
   const int nchunks = (P + kChunkPairs - 1) / kChunkPairs;
@@ -325,7 +338,7 @@ hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const Route
                      o.chunk_cnt, o.rank);
   size_t lds2 = (size_t)2 * nb * 4 + 1024 * 4;
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), lds2, s, E, P, nchunks, o.chunk_cnt,
-                     o.offsets, o.active, o.meta, o.tiles, o.counters, o.max_tiles, o.tile_rows);
+                     o.offsets, o.active, o.meta, o.tiles, o.counters, o.max_tiles, o.tile_rows, o.wide);
   hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(kRoundThreads), 0, s, ids, E, P,
                      nchunks, o.chunk_cnt, o.rank, o.perm);
   return hipGetLastError();

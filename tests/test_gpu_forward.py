@@ -357,13 +357,73 @@ def test_stages_in_order_equal_forward(gpu, T, path, zipf):
 
 
 @pytest.mark.parametrize("T,zipf", [(2, False), (5, True), (24, False), (48, True), (64, True), (64, False)])
-def test_sorted_and_routed_decode_are_bit_identical(gpu, T, zipf):
-    """The two decode organisations process the same chunks of each expert's pairs with the same
-    per-row arithmetic (only the workgroup order differs), so their outputs agree bit for bit, on
-    uniform and skewed routing up to the 512-pair limit (K=1024, I=512, E=64, top-8)."""
+def test_sorted_and_routed_decode_agree(gpu, T, zipf):
+    """The two decode organisations process the same 4-row chunks of each expert with the same
+    per-row arithmetic where no expert has more than 4 pairs (only the workgroup order differs):
+    their outputs agree bit for bit. Where an expert has more, the sorted organisation passes its
+    weights once per 16 rows, splitting the gate_up reduction into slices summed afterwards, so
+    the two agree to rounding (within 2e-3 of rms) and each meets the oracle bar (K=1024, I=512,
+    E=64, top-8, up to the 512-pair limit of the routed organisation)."""
     K, I, E, top_k = 1024, 512, 64, 8
     c = _case(T, K, I, E, top_k, 300 + T, zipf=zipf)
     h = pack(c)
     a = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, moe.PATH_DECODE)
     b = forward(h, c["x"], c["topk_ids"], c["topk_w"], moe.OUT_F32, moe.PATH_DECODE_SORTED)
-    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    largest = int(np.bincount(np.asarray(c["topk_ids"]).ravel(), minlength=E).max())
+    if largest <= 4:
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        return
+    d = rel_max_err(b.cpu().numpy(), a.cpu().numpy().astype(np.float64))
+    print(f"T={T} zipf={zipf}: largest group {largest}, routed vs sorted rel max diff {d:.2e}")
+    assert d <= 2e-3
+    y_ref = _oracle(c)
+    assert rel_max_err(a.cpu().numpy(), y_ref) <= TOL and rel_max_err(b.cpu().numpy(), y_ref) <= TOL
+
+
+GROUPS = [5, 8, 9, 15, 16, 17, 31, 33, 64, 1, 2, 3, 4]
+
+
+@pytest.mark.parametrize("E,fmt", [(24, "w2"), (96, "w2"), (96, "w4"), (96, "nvfp4")],
+                         ids=["few-groups-w2", "w2", "w4", "nvfp4"])
+def test_sorted_wide_groups(gpu, E, fmt):
+    """The sorted organisation's split groups: experts with 5, 8, 9, 15, 16, 17, 31, 33 and 64
+    pairs (groups of 16 rows split into 2 to 4 reduction slices, and ragged last groups of 1 to 4
+    rows that run unsplit) next to experts with 1 to 4 pairs, on workgroups of one row pair
+    (fewer than 32 groups) and of four; all three weight formats against the f64 oracle, the
+    forward's stages one at a time bit-identical to the forward, repeats bit-identical."""
+    T, K, I, top_k = 64, 768, 512, 8
+    rng = np.random.default_rng(500 + E)
+    if fmt == "w2":
+        planes = workloads.draw_planes(rng, E, K, I)
+    elif fmt == "w4":
+        planes = workloads.draw_planes_fp4(rng, E, K, I)
+    else:
+        planes = workloads.draw_planes_nvfp4(rng, E, K, I)
+    x = workloads.draw_x(rng, T, K)
+    sizes = GROUPS if E > 24 else GROUPS[:9]
+    ids, w = workloads.grouped_routing(rng, T, E, top_k, sizes)
+    if fmt == "w2":
+        h = pack(planes)
+        fwd = moe.moe_w2_forward
+    elif fmt == "w4":
+        h = moe.moe_w4_pack(*[dev(planes[k]) for k in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")])
+        fwd = moe.moe_w4_forward
+    else:
+        h = moe.moe_w4_pack_nvfp4(*[dev(planes[k]) for k in ("gu_codes", "gu_scales", "gu_scale2", "dn_codes",
+                                                              "dn_scales", "dn_scale2")])
+        fwd = moe.moe_w4_forward
+    x_d, ids_d, w_d = dev_bf16(x), dev(ids), dev(w)
+    ws = moe.alloc_workspace(h, T, top_k)
+    y = fwd(h, x_d, ids_d, w_d, out_dtype=moe.OUT_F32, path=moe.PATH_DECODE_SORTED, workspace=ws)
+    y_again = fwd(h, x_d, ids_d, w_d, out_dtype=moe.OUT_F32, path=moe.PATH_DECODE_SORTED, workspace=ws)
+    y2 = torch.full_like(y, 7.0)
+    for st in (moe.STAGE_ROUTE, moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE):
+        moe.moe_w2_forward_stage(st, h, x_d, ids_d, w_d, y2, ws, moe.OUT_F32, moe.PATH_DECODE_SORTED)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_again) and torch.equal(y2, y)
+    nv = (planes["gu_scale2"], planes["dn_scale2"]) if fmt == "nvfp4" else None
+    y_ref = oracle_fwd.moe_forward(formats.bf16_bits_to_f64(x), ids, w, planes["gu_codes"], planes["gu_scales"],
+                                   planes["dn_codes"], planes["dn_scales"], fp4=fmt == "w4", nvfp4=nv)
+    err = rel_max_err(y.cpu().numpy(), y_ref)
+    print(f"E={E} {fmt}: rel max err {err:.2e}")
+    assert err <= TOL

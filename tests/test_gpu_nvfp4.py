@@ -10,8 +10,8 @@ The block scales drawn here span 11 octaves, so a few products dominate each out
 about 13 rms) and that bound reaches about half the bar: an f64 forward with only the
 intermediate rounded to fp16 is off by 5.1e-3 rms on the worst random shape below, as is the
 kernel. Pack/unpack is exact; both kernel families (the decode organisations - direct, routed,
-sorted - and the grouped GEMMs) on every shape, the routed and sorted organisations bit-identical,
-the two families within 5e-3 of rms of each other."""
+sorted - and the grouped GEMMs) on every shape, the routed and sorted organisations bit-identical
+where no expert has more than 4 pairs, the two families within 5e-3 of rms of each other."""
 import numpy as np
 import pytest
 import torch
@@ -109,14 +109,21 @@ def test_nvfp4_every_finite_scale_encoding(gpu):
         assert err <= TOL
 
 
-def test_nvfp4_routed_and_sorted_agree_bit_identically_and_repeat(gpu):
-    c = _case(64, 512, 512, 8, 4, 59, zipf=True)
+@pytest.mark.parametrize("T,E,k", [(8, 64, 2), (64, 8, 4)], ids=["small-groups", "split-groups"])
+def test_nvfp4_routed_and_sorted_agree_and_repeat(gpu, T, E, k):
+    """Bit for bit where no expert has more than 4 pairs; to rounding where the sorted
+    organisation splits an expert's 16-row groups into reduction slices."""
+    c = _case(T, 512, 512, E, k, 59, zipf=True)
     h = pack_nv(c)
     a = _fwd(h, c, moe.PATH_DECODE)
     b = _fwd(h, c, moe.PATH_DECODE_SORTED)
-    assert np.array_equal(a.view(np.int32), b.view(np.int32))
+    if np.bincount(c["topk_ids"].ravel(), minlength=E).max() <= 4:
+        assert np.array_equal(a.view(np.int32), b.view(np.int32))
+    else:
+        assert rel_max_err(b, a.astype(np.float64)) <= 2e-3
     assert np.array_equal(a.view(np.int32), _fwd(h, c, moe.PATH_DECODE).view(np.int32))
-    assert rel_max_err(a, _oracle(c)) <= TOL
+    assert np.array_equal(b.view(np.int32), _fwd(h, c, moe.PATH_DECODE_SORTED).view(np.int32))
+    assert rel_max_err(a, _oracle(c)) <= TOL and rel_max_err(b, _oracle(c)) <= TOL
     g = _fwd(h, c, moe.PATH_GEMM)
     assert np.array_equal(g.view(np.int32), _fwd(h, c, moe.PATH_GEMM).view(np.int32))
     d = rel_max_err(g, a.astype(np.float64))

@@ -115,6 +115,25 @@ def zipf_routing(rng, T, E, top_k, s=1.1, rank_perm=None):
     return ids, w
 
 
+def grouped_routing(rng, T, E, top_k, sizes):
+    """Routing with prescribed group sizes: expert i (i < len(sizes)) gets sizes[i] pairs, the
+    remaining pairs go to experts len(sizes) .. E-1 in turn; the pair positions are a random
+    permutation of the T*top_k pairs (a token may route to one expert more than once). Weights as
+    in uniform_routing. sum(sizes) <= T*top_k."""
+    P = T * top_k
+    flat = []
+    for i, n in enumerate(sizes):
+        flat += [i] * int(n)
+    rest = P - len(flat)
+    if rest < 0:
+        raise ValueError("more pairs in the groups than the batch has")
+    others = max(1, E - len(sizes))
+    flat += [len(sizes) + (k % others) for k in range(rest)]
+    ids = np.asarray(flat, dtype=np.int32)[rng.permutation(P)].reshape(T, top_k)
+    w = _softmax_f32(rng.standard_normal((T, top_k), dtype=np.float32))
+    return ids, w
+
+
 def decode_layer(seed=DECODE["seed"], K=DECODE["K"], I=DECODE["I"], E=DECODE["E"]):
     """Planes of the K=4096 decode layer (draw_planes with the given seed)."""
     return draw_planes(np.random.default_rng(seed), E, K, I)
