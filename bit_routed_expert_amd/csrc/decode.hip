@@ -593,12 +593,12 @@ decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restri
 // up to 16 rows instead of 4, and writes the gate and up partial sums (times scale_2 for NVFP4
 // planes) to gu_part[cs][pair]; wide_finish_kernel sums the slices and forms the gated rows.
 // ---------------------------------------------------------------------------------------------
-template <int NPW, int FMT>
-__global__ void __launch_bounds__(kThreads)
+template <int NPW, int FMT, int NW>
+__global__ void __launch_bounds__(64 * NW)
 decode_gate_up_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                              const uint16_t* __restrict__ x, _Float16* __restrict__ act, float* __restrict__ gu_part,
                              int P, int K, int I, int top_k, SortedChunk sc, const float* __restrict__ scale2) {
-  constexpr int KS = kWaves / NPW;
+  constexpr int KS = NW / NPW;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int row_pair[kWideRows];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -625,7 +625,7 @@ decode_gate_up_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* _
   TileRegs<2, FMT> ring[kRing];
   auto row_off = [&](int m) -> size_t { return (size_t)(row_pair[m] / top_k) * K + (size_t)k0 * kTileK; };
   int ninf = 0;
-  stage_and_prime<kThreads, XR, 2, FMT>(ring, wt, kb, ke, lane, lds, stride, x, KR, n, row_off, tid, false, ninf);
+  stage_and_prime<64 * NW, XR, 2, FMT>(ring, wt, kb, ke, lane, lds, stride, x, KR, n, row_off, tid, false, ninf);
   __syncthreads();
   const int ma = min(lane & 15, n - 1);
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -768,6 +768,76 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
+// down of the sorted organisation: grid (K / (32*NPW*R), chunk entries), NW waves per workgroup.
+// With the wide list an even entry cs of a group takes its rows 8 (cs / 2) .. + 7 (odd entries
+// exit), so one weight pass serves up to 8 rows over the whole reduction; with the plain list an
+// entry is its 4-row chunk. Per-row arithmetic as in the routed kernel (bit-identical rows).
+// ---------------------------------------------------------------------------------------------
+constexpr int kDownRows = 2 * kChunk;
+template <int NPW, int FMT, int R, int NW>
+__global__ void __launch_bounds__(64 * NW)
+decode_down_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                          const _Float16* __restrict__ act, float* __restrict__ pair_out,
+                          long long* __restrict__ counters, int K, int I, int wide, SortedChunk sc,
+                          const float* __restrict__ scale2) {
+  constexpr int KS = NW / NPW;
+  static_assert(R == 1 || KS == 1, "row pairs per wave need the whole reduction in each wave");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int row_pair[kDownRows];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
+  ChunkEntry c;
+  if (!chunk_entry(sc, blockIdx.y, c)) return;
+  if (wide && (c.cs & 1)) return;
+  const int e = c.e;
+  const int row0 = wide ? c.rs + kDownRows * (c.cs >> 1) : c.rs + kChunk * c.cs;
+  const int n = min(wide ? kDownRows : kChunk, sc.offsets[e + 1] - row0);
+  if (tid < kDownRows) row_pair[tid] = sc.perm[row0 + min(tid, n - 1)];
+  const int nkt = I / kTileK, nrg = K / kTileRows;
+  const int pw = w / KS, ks = w % KS;
+  const int rq = (blockIdx.x * NPW + pw) * R;   // the wave's first row pair
+  WaveTiles wt = wave_tiles<FMT>(codes, scales, e, (uint32_t)(nrg * nkt));
+  wt.tile[0] = (uint32_t)(2 * rq * nkt);
+  wt.tile[1] = (uint32_t)((2 * rq + 1) * nkt);
+  const int kb = ks * nkt / KS, ke = (ks + 1) * nkt / KS;
+  constexpr int AR = kARow<FMT>;
+  const int stride = MxRow<AR>::stride(I);
+  const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
+  const float sd = FMT == kFmtNV4 ? scale2[3 * e + 2] : 1.f;   // NVFP4: the down tensor's scale_2
+  __syncthreads();   // row_pair
+  TileRegs<2, FMT> ring[kRing];
+  auto row_off = [&](int m) -> size_t { return (size_t)row_pair[m] * I; };
+  int ninf = 0;
+  stage_and_prime<64 * NW, AR, 2, FMT>(ring, wt, kb, ke, lane, lds, stride, act16, I, n, row_off, tid,
+                                       blockIdx.x == 0, ninf);
+  if (ninf) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)ninf);
+  __syncthreads();
+  const int ma = min(lane & 15, n - 1);
+  f32x4_t acc[R][2];
+#pragma unroll
+  for (int q = 0; q < R; ++q) acc[q][0] = acc[q][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (R == 1) {
+    stream_k<AR, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, I, lane >> 4, acc[0], lane);
+    reduce_split_k16<KS>(acc[0], reinterpret_cast<float*>(lds), w, ks, lane);
+  } else {
+    stream_rows<AR, 2, FMT, R>(ring, wt, nkt, lds + (size_t)ma * stride, I, lane >> 4, acc, lane);
+  }
+  if (ks != 0 || lane >= 4 * kDownRows) return;
+  // accumulator register r of lane l holds token row 4 (l / 16) + r, column l % 16
+#pragma unroll
+  for (int q = 0; q < R; ++q)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int col = 16 * (2 * (rq + q) + b) + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * (lane >> 4) + r;
+        if (row < n) pair_out[(size_t)row_pair[row] * K + col] = acc[q][b][r] * sd;
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // direct down + combine for tiny batches: grid (K/16). The workgroup covers one row group (16
 // output columns) for every pair; wave w takes pair w/2 and half w%2 of the reduction; per-pair
 // results meet in LDS and are combined per token in j order. Block 0 also records the two
@@ -898,6 +968,12 @@ __global__ void combine_kernel(const int32_t* __restrict__ ids, const float* __r
 
 inline int pick_np(int slots) { return slots >= 32 ? 4 : 1; }
 
+// The sorted organisation's kernels run 8-wave workgroups where their LDS would fit fewer than
+// four 4-wave workgroups per CU (160 KB of LDS): the same waves per CU in fewer, wider workgroups
+// whose staged rows serve twice the columns.
+constexpr size_t kLdsPerCu = 160 * 1024;
+inline bool sorted_wide8(size_t lds) { return lds > kLdsPerCu / 4; }
+
 }  // namespace
 
 size_t decode_direct_lds(int I) {
@@ -937,12 +1013,17 @@ static hipError_t decode_gate_up_fmt(const moe_w2_planes* p, int T, int top_k, c
     }
     lds_s = std::max(lds_s, (size_t)kWaves * 2 * 4 * 64 * 4);
     float* gu_part = (float*)(wsb + ws.gu_part);
-    if (pick_np(min(p->E, P)) == 4)
-      hipLaunchKernelGGL((decode_gate_up_sorted_kernel<4, FMT>), dim3(p->I / 64, ws.max_chunks), dim3(kThreads),
+    if (pick_np(min(p->E, P)) == 4 && sorted_wide8(lds_s))
+      hipLaunchKernelGGL((decode_gate_up_sorted_kernel<8, FMT, 8>), dim3(p->I / 128, ws.max_chunks), dim3(512),
                          lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, P, p->K, p->I, top_k, sc, p->scale2);
+    else if (pick_np(min(p->E, P)) == 4)
+      hipLaunchKernelGGL((decode_gate_up_sorted_kernel<4, FMT, kWaves>), dim3(p->I / 64, ws.max_chunks),
+                         dim3(kThreads), lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, P, p->K, p->I, top_k,
+                         sc, p->scale2);
     else
-      hipLaunchKernelGGL((decode_gate_up_sorted_kernel<1, FMT>), dim3(p->I / 16, ws.max_chunks), dim3(kThreads),
-                         lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, P, p->K, p->I, top_k, sc, p->scale2);
+      hipLaunchKernelGGL((decode_gate_up_sorted_kernel<1, FMT, kWaves>), dim3(p->I / 16, ws.max_chunks),
+                         dim3(kThreads), lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, P, p->K, p->I, top_k,
+                         sc, p->scale2);
     if (wide)
       hipLaunchKernelGGL(wide_finish_kernel, dim3(P), dim3(256), 0, s, sc.offsets, sc.perm, ids, gu_part, act, P,
                          p->E, p->I);
@@ -987,6 +1068,40 @@ static hipError_t decode_down_routed(const moe_w2_planes* p, int rows, int P, co
   return hipGetLastError();
 }
 
+// down of the sorted organisation: one workgroup row per chunk entry; the same kernel shapes as the
+// routed organisation (two row pairs per wave for 2-bit planes), 8-wave workgroups by LDS.
+template <int FMT>
+static hipError_t decode_down_sorted(const moe_w2_planes* p, int P, const Workspace& ws, uint8_t* wsb, hipStream_t s) {
+  const int wide = P <= kWideMaxPairs ? 1 : 0;
+  const int groups = min(p->E, P);
+  const size_t rows_lds = (size_t)(wide ? kDownRows : kChunk) * MxRow<kARow<FMT>>::stride(p->I);
+  const float* sc2 = p->scale2;
+  const _Float16* act = (const _Float16*)(wsb + ws.act);
+  long long* cnt = (long long*)(wsb + ws.counters);
+  float* po = (float*)(wsb + ws.pair_out);
+  const SortedChunk sc = sorted_chunks(ws, wsb);
+  const unsigned rows = (unsigned)ws.max_chunks;
+  const bool two_pairs = FMT == kFmtW2 && (p->I / kTileK) % kRing == 0;
+  const bool w8 = pick_np(groups) == 4 && sorted_wide8(rows_lds);
+  if (w8 && two_pairs && p->K % 512 == 0)
+    hipLaunchKernelGGL((decode_down_sorted_kernel<8, FMT, 2, 8>), dim3(p->K / 512, rows), dim3(512), rows_lds, s,
+                       p->dn_codes, p->dn_scales, act, po, cnt, p->K, p->I, wide, sc, sc2);
+  else if (w8)
+    hipLaunchKernelGGL((decode_down_sorted_kernel<8, FMT, 1, 8>), dim3(p->K / 256, rows), dim3(512), rows_lds, s,
+                       p->dn_codes, p->dn_scales, act, po, cnt, p->K, p->I, wide, sc, sc2);
+  else if (pick_np(groups) == 4 && two_pairs)
+    hipLaunchKernelGGL((decode_down_sorted_kernel<4, FMT, 2, kWaves>), dim3(p->K / 256, rows), dim3(kThreads),
+                       rows_lds, s, p->dn_codes, p->dn_scales, act, po, cnt, p->K, p->I, wide, sc, sc2);
+  else if (pick_np(groups) == 4)
+    hipLaunchKernelGGL((decode_down_sorted_kernel<4, FMT, 1, kWaves>), dim3(p->K / 128, rows), dim3(kThreads),
+                       rows_lds, s, p->dn_codes, p->dn_scales, act, po, cnt, p->K, p->I, wide, sc, sc2);
+  else
+    hipLaunchKernelGGL((decode_down_sorted_kernel<1, FMT, 1, kWaves>), dim3(p->K / 32, rows), dim3(kThreads),
+                       std::max(rows_lds, (size_t)kWaves * 2 * 4 * 64 * 4), s, p->dn_codes, p->dn_scales, act, po,
+                       cnt, p->K, p->I, wide, sc, sc2);
+  return hipGetLastError();
+}
+
 template <int FMT>
 static hipError_t decode_down_fmt(const moe_w2_planes* p, int T, int top_k, const int32_t* ids, const float* w,
                                   void* y, int out_dtype, const Workspace& ws, uint8_t* wsb, int mode,
@@ -999,7 +1114,7 @@ static hipError_t decode_down_fmt(const moe_w2_planes* p, int T, int top_k, cons
                        s, p->dn_codes, p->dn_scales, act, ids, w, y, cnt, out_dtype, T, p->E, p->K, p->I, top_k, p->scale2);
     return hipGetLastError();
   }
-  return mode == kDecodeSorted ? decode_down_routed<FMT, kDecodeSorted>(p, ws.max_chunks, P, ids, ws, wsb, s)
+  return mode == kDecodeSorted ? decode_down_sorted<FMT>(p, P, ws, wsb, s)
                                : decode_down_routed<FMT, kDecodeRouted>(p, P, P, ids, ws, wsb, s);
 }
 
