@@ -968,9 +968,9 @@ __global__ void combine_kernel(const int32_t* __restrict__ ids, const float* __r
 
 inline int pick_np(int slots) { return slots >= 32 ? 4 : 1; }
 
-// The sorted organisation's kernels run 8-wave workgroups where their LDS would fit fewer than
-// four 4-wave workgroups per CU (160 KB of LDS): the same waves per CU in fewer, wider workgroups
-// whose staged rows serve twice the columns.
+// The sorted organisation's gate_up runs 8-wave workgroups where its LDS would fit fewer than four
+// 4-wave workgroups per CU (160 KB of LDS): the same waves per CU in fewer, wider workgroups whose
+// staged rows serve twice the columns (Zipf T=64 batch at K=6144: gate_up 202 -> 192 us).
 constexpr size_t kLdsPerCu = 160 * 1024;
 inline bool sorted_wide8(size_t lds) { return lds > kLdsPerCu / 4; }
 
@@ -1069,7 +1069,10 @@ static hipError_t decode_down_routed(const moe_w2_planes* p, int rows, int P, co
 }
 
 // down of the sorted organisation: one workgroup row per chunk entry; the same kernel shapes as the
-// routed organisation (two row pairs per wave for 2-bit planes), 8-wave workgroups by LDS.
+// routed organisation (two row pairs per wave for 2-bit planes). 4-wave workgroups even where the
+// 8 staged rows limit them to three per CU: measured against 8-wave ones (two per CU) on T=64
+// batches, uniform and Zipf(1.1) at K=4096 and 6144, they were faster in all four (down 91 vs
+// 100 us uniform at K=4096), the wider workgroups' fewer, longer rows of work balancing worse.
 template <int FMT>
 static hipError_t decode_down_sorted(const moe_w2_planes* p, int P, const Workspace& ws, uint8_t* wsb, hipStream_t s) {
   const int wide = P <= kWideMaxPairs ? 1 : 0;
@@ -1082,14 +1085,7 @@ static hipError_t decode_down_sorted(const moe_w2_planes* p, int P, const Worksp
   const SortedChunk sc = sorted_chunks(ws, wsb);
   const unsigned rows = (unsigned)ws.max_chunks;
   const bool two_pairs = FMT == kFmtW2 && (p->I / kTileK) % kRing == 0;
-  const bool w8 = pick_np(groups) == 4 && sorted_wide8(rows_lds);
-  if (w8 && two_pairs && p->K % 512 == 0)
-    hipLaunchKernelGGL((decode_down_sorted_kernel<8, FMT, 2, 8>), dim3(p->K / 512, rows), dim3(512), rows_lds, s,
-                       p->dn_codes, p->dn_scales, act, po, cnt, p->K, p->I, wide, sc, sc2);
-  else if (w8)
-    hipLaunchKernelGGL((decode_down_sorted_kernel<8, FMT, 1, 8>), dim3(p->K / 256, rows), dim3(512), rows_lds, s,
-                       p->dn_codes, p->dn_scales, act, po, cnt, p->K, p->I, wide, sc, sc2);
-  else if (pick_np(groups) == 4 && two_pairs)
+  if (pick_np(groups) == 4 && two_pairs)
     hipLaunchKernelGGL((decode_down_sorted_kernel<4, FMT, 2, kWaves>), dim3(p->K / 256, rows), dim3(kThreads),
                        rows_lds, s, p->dn_codes, p->dn_scales, act, po, cnt, p->K, p->I, wide, sc, sc2);
   else if (pick_np(groups) == 4)
