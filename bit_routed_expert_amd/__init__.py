@@ -268,7 +268,7 @@ def moe_w2_forward(planes, x, topk_ids, topk_w, out_dtype=OUT_BF16, workspace=No
     return y
 
 
-NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_W2_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_W2_NOALLOC_SCRATCH_BYTES
 
 
 def moe_w2_forward_noalloc(planes, x, topk_ids, topk_w, y, out_dtype=OUT_BF16, path=PATH_AUTO):

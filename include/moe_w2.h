@@ -233,18 +233,18 @@ int moe_w2_forward(const moe_w2_planes* planes, int T, int top_k,
  * moe_w2_forward_noalloc - moe_w2_forward without a caller workspace, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation. The workspace is a library-owned device array of MOE_W2_NOALLOC_SCRATCH_BYTES
- * (32 MiB) per GPU, held until the process ends; its address is looked up on the first call on
+ * (64 MiB) per GPU, held until the process ends; its address is looked up on the first call on
  * each device. The call allocates nothing (no hipMalloc, no allocating library routine).
  *   Arguments as moe_w2_forward, minus workspace/workspace_bytes; the planes must be on the
  *   current device (MOE_W2_EINVAL otherwise).
  *   Limit: moe_w2_workspace_bytes(planes, T, top_k) <= MOE_W2_NOALLOC_SCRATCH_BYTES, else
  *   MOE_W2_EUNSUPPORTED before anything is enqueued (e.g. up to 64 tokens x top-8 at K = 6144,
- *   I = 2048, E = 256, whose workspace is about 18 MB).
+ *   I = 2048, E = 256, whose workspace is about 52 MB).
  *   Every call on a GPU shares that GPU's array, which keeps the last call's contents: calls
  *   that may overlap on one GPU (concurrent streams, or host threads) race and must be
  *   serialised by the caller; moe_w2_read_counters cannot read this workspace.
  */
-#define MOE_W2_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define MOE_W2_NOALLOC_SCRATCH_BYTES (64u << 20)
 int moe_w2_forward_noalloc(const moe_w2_planes* planes, int T, int top_k,
                            const void* x, const int32_t* topk_ids, const float* topk_w,
                            void* y, int out_dtype, int path, void* stream);

@@ -1,8 +1,8 @@
 """moe_w2_forward_noalloc (the forward with the library's own per-GPU scratch as workspace, for
 callers that cannot allocate) against moe_w2_forward with a caller workspace: bit-identical
-outputs on successive calls of decreasing size over all three kernel organisations (grouped GEMM,
-routed decode, tiny-batch direct), and calls whose workspace would exceed the scratch refused on
-the host."""
+outputs on successive calls of decreasing size over every kernel organisation (grouped GEMM,
+sorted decode with split groups, routed decode, tiny-batch direct), and calls whose workspace
+would exceed the scratch refused on the host."""
 import numpy as np
 import pytest
 import torch
@@ -35,8 +35,9 @@ def _inputs(T, top_k, E, K, seed):
 def test_noalloc_matches_forward_on_shrinking_calls(layer, out_dtype):
     K, E, top_k = 1024, 64, 8
     dt = torch.float32 if out_dtype == moe.OUT_F32 else torch.bfloat16
-    # GEMM organisation (P = 768), routed decode (P = 256), direct (P = 8), routed decode again (P = 40)
-    for i, T in enumerate((96, 32, 1, 5)):
+    # GEMM organisation (P = 768), sorted decode with split groups (P = 512, ~8 pairs per expert),
+    # routed decode (P = 256), direct (P = 8), routed decode again (P = 40)
+    for i, T in enumerate((96, 64, 32, 1, 5)):
         x, ids, w = _inputs(T, top_k, E, K, 100 + i)
         want = moe.moe_w2_forward(layer, x, ids, w, out_dtype=out_dtype)
         y = torch.full((T, K), float("nan"), dtype=dt, device="cuda")
@@ -52,7 +53,7 @@ def test_noalloc_forced_paths_and_repeat(layer):
     workspace entry point."""
     K, E, top_k = 1024, 64, 8
     x, ids, w = _inputs(24, top_k, E, K, 7)
-    for path in (moe.PATH_GEMM, moe.PATH_DECODE):
+    for path in (moe.PATH_GEMM, moe.PATH_DECODE, moe.PATH_DECODE_SORTED):
         want = moe.moe_w2_forward(layer, x, ids, w, out_dtype=moe.OUT_F32, path=path)
         for _ in range(2):
             y = torch.empty((24, K), dtype=torch.float32, device="cuda")
