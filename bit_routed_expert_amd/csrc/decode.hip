@@ -5,11 +5,13 @@
 // cores consume the previous ones, with the expert's tokens (up to kChunk at a time) as the
 // 16-row A operand staged in LDS.
 //
-// Both projections run on the block-scaled instruction (fp8 A x fp4 B, operand order in
-// common.h): the 2-bit codes become e2m1 operands with two bit operations per 8 values and their
-// UE8M0 bytes are the instruction's B scales. The A operand is split into e4m3 parts while it is
-// staged: x (bf16) into two parts, the gated intermediate (fp16) into three; both splits are
-// exact for every value within 2^-10 of its block maximum.
+// For 2-bit and MXFP4 planes both projections run on the block-scaled instruction (fp8 A x fp4 B,
+// operand order in common.h): the 2-bit codes become e2m1 operands with two bit operations per 8
+// values and their UE8M0 bytes are the instruction's B scales. The A operand is split into e4m3
+// parts while it is staged: x (bf16) into two parts, the gated intermediate (fp16) into three;
+// both splits are exact for every value within 2^-10 of its block maximum. NVFP4 planes run on
+// the 16 x 16 x 32 bf16 / fp16 instructions with the rows staged as they are and each B operand
+// formed exactly in registers (e2m1 x e4m3), scale_2 applied to the fp32 results.
 // gate_up: a = silu(g) * u from fp32 accumulators, rounded to fp16.
 // down:    per-pair fp32 rows.
 // combine: y[t] = sum over j ascending of w[t, j] * o[t*top_k + j] in fp32.
@@ -20,11 +22,15 @@
 // requested at an out-of-range offset (no memory access), so the load sequence never branches
 // and the ring's waits stay exact.
 //
-// Two organisations ("The v0.24.0 port", bullet "Deterministic unpermute": per-pair outputs are
+// Three organisations ("The v0.24.0 port", bullet "Deterministic unpermute": per-pair outputs are
 // placed bijectively and summed in a fixed order, no atomics on values):
 //  * routed (8 < P <= kDecodeMaxPairs): one group per kChunk pairs of an active expert, found
 //    by each workgroup from the ids (no routing pass, see pair_group); the down kernel writes
 //    per-pair rows o[p] and combine_kernel sums them in j order per token.
+//  * sorted (any P; AUTO from kSortedMinPairs): workgroup rows walk the chunk list of a routing
+//    pass in expert order; up to kWideMaxPairs pairs an expert's rows form groups of 16 whose
+//    gate_up reduction is split over workgroups (one weight pass per 16 rows) and whose down
+//    stage takes 8 rows per pass (decode_gate_up_sorted_kernel, decode_down_sorted_kernel).
 //  * direct (tiny batches, P = T*top_k <= kDirectMaxPairs): no routing pass; gate_up runs one
 //    group per pair, and one down kernel covers every pair of a column block and combines in LDS.
 #include <algorithm>

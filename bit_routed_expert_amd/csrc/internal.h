@@ -112,7 +112,9 @@ hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const Route
 //  kDecodeRouted - each workgroup row finds its expert's pairs from the ids (no routing pass);
 //  kDecodeDirect - P <= kDirectMaxPairs, one group per pair; the down launch also writes y;
 //  kDecodeSorted - workgroup rows walk the chunk list of a routing pass (kDecodeChunk rows per
-//                  chunk, in expert order), so one expert's chunks run together.
+//                  chunk, in expert order), so one expert's chunks run together; with the wide
+//                  list (P <= kWideMaxPairs) groups of 4 chunks share one weight pass (split
+//                  gate_up reduction, 8-row down).
 enum { kDecodeRouted = 0, kDecodeDirect = 1, kDecodeSorted = 2 };
 hipError_t launch_decode_gate_up(const moe_w2_planes* p, int T, int top_k, const void* x,
                                  const int32_t* ids, const Workspace& ws, uint8_t* wsb, int mode,
