@@ -168,9 +168,9 @@ def test_nvfp4_errors_and_invalid_ids(gpu):
 
 
 @pytest.mark.parametrize("T", [1, 8, 32, 96])
-def test_nvfp4_decode_full_shape_sampled_tokens(gpu, T):
+def test_nvfp4_decode_full_shape_every_token(gpu, T):
     """K=4096, I=2048 (the decode shape) with E=64 experts and uniform top-8 routing, AUTO path
-    (T = 96 is 768 pairs: the sorted organisation); tokens sampled for the f64 oracle."""
+    (T = 96 is 768 pairs: the GEMMs): every token against the f64 oracle."""
     rng = np.random.default_rng(70 + T)
     K, I, E = 4096, 2048, 64
     planes = workloads.draw_planes_nvfp4(rng, E, K, I)
@@ -179,9 +179,8 @@ def test_nvfp4_decode_full_shape_sampled_tokens(gpu, T):
     c = dict(planes, x=x, topk_ids=ids, topk_w=w)
     h = pack_nv(c)
     y = _fwd(h, c, moe.PATH_AUTO)
-    toks = np.unique(np.array([0, T // 2, T - 1]))
-    err = rel_max_err(y[toks], _oracle(c, tokens=toks, workers=4))
-    print(f"nvfp4 decode T={T}: tokens {toks.tolist()} rel max err {err:.2e}")
+    err = rel_max_err(y, _oracle(c, workers=4))
+    print(f"nvfp4 decode T={T}: every token rel max err {err:.2e}")
     assert err <= TOL
 
 
