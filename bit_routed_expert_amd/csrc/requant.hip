@@ -126,62 +126,36 @@ nvfp4_to_w2_kernel(long long nblocks, long long blocks_per_tensor,
 // of one block differ by at most 14 for fp8 and not at all for MXFP4, so a_k < 2^42):
 //   D(e) 2^-Z = Q(e) 2^(2e - Z) - A(e) 2^(e + 1 + Pm - Z),  Q = 32 + 15 n4(e),
 //   A(e) = sum a_k + 3 * sum over {t_k > e} a_k,
-// with the same thresholds t_k and window [top-6, top] as above.
+// with the same thresholds t_k and window [top-6, top] as above. Each format's structure shrinks
+// the per-candidate work: FP8 blocks share the scale's significand, MXFP4 blocks also the exponent.
 // ------------------------------------------------------------------------------------------------
-__device__ void search_block(const uint32_t (&N)[32], const int (&P)[32], uint32_t neg, uint32_t& c0, uint32_t& c1,
-                             int& best) {
-  constexpr int kNone = -100000;
-  int t[32];
-  int top = kNone, Pm = 1 << 30;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    t[k] = kNone;
-    if (N[k]) {
-      const int L = ilog2_u32(N[k]);
-      t[k] = P[k] + L - 1 + (4ull * N[k] > (5ull << L) ? 1 : 0);
-      const int c = P[k] + L + ((N[k] & (N[k] - 1)) ? 1 : 0);
-      top = c > top ? c : top;
-      Pm = P[k] < Pm ? P[k] : Pm;
-    }
+
+// Candidate exponents [top-6, top] of a block (clamped to [-127, 127]) scored by D(e) 2^-Z, ties
+// to the lower exponent, from per-candidate sums: n4(e) elements above their threshold and a4(e)
+// the sum of their a_k / F. SUMS(e, n4, a4) computes them; A = F (tot + 3 a4) in units of 2^Pm.
+template <class V = __int128, class Sums>
+__device__ int best_exponent(int top, int Pm, uint64_t F, uint64_t tot, Sums sums) {
+  const int lo = max(-127, min(127, top - 6));
+  const int hi = max(-127, min(127, top));
+  const int Z = min(2 * lo, lo + 1 + Pm);
+  V best_v = 0;
+  int best = lo;
+  for (int e = lo; e <= hi; ++e) {
+    uint32_t n4;
+    uint64_t a4;
+    sums(e, n4, a4);
+    const V A = (V)(F * (tot + 3ull * a4));
+    const V Q = 32 + 15 * (int)n4;
+    const V v = (Q << (2 * e - Z)) - (A << (e + 1 + Pm - Z));
+    if (e == lo || v < best_v) { best_v = v; best = e; }
   }
-  best = -127;
-  if (top != kNone) {
-    const int lo = max(-127, min(127, top - 6));
-    const int hi = max(-127, min(127, top));
-    const int Z = min(2 * lo, lo + 1 + Pm);
-    uint64_t a[32], tot = 0;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      a[k] = N[k] ? (uint64_t)N[k] << (P[k] - Pm) : 0ull;
-      tot += a[k];
-    }
-    __int128 best_v = 0;
-    for (int e = lo; e <= hi; ++e) {
-      uint64_t a4 = 0;
-      int n4 = 0;
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const bool q4 = t[k] > e;
-        a4 += q4 ? a[k] : 0ull;
-        n4 += q4 ? 1 : 0;
-      }
-      const __int128 A = (__int128)(tot + 3ull * a4);
-      const __int128 Q = 32 + 15 * n4;
-      const __int128 v = (Q << (2 * e - Z)) - (A << (e + 1 + Pm - Z));
-      if (e == lo || v < best_v) { best_v = v; best = e; }
-    }
-  }
-  c0 = c1 = 0;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const bool q4 = t[k] > best;
-    const bool ng = (neg >> k) & 1u;
-    const uint32_t c = ng ? (q4 ? 0u : 1u) : (q4 ? 3u : 2u);
-    if (k < 16) c0 |= c << (2 * k); else c1 |= c << (2 * (k - 16));
-  }
+  return best;
 }
 
-// fp8 e4m3 [n][R][C] with fp32 scales [n][R/128][C/128]: one thread per 32-element block.
+// fp8 e4m3 [n][R][C] with fp32 scales [n][R/128][C/128]: one thread per 32-element block. The
+// block's scale significand F is common to its elements, so a_k = F * (S_k << (P_k - Pm)) with
+// the e4m3 significand S_k <= 15 and P_k - Pm <= 14: the per-candidate sums run in 32 bits over
+// S_k << (P_k - Pm) (< 2^18 each, < 2^23 over the block) with the count packed in bits 24 up.
 __global__ void __launch_bounds__(256)
 fp8_block128_to_w2_kernel(long long nblocks, int R, int C, const uint8_t* __restrict__ e4m3,
                           const float* __restrict__ bscale, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -202,30 +176,67 @@ fp8_block128_to_w2_kernel(long long nblocks, int R, int C, const uint8_t* __rest
   const uint32_t sneg = su >> 31;
   const u32x4_t w0 = *reinterpret_cast<const u32x4_t*>(e4m3 + 32 * b);
   const u32x4_t w1 = *reinterpret_cast<const u32x4_t*>(e4m3 + 32 * b + 16);
-  uint32_t N[32];
-  int P[32];
+  constexpr int kNone = -100000;
+  uint32_t S[32];
+  int P[32], t[32];
   uint32_t neg = 0;
   bool nan = false;
+  int top = kNone, Pm = 1 << 30;
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
     const uint32_t word = k < 16 ? w0[k >> 2] : w1[(k - 16) >> 2];
     const uint32_t byte = (word >> (8 * (k & 3))) & 0xffu;
     const int ex = (byte >> 3) & 15, mt = byte & 7;
     nan |= ex == 15 && mt == 7;
-    const uint32_t S = ex ? 8u + mt : (uint32_t)mt;
-    N[k] = S * F;                            // < 2^28
+    S[k] = ex ? 8u + mt : (uint32_t)mt;
     P[k] = (ex ? ex - 10 : -9) + G;
     neg |= (((byte >> 7) ^ sneg) & 1u) << k;
+    const uint32_t N = S[k] * F;                // < 2^28
+    t[k] = kNone;
+    if (N) {
+      const int L = ilog2_u32(N);
+      t[k] = P[k] + L - 1 + (4ull * N > (5ull << L) ? 1 : 0);
+      const int c = P[k] + L + ((N & (N - 1)) ? 1 : 0);
+      top = c > top ? c : top;
+      Pm = P[k] < Pm ? P[k] : Pm;
+    }
   }
   if (nan) { atomicOr(flag, 1); *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{0, 0}; scales[b] = 0; return; }
-  uint32_t c0, c1;
-  int best;
-  search_block(N, P, neg, c0, c1, best);
+  int best = -127;
+  if (top != kNone) {
+    uint32_t w[32], tot = 0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const uint32_t a = S[k] ? S[k] << (P[k] - Pm) : 0u;
+      tot += a;
+      w[k] = a + (1u << 24);
+    }
+    best = best_exponent(top, Pm, F, tot, [&](int e, uint32_t& n4, uint64_t& a4) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) acc += t[k] > e ? w[k] : 0u;
+      n4 = acc >> 24;
+      a4 = acc & 0xffffffu;
+    });
+  }
+  uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const bool q4 = t[k] > best;
+    const bool ng = (neg >> k) & 1u;
+    const uint32_t c = ng ? (q4 ? 0u : 1u) : (q4 ? 3u : 2u);
+    if (k < 16) c0 |= c << (2 * k); else c1 |= c << (2 * (k - 16));
+  }
   *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{c0, c1};
   scales[b] = (uint8_t)(best + 127);
 }
 
-// MXFP4 e2m1 [n][R][C/2] with UE8M0 bytes [n][R][C/32]: one thread per 32-element block.
+// MXFP4 e2m1 [n][R][C/2] with UE8M0 bytes [n][R][C/32]: one thread per 32-element block. Every
+// element shares the exponent P = b - 128 and N = twice its e2m1 magnitude (0, 1, 2, 3, 4, 6, 8,
+// 12), so its threshold is P + d with d = -1, 0, 1, 1, 2, 2, 3 by magnitude (from the formula
+// above: L - 1 + [4N > 5 * 2^L]), and its ceil(log2 N) is 0, 1, 2, 2, 3, 3, 4. Each candidate then
+// needs only per-class counts and magnitude sums, accumulated once per block in packed fields
+// (class c = d + 2 = 1..5: count in 6 bits at 6c, sum of N in 9 bits at 9c).
 __global__ void __launch_bounds__(256)
 mxfp4_to_w2_kernel(long long nblocks, const uint8_t* __restrict__ e2m1, const uint8_t* __restrict__ ue8m0,
                    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int32_t* __restrict__ flag) {
@@ -235,19 +246,48 @@ mxfp4_to_w2_kernel(long long nblocks, const uint8_t* __restrict__ e2m1, const ui
   if (sb == 255) { atomicOr(flag, 1); *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{0, 0}; scales[b] = 0; return; }
   const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(e2m1 + 16 * b);
   constexpr uint64_t kTwiceMag = 0x0C08060403020100ull;
-  uint32_t N[32];
-  int P[32];
-  uint32_t neg = 0;
+  // per magnitude index i = nibble & 7: class (3 bits each) and ceil(log2 N) (3 bits each)
+  constexpr uint32_t kClass = (1u << 3) | (2u << 6) | (3u << 9) | (3u << 12) | (4u << 15) | (4u << 18) | (5u << 21);
+  constexpr uint32_t kCeilLog = (0u << 3) | (1u << 6) | (2u << 9) | (2u << 12) | (3u << 15) | (3u << 18) | (4u << 21);
+  const int P = sb - 128;                     // 2^(b-127), halved
+  uint32_t neg = 0, imax = 0;
+  uint64_t cnt = 0, msum = 0;
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
     const uint32_t nib = (raw[k >> 3] >> (4 * (k & 7))) & 15u;
-    N[k] = (uint32_t)((kTwiceMag >> (8 * (nib & 7))) & 0xff);   // twice the e2m1 magnitude
-    P[k] = sb - 128;                                              // 2^(b-127), halved
+    const uint32_t i = nib & 7u;
+    const uint32_t c = (kClass >> (3 * i)) & 7u;
+    cnt += 1ull << (6 * c);
+    msum += ((kTwiceMag >> (8 * i)) & 0xffull) << (9 * c);
     neg |= ((nib >> 3) & 1u) << k;
+    imax = i > imax ? i : imax;
   }
-  uint32_t c0, c1;
-  int best;
-  search_block(N, P, neg, c0, c1, best);
+  int best = -127;
+  if (imax) {
+    const int top = P + (int)((kCeilLog >> (3 * imax)) & 7u);
+    uint64_t tot = 0;
+#pragma unroll
+    for (int c = 1; c <= 5; ++c) tot += (msum >> (9 * c)) & 511ull;
+    // every exponent lies within 6 below and 4 above P, so both shifts stay below 21 and the
+    // scores (< 2^31) fit in 64 bits
+    best = best_exponent<int64_t>(top, P, 1ull, tot, [&](int e, uint32_t& n4, uint64_t& a4) {
+      n4 = 0;
+      a4 = 0;
+#pragma unroll
+      for (int c = 1; c <= 5; ++c)
+        if (P + c - 2 > e) { n4 += (uint32_t)((cnt >> (6 * c)) & 63ull); a4 += (msum >> (9 * c)) & 511ull; }
+    });
+  }
+  uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t nib = (raw[k >> 3] >> (4 * (k & 7))) & 15u;
+    const uint32_t c = (kClass >> (3 * (nib & 7u))) & 7u;
+    const bool q4 = c && P + (int)c - 2 > best;
+    const bool ng = (neg >> k) & 1u;
+    const uint32_t code = ng ? (q4 ? 0u : 1u) : (q4 ? 3u : 2u);
+    if (k < 16) c0 |= code << (2 * k); else c1 |= code << (2 * (k - 16));
+  }
   *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{c0, c1};
   scales[b] = (uint8_t)(best + 127);
 }
