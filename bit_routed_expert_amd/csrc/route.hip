@@ -164,7 +164,9 @@ route_fast_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __rest
   extern __shared__ int lds[];
   const int nb = E + 1;
   uint32_t* masks = reinterpret_cast<uint32_t*>(lds);     // [nb][32]
-  int* start = lds + nb * kFastWords;                      // [nb]
+  int* pre = lds + nb * kFastWords;                        // [nb][32] pairs of the bin in earlier words
+  int* cntb = pre + nb * kFastWords;                       // [nb] pairs of the bin
+  int* start = cntb + nb;                                  // [nb]
   int* wsum = start + nb;                                  // [16]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int i = tid; i < nb * kFastWords; i += kFastThreads) masks[i] = 0;
@@ -172,16 +174,29 @@ route_fast_kernel(const int32_t* __restrict__ ids, int E, int P, int32_t* __rest
   const int bin = tid < P ? bin_of(ids[tid], E) : -1;
   if (bin >= 0) atomicOr(&masks[bin * kFastWords + tid / 32], 1u << (tid % 32));
   __syncthreads();
+  // per (bin, word): the word's pair count and the exclusive prefix over the bin's words, one
+  // bin per 32 lanes (kFastWords = 32 words per bin, and 1024 % 32 == 0 keeps a segment on one bin)
+  for (int i = tid; i < nb * kFastWords; i += kFastThreads) {
+    const int pc = __popc(masks[i]);
+    int inc = pc;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const int o = __shfl_up(inc, d, 32);
+      if ((lane & 31) >= d) inc += o;
+    }
+    pre[i] = inc - pc;
+    if ((i & 31) == 31) cntb[i >> 5] = inc;
+  }
+  __syncthreads();
   int rank = 0;
   if (bin >= 0) {
-    const uint32_t* m = masks + bin * kFastWords;
-    for (int w = 0; w < tid / 32; ++w) rank += __popc(m[w]);
-    rank += __popc(m[tid / 32] & ((1u << (tid % 32)) - 1u));
+    const int wi = bin * kFastWords + tid / 32;
+    rank = pre[wi] + __popc(masks[wi] & ((1u << (tid % 32)) - 1u));
   }
   int c = 0;
   uint32_t v = 0;
   if (tid < nb) {
-    for (int w = 0; w < kFastWords; ++w) c += __popc(masks[tid * kFastWords + w]);
+    c = cntb[tid];
     v = (uint32_t)c << 20;
     if (tid < E && c > 0) v |= ((uint32_t)((c + bm - 1) / bm) << 10) | 1u;
   }
@@ -320,7 +335,7 @@ hipError_t launch_route(int E, int T, int top_k, const int32_t* ids, const Route
   const int P = T * top_k;
   const int nb = E + 1;
   if (P <= kFastThreads && E <= 256) {
-    size_t lds = (size_t)nb * kFastWords * 4 + (size_t)nb * 4 + 16 * 4;
+    size_t lds = (size_t)2 * nb * kFastWords * 4 + (size_t)2 * nb * 4 + 16 * 4;
     hipLaunchKernelGGL(route_fast_kernel, dim3(1), dim3(kFastThreads), lds, s, ids, E, P, o.offsets, o.perm,
                        o.active, o.meta, o.tiles, o.counters, o.max_tiles, o.tile_rows, o.wide);
     return hipGetLastError();
