@@ -32,6 +32,7 @@ Workspace workspace_layout(int E, int K, int I, int T, int top_k) {
   w.aq = o;        o += align_up((size_t)P * (I / kTileK) * kA6Bytes);
   w.pair_out = o;  o += align_up((size_t)P * K * 4);
   w.gu_part = o;   o += P <= kWideMaxPairs ? align_up((size_t)kWideSlices * P * 2 * I * 4) : 0;
+  w.pair_ncs = o;  o += align_up((size_t)P * 4);
   w.slot_ids = o;  o += align_up((size_t)P * 4);
   w.total = o;
   return w;

@@ -603,7 +603,8 @@ template <int NPW, int FMT, int NW>
 __global__ void __launch_bounds__(64 * NW)
 decode_gate_up_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                              const uint16_t* __restrict__ x, _Float16* __restrict__ act, float* __restrict__ gu_part,
-                             int P, int K, int I, int top_k, SortedChunk sc, const float* __restrict__ scale2) {
+                             int32_t* __restrict__ pair_ncs, int P, int K, int I, int top_k, SortedChunk sc,
+                             const float* __restrict__ scale2) {
   constexpr int KS = NW / NPW;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int row_pair[kWideRows];
@@ -614,7 +615,12 @@ decode_gate_up_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* _
   const int e = c.e;
   const bool wide = c.ncs > 1;
   const int n = min(wide ? kWideRows : kChunk, sc.offsets[e + 1] - c.rs);
-  if (tid < kWideRows) row_pair[tid] = sc.perm[c.rs + min(tid, n - 1)];
+  if (tid < kWideRows) {
+    const int pp = sc.perm[c.rs + min(tid, n - 1)];
+    row_pair[tid] = pp;
+    // the slice count of each pair's group, for wide_finish_kernel (one writer per pair)
+    if (blockIdx.x == 0 && c.cs == 0 && tid < n) pair_ncs[pp] = c.ncs;
+  }
   const int nkt = K / kTileK, nrg = 2 * I / kTileRows;
   const int k0 = c.cs * nkt / c.ncs, nk = (c.cs + 1) * nkt / c.ncs - k0;
   const int pw = w / KS, ks = w % KS;
@@ -656,22 +662,16 @@ decode_gate_up_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* _
   }
 }
 
-// Gated rows of the split groups: for sorted row blockIdx.x whose group has more than one slice,
-// a = silu(sum of the gate slices) * (sum of the up slices), slices added in order, rounded to
-// fp16 into act[pair]. Other rows return at once.
+// Gated rows of the split groups: for pair blockIdx.x whose group has more than one slice (its
+// slice count written by the gate_up kernel this forward), a = silu(sum of the gate slices) *
+// (sum of the up slices), slices added in order, rounded to fp16 into act[pair]. Other pairs, and
+// pairs whose id is outside [0, E) (never written), return at once.
 __global__ void __launch_bounds__(256)
-wide_finish_kernel(const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-                   const int32_t* __restrict__ ids, const float* __restrict__ gu_part, _Float16* __restrict__ act,
-                   int P, int E, int I) {
-  const int r = blockIdx.x;
-  if (r >= offsets[E]) return;
-  const int p = perm[r];
-  const int e = ids[p];
-  const int base = offsets[e], ne = offsets[e + 1] - base;
-  const int g = (r - base) / kWideRows;
-  const int ng = min(kWideRows, ne - g * kWideRows);
-  const int ncs = (ng + kChunk - 1) / kChunk;
-  if (ncs < 2) return;
+wide_finish_kernel(const int32_t* __restrict__ ids, const int32_t* __restrict__ pair_ncs,
+                   const float* __restrict__ gu_part, _Float16* __restrict__ act, int P, int E, int I) {
+  const int p = blockIdx.x;
+  const int id = ids[p], ncs = pair_ncs[p];
+  if (id < 0 || id >= E || ncs < 2) return;
   for (int i = 4 * (int)threadIdx.x; i < I; i += 4 * 256) {
     f32x4_t gs = *reinterpret_cast<const f32x4_t*>(gu_part + (size_t)p * 2 * I + i);
     f32x4_t us = *reinterpret_cast<const f32x4_t*>(gu_part + (size_t)p * 2 * I + I + i);
@@ -1019,20 +1019,20 @@ static hipError_t decode_gate_up_fmt(const moe_w2_planes* p, int T, int top_k, c
     }
     lds_s = std::max(lds_s, (size_t)kWaves * 2 * 4 * 64 * 4);
     float* gu_part = (float*)(wsb + ws.gu_part);
+    int32_t* pair_ncs = (int32_t*)(wsb + ws.pair_ncs);
     if (pick_np(min(p->E, P)) == 4 && sorted_wide8(lds_s))
       hipLaunchKernelGGL((decode_gate_up_sorted_kernel<8, FMT, 8>), dim3(p->I / 128, ws.max_chunks), dim3(512),
-                         lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, P, p->K, p->I, top_k, sc, p->scale2);
+                         lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, pair_ncs, P, p->K, p->I, top_k, sc, p->scale2);
     else if (pick_np(min(p->E, P)) == 4)
       hipLaunchKernelGGL((decode_gate_up_sorted_kernel<4, FMT, kWaves>), dim3(p->I / 64, ws.max_chunks),
-                         dim3(kThreads), lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, P, p->K, p->I, top_k,
-                         sc, p->scale2);
+                         dim3(kThreads), lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, pair_ncs, P, p->K,
+                         p->I, top_k, sc, p->scale2);
     else
       hipLaunchKernelGGL((decode_gate_up_sorted_kernel<1, FMT, kWaves>), dim3(p->I / 16, ws.max_chunks),
-                         dim3(kThreads), lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, P, p->K, p->I, top_k,
-                         sc, p->scale2);
+                         dim3(kThreads), lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, pair_ncs, P, p->K,
+                         p->I, top_k, sc, p->scale2);
     if (wide)
-      hipLaunchKernelGGL(wide_finish_kernel, dim3(P), dim3(256), 0, s, sc.offsets, sc.perm, ids, gu_part, act, P,
-                         p->E, p->I);
+      hipLaunchKernelGGL(wide_finish_kernel, dim3(P), dim3(256), 0, s, ids, pair_ncs, gu_part, act, P, p->E, p->I);
   } else if (pick_np(min(p->E, P)) == 4) {   // at most this many workgroup rows do work
     hipLaunchKernelGGL((decode_gate_up_kernel<4, kDecodeRouted, FMT>), dim3(p->I / 64, P), dim3(kThreads), lds, s,
                        p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc, p->scale2);

@@ -57,6 +57,7 @@ struct Workspace {
   size_t pair_out;    // fp32 [P][K] per-pair down outputs, indexed by pair id
   size_t gu_part;     // fp32 [kWideSlices][P][2I] gate (first I) and up partial sums of the sorted
                       // decode organisation's reduction slices, by pair id (P <= kWideMaxPairs)
+  size_t pair_ncs;    // int32 [P] reduction slices of each valid pair's group (sorted organisation)
   size_t slot_ids;    // int32 [P] the ids mapped to slots (slot forward)
   size_t total;
   int P, nchunks, max_tiles, max_chunks;
