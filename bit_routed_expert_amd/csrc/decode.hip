@@ -499,16 +499,6 @@ MOEW2_DEV bool chunk_entry(const SortedChunk& sc, int ti, ChunkEntry& c) {
   c.ncs = ((v >> 22) & 3) + 1;
   return true;
 }
-MOEW2_DEV bool sorted_chunk(const SortedChunk& sc, int ti, int& e, int& n, int (&pr)[kChunk]) {
-  ChunkEntry c;
-  if (!chunk_entry(sc, ti, c)) return false;
-  e = c.e;
-  const int rs = c.rs + kChunk * c.cs;
-  n = min(kChunk, sc.offsets[e + 1] - rs);
-#pragma unroll
-  for (int m = 0; m < kChunk; ++m) pr[m] = sc.perm[rs + min(m, n - 1)];
-  return true;
-}
 static_assert(kChunk == kDecodeChunk, "the routing pass cuts chunks of the decode kernels' size");
 
 // ---------------------------------------------------------------------------------------------
@@ -516,15 +506,14 @@ static_assert(kChunk == kDecodeChunk, "the routing pass cuts chunks of the decod
 // group 2q, up row group 2q+1) over the reduction slice w%KS of KS = 4/NP.
 // kDecodeDirect: group = pair blockIdx.y (expert ids[p]). kDecodeRouted: group = the kChunk pairs
 // of expert ids[blockIdx.y] from blockIdx.y on, when blockIdx.y starts such a chunk (pair_group).
-// kDecodeSorted: group = chunk blockIdx.y of the routing pass. The gated row of pair p is act[p]
-// in all three.
+// The gated row of pair p is act[p] in both.
 // ---------------------------------------------------------------------------------------------
 template <int NPW, int MODE, int FMT>
 __global__ void __launch_bounds__(kThreads)
 decode_gate_up_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                       const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
                       _Float16* __restrict__ act, long long* __restrict__ counters,
-                      int P, int E, int K, int I, int top_k, SortedChunk sc, const float* __restrict__ scale2) {
+                      int P, int E, int K, int I, int top_k, const float* __restrict__ scale2) {
   constexpr int KS = kWaves / NPW;
   constexpr bool DIRECT = MODE == kDecodeDirect;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -698,30 +687,24 @@ wide_finish_kernel(const int32_t* __restrict__ ids, const int32_t* __restrict__ 
 // combine_kernel then sums them per token in j order. The blockIdx.x == 0 workgroups count the
 // gated intermediates that overflowed fp16 (each pair belongs to one group).
 // ---------------------------------------------------------------------------------------------
-template <int NPW, int FMT, int R, int MODE>
+template <int NPW, int FMT, int R>
 __global__ void __launch_bounds__(kThreads)
 decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                    const _Float16* __restrict__ act, const int32_t* __restrict__ ids,
                    float* __restrict__ pair_out, long long* __restrict__ counters, int P, int E, int K,
-                   int I, SortedChunk sc, const float* __restrict__ scale2) {
+                   int I, const float* __restrict__ scale2) {
   constexpr int KS = kWaves / NPW;
   static_assert(R == 1 || KS == 1, "row pairs per wave need the whole reduction in each wave");
-  static_assert(MODE == kDecodeRouted || MODE == kDecodeSorted, "the direct organisation has its own down kernel");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ ScanLds sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
-  int e, n;
+  int e, n_e, first;
+  if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, nullptr, e, n_e, first)) return;
+  const int n = min(kChunk, n_e - first);
   int pr[kChunk];
-  if constexpr (MODE == kDecodeSorted) {
-    if (!sorted_chunk(sc, blockIdx.y, e, n, pr)) return;
-  } else {
-    int n_e, first;
-    if (!pair_group(ids, P, E, blockIdx.y, sh, tid, lane, w, nullptr, e, n_e, first)) return;
-    n = min(kChunk, n_e - first);
 #pragma unroll
-    for (int m = 0; m < kChunk; ++m) pr[m] = pair_at(sh, first + min(m, n - 1));
-  }
+  for (int m = 0; m < kChunk; ++m) pr[m] = pair_at(sh, first + min(m, n - 1));
   const int nkt = I / kTileK, nrg = K / kTileRows;
   const int pw = w / KS, ks = w % KS;
   const int rq = (blockIdx.x * NPW + pw) * R;   // the wave's first row pair
@@ -1000,10 +983,9 @@ static hipError_t decode_gate_up_fmt(const moe_w2_planes* p, int T, int top_k, c
   const uint16_t* xb = (const uint16_t*)x;
   _Float16* act = (_Float16*)(wsb + ws.act);
   long long* cnt = (long long*)(wsb + ws.counters);
-  const SortedChunk sc = sorted_chunks(ws, wsb);
   if (mode == kDecodeDirect) {
     hipLaunchKernelGGL((decode_gate_up_kernel<1, kDecodeDirect, FMT>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc, p->scale2);
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, p->scale2);
   } else if (mode == kDecodeSorted) {
     // one workgroup row per chunk entry of the routing pass (at most max_chunks; rows past meta[1]
     // exit); the same split of the reduction over waves as the routed organisation, so that
@@ -1020,6 +1002,7 @@ static hipError_t decode_gate_up_fmt(const moe_w2_planes* p, int T, int top_k, c
     lds_s = std::max(lds_s, (size_t)kWaves * 2 * 4 * 64 * 4);
     float* gu_part = (float*)(wsb + ws.gu_part);
     int32_t* pair_ncs = (int32_t*)(wsb + ws.pair_ncs);
+    const SortedChunk sc = sorted_chunks(ws, wsb);
     if (pick_np(min(p->E, P)) == 4 && sorted_wide8(lds_s))
       hipLaunchKernelGGL((decode_gate_up_sorted_kernel<8, FMT, 8>), dim3(p->I / 128, ws.max_chunks), dim3(512),
                          lds_s, s, p->gu_codes, p->gu_scales, xb, act, gu_part, pair_ncs, P, p->K, p->I, top_k, sc, p->scale2);
@@ -1035,10 +1018,10 @@ static hipError_t decode_gate_up_fmt(const moe_w2_planes* p, int T, int top_k, c
       hipLaunchKernelGGL(wide_finish_kernel, dim3(P), dim3(256), 0, s, ids, pair_ncs, gu_part, act, P, p->E, p->I);
   } else if (pick_np(min(p->E, P)) == 4) {   // at most this many workgroup rows do work
     hipLaunchKernelGGL((decode_gate_up_kernel<4, kDecodeRouted, FMT>), dim3(p->I / 64, P), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc, p->scale2);
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, p->scale2);
   } else {
     hipLaunchKernelGGL((decode_gate_up_kernel<1, kDecodeRouted, FMT>), dim3(p->I / 16, P), dim3(kThreads), lds, s,
-                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, sc, p->scale2);
+                       p->gu_codes, p->gu_scales, xb, ids, act, cnt, P, p->E, p->K, p->I, top_k, p->scale2);
   }
   return hipGetLastError();
 }
@@ -1052,7 +1035,7 @@ hipError_t launch_decode_gate_up(const moe_w2_planes* p, int T, int top_k, const
                           : decode_gate_up_fmt<kFmtW2>(p, T, top_k, x, ids, ws, wsb, mode, s);
 }
 
-template <int FMT, int MODE>
+template <int FMT>
 static hipError_t decode_down_routed(const moe_w2_planes* p, int rows, int P, const int32_t* ids, const Workspace& ws,
                                      uint8_t* wsb, hipStream_t s) {
   const int groups = min(p->E, P);   // both organisations split the reduction alike (bit-identical results)
@@ -1060,17 +1043,16 @@ static hipError_t decode_down_routed(const moe_w2_planes* p, int rows, int P, co
   const _Float16* act = (const _Float16*)(wsb + ws.act);
   long long* cnt = (long long*)(wsb + ws.counters);
   float* po = (float*)(wsb + ws.pair_out);
-  const SortedChunk sc = sorted_chunks(ws, wsb);
   const bool two_pairs = FMT == kFmtW2 && (p->I / kTileK) % kRing == 0 && p->K % 256 == 0;
   if (pick_np(groups) == 4 && two_pairs)
-    hipLaunchKernelGGL((decode_down_kernel<4, FMT, 2, MODE>), dim3(p->K / 256, rows), dim3(kThreads), lds, s,
-                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc, p->scale2);
+    hipLaunchKernelGGL((decode_down_kernel<4, FMT, 2>), dim3(p->K / 256, rows), dim3(kThreads), lds, s,
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, p->scale2);
   else if (pick_np(groups) == 4)
-    hipLaunchKernelGGL((decode_down_kernel<4, FMT, 1, MODE>), dim3(p->K / 128, rows), dim3(kThreads), lds, s,
-                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc, p->scale2);
+    hipLaunchKernelGGL((decode_down_kernel<4, FMT, 1>), dim3(p->K / 128, rows), dim3(kThreads), lds, s,
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, p->scale2);
   else
-    hipLaunchKernelGGL((decode_down_kernel<1, FMT, 1, MODE>), dim3(p->K / 32, rows), dim3(kThreads), lds, s,
-                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, sc, p->scale2);
+    hipLaunchKernelGGL((decode_down_kernel<1, FMT, 1>), dim3(p->K / 32, rows), dim3(kThreads), lds, s,
+                       p->dn_codes, p->dn_scales, act, ids, po, cnt, P, p->E, p->K, p->I, p->scale2);
   return hipGetLastError();
 }
 
@@ -1117,7 +1099,7 @@ static hipError_t decode_down_fmt(const moe_w2_planes* p, int T, int top_k, cons
     return hipGetLastError();
   }
   return mode == kDecodeSorted ? decode_down_sorted<FMT>(p, P, ws, wsb, s)
-                               : decode_down_routed<FMT, kDecodeRouted>(p, P, P, ids, ws, wsb, s);
+                               : decode_down_routed<FMT>(p, P, P, ids, ws, wsb, s);
 }
 
 hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const int32_t* ids, const float* w,
