@@ -604,12 +604,7 @@ decode_gate_up_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* _
   const int e = c.e;
   const bool wide = c.ncs > 1;
   const int n = min(wide ? kWideRows : kChunk, sc.offsets[e + 1] - c.rs);
-  if (tid < kWideRows) {
-    const int pp = sc.perm[c.rs + min(tid, n - 1)];
-    row_pair[tid] = pp;
-    // the slice count of each pair's group, for wide_finish_kernel (one writer per pair)
-    if (blockIdx.x == 0 && c.cs == 0 && tid < n) pair_ncs[pp] = c.ncs;
-  }
+  if (tid < kWideRows) row_pair[tid] = sc.perm[c.rs + min(tid, n - 1)];
   const int nkt = K / kTileK, nrg = 2 * I / kTileRows;
   const int k0 = c.cs * nkt / c.ncs, nk = (c.cs + 1) * nkt / c.ncs - k0;
   const int pw = w / KS, ks = w % KS;
@@ -649,6 +644,11 @@ decode_gate_up_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* _
       }
     }
   }
+  // the slice count of each pair's group, for wide_finish_kernel (one writer per pair). Last, after
+  // every use of blockIdx.x: under a blockIdx.x == 0 test the compiler substitutes 0 for it, and a
+  // use past the test's lane-divergent join then takes a vector register, which turns every weight
+  // offset derived from it into a per-load loop over the lanes' values.
+  if (blockIdx.x == 0 && c.cs == 0 && w == 0 && lane < n) pair_ncs[row_pair[lane]] = c.ncs;
 }
 
 // Gated rows of the split groups: for pair blockIdx.x whose group has more than one slice (its
