@@ -22,6 +22,33 @@ namespace {
 
 __device__ __forceinline__ int ilog2_u32(uint32_t v) { return 31 - __clz(v); }  // v > 0
 
+// Per half-block the search works on magnitude classes instead of elements: the 16 elements share
+// SF and P, so an element's threshold depends only on its e2m1 magnitude class m (m2 = 1, 2, 3,
+// 4, 6, 8, 12 for m = 1..7; class 0 is zero and never takes magnitude 4). The thresholds rise with
+// m and come in two runs: m2 = 2^a (classes 1, 2, 4, 6) gives T1 + a, m2 = 3 * 2^a (classes 3, 5,
+// 7) gives T3 + a, with T1, T3 from SF and 3 SF alone. At a candidate e the elements taking
+// magnitude 4 are therefore those of class >= m*(e) = 1 + #{classes with threshold <= e}, and the
+// counts and m2 sums over such suffixes of classes are tabulated once per half (counts by a
+// compare on all 8 nibbles of a word at once). The candidate scores are exact in 64 bits: the
+// scaled terms stay below 2^61 (top - min P <= 46, |P0 - P1| <= 14).
+__device__ __forceinline__ uint32_t byte_at(uint32_t lo, uint32_t hi, int i) {   // byte i (0..7) of hi:lo
+  return __builtin_amdgcn_ubfe(i < 4 ? lo : hi, 8 * (i & 3), 8);
+}
+// number of nibbles of w whose low three bits are >= m (1 <= m <= 8)
+__device__ __forceinline__ int nibbles_ge(uint32_t y, int m) {
+  return __popc((y + (uint32_t)(8 - m) * 0x11111111u) & 0x88888888u);
+}
+// 2-bit codes of 8 elements (nibbles of w): sign from bit 3 (flipped by nsg), magnitude 4 for the
+// classes >= ms; code = 2 (+1), 3 (+4), 1 (-1), 0 (-4), element i at bits 2i..2i+1
+__device__ __forceinline__ uint32_t word_codes(uint32_t w, uint32_t nsg, int ms) {
+  const uint32_t negw = (w ^ (nsg ? 0x88888888u : 0u)) & 0x88888888u;
+  const uint32_t q4w = ((w & 0x77777777u) + (uint32_t)(8 - ms) * 0x11111111u) & 0x88888888u;
+  uint32_t x = ((~negw & 0x88888888u) >> 2) | ((q4w ^ negw) >> 3);
+  x = (x | (x >> 2)) & 0x0F0F0F0Fu;
+  x = (x | (x >> 4)) & 0x00FF00FFu;
+  return (x | (x >> 8)) & 0x0000FFFFu;
+}
+
 __global__ void __launch_bounds__(256)
 nvfp4_to_w2_kernel(long long nblocks, long long blocks_per_tensor,
                    const uint8_t* __restrict__ e2m1, const uint8_t* __restrict__ e4m3,
@@ -40,9 +67,13 @@ nvfp4_to_w2_kernel(long long nblocks, long long blocks_per_tensor,
   if (sexp == 0) { F = su & 0x7fffffu; G = -149; } else { F = (su & 0x7fffffu) | 0x800000u; G = sexp - 150; }
   // e4m3 per half: significand S (<= 15) and exponent
   const uint16_t sb = *reinterpret_cast<const uint16_t*>(e4m3 + 2 * b);
-  uint32_t SF[2];
-  int P[2];
-  uint32_t nsg[2];
+  const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(e2m1 + 16 * b);
+  constexpr int kNone = -100000;
+  constexpr int kLow = -(1 << 20);   // thresholds of a half whose scale is zero: below every candidate
+  uint32_t SF[2], nsg[2], cl[2], ch[2], sl[2], sh[2], tot[2];
+  int P[2], T1[2], T3[2];
+  int top = kNone;
+#pragma unroll
   for (int j = 0; j < 2; ++j) {
     const uint32_t byte = (sb >> (8 * j)) & 0xffu;
     const int ex = (byte >> 3) & 15, mt = byte & 7;
@@ -53,66 +84,67 @@ nvfp4_to_w2_kernel(long long nblocks, long long blocks_per_tensor,
     SF[j] = S * F;               // < 2^28
     P[j] = pe + G - 1;           // the -1 undoes the doubled e2m1 magnitude
     nsg[j] = (byte >> 7) ^ neg2;
-  }
-  const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(e2m1 + 16 * b);
-  // twice the e2m1 magnitude of nibble n&7: 0,1,2,3,4,6,8,12
-  constexpr uint64_t kTwiceMag = 0x0C08060403020100ull;
-  constexpr int kNone = -100000;
-  uint32_t m2[32];
-  int t[32];
-  uint32_t neg = 0, tot[2] = {0, 0};
-  int top = kNone;
+    // suffix counts c[m] (elements of class >= m) and m2 sums s[m], m = 1..8, as bytes m - 1
+    const uint32_t y0 = raw[2 * j] & 0x77777777u, y1 = raw[2 * j + 1] & 0x77777777u;
+    int c[9], sm[9];
+    c[8] = 0;
+    sm[8] = 0;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const uint32_t word = raw[k >> 3];
-    const uint32_t nib = (word >> (4 * (k & 7))) & 15u;
-    const int j = k >> 4;
-    m2[k] = (uint32_t)((kTwiceMag >> (8 * (nib & 7))) & 0xff);
-    tot[j] += m2[k];
-    neg |= (((nib >> 3) ^ nsg[j]) & 1u) << k;
-    const uint32_t N = m2[k] * SF[j];
-    t[k] = kNone;
-    if (N) {
-      const int L = ilog2_u32(N);
-      t[k] = P[j] + L - 1 + (4ull * N > (5ull << L) ? 1 : 0);
-      const int c = P[j] + L + ((N & (N - 1)) ? 1 : 0);
-      top = c > top ? c : top;
+    for (int m = 7; m >= 1; --m) {
+      c[m] = nibbles_ge(y0, m) + nibbles_ge(y1, m);
+      const int m2 = m == 1 ? 1 : m == 2 ? 2 : m == 3 ? 3 : m == 4 ? 4 : m == 5 ? 6 : m == 6 ? 8 : 12;
+      sm[m] = sm[m + 1] + (c[m] - c[m + 1]) * m2;
+    }
+    cl[j] = (uint32_t)c[1] | (uint32_t)c[2] << 8 | (uint32_t)c[3] << 16 | (uint32_t)c[4] << 24;
+    ch[j] = (uint32_t)c[5] | (uint32_t)c[6] << 8 | (uint32_t)c[7] << 16;
+    sl[j] = (uint32_t)sm[1] | (uint32_t)sm[2] << 8 | (uint32_t)sm[3] << 16 | (uint32_t)sm[4] << 24;
+    sh[j] = (uint32_t)sm[5] | (uint32_t)sm[6] << 8 | (uint32_t)sm[7] << 16;
+    tot[j] = (uint32_t)sm[1];
+    if (SF[j] == 0) {
+      T1[j] = T3[j] = kLow;
+    } else {
+      const uint32_t s3 = 3u * SF[j];
+      const int L1 = ilog2_u32(SF[j]), L3 = ilog2_u32(s3);
+      T1[j] = P[j] - 1 + L1 + (4ull * SF[j] > (5ull << L1) ? 1 : 0);
+      T3[j] = P[j] - 1 + L3 + (4ull * s3 > (5ull << L3) ? 1 : 0);
+      // the half's largest magnitude: its highest class present
+      const int mhi = (c[1] > 0) + (c[2] > 0) + (c[3] > 0) + (c[4] > 0) + (c[5] > 0) + (c[6] > 0) + (c[7] > 0);
+      if (mhi > 0) {
+        const uint32_t m2 = (uint32_t)((0x0C08060403020100ull >> (8 * mhi)) & 0xff);
+        const uint32_t N = m2 * SF[j];
+        const int L = ilog2_u32(N);
+        const int ct = P[j] + L + ((N & (N - 1)) ? 1 : 0);
+        top = ct > top ? ct : top;
+      }
     }
   }
+  // first class taking magnitude 4 at exponent e, per half
+  auto mstar = [&](int j, int e) {
+    return 1 + min(max(e - T1[j] + 1, 0), 4) + min(max(e - T3[j] + 1, 0), 3);
+  };
   int best = -127;
   if (top != kNone) {
-    int lo = max(-127, min(127, top - 6));
-    int hi = max(-127, min(127, top));
+    const int lo = max(-127, min(127, top - 6));
+    const int hi = max(-127, min(127, top));
     const int Pm = min(P[0], P[1]);
     const int Z = min(2 * lo, lo + 1 + Pm);
-    __int128 best_v = 0;
+    long long best_v = 0;
     for (int e = lo; e <= hi; ++e) {
-      // m2 sums of the elements above their threshold, and their count (bits 16 up)
-      uint32_t acc0 = 0, acc1 = 0;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) acc0 += t[k] > e ? m2[k] + 65536u : 0u;
-#pragma unroll
-      for (int k = 16; k < 32; ++k) acc1 += t[k] > e ? m2[k] + 65536u : 0u;
-      const int n4 = (int)((acc0 >> 16) + (acc1 >> 16));
-      // A_j = SF_j * sum over the half of (q4 ? 4 : 1) * m2
-      const uint64_t A0 = (uint64_t)SF[0] * (tot[0] + 3u * (acc0 & 0xffffu));
-      const uint64_t A1 = (uint64_t)SF[1] * (tot[1] + 3u * (acc1 & 0xffffu));
-      const __int128 A = ((__int128)A0 << (P[0] - Pm)) + ((__int128)A1 << (P[1] - Pm));
+      const int m0 = mstar(0, e) - 1, m1 = mstar(1, e) - 1;
+      const int n4 = (int)(byte_at(cl[0], ch[0], m0) + byte_at(cl[1], ch[1], m1));
+      const uint64_t A0 = (uint64_t)SF[0] * (tot[0] + 3u * byte_at(sl[0], sh[0], m0));
+      const uint64_t A1 = (uint64_t)SF[1] * (tot[1] + 3u * byte_at(sl[1], sh[1], m1));
+      const uint64_t A = (A0 << (P[0] - Pm)) + (A1 << (P[1] - Pm));
       // D(e) = Q 2^(2e) - A 2^(e+1+Pm), scaled by 2^-Z with Z below both exponents for every
-      // candidate, so both shifts are non-negative and every value is an exact integer.
-      const __int128 Q = 32 + 15 * n4;
-      const __int128 v = (Q << (2 * e - Z)) - (A << (e + 1 + Pm - Z));
+      // candidate, so both shifts are non-negative and every value is an exact integer
+      const uint64_t Q = 32u + 15u * (uint32_t)n4;
+      const long long v = (long long)(Q << (2 * e - Z)) - (long long)(A << (e + 1 + Pm - Z));
       if (e == lo || v < best_v) { best_v = v; best = e; }
     }
   }
-  uint32_t c0 = 0, c1 = 0;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const bool q4 = t[k] > best;
-    const bool ng = (neg >> k) & 1u;
-    const uint32_t c = ng ? (q4 ? 0u : 1u) : (q4 ? 3u : 2u);
-    if (k < 16) c0 |= c << (2 * k); else c1 |= c << (2 * (k - 16));
-  }
+  const int ms0 = top != kNone ? mstar(0, best) : 8, ms1 = top != kNone ? mstar(1, best) : 8;
+  const uint32_t c0 = word_codes(raw[0], nsg[0], ms0) | word_codes(raw[1], nsg[0], ms0) << 16;
+  const uint32_t c1 = word_codes(raw[2], nsg[1], ms1) | word_codes(raw[3], nsg[1], ms1) << 16;
   *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{c0, c1};
   scales[b] = (uint8_t)(best + 127);
 }

@@ -48,6 +48,25 @@ def test_full_range_inputs_bit_exact(gpu):
     assert np.array_equal(c, wc)
 
 
+def test_half_blocks_at_opposite_scale_ends_bit_exact(gpu):
+    """The two 16-element halves of each 32-block with e4m3 scales at opposite ends of the range
+    (one near 448, one subnormal or zero), over scale_2 from the smallest subnormal to 2^100: the
+    widest spread between the halves' exponents, where the candidates' exact scores are largest."""
+    rng = np.random.default_rng(17)
+    n, R, C = 8, 32, 512
+    e2m1 = rng.integers(0, 256, size=(n, R, C // 2), dtype=np.uint8)
+    e4m3 = np.empty((n, R, C // 16), np.uint8)
+    e4m3[..., 0::2] = rng.integers(0x70, 0x7F, size=(n, R, C // 32))            # large, finite
+    e4m3[..., 1::2] = rng.integers(0, 8, size=(n, R, C // 32))                  # subnormal or zero
+    e4m3[:, ::2] = np.flip(e4m3[:, ::2], axis=-1)                               # either half large
+    e4m3 |= (rng.integers(0, 2, size=e4m3.shape) << 7).astype(np.uint8)         # random signs
+    s2 = np.array([1.4e-45, 2.0 ** -126, 3.7e-3, 1.0, -0.75, 7.0, 2.0 ** 100, -3.0e38], np.float32)
+    c, s = _gpu(e2m1, e4m3, s2)
+    wc, ws = requant.nvfp4_to_w2(e2m1, e4m3, s2, window=False)
+    assert np.array_equal(s, ws)
+    assert np.array_equal(c, wc)
+
+
 def test_nan_inputs_are_reported(gpu):
     e2m1 = np.zeros((1, 1, 16), np.uint8)
     e4m3 = np.array([[[0x38, 0x7F]]], np.uint8)
