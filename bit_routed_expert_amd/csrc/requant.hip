@@ -185,14 +185,23 @@ __device__ int best_exponent(int top, int Pm, uint64_t F, uint64_t tot, Sums sum
 }
 
 // fp8 e4m3 [n][R][C] with fp32 scales [n][R/128][C/128]: one thread per 32-element block. The
-// block's scale significand F is common to its elements, so a_k = F * (S_k << (P_k - Pm)) with
-// the e4m3 significand S_k <= 15 and P_k - Pm <= 14: the per-candidate sums run in 32 bits over
-// S_k << (P_k - Pm) (< 2^18 each, < 2^23 over the block) with the count packed in bits 24 up.
-__global__ void __launch_bounds__(256)
+// block's scale significand F is common to its elements, and every element's exponent P_k is at
+// least G - 9 (the e4m3 subnormal exponent under the block scale), so a_k = F * (S_k << (P_k -
+// G + 9)) in units of 2^(G-9), with the e4m3 significand S_k <= 15 and P_k - G + 9 <= 14: the
+// per-candidate sums run in 32 bits over S_k << (P_k - G + 9) (< 2^18 each, < 2^23 over the block)
+// with the count packed in bits 24 up. Each element takes magnitude 4 at the candidates lo + i
+// with i < d = clamp(t - lo, 0, 7), so it is added once, to bucket d of its thread (LDS,
+// bucket-major so that the lanes of a wave hit distinct banks), and candidate i reads the sum of
+// the buckets above i. The scores are exact in 64 bits: A = F (tot + 3 a4) < 2^49 and the scaled
+// terms stay below 2^57.
+constexpr int kFp8Threads = 256;
+__global__ void __launch_bounds__(kFp8Threads)
 fp8_block128_to_w2_kernel(long long nblocks, int R, int C, const uint8_t* __restrict__ e4m3,
                           const float* __restrict__ bscale, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                           int32_t* __restrict__ flag) {
-  const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ uint32_t bucket[8][kFp8Threads];   // this thread's column only: no barriers
+  const int tid = threadIdx.x;
+  const long long b = (long long)blockIdx.x * blockDim.x + tid;
   if (b >= nblocks) return;
   const int nb_row = C / 32;
   const long long row = b / nb_row;           // row over all tensors
@@ -202,54 +211,71 @@ fp8_block128_to_w2_kernel(long long nblocks, int R, int C, const uint8_t* __rest
   const float sc = bscale[(tensor * (R / 128) + r / 128) * (C / 128) + c32 / 4];
   const uint32_t su = __builtin_bit_cast(uint32_t, sc);
   const int sexp = (su >> 23) & 255;
-  if (sexp == 255) { atomicOr(flag, 1); *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{0, 0}; scales[b] = 0; return; }
-  const uint32_t F = sexp ? ((su & 0x7fffffu) | 0x800000u) : (su & 0x7fffffu);
-  const int G = sexp ? sexp - 150 : -149;
-  const uint32_t sneg = su >> 31;
   const u32x4_t w0 = *reinterpret_cast<const u32x4_t*>(e4m3 + 32 * b);
   const u32x4_t w1 = *reinterpret_cast<const u32x4_t*>(e4m3 + 32 * b + 16);
-  constexpr int kNone = -100000;
-  uint32_t S[32];
-  int P[32], t[32];
+  const uint32_t wd[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+  // NaN bytes (0x7f / 0xff) and the sign bits, four bytes at a time
+  bool nan = sexp == 255;
   uint32_t neg = 0;
-  bool nan = false;
-  int top = kNone, Pm = 1 << 30;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const uint32_t word = k < 16 ? w0[k >> 2] : w1[(k - 16) >> 2];
-    const uint32_t byte = (word >> (8 * (k & 3))) & 0xffu;
-    const int ex = (byte >> 3) & 15, mt = byte & 7;
-    nan |= ex == 15 && mt == 7;
-    S[k] = ex ? 8u + mt : (uint32_t)mt;
-    P[k] = (ex ? ex - 10 : -9) + G;
-    neg |= (((byte >> 7) ^ sneg) & 1u) << k;
-    const uint32_t N = S[k] * F;                // < 2^28
-    t[k] = kNone;
-    if (N) {
-      const int L = ilog2_u32(N);
-      t[k] = P[k] + L - 1 + (4ull * N > (5ull << L) ? 1 : 0);
-      const int c = P[k] + L + ((N & (N - 1)) ? 1 : 0);
-      top = c > top ? c : top;
-      Pm = P[k] < Pm ? P[k] : Pm;
-    }
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t x = (wd[q] & 0x7f7f7f7fu) ^ 0x7f7f7f7fu;            // zero byte <=> NaN
+    nan |= ((x - 0x01010101u) & ~x & 0x80808080u) != 0u;
+    const uint32_t sg = (wd[q] >> 7) & 0x01010101u;                      // sign of byte i at bit 8i
+    neg |= ((sg * 0x00204081u) >> 21 & 0xfu) << (4 * q);                 // bits 21..24: bytes 0..3
   }
   if (nan) { atomicOr(flag, 1); *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{0, 0}; scales[b] = 0; return; }
+  if (su >> 31) neg = ~neg;
+  const uint32_t F = sexp ? ((su & 0x7fffffu) | 0x800000u) : (su & 0x7fffffu);
+  const int G = sexp ? sexp - 150 : -149;
+  constexpr int kNone = -100000;
+  int t[32];
+  int top = kNone;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t byte = (wd[k >> 2] >> (8 * (k & 3))) & 0xffu;
+    const int ex = (byte >> 3) & 15, mt = byte & 7;
+    const uint32_t N = (ex ? 8u + mt : (uint32_t)mt) * F;   // < 2^28, so 4N and 5 * 2^L fit 32 bits
+    const int P = (ex ? ex - 10 : -9) + G;
+    // branch-free: a zero N gets the threshold kNone and no say in top
+    const int L = ilog2_u32(N | 1u);
+    const int tk = P + L - 1 + (4u * N > (5u << L) ? 1 : 0);
+    const int c = P + L + ((N & (N - 1)) ? 1 : 0);
+    t[k] = N ? tk : kNone;
+    top = max(top, N ? c : kNone);
+  }
   int best = -127;
   if (top != kNone) {
-    uint32_t w[32], tot = 0;
+    const int lo = max(-127, min(127, top - 6));
+    const int hi = max(-127, min(127, top));
+    const int Pr = G - 9;                    // reference exponent, below every element's
+    const int Z = min(2 * lo, lo + 1 + Pr);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) bucket[d][tid] = 0u;
+    uint32_t tot = 0;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
-      const uint32_t a = S[k] ? S[k] << (P[k] - Pm) : 0u;
+      const uint32_t byte = (wd[k >> 2] >> (8 * (k & 3))) & 0xffu;
+      const int ex = (byte >> 3) & 15, mt = byte & 7;
+      const uint32_t a = (ex ? 8u + mt : (uint32_t)mt) << (ex ? ex - 1 : 0);   // S << (P - Pr)
       tot += a;
-      w[k] = a + (1u << 24);
+      const int d = min(max(t[k] - lo, 0), 7);
+      atomicAdd(&bucket[d][tid], a + (1u << 24));   // bucket 0: never magnitude 4 (unused)
     }
-    best = best_exponent(top, Pm, F, tot, [&](int e, uint32_t& n4, uint64_t& a4) {
-      uint32_t acc = 0;
+    // candidates from the top down; ties go to the lower exponent
+    uint32_t acc = 0;
+    long long best_v = 0;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) acc += t[k] > e ? w[k] : 0u;
-      n4 = acc >> 24;
-      a4 = acc & 0xffffffu;
-    });
+    for (int i = 6; i >= 0; --i) {
+      acc += bucket[i + 1][tid];
+      const int e = lo + i;
+      const uint64_t A = (uint64_t)F * (tot + 3ull * (acc & 0xffffffu));
+      const uint64_t Q = 32u + 15u * (acc >> 24);
+      if (e <= hi) {
+        const long long v = (long long)(Q << (2 * e - Z)) - (long long)(A << (e + 1 + Pr - Z));
+        if (e == hi || v <= best_v) { best_v = v; best = e; }
+      }
+    }
   }
   uint32_t c0 = 0, c1 = 0;
 #pragma unroll
@@ -330,7 +356,8 @@ hipError_t launch_fp8_block128_to_w2(int n, int R, int C, const uint8_t* e4m3, c
                                      uint8_t* codes, uint8_t* scales, int32_t* flag, hipStream_t s) {
   const long long nb = (long long)n * R * (C / 32);
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL(fp8_block128_to_w2_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, nb, R, C, e4m3,
+  hipLaunchKernelGGL(fp8_block128_to_w2_kernel, dim3((unsigned)((nb + kFp8Threads - 1) / kFp8Threads)), dim3(kFp8Threads), 0,
+                     s, nb, R, C, e4m3,
                      bscale, codes, scales, flag);
   return hipGetLastError();
 }
