@@ -479,7 +479,7 @@ MOEW2_DEV int pair_at(const ScanLds& sh, int m) {
 // << 20 | (slices - 1) << 22. A group of at most kChunk rows is one entry (cs = 0, one slice);
 // with the wide list (forwards of at most kWideMaxPairs pairs) an expert's rows form groups of
 // kWideRows, each entry of a larger group one of its ceil(rows / kChunk) slices. The down stage
-// takes entry (rs, cs) as the kChunk rows rs + kChunk * cs .. of the group.
+// takes such a group as halves of kDownRows rows, one per even entry.
 constexpr int kWideRows = kWideSlices * kChunk;   // 16: one full MFMA row tile
 struct SortedChunk {
   const int32_t* offsets;
