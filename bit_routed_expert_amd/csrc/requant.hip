@@ -291,10 +291,13 @@ fp8_block128_to_w2_kernel(long long nblocks, int R, int C, const uint8_t* __rest
 
 // MXFP4 e2m1 [n][R][C/2] with UE8M0 bytes [n][R][C/32]: one thread per 32-element block. Every
 // element shares the exponent P = b - 128 and N = twice its e2m1 magnitude (0, 1, 2, 3, 4, 6, 8,
-// 12), so its threshold is P + d with d = -1, 0, 1, 1, 2, 2, 3 by magnitude (from the formula
-// above: L - 1 + [4N > 5 * 2^L]), and its ceil(log2 N) is 0, 1, 2, 2, 3, 3, 4. Each candidate then
-// needs only per-class counts and magnitude sums, accumulated once per block in packed fields
-// (class c = d + 2 = 1..5: count in 6 bits at 6c, sum of N in 9 bits at 9c).
+// 12 for magnitude index m = 0..7), so its threshold is P + d_m with d = -1, 0, 1, 1, 2, 2, 3 for
+// m = 1..7 (from the formula above: L - 1 + [4N > 5 * 2^L]), rising with m: at a candidate e the
+// elements taking magnitude 4 are those of index >= m*(e) = 1 + #{m : d_m <= e - P}. The suffix
+// counts and m2 sums over m are tabulated once per block (counts by a compare on all 8 nibbles of
+// a word at once) and each candidate reads one table entry; the final codes come from the same
+// nibble compare. Every exponent lies within 6 below and 4 above P, so both shifts of the scores
+// stay below 21 and the scores (< 2^31) fit in 64 bits.
 __global__ void __launch_bounds__(256)
 mxfp4_to_w2_kernel(long long nblocks, const uint8_t* __restrict__ e2m1, const uint8_t* __restrict__ ue8m0,
                    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int32_t* __restrict__ flag) {
@@ -303,49 +306,46 @@ mxfp4_to_w2_kernel(long long nblocks, const uint8_t* __restrict__ e2m1, const ui
   const int sb = ue8m0[b];
   if (sb == 255) { atomicOr(flag, 1); *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{0, 0}; scales[b] = 0; return; }
   const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(e2m1 + 16 * b);
-  constexpr uint64_t kTwiceMag = 0x0C08060403020100ull;
-  // per magnitude index i = nibble & 7: class (3 bits each) and ceil(log2 N) (3 bits each)
-  constexpr uint32_t kClass = (1u << 3) | (2u << 6) | (3u << 9) | (3u << 12) | (4u << 15) | (4u << 18) | (5u << 21);
-  constexpr uint32_t kCeilLog = (0u << 3) | (1u << 6) | (2u << 9) | (2u << 12) | (3u << 15) | (3u << 18) | (4u << 21);
   const int P = sb - 128;                     // 2^(b-127), halved
-  uint32_t neg = 0, imax = 0;
-  uint64_t cnt = 0, msum = 0;
+  uint32_t y[4];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const uint32_t nib = (raw[k >> 3] >> (4 * (k & 7))) & 15u;
-    const uint32_t i = nib & 7u;
-    const uint32_t c = (kClass >> (3 * i)) & 7u;
-    cnt += 1ull << (6 * c);
-    msum += ((kTwiceMag >> (8 * i)) & 0xffull) << (9 * c);
-    neg |= ((nib >> 3) & 1u) << k;
-    imax = i > imax ? i : imax;
+  for (int q = 0; q < 4; ++q) y[q] = raw[q] & 0x77777777u;
+  // suffix counts c[m] and m2 sums s[m] (m = 1..8) of the indices >= m, as (c | s << 6) pairs,
+  // two per word: entry m - 1 in bits 16 ((m - 1) & 1) of word (m - 1) >> 1
+  int c[9], sm[9];
+  c[8] = 0;
+  sm[8] = 0;
+#pragma unroll
+  for (int m = 7; m >= 1; --m) {
+    c[m] = nibbles_ge(y[0], m) + nibbles_ge(y[1], m) + nibbles_ge(y[2], m) + nibbles_ge(y[3], m);
+    const int m2 = m == 1 ? 1 : m == 2 ? 2 : m == 3 ? 3 : m == 4 ? 4 : m == 5 ? 6 : m == 6 ? 8 : 12;
+    sm[m] = sm[m + 1] + (c[m] - c[m + 1]) * m2;
   }
+  uint32_t tab[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    tab[q] = ((uint32_t)c[2 * q + 1] | (uint32_t)sm[2 * q + 1] << 6) |
+             ((uint32_t)c[2 * q + 2] | (uint32_t)sm[2 * q + 2] << 6) << 16;
+  const int imax = (c[1] > 0) + (c[2] > 0) + (c[3] > 0) + (c[4] > 0) + (c[5] > 0) + (c[6] > 0) + (c[7] > 0);
+  // #{m in 1..7 : d_m <= x} for x = -2 (or less) .. 3 (or more): 0, 1, 2, 4, 6, 7
+  auto mstar = [&](int e) {
+    const int x = min(max(e - P + 2, 0), 5);
+    return 1 + (int)((0x764210u >> (4 * x)) & 15u);
+  };
   int best = -127;
   if (imax) {
-    const int top = P + (int)((kCeilLog >> (3 * imax)) & 7u);
-    uint64_t tot = 0;
-#pragma unroll
-    for (int c = 1; c <= 5; ++c) tot += (msum >> (9 * c)) & 511ull;
-    // every exponent lies within 6 below and 4 above P, so both shifts stay below 21 and the
-    // scores (< 2^31) fit in 64 bits
-    best = best_exponent<int64_t>(top, P, 1ull, tot, [&](int e, uint32_t& n4, uint64_t& a4) {
-      n4 = 0;
-      a4 = 0;
-#pragma unroll
-      for (int c = 1; c <= 5; ++c)
-        if (P + c - 2 > e) { n4 += (uint32_t)((cnt >> (6 * c)) & 63ull); a4 += (msum >> (9 * c)) & 511ull; }
+    // ceil(log2 N) of the largest magnitude: 0, 1, 2, 2, 3, 3, 4 for m = 1..7
+    const int top = P + (int)((0x4332210u >> (4 * (imax - 1))) & 15u);
+    best = best_exponent<int64_t>(top, P, 1ull, (uint64_t)sm[1], [&](int e, uint32_t& n4, uint64_t& a4) {
+      const int q = mstar(e) - 1;
+      const uint32_t v = (q & 2 ? (q & 4 ? tab[3] : tab[1]) : (q & 4 ? tab[2] : tab[0])) >> (16 * (q & 1));
+      n4 = v & 63u;
+      a4 = (v >> 6) & 1023u;
     });
   }
-  uint32_t c0 = 0, c1 = 0;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const uint32_t nib = (raw[k >> 3] >> (4 * (k & 7))) & 15u;
-    const uint32_t c = (kClass >> (3 * (nib & 7u))) & 7u;
-    const bool q4 = c && P + (int)c - 2 > best;
-    const bool ng = (neg >> k) & 1u;
-    const uint32_t code = ng ? (q4 ? 0u : 1u) : (q4 ? 3u : 2u);
-    if (k < 16) c0 |= code << (2 * k); else c1 |= code << (2 * (k - 16));
-  }
+  const int ms = imax ? mstar(best) : 8;
+  const uint32_t c0 = word_codes(raw[0], 0u, ms) | word_codes(raw[1], 0u, ms) << 16;
+  const uint32_t c1 = word_codes(raw[2], 0u, ms) | word_codes(raw[3], 0u, ms) << 16;
   *reinterpret_cast<u32x2_t*>(codes + 8 * b) = u32x2_t{c0, c1};
   scales[b] = (uint8_t)(best + 127);
 }
