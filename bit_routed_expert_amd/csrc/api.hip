@@ -2,6 +2,7 @@
 // sequence of kernel launches for each entry point.
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -31,7 +32,7 @@ Workspace workspace_layout(int E, int K, int I, int T, int top_k) {
   w.act = o;       o += align_up((size_t)P * I * 2);
   w.aq = o;        o += align_up((size_t)P * (I / kTileK) * kA6Bytes);
   w.pair_out = o;  o += align_up((size_t)P * K * 4);
-  w.gu_part = o;   o += P <= kWideMaxPairs ? align_up((size_t)kWideSlices * P * 2 * I * 4) : 0;
+  w.gu_part = o;   o += P <= kWideMaxPairs ? align_up((size_t)P * std::max(kWideSlices * 2 * I, K) * 4) : 0;
   w.pair_ncs = o;  o += align_up((size_t)P * 4);
   w.slot_ids = o;  o += align_up((size_t)P * 4);
   w.total = o;
@@ -330,9 +331,13 @@ int moe_w2_forward_stage(const moe_w2_planes* p, int stage, int T, int top_k, co
       break;
     default:
       // the direct decode down stage already combined into y
-      if (!direct)
+      if (!direct) {
+        // the sorted organisation's wide list splits the down stage of large groups in two halves
+        const bool wide = mode == kDecodeSorted && T * top_k <= kWideMaxPairs;
         err = launch_combine(T, top_k, p->E, p->K, topk_ids, topk_w, (const float*)(wsb + ws.pair_out), y,
-                             out_dtype, s);
+                             out_dtype, s, wide ? (const int32_t*)(wsb + ws.pair_ncs) : nullptr,
+                             wide ? (const float*)(wsb + ws.gu_part) : nullptr);
+      }
   }
   return hip_status(err);
 }

@@ -292,24 +292,26 @@ MOEW2_DEV void stream_k(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt, i
   }
 }
 
-// R row pairs of one wave as one continuous stream (KS = 1, nkt a multiple of kRing): the slot
-// that held k-tile kt of row pair r is refilled with step r * nkt + kt + kRing of the sequence,
+// R row pairs of one wave as one continuous stream (KS = 1, nk a multiple of kRing): the slot
+// that held k-tile kt of row pair r is refilled with step r * nk + kt + kRing of the sequence,
 // which past the pair's last k-tile is the next pair's first, so the ring never drains between
-// pairs. Row pair r accumulates into acc[r]; rows of pair r + 1 start at tile 2 * nkt further.
+// pairs. Row pair r accumulates into acc[r]. The stream covers k-tiles koff .. koff + nk - 1 of
+// rows with nkt k-tiles each (rows of pair r + 1 start at tile 2 * nkt further); the staged rows
+// hold the reduction from k-tile koff on.
 template <int NP, int NB, int FMT, int R>
-MOEW2_DEV void stream_rows(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt, int nkt, const uint8_t* arow,
-                           int KR, int g, f32x4_t (&acc)[R][NB], int lane) {
+MOEW2_DEV void stream_rows(TileRegs<NB, FMT> (&ring)[kRing], const WaveTiles& wt, int nk, const uint8_t* arow,
+                           int KR, int g, f32x4_t (&acc)[R][NB], int lane, int nkt, int koff = 0) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    for (int k0 = 0; k0 < nkt; k0 += kRing) {
+    for (int k0 = 0; k0 < nk; k0 += kRing) {
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         const int kt = k0 + i;
         mma_tile<NP, NB, FMT>(ring[i], arow, KR, kt, g, acc[r]);
         const int kn = kt + kRing;
-        const bool wrap = kn >= nkt;
+        const bool wrap = kn >= nk;
         const int rn = wrap ? r + 1 : r;
-        load_tile<NB, FMT>(ring[i], wt, 2 * rn * nkt + (wrap ? kn - nkt : kn), rn < R, lane);
+        load_tile<NB, FMT>(ring[i], wt, 2 * rn * nkt + koff + (wrap ? kn - nk : kn), rn < R, lane);
       }
     }
   }
@@ -736,7 +738,7 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
       stream_k<AR, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, I, lane >> 4, acc[0], lane);
       reduce_split_k<KS>(acc[0], red, w, ks, lane);
     } else {
-      stream_rows<AR, 2, FMT, R>(ring, wt, nkt, lds + (size_t)ma * stride, I, lane >> 4, acc, lane);
+      stream_rows<AR, 2, FMT, R>(ring, wt, nkt, lds + (size_t)ma * stride, I, lane >> 4, acc, lane, nkt);
     }
     if (ks == 0 && lane < 16) {
 #pragma unroll
@@ -758,46 +760,54 @@ decode_down_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict_
 
 // ---------------------------------------------------------------------------------------------
 // down of the sorted organisation: grid (K / (32*NPW*R), chunk entries), NW waves per workgroup.
-// With the wide list an even entry cs of a group takes its rows 8 (cs / 2) .. + 7 (odd entries
-// exit), so one weight pass serves up to 8 rows over the whole reduction; with the plain list an
-// entry is its 4-row chunk. Per-row arithmetic as in the routed kernel (bit-identical rows).
+// With the wide list a group of at most kDownRows rows is taken by its entry 0 over the whole
+// reduction (its other entry exits); a larger group (three or four entries) by its entries 0 and
+// 1, each over all its rows and one half of the reduction (k-tiles [0, nkt/2) and [nkt/2, nkt)),
+// writing fp32 partial rows to pair_out and pair_out2 (summed by the combine), so one weight pass
+// serves up to 16 rows; entries 2 and 3 exit. With the plain list an entry is its 4-row chunk.
+// Per-row arithmetic of an unsplit group as in the routed kernel (bit-identical rows).
 // ---------------------------------------------------------------------------------------------
 constexpr int kDownRows = 2 * kChunk;
 template <int NPW, int FMT, int R, int NW>
 __global__ void __launch_bounds__(64 * NW)
 decode_down_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                          const _Float16* __restrict__ act, float* __restrict__ pair_out,
+                          const _Float16* __restrict__ act, float* __restrict__ pair_out, float* __restrict__ pair_out2,
                           long long* __restrict__ counters, int K, int I, int wide, SortedChunk sc,
                           const float* __restrict__ scale2) {
   constexpr int KS = NW / NPW;
   static_assert(R == 1 || KS == 1, "row pairs per wave need the whole reduction in each wave");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int row_pair[kDownRows];
+  __shared__ int row_pair[kWideRows];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform in the wave)
   ChunkEntry c;
   if (!chunk_entry(sc, blockIdx.y, c)) return;
-  if (wide && (c.cs & 1)) return;
+  const bool split = wide && c.ncs > 2;                      // more than kDownRows rows
+  if (wide && c.cs >= (split ? 2 : 1)) return;
   const int e = c.e;
-  const int row0 = wide ? c.rs + kDownRows * (c.cs >> 1) : c.rs + kChunk * c.cs;
-  const int n = min(wide ? kDownRows : kChunk, sc.offsets[e + 1] - row0);
-  if (tid < kDownRows) row_pair[tid] = sc.perm[row0 + min(tid, n - 1)];
+  const int h = split ? c.cs : 0;                            // reduction half of a split group
+  const int row0 = c.rs + kChunk * c.cs * !wide;
+  const int n = min(wide ? (split ? kWideRows : kDownRows) : kChunk, sc.offsets[e + 1] - row0);
+  if (tid < kWideRows) row_pair[tid] = sc.perm[row0 + min(tid, n - 1)];
   const int nkt = I / kTileK, nrg = K / kTileRows;
+  const int k0 = h * (nkt / 2), nk = split ? (h ? nkt - nkt / 2 : nkt / 2) : nkt;   // this entry's k-tiles
   const int pw = w / KS, ks = w % KS;
   const int rq = (blockIdx.x * NPW + pw) * R;   // the wave's first row pair
   WaveTiles wt = wave_tiles<FMT>(codes, scales, e, (uint32_t)(nrg * nkt));
   wt.tile[0] = (uint32_t)(2 * rq * nkt);
   wt.tile[1] = (uint32_t)((2 * rq + 1) * nkt);
-  const int kb = ks * nkt / KS, ke = (ks + 1) * nkt / KS;
+  const int kb = k0 + ks * nk / KS, ke = k0 + (ks + 1) * nk / KS;
   constexpr int AR = kARow<FMT>;
-  const int stride = MxRow<AR>::stride(I);
+  const int KR = nk * kTileK;
+  const int stride = MxRow<AR>::stride(KR);
   const uint16_t* act16 = reinterpret_cast<const uint16_t*>(act);
   const float sd = FMT == kFmtNV4 ? scale2[3 * e + 2] : 1.f;   // NVFP4: the down tensor's scale_2
   __syncthreads();   // row_pair
   TileRegs<2, FMT> ring[kRing];
-  auto row_off = [&](int m) -> size_t { return (size_t)row_pair[m] * I; };
+  auto row_off = [&](int m) -> size_t { return (size_t)row_pair[m] * I + (size_t)k0 * kTileK; };
   int ninf = 0;
-  stage_and_prime<64 * NW, AR, 2, FMT>(ring, wt, kb, ke, lane, lds, stride, act16, I, n, row_off, tid,
+  // every staged value is counted once: by the first column slice, in each half of a split group
+  stage_and_prime<64 * NW, AR, 2, FMT>(ring, wt, kb, ke, lane, lds, stride, act16, KR, n, row_off, tid,
                                        blockIdx.x == 0, ninf);
   if (ninf) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)ninf);
   __syncthreads();
@@ -806,12 +816,13 @@ decode_down_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
 #pragma unroll
   for (int q = 0; q < R; ++q) acc[q][0] = acc[q][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (R == 1) {
-    stream_k<AR, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, I, lane >> 4, acc[0], lane);
+    stream_k<AR, 2, FMT>(ring, wt, kb, ke, lds + (size_t)ma * stride, KR, lane >> 4, acc[0], lane, k0);
     reduce_split_k16<KS>(acc[0], reinterpret_cast<float*>(lds), w, ks, lane);
   } else {
-    stream_rows<AR, 2, FMT, R>(ring, wt, nkt, lds + (size_t)ma * stride, I, lane >> 4, acc, lane);
+    stream_rows<AR, 2, FMT, R>(ring, wt, nk, lds + (size_t)ma * stride, KR, lane >> 4, acc, lane, nkt, k0);
   }
-  if (ks != 0 || lane >= 4 * kDownRows) return;
+  if (ks != 0) return;
+  float* out = h ? pair_out2 : pair_out;
   // accumulator register r of lane l holds token row 4 (l / 16) + r, column l % 16
 #pragma unroll
   for (int q = 0; q < R; ++q)
@@ -821,7 +832,7 @@ decode_down_sorted_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * (lane >> 4) + r;
-        if (row < n) pair_out[(size_t)row_pair[row] * K + col] = acc[q][b][r] * sd;
+        if (row < n) out[(size_t)row_pair[row] * K + col] = acc[q][b][r] * sd;
       }
     }
 }
@@ -913,9 +924,12 @@ decode_down_direct_kernel(const uint8_t* __restrict__ codes, const uint8_t* __re
 // y[t] = sum_j (ascending) w[t, j] * o[t*top_k + j]; ids outside [0, E) contribute nothing.
 // One thread per 4 output columns of one token. A group of up to 8 pairs has its ids, weights and
 // pair rows requested together (rows of invalid pairs are read but not used), so a token costs
-// one memory round trip per 8 pairs; the sum itself runs in ascending j.
+// one memory round trip per 8 pairs; the sum itself runs in ascending j. With pair_ncs (the
+// sorted decode organisation's wide list), a pair of a group of more than kDownRows rows has its
+// down output in two reduction halves, o = pair_out[p] + pair_out2[p], added before weighting.
 __global__ void combine_kernel(const int32_t* __restrict__ ids, const float* __restrict__ wts,
-                               const float* __restrict__ pair_out, void* __restrict__ y,
+                               const float* __restrict__ pair_out, const int32_t* __restrict__ pair_ncs,
+                               const float* __restrict__ pair_out2, void* __restrict__ y,
                                int T, int top_k, int E, int K, int out_dtype) {
   constexpr int G = 8;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -924,7 +938,7 @@ __global__ void combine_kernel(const int32_t* __restrict__ ids, const float* __r
   const int t = (int)(gid / q), c = (int)(gid - (long long)t * q) * 4;
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
   for (int j0 = 0; j0 < top_k; j0 += G) {
-    int id[G];
+    int id[G], ns[G];
     float w[G];
     float4 o[G];
 #pragma unroll
@@ -933,9 +947,23 @@ __global__ void combine_kernel(const int32_t* __restrict__ ids, const float* __r
         const int p = t * top_k + j0 + i;
         id[i] = ids[p];
         w[i] = wts[p];
+        ns[i] = pair_ncs ? pair_ncs[p] : 0;
         // each per-pair row is read once: nontemporal keeps it from evicting L2 lines
         const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pair_out + (size_t)p * K + c));
         o[i] = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+    if (pair_ncs) {
+      // second halves, requested only for the pairs whose group was split (a second round trip
+      // for those tokens; reading every pair's would cost batches without split groups as much)
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        if (j0 + i < top_k && id[i] >= 0 && id[i] < E && ns[i] > 2) {
+          const int p = t * top_k + j0 + i;
+          const f32x4_t v =
+              __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pair_out2 + (size_t)p * K + c));
+          o[i].x += v[0]; o[i].y += v[1]; o[i].z += v[2]; o[i].w += v[3];
+        }
       }
     }
 #pragma unroll
@@ -1065,24 +1093,33 @@ template <int FMT>
 static hipError_t decode_down_sorted(const moe_w2_planes* p, int P, const Workspace& ws, uint8_t* wsb, hipStream_t s) {
   const int wide = P <= kWideMaxPairs ? 1 : 0;
   const int groups = min(p->E, P);
-  const size_t rows_lds = (size_t)(wide ? kDownRows : kChunk) * MxRow<kARow<FMT>>::stride(p->I);
+  const int nkt = p->I / kTileK;
+  constexpr int AR = kARow<FMT>;
+  // staged rows: kChunk whole rows (plain list), or kDownRows whole rows / kWideRows rows over the
+  // larger reduction half (wide list)
+  const size_t rows_lds =
+      wide ? std::max((size_t)kDownRows * MxRow<AR>::stride(p->I),
+                      (size_t)kWideRows * MxRow<AR>::stride((nkt - nkt / 2) * kTileK))
+           : (size_t)kChunk * MxRow<AR>::stride(p->I);
   const float* sc2 = p->scale2;
   const _Float16* act = (const _Float16*)(wsb + ws.act);
   long long* cnt = (long long*)(wsb + ws.counters);
   float* po = (float*)(wsb + ws.pair_out);
+  float* po2 = wide ? (float*)(wsb + ws.gu_part) : nullptr;   // the gate_up partials are summed by now
   const SortedChunk sc = sorted_chunks(ws, wsb);
   const unsigned rows = (unsigned)ws.max_chunks;
-  const bool two_pairs = FMT == kFmtW2 && (p->I / kTileK) % kRing == 0;
+  // two row pairs per wave stream whole multiples of the ring: nkt, and with the wide list its halves
+  const bool two_pairs = FMT == kFmtW2 && nkt % (wide ? 2 * kRing : kRing) == 0;
   if (pick_np(groups) == 4 && two_pairs)
     hipLaunchKernelGGL((decode_down_sorted_kernel<4, FMT, 2, kWaves>), dim3(p->K / 256, rows), dim3(kThreads),
-                       rows_lds, s, p->dn_codes, p->dn_scales, act, po, cnt, p->K, p->I, wide, sc, sc2);
+                       rows_lds, s, p->dn_codes, p->dn_scales, act, po, po2, cnt, p->K, p->I, wide, sc, sc2);
   else if (pick_np(groups) == 4)
     hipLaunchKernelGGL((decode_down_sorted_kernel<4, FMT, 1, kWaves>), dim3(p->K / 128, rows), dim3(kThreads),
-                       rows_lds, s, p->dn_codes, p->dn_scales, act, po, cnt, p->K, p->I, wide, sc, sc2);
+                       rows_lds, s, p->dn_codes, p->dn_scales, act, po, po2, cnt, p->K, p->I, wide, sc, sc2);
   else
     hipLaunchKernelGGL((decode_down_sorted_kernel<1, FMT, 1, kWaves>), dim3(p->K / 32, rows), dim3(kThreads),
                        std::max(rows_lds, (size_t)kWaves * 2 * 4 * 64 * 4), s, p->dn_codes, p->dn_scales, act, po,
-                       cnt, p->K, p->I, wide, sc, sc2);
+                       po2, cnt, p->K, p->I, wide, sc, sc2);
   return hipGetLastError();
 }
 
@@ -1112,12 +1149,13 @@ hipError_t launch_decode_down(const moe_w2_planes* p, int T, int top_k, const in
 }
 
 hipError_t launch_combine(int T, int top_k, int E, int K, const int32_t* ids, const float* w,
-                          const float* pair_out, void* y, int out_dtype, hipStream_t s) {
+                          const float* pair_out, void* y, int out_dtype, hipStream_t s, const int32_t* pair_ncs,
+                          const float* pair_out2) {
   const long long n = (long long)T * (K / 4);
   if (n == 0) return hipSuccess;
   const int B = 256;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + B - 1) / B)), dim3(B), 0, s, ids, w, pair_out, y,
-                     T, top_k, E, K, out_dtype);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + B - 1) / B)), dim3(B), 0, s, ids, w, pair_out, pair_ncs,
+                     pair_out2, y, T, top_k, E, K, out_dtype);
   return hipGetLastError();
 }
 

@@ -56,7 +56,9 @@ struct Workspace {
                       // one 608-byte three-part e2m3 record per (sorted row, k-tile)
   size_t pair_out;    // fp32 [P][K] per-pair down outputs, indexed by pair id
   size_t gu_part;     // fp32 [kWideSlices][P][2I] gate (first I) and up partial sums of the sorted
-                      // decode organisation's reduction slices, by pair id (P <= kWideMaxPairs)
+                      // decode organisation's reduction slices, by pair id (P <= kWideMaxPairs);
+                      // once they are summed, fp32 [P][K]: the second reduction half of the down
+                      // stage's split groups, by pair id
   size_t pair_ncs;    // int32 [P] reduction slices of each valid pair's group (sorted organisation)
   size_t slot_ids;    // int32 [P] the ids mapped to slots (slot forward)
   size_t total;
@@ -129,8 +131,10 @@ hipError_t launch_gemm_gate_up(const moe_w2_planes* p, int T, int top_k, const v
                                const Workspace& ws, uint8_t* wsb, hipStream_t s);
 hipError_t launch_gemm_down(const moe_w2_planes* p, int T, int top_k, const Workspace& ws,
                             uint8_t* wsb, hipStream_t s);
+// pair_ncs, pair_out2: the sorted decode organisation's wide list (split down groups), else null
 hipError_t launch_combine(int T, int top_k, int E, int K, const int32_t* ids, const float* w,
-                          const float* pair_out, void* y, int out_dtype, hipStream_t s);
+                          const float* pair_out, void* y, int out_dtype, hipStream_t s,
+                          const int32_t* pair_ncs = nullptr, const float* pair_out2 = nullptr);
 
 // Re-quantizers
 hipError_t launch_fp8_block128_to_w2(int n, int R, int C, const uint8_t* e4m3, const float* bscale,
