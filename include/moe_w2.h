@@ -68,12 +68,14 @@ enum moe_w2_out_dtype { MOE_W2_OUT_BF16 = 0, MOE_W2_OUT_F32 = 1 };
  * DECODE_SORTED from 384 pairs up, DECODE below. DECODE supports T*top_k <= 512 only
  * (MOE_W2_EUNSUPPORTED above); DECODE_SORTED any number of pairs P = T*top_k with
  * P/4 + min(E, P) + 1 <= 65535 (its launch has that many workgroup rows, one per chunk of up to 4
- * pairs of one expert). Both stream an expert's weights once
- * per 4 of its pairs. DECODE finds each expert's pairs from the
- * ids inside the kernels (no routing pass); DECODE_SORTED runs a routing pass first and walks its
- * chunks in expert order, so the chunks of a popular expert run together and re-read its weights
- * from L2 rather than HBM. All paths give results within the same tolerance, and the two decode
- * organisations give bit-identical results (same per-pair arithmetic). */
+ * pairs of one expert). DECODE streams an expert's weights once per 4 of its pairs, finding
+ * each expert's pairs from the ids inside the kernels (no routing pass). DECODE_SORTED runs a
+ * routing pass first and walks its chunks in expert order, so the chunks of a popular expert run
+ * together; up to 512 pairs it groups an expert's pairs by 16 and splits a group's reductions
+ * over workgroups, so its weights stream once per 16 pairs. All paths give results within the
+ * same tolerance; the two decode organisations give bit-identical results when no expert has
+ * more than 4 pairs (same per-pair arithmetic), and otherwise differ only by the order of the
+ * fp32 sums of a split reduction. */
 enum moe_w2_path {
   MOE_W2_PATH_AUTO = 0,
   MOE_W2_PATH_DECODE = 1,
