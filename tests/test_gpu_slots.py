@@ -18,7 +18,9 @@ from gpu_helpers import dev, dev_bf16, pack, rel_max_err
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
-CASES = [(48, moe.PATH_DECODE), (300, moe.PATH_GEMM)]   # (T, path); top_k = 4
+# (T, path); top_k = 4. The sorted decode case (Zipf routing over 16 experts, ~12 pairs each) has
+# split groups in both stages.
+CASES = [(48, moe.PATH_DECODE), (48, moe.PATH_DECODE_SORTED), (300, moe.PATH_GEMM)]
 
 
 def _layer(T, seed, K=512, I=256, E=16, top_k=4):
