@@ -296,8 +296,12 @@ static_assert(kA6Bytes % 16 == 0, "split record is whole chunks");
 // stall).
 template <int FMT, class Part>
 MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][kRGW], const uint8_t* abuf, const BRegs<FMT>& br, Part part, bool mma,
-                        int rows_valid, int lane, const Fp4Masks& fm) {
+                        int rows_valid, int lane, const Fp4Masks& fm, int sshift = 0) {
   const int g = lane >> 4;
+  // scale words: the row group's two UE8M0 bytes in the low half (sshift bits down)
+  uint32_t bs[kRGW];
+#pragma unroll
+  for (int t = 0; t < kRGW; ++t) bs[t] = br.s[t][0] >> sshift;
   const uint8_t* arow = abuf + (lane & 15) * kA6Stride;
   static_for<0, 2>([&](auto cc) {
     constexpr int C = decltype(cc)::value;
@@ -313,11 +317,11 @@ MOEW2_DEV void a6_ktile(f32x4_t (&acc)[4][kRGW], const uint8_t* abuf, const BReg
       // a row tile with no valid row (the ragged end of an expert's group) skips its instructions
       if (mma && 16 * m < rows_valid) {
 #pragma unroll
-        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<0, C>(cur.p[0], bo[t], acc[m][t], cur.s, br.s[t][0]);
+        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<0, C>(cur.p[0], bo[t], acc[m][t], cur.s, bs[t]);
 #pragma unroll
-        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<1, C>(cur.p[1], bo[t], acc[m][t], cur.s, br.s[t][0]);
+        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<1, C>(cur.p[1], bo[t], acc[m][t], cur.s, bs[t]);
 #pragma unroll
-        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<2, C>(cur.p[2], bo[t], acc[m][t], cur.s, br.s[t][0]);
+        for (int t = 0; t < kRGW; ++t) acc[m][t] = mx6_mfma<2, C>(cur.p[2], bo[t], acc[m][t], cur.s, bs[t]);
       }
       if constexpr (m < 3) cur = nxt;
     });
@@ -495,6 +499,253 @@ gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict
 }
 
 // ------------------------------------------------------------------------------------------------
+// down, streamed across tiles: one workgroup per CU walks its XCD's share of the tile list (the
+// logical order of map_tile: workgroup j of an XCD takes logical tiles lo + j, lo + j + G, ...
+// with G workgroups per XCD, so the tiles in flight on an XCD are still a run of consecutive
+// logical tiles). The k-tiles of consecutive tiles form one stream of steps; a tile is NKT
+// compute steps and one epilogue step, NKT + 1 a multiple of 3, so the three B register sets
+// and three A stages keep static roles (position p of a tile reads B set p % 3 and A stage
+// p % 3). Step p requests A k-tile p + 1 and B k-tile p + 2; past the tile's end those are the
+// next tile's first k-tiles (its A k-tile 0 goes to stage 0 from the last compute step on, B
+// k-tiles 0 and 1 to sets 0 and 1), and the B load aimed at the epilogue position repeats the
+// last k-tile. So a tile starts on loads already in flight and no step only fills or drains.
+//
+// The epilogue step stores the finished tile's rows first and then issues its loads, so "at
+// most kBLoads outstanding" at the next step still means the step's A stage and B k-tile have
+// landed. Its rows go out through the epilogue position's A stage (free in that step): each
+// wave passes 16 rows of its 64 columns at a time through its own part of the stage and stores
+// them as 16-byte pieces, 4 rows x 256 contiguous bytes per instruction.
+// ------------------------------------------------------------------------------------------------
+constexpr int kDnTpStride = 16 * kRGW + 4;           // floats per row (4 mod 8 dwords)
+constexpr int kDnTpRows = 16;                        // rows per pass
+constexpr int kDnTpFloats = kDnTpRows * kDnTpStride; // one wave's part of the stage
+constexpr int kDnPairsOff = 3 * A6Tile::kBytes;
+constexpr int kDnStreamLds = kDnPairsOff + kWaves * 2 * BM * 4;
+static_assert(kWaves * kDnTpFloats * 4 <= A6Tile::kBytes, "epilogue passes fit in one A stage");
+
+// The step loads of the streamed kernel: the same items and groups as KLoads, with the B code and
+// scale loads as raw buffer loads (tile offset in a scalar register, one lane offset for all), so
+// that no per-lane 64-bit B address has to stay live across the stream.
+// Volatile (the compiler-implemented bit of the buffer intrinsics' policy operand): each load
+// stays in its step, is issued once and is never merged with an equal one, so every step issues
+// the loads its counted waits assume.
+constexpr int kVolatileLoad = (int)0x80000000u;
+constexpr uint32_t kOobLoad = 0x7FFFF000u;   // past any plane view (host bound below 2^31)
+template <int FMT>
+struct SLoads {
+  static constexpr int kItems = A6Tile::kPerWave + kBLoads<FMT>;
+  const uint8_t* abase;
+  const uint32_t* aoff;
+  __amdgpu_buffer_rsrc_t codes, scales;
+  uint32_t tb0;
+  int nkt, w, lane;
+
+  template <int N>
+  MOEW2_DEV void item(int ka, uint8_t* stage, int kb, BRegs<FMT>& r) const {
+    if constexpr (N < A6Tile::kPerWave) {
+      const int j = min(w + kWaves * N, A6Tile::kInstr - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(abase + (aoff[N] + (uint32_t)ka * A6Tile::kSrcBytes)),
+                                       (__attribute__((address_space(3))) void*)(stage + 1024 * j), 16, 0, 0);
+      if constexpr (N == A6Tile::kPerWave - 1) {
+        // every DMA instruction of the step goes out before its B loads (see KLoads)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      constexpr int L = WFmt<FMT>::kLoads;
+      constexpr int n = N - A6Tile::kPerWave, t = n / (L + 1), q = n % (L + 1);
+      // kb < 0: a load that only keeps the count, at an out-of-range offset (no memory access)
+      const uint32_t ti = kb < 0 ? (uint32_t)t : tb0 + (uint32_t)(t * nkt + kb);
+      const uint32_t oob = kb < 0 ? kOobLoad : 0u;
+      if constexpr (q < L) {
+        r.c[t][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+            codes, (int)(oob + 1024 * q + 16 * lane), (int)(ti * (uint32_t)WFmt<FMT>::kCodeBytes), kVolatileLoad));
+      } else {
+        // the aligned dword holding this lane's two scale bytes (the upper half for odd lanes,
+        // shifted down where the operand is formed): a 32-bit load needs no zero-extension
+        r.s[t][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(scales, (int)(oob + 4 * (lane >> 1)),
+                                                                    (int)(ti * (uint32_t)kTileScaleBytes), kVolatileLoad);
+      }
+    }
+  }
+  template <int N0, int N1>
+  MOEW2_DEV void items(int ka, uint8_t* stage, int kb, BRegs<FMT>& r) const {
+    if constexpr (N0 < N1) {
+      item<N0>(ka, stage, kb, r);
+      items<N0 + 1, N1>(ka, stage, kb, r);
+    }
+  }
+  template <int I>
+  MOEW2_DEV void group(int ka, uint8_t* stage, int kb, BRegs<FMT>& r) const {
+    items<I * kItems / kGroups, (I + 1) * kItems / kGroups>(ka, stage, kb, r);
+  }
+};
+
+struct DnTile {
+  int e, rs, rows_valid, nb;
+};
+MOEW2_DEV DnTile dn_tile(int logical, const int32_t* tiles, const int32_t* offsets, int n_blocks) {
+  DnTile t;
+  const int ti = logical / n_blocks;
+  t.nb = logical - ti * n_blocks;
+  t.e = tiles[2 * ti];
+  t.rs = tiles[2 * ti + 1];
+  t.rows_valid = min(BM, offsets[t.e + 1] - t.rs);
+  return t;
+}
+
+template <int FMT, int NKT>
+__global__ void __launch_bounds__(kThreads, 1)
+gemm_down_mx_stream_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                           const uint8_t* __restrict__ aq, const int32_t* __restrict__ offsets,
+                           const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
+                           const int32_t* __restrict__ meta, float* __restrict__ pair_out, int P, int K,
+                           int n_blocks, uint32_t n_tiles_b) {
+  static_assert((NKT + 1) % 3 == 0, "a tile is whole rounds of three steps");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int total = meta[1] * n_blocks;
+  const int per_xcd = (total + 7) / 8;
+  const int G = (int)(gridDim.x >> 3);
+  const int lo = (int)(blockIdx.x & 7) * per_xcd, hi = min(lo + per_xcd, total);
+  int lg = lo + (int)(blockIdx.x >> 3);
+  if (lg >= hi) return;
+  const int nrg = K / kTileRows;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const __amdgpu_buffer_rsrc_t out = buffer_view(pair_out, (uint32_t)P * (uint32_t)K * 4u);
+  constexpr int LB = kBLoads<FMT>;
+
+  // the current tile and the next one of this workgroup's walk (the current one again past the
+  // end, so that the loads issued for it stay valid and counted)
+  DnTile cur = dn_tile(lg, tiles, offsets, n_blocks);
+  DnTile nxt = lg + G < hi ? dn_tile(lg + G, tiles, offsets, n_blocks) : cur;
+  auto tb0_of = [&](const DnTile& t) {
+    return (uint32_t)t.e * (uint32_t)(nrg * NKT) + (uint32_t)(kRGW * (t.nb * kWaves + w) * NKT);
+  };
+  const __amdgpu_buffer_rsrc_t crs = buffer_view(codes, (uint32_t)(n_tiles_b * WFmt<FMT>::kCodeBytes));
+  const __amdgpu_buffer_rsrc_t srs = buffer_view(scales, (uint32_t)(n_tiles_b * kTileScaleBytes));
+  // per DMA instruction of this lane, 16 bits: its tile row (bits 10..15) and byte offset within
+  // the row's record (bits 0..9), two to a register; a tile's source offsets are formed from these
+  constexpr int kDesc = (A6Tile::kPerWave + 1) / 2;
+  uint32_t adesc[kDesc];
+  {
+    uint32_t d[A6Tile::kPerWave];
+    a_sources<A6Tile>(d, w, lane, [&](int r) { return (uint32_t)r << 10; });
+#pragma unroll
+    for (int i = 0; i < kDesc; ++i) adesc[i] = d[2 * i] | (2 * i + 1 < A6Tile::kPerWave ? d[2 * i + 1] << 16 : 0u);
+  }
+  static_assert(A6Tile::kSrcBytes <= 1024 && BM <= 64, "descriptor fields");
+  constexpr uint32_t kRecStride = (uint32_t)(NKT * A6Tile::kSrcBytes);
+  auto loads_for = [&](const DnTile& ta, const DnTile& tb, uint32_t (&ao)[A6Tile::kPerWave]) {
+#pragma unroll
+    for (int i = 0; i < A6Tile::kPerWave; ++i) {
+      const uint32_t d = (adesc[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+      ao[i] = (uint32_t)(ta.rs + min((int)(d >> 10), ta.rows_valid - 1)) * kRecStride + (d & 1023u);
+    }
+    return SLoads<FMT>{aq, ao, crs, srs, tb0_of(tb), NKT, w, lane};
+  };
+  // the pair index of each tile row, per wave in LDS past the stages: two tiles' worth (this
+  // tile's for its epilogue, the next one's written during this tile)
+  int* wpairs = reinterpret_cast<int*>(lds + kDnPairsOff) + w * 2 * BM;
+  auto pair_of = [&](const DnTile& t) { return perm[t.rs + min(lane, t.rows_valid - 1)]; };
+  int par = 0;   // buffer of the current tile's pairs
+  int pr_nxt = 0;
+
+  f32x4_t acc[4][kRGW];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < kRGW; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const Fp4Masks fm = fp4_masks();
+  const int sshift = 16 * (lane & 1);
+  BRegs<FMT> b[3];
+
+  // prologue: the first tile's pairs, A k-tile 0 into stage 0, B k-tiles 0 and 1 into sets 0 and 1
+  {
+    const int pr = pair_of(cur);
+    uint32_t ao[A6Tile::kPerWave];
+    const SLoads<FMT> ld = loads_for(cur, cur, ao);
+    static_for<0, kGroups>([&](auto ic) { ld.template group<decltype(ic)::value>(0, lds, 0, b[0]); });
+    static_for<A6Tile::kPerWave, SLoads<FMT>::kItems>(
+        [&](auto ic) { ld.template item<decltype(ic)::value>(0, lds, 1, b[1]); });
+    wpairs[lane] = pr;   // waits for the pair load only (the oldest)
+  }
+
+  for (;;) {
+    static_for<0, NKT + 1>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      // the step's k-tile (or, at the epilogue position, the previous steps' loads) has landed
+      wait_vm<LB>();
+      lds_barrier();
+      if constexpr (p == 0) pr_nxt = pair_of(nxt);   // landed by the next step's wait
+      if constexpr (p == 1) wpairs[(par ^ 1) * BM + lane] = pr_nxt;
+      // this step's loads: A k-tile p + 1 (the next tile's k-tile 0 into stage 0 from the last
+      // compute step on), B k-tile p + 2 (the epilogue position's set gets out-of-range loads
+      // that only keep the count; then the next tile's k-tiles 0 and 1)
+      constexpr bool a_nxt = p + 1 >= NKT;
+      constexpr int a_stage = a_nxt ? 0 : (p + 1) % 3;
+      constexpr int ka = a_nxt ? 0 : p + 1;
+      constexpr int pb = p + 2;
+      constexpr bool b_nxt = pb > NKT;
+      constexpr int kb = pb < NKT ? pb : (pb == NKT ? -1 : pb - NKT - 1);
+      constexpr int b_set = pb % 3;
+      uint32_t ao[A6Tile::kPerWave];
+      const SLoads<FMT> ld = loads_for(a_nxt ? nxt : cur, b_nxt ? nxt : cur, ao);
+      uint8_t* stage = lds + a_stage * A6Tile::kBytes;
+      if constexpr (p < NKT) {
+        auto part = [&](auto ic) { ld.template group<decltype(ic)::value>(ka, stage, kb, b[b_set]); };
+        a6_ktile(acc, lds + (p % 3) * A6Tile::kBytes, b[p % 3], part, true, cur.rows_valid, lane, fm, sshift);
+      } else {
+        // The B set of this position holds a repeat nobody multiplies; naming its registers here
+        // (landed by this step's wait, so no wait is added) keeps those loads in the instruction
+        // stream, where the counted waits expect them.
+#pragma unroll
+        for (int t = 0; t < kRGW; ++t)
+#pragma unroll
+          for (int q = 0; q < WFmt<FMT>::kLoads; ++q)
+            asm volatile("" ::"v"(b[p % 3].c[t][q]), "v"(b[p % 3].s[t][0]));
+        // epilogue: the finished tile's rows, 16 at a time through this wave's part of the
+        // epilogue position's stage, then the step's loads
+        float* tp = reinterpret_cast<float*>(lds + (p % 3) * A6Tile::kBytes) + w * kDnTpFloats;
+        const uint32_t col = (uint32_t)(16 * kRGW * (cur.nb * kWaves + w) + 4 * (lane & 15));
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int t = 0; t < kRGW; ++t)
+              tp[(4 * (lane >> 4) + r) * kDnTpStride + 16 * t + (lane & 15)] = acc[m][t][r];
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // this wave's part alone
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int rl = 4 * j + (lane >> 4), row = 16 * m + rl;
+            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(tp + rl * kDnTpStride + 4 * (lane & 15));
+            const int pp = wpairs[par * BM + row];
+            // a row past the valid rows goes to an out-of-range offset: dropped, still counted
+            const uint32_t off = row < cur.rows_valid ? ((uint32_t)pp * (uint32_t)K) * 4u + 4u * col : 0xFFFFFFF0u;
+            __builtin_amdgcn_raw_buffer_store_b128(v, out, (int)off, 0, 0);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // reads done before the next pass
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);   // the stores go out before the step's loads
+        static_for<0, kGroups>([&](auto ic) { ld.template group<decltype(ic)::value>(ka, stage, kb, b[b_set]); });
+      }
+    });
+    lg += G;
+    if (lg >= hi) break;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < kRGW; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    cur = nxt;
+    par ^= 1;
+    nxt = lg + G < hi ? dn_tile(lg + G, tiles, offsets, n_blocks) : cur;
+  }
+  wait_vm<0>();   // no DMA may still target this workgroup's LDS
+}
+
+// ------------------------------------------------------------------------------------------------
 // NVFP4 planes (e2m1 codes, one E4M3 scale per 16 values, fp32 scale_2 per tensor; layout in
 // common.h). Their block-16 scales carry mantissa bits, which the block-scaled instruction's
 // UE8M0 scales cannot, so these GEMMs run on the 16 x 16 x 32 bf16 (gate_up: A = x as it is) and
@@ -658,6 +909,20 @@ gemm_down_nv4_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restric
 
 }  // namespace
 
+// One workgroup per compute unit (a whole number per XCD) for the streamed kernels; the count is
+// read once per device.
+inline unsigned stream_grid() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 256;
+    cus[dev] = n;
+  }
+  return (unsigned)(cus[dev] / 8 * 8);
+}
+
 inline unsigned gemm_grid(int max_tiles, int n_blocks) {
   const long long g = (long long)max_tiles * n_blocks;
   return (unsigned)((g + 7) / 8 * 8);
@@ -699,6 +964,19 @@ hipError_t launch_gemm_down(const moe_w2_planes* p, int T, int top_k, const Work
                        (const _Float16*)(wsb + ws.aq), (const int32_t*)(wsb + ws.offsets),
                        (const int32_t*)(wsb + ws.perm), (const int32_t*)(wsb + ws.tiles),
                        (const int32_t*)(wsb + ws.meta), (float*)(wsb + ws.pair_out), p->K, p->I, nblk);
+    return hipGetLastError();
+  }
+  // the streamed kernel (2-bit planes; the MXFP4 instance would not fit its registers): tiles of
+  // 8 k-tiles, whole N-blocks, pair rows and planes addressable by 31-bit buffer offsets
+  const long long b_tiles = (long long)p->E * (p->K / kTileRows) * (p->I / kTileK);   // down B tiles
+  if (p->fmt == kFmtW2 && p->I == 8 * kTileK && p->K % BN == 0 && (long long)P * p->K * 4 < (1ll << 31) &&
+      b_tiles * kTileCodeBytes < (1ll << 30)) {
+    auto kern = gemm_down_mx_stream_kernel<kFmtW2, 8>;
+    hipLaunchKernelGGL(kern, dim3(stream_grid()), dim3(kThreads), kDnStreamLds, s,
+                       p->dn_codes, p->dn_scales, (const uint8_t*)(wsb + ws.aq),
+                       (const int32_t*)(wsb + ws.offsets), (const int32_t*)(wsb + ws.perm),
+                       (const int32_t*)(wsb + ws.tiles), (const int32_t*)(wsb + ws.meta),
+                       (float*)(wsb + ws.pair_out), P, p->K, nblk, (uint32_t)b_tiles);
     return hipGetLastError();
   }
   auto kern = p->fmt == kFmtW4 ? gemm_down_mx_kernel<kFmtW4> : gemm_down_mx_kernel<kFmtW2>;

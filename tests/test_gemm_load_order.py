@@ -66,3 +66,51 @@ def test_no_lds_read_after_last_mfma_before_barrier(asm):
         n += 1
         assert not any(op.startswith("ds_read") for op in s[mf[-1] + 1:]), kern
     assert n >= 8
+
+
+def _kernel_sections(lines, name_part):
+    """Instruction lists of one kernel, split at each s_barrier; each section but the first is
+    preceded by the last instruction of the previous one (the step's wait)."""
+    out, cur, inside = [], [], False
+    for l in lines:
+        if re.match(r"^_Z\w+:", l):
+            if inside:
+                break
+            inside = name_part in l
+            continue
+        t = l.strip()
+        if not inside or not t or t.startswith((";", ".")):
+            continue
+        if t == "s_barrier":
+            out.append(cur)
+            cur = []
+        else:
+            cur.append(t)
+    out.append(cur)
+    return out
+
+
+def test_streamed_down_gemm_keeps_its_load_counts(asm):
+    """The streamed down GEMM (k-tiles of consecutive tiles as one stream) relies on every step
+    issuing the same loads: 5 direct-to-LDS A loads, then 8 B loads (4 code, 4 scale), before the
+    next step's wait for at most 8 outstanding; and on the epilogue step issuing its 16 row stores
+    before its loads. Nothing may wait for every outstanding load inside the tile loop."""
+    secs = _kernel_sections(asm, "gemm_down_mx_stream_kernelILi0ELi8E")
+    assert len(secs) == 10, len(secs)            # prologue, then positions 0..8 of a tile
+    ops = [[x.split()[0] for x in s] for s in secs]
+    for i in range(9):                           # the wait ending each section
+        waits = [x for x in secs[i] if x.startswith("s_waitcnt") and "vmcnt" in x]
+        assert waits and waits[-1] == "s_waitcnt vmcnt(8)", (i, waits)
+    for i, s in enumerate(ops[1:], start=1):
+        dma = [j for j, op in enumerate(s) if op == "global_load_lds_dwordx4"]
+        bl = [j for j, op in enumerate(s) if op in ("buffer_load_dwordx4", "buffer_load_dword")]
+        assert len(dma) == 5 and len(bl) == 8, (i, len(dma), len(bl))
+        assert max(dma) < min(bl), i
+        assert s.count("buffer_load_dwordx4") == 4, i
+        if i < 9:
+            assert not any(x.startswith("s_waitcnt") and "vmcnt(0)" in x for x in secs[i]), i
+    st = [j for j, op in enumerate(ops[9]) if op == "buffer_store_dwordx4"]
+    loads = [j for j, op in enumerate(ops[9]) if op in ("global_load_lds_dwordx4", "buffer_load_dwordx4",
+                                                         "buffer_load_dword")]
+    assert len(st) == 16 and max(st) < min(loads)
+    assert not any(op.startswith("scratch_") for s in ops for op in s)   # no spills

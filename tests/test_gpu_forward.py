@@ -69,6 +69,10 @@ CASES = [
     (20, 512, 1024, 64, 8, 27, False),  # >= 32 groups, I/256 a multiple of 4: two row pairs per wave in down
     (24, 768, 768, 48, 6, 28, True),    # >= 32 groups, I/256 = 3: one row pair per wave, 4 per workgroup
     (40, 256, 256, 1024, 8, 29, True),  # E = 1024, the most experts a layer may have
+    # I = 2048 with K a multiple of 512: the down GEMM streams k-tiles across the tiles a workgroup
+    # walks (one workgroup per compute unit)
+    (256, 1024, 2048, 256, 8, 30, False),  # ~8 rows per expert: 512 down tiles, 2 per workgroup, ragged
+    (512, 2048, 2048, 16, 8, 31, True),    # Zipf groups of several M-tiles: 320 down tiles
 ]
 
 
