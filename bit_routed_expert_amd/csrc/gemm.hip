@@ -530,7 +530,8 @@ static_assert(kWaves * kDnTpFloats * 4 <= A6Tile::kBytes, "epilogue passes fit i
 // stays in its step, is issued once and is never merged with an equal one, so every step issues
 // the loads its counted waits assume.
 constexpr int kVolatileLoad = (int)0x80000000u;
-constexpr uint32_t kOobLoad = 0x7FFFF000u;   // past any plane view (host bound below 2^31)
+constexpr uint32_t kOobLoad = 0x7FFFF000u;   // past any plane view (views up to kMaxPlaneView bytes)
+constexpr long long kMaxPlaneView = 0x7FFF0000ll;
 template <int FMT>
 struct SLoads {
   static constexpr int kItems = A6Tile::kPerWave + kBLoads<FMT>;
@@ -970,7 +971,7 @@ hipError_t launch_gemm_down(const moe_w2_planes* p, int T, int top_k, const Work
   // 8 k-tiles, whole N-blocks, pair rows and planes addressable by 31-bit buffer offsets
   const long long b_tiles = (long long)p->E * (p->K / kTileRows) * (p->I / kTileK);   // down B tiles
   if (p->fmt == kFmtW2 && p->I == 8 * kTileK && p->K % BN == 0 && (long long)P * p->K * 4 < (1ll << 31) &&
-      b_tiles * kTileCodeBytes < (1ll << 30)) {
+      b_tiles * kTileCodeBytes <= kMaxPlaneView) {
     auto kern = gemm_down_mx_stream_kernel<kFmtW2, 8>;
     hipLaunchKernelGGL(kern, dim3(stream_grid()), dim3(kThreads), kDnStreamLds, s,
                        p->dn_codes, p->dn_scales, (const uint8_t*)(wsb + ws.aq),
