@@ -12,10 +12,12 @@ from gpu_helpers import dev, dev_bf16, pack
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T,path", [(8, moe.PATH_DECODE), (100, moe.PATH_DECODE_SORTED), (200, moe.PATH_GEMM)])
-def test_graph_replays_match_eager(gpu, T, path):
+@pytest.mark.parametrize("T,path,I", [(8, moe.PATH_DECODE, 512), (100, moe.PATH_DECODE_SORTED, 512),
+                                      (200, moe.PATH_GEMM, 512),
+                                      (200, moe.PATH_GEMM, 2048)])   # the down GEMM streamed across tiles
+def test_graph_replays_match_eager(gpu, T, path, I):
     rng = np.random.default_rng(5 + T)
-    K, I, E, top_k = 512, 512, 16, 4
+    K, E, top_k = 512, 16, 4
     planes = workloads.draw_planes(rng, E, K, I)
     h = pack(planes)
     a = [(dev_bf16(workloads.draw_x(rng, T, K)),) + tuple(dev(v) for v in workloads.uniform_routing(rng, T, E, top_k))

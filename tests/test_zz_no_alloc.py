@@ -62,6 +62,26 @@ def test_noalloc_forced_paths_and_repeat(layer):
             assert torch.equal(y.view(torch.int32), want.view(torch.int32))
 
 
+def test_noalloc_streamed_down_gemm(gpu):
+    """I = 2048 with K a multiple of 512: the GEMM organisation's down stage is the streamed kernel
+    (one workgroup per compute unit); two calls in a row, the second smaller, bit-identical to the
+    workspace entry point."""
+    rng = np.random.default_rng(43)
+    K, I, E, top_k = 512, 2048, 32, 4
+    h = pack(workloads.draw_planes(rng, E, K, I))
+    try:
+        for i, T in enumerate((300, 150)):   # 1200 and 600 pairs
+            x, ids, w = _inputs(T, top_k, E, K, 200 + i)
+            want = moe.moe_w2_forward(h, x, ids, w, out_dtype=moe.OUT_F32, path=moe.PATH_GEMM)
+            y = torch.full((T, K), float("nan"), dtype=torch.float32, device="cuda")
+            moe.moe_w2_forward_noalloc(h, x, ids, w, y, out_dtype=moe.OUT_F32, path=moe.PATH_GEMM)
+            torch.cuda.synchronize()
+            print(f"noalloc streamed down T={T}", flush=True)
+            assert torch.equal(y.view(torch.int32), want.view(torch.int32))
+    finally:
+        h.free()
+
+
 def test_noalloc_rejects_calls_beyond_the_scratch(layer):
     """A call whose workspace exceeds MOE_W2_NOALLOC_SCRATCH_BYTES returns EUNSUPPORTED on the host."""
     K, top_k = 1024, 8
