@@ -507,8 +507,9 @@ gemm_down_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict
 // and three A stages keep static roles (position p of a tile reads B set p % 3 and A stage
 // p % 3). Step p requests A k-tile p + 1 and B k-tile p + 2; past the tile's end those are the
 // next tile's first k-tiles (its A k-tile 0 goes to stage 0 from the last compute step on, B
-// k-tiles 0 and 1 to sets 0 and 1), and the B load aimed at the epilogue position repeats the
-// last k-tile. So a tile starts on loads already in flight and no step only fills or drains.
+// k-tiles 0 and 1 to sets 0 and 1), and the B loads aimed at the epilogue position (which
+// multiplies nothing) only keep the count (out-of-range offsets, no memory access). So a tile
+// starts on loads already in flight and no step only fills or drains.
 //
 // The epilogue step stores the finished tile's rows first and then issues its loads, so "at
 // most kBLoads outstanding" at the next step still means the step's A stage and B k-tile have
@@ -526,9 +527,11 @@ static_assert(kWaves * kDnTpFloats * 4 <= A6Tile::kBytes, "epilogue passes fit i
 // The step loads of the streamed kernel: the same items and groups as KLoads, with the B code and
 // scale loads as raw buffer loads (tile offset in a scalar register, one lane offset for all), so
 // that no per-lane 64-bit B address has to stay live across the stream.
-// Volatile (the compiler-implemented bit of the buffer intrinsics' policy operand): each load
-// stays in its step, is issued once and is never merged with an equal one, so every step issues
-// the loads its counted waits assume.
+// Volatile (the compiler-implemented bit of the buffer intrinsics' policy operand): the compiler
+// keeps each load in its step instead of moving it to another one. Loads with equal operands can
+// still be merged into one, so the count-keeping loads use distinct offsets (one per row group)
+// and their registers are named at the epilogue position; every step then issues the loads its
+// counted waits assume (checked in the assembly by the tests).
 constexpr int kVolatileLoad = (int)0x80000000u;
 constexpr uint32_t kOobLoad = 0x7FFFF000u;   // past any plane view (views up to kMaxPlaneView bytes)
 constexpr long long kMaxPlaneView = 0x7FFF0000ll;
