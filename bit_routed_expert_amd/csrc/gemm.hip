@@ -971,11 +971,12 @@ hipError_t launch_gemm_down(const moe_w2_planes* p, int T, int top_k, const Work
     return hipGetLastError();
   }
   // the streamed kernel (2-bit planes; the MXFP4 instance would not fit its registers): tiles of
-  // 8 k-tiles, whole N-blocks, pair rows and planes addressable by 31-bit buffer offsets
+  // 8 or 2 k-tiles (I = 2048, or 512 as on a 4-way tensor-parallel rank: with the epilogue
+  // position a multiple of 3), whole N-blocks, pair rows and planes addressable by 31-bit offsets
   const long long b_tiles = (long long)p->E * (p->K / kTileRows) * (p->I / kTileK);   // down B tiles
-  if (p->fmt == kFmtW2 && p->I == 8 * kTileK && p->K % BN == 0 && (long long)P * p->K * 4 < (1ll << 31) &&
-      b_tiles * kTileCodeBytes <= kMaxPlaneView) {
-    auto kern = gemm_down_mx_stream_kernel<kFmtW2, 8>;
+  if (p->fmt == kFmtW2 && (p->I == 8 * kTileK || p->I == 2 * kTileK) && p->K % BN == 0 &&
+      (long long)P * p->K * 4 < (1ll << 31) && b_tiles * kTileCodeBytes <= kMaxPlaneView) {
+    auto kern = p->I == 8 * kTileK ? gemm_down_mx_stream_kernel<kFmtW2, 8> : gemm_down_mx_stream_kernel<kFmtW2, 2>;
     hipLaunchKernelGGL(kern, dim3(stream_grid()), dim3(kThreads), kDnStreamLds, s,
                        p->dn_codes, p->dn_scales, (const uint8_t*)(wsb + ws.aq),
                        (const int32_t*)(wsb + ws.offsets), (const int32_t*)(wsb + ws.perm),

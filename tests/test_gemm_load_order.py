@@ -90,15 +90,17 @@ def _kernel_sections(lines, name_part):
     return out
 
 
-def test_streamed_down_gemm_keeps_its_load_counts(asm):
+@pytest.mark.parametrize("nkt", [8, 2])
+def test_streamed_down_gemm_keeps_its_load_counts(asm, nkt):
     """The streamed down GEMM (k-tiles of consecutive tiles as one stream) relies on every step
     issuing the same loads: 5 direct-to-LDS A loads, then 8 B loads (4 code, 4 scale), before the
     next step's wait for at most 8 outstanding; and on the epilogue step issuing its 16 row stores
     before its loads. Nothing may wait for every outstanding load inside the tile loop."""
-    secs = _kernel_sections(asm, "gemm_down_mx_stream_kernelILi0ELi8E")
-    assert len(secs) == 10, len(secs)            # prologue, then positions 0..8 of a tile
+    secs = _kernel_sections(asm, f"gemm_down_mx_stream_kernelILi0ELi{nkt}E")
+    last = nkt + 1                               # the epilogue position's section
+    assert len(secs) == nkt + 2, len(secs)       # prologue, then positions 0..nkt of a tile
     ops = [[x.split()[0] for x in s] for s in secs]
-    for i in range(9):                           # the wait ending each section
+    for i in range(last):                        # the wait ending each section
         waits = [x for x in secs[i] if x.startswith("s_waitcnt") and "vmcnt" in x]
         assert waits and waits[-1] == "s_waitcnt vmcnt(8)", (i, waits)
     for i, s in enumerate(ops[1:], start=1):
@@ -107,10 +109,10 @@ def test_streamed_down_gemm_keeps_its_load_counts(asm):
         assert len(dma) == 5 and len(bl) == 8, (i, len(dma), len(bl))
         assert max(dma) < min(bl), i
         assert s.count("buffer_load_dwordx4") == 4, i
-        if i < 9:
+        if i < last:
             assert not any(x.startswith("s_waitcnt") and "vmcnt(0)" in x for x in secs[i]), i
-    st = [j for j, op in enumerate(ops[9]) if op == "buffer_store_dwordx4"]
-    loads = [j for j, op in enumerate(ops[9]) if op in ("global_load_lds_dwordx4", "buffer_load_dwordx4",
-                                                         "buffer_load_dword")]
+    st = [j for j, op in enumerate(ops[last]) if op == "buffer_store_dwordx4"]
+    loads = [j for j, op in enumerate(ops[last]) if op in ("global_load_lds_dwordx4", "buffer_load_dwordx4",
+                                                            "buffer_load_dword")]
     assert len(st) == 16 and max(st) < min(loads)
     assert not any(op.startswith("scratch_") for s in ops for op in s)   # no spills

@@ -75,6 +75,7 @@ CASES = [
     (512, 2048, 2048, 16, 8, 31, True),    # Zipf groups of several M-tiles: 320 down tiles
     (65, 512, 2048, 8, 8, 34, False),      # 520 pairs, one N-block: 16 down tiles (8 of one valid row), most workgroups idle
     (150, 768, 2048, 8, 4, 35, True),      # I = 2048 but K not a multiple of 512: the tile-at-a-time down GEMM
+    (300, 1024, 512, 32, 4, 36, True),     # I = 512 (2 k-tiles per tile): the streamed down GEMM's short form
     # K = 3072 and 6144 (12 and 24 k-tiles) over many experts of few rows: several gate_up tiles per
     # row of workgroups
     (256, 3072, 512, 256, 8, 32, False),   # ~8 rows per expert: ~520 gate_up tiles
