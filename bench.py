@@ -335,6 +335,10 @@ def main():
     }
 
     out["cold_calls"] = bench_cold_calls(torch, moe, layers, inst, ws, ys, per_batch)
+    # the 2-bit prefill leg (the other headline workload) next, then the secondary legs
+    zipf_host = None
+    if not args.no_prefill:
+        out["prefill"], out["zipf_decode"], zipf_host = bench_prefill(args, moe, workloads, torch, dev)
     if not args.no_shards:
         out["tp_shards"] = bench_shards(args, moe, workloads, torch, dev, inst)
     if not args.no_slots:
@@ -342,9 +346,6 @@ def main():
     if not args.no_w4:
         out["w4"] = bench_w4(args, moe, workloads, torch, dev, inst, E, top_k, K, I)
         out["nvfp4"] = bench_nvfp4(args, moe, workloads, torch, dev, inst, E, top_k, K, I)
-    zipf_host = None
-    if not args.no_prefill:
-        out["prefill"], out["zipf_decode"], zipf_host = bench_prefill(args, moe, workloads, torch, dev)
     if not args.no_requant:
         out["requant"] = bench_requant(args, moe, workloads, torch, dev)
     if not args.no_sweep:
@@ -461,6 +462,41 @@ def bench_shards(args, moe, workloads, torch, dev, inst):
         return dict(fwd_us=round(us, 2), hbm_GBps=round(gbps, 1), hbm_frac=round(gbps / HBM_PEAK_GBPS, 4),
                     tokens_per_s=round(T / (us * 1e-6), 1))
 
+    # the 8192-token prefill batch (the prefill leg's Zipf instance) on a rank's share at K=6144:
+    # forward and GEMM stage times, algorithmic flops 2*P*3*(I/G)*K against the bf16 peak
+    pre = None
+    if not args.no_prefill:
+        cp = workloads.PREFILL
+        dp = workloads.zipf_instances(cp["T"], 1, cp["seed"], cp["K"], E, top_k)[0]
+        pre = (torch.from_numpy(dp["x"].view(np.int16)).view(torch.bfloat16).cuda(), dev(dp["topk_ids"]),
+               dev(dp["topk_w"]))
+
+    def prefill_stages(planes, K, I):
+        x, ids, w = pre
+        T = x.shape[0]
+        ws = moe.alloc_workspace(planes, T, top_k)
+        y = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+        for _ in range(2):
+            moe.moe_w2_forward(planes, x, ids, w, workspace=ws, y=y)
+        torch.cuda.synchronize()
+        t = {}
+        for name, st in (("forward", None), ("gate_up", moe.STAGE_GATE_UP), ("down", moe.STAGE_DOWN)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.prefill_iters):
+                if st is None:
+                    moe.moe_w2_forward(planes, x, ids, w, workspace=ws, y=y)
+                else:
+                    moe.moe_w2_forward_stage(st, planes, x, ids, w, y, ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t[name] = e0.elapsed_time(e1) / args.prefill_iters
+        del ws, y
+        fl = 2.0 * T * top_k * 3 * I * K
+        return dict(fwd_ms=round(t["forward"], 4), gate_up_ms=round(t["gate_up"], 4), down_ms=round(t["down"], 4),
+                    gemm_mfma_frac=round(fl / ((t["gate_up"] + t["down"]) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    fwd_mfma_frac=round(fl / (t["forward"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
+
     out = {}
     cz = workloads.DECODE_ZIPF
     zi = workloads.zipf_instances(cz["T"], 16, cz["seed"], cz["K"], E, top_k)
@@ -477,12 +513,15 @@ def bench_shards(args, moe, workloads, torch, dev, inst):
             for T, insts in insts_by_T.items():
                 key = f"T{T}" if K == 4096 else f"zipf_T{T}_K{K}"
                 res[key] = timed(layers, insts, K, I)
+            if K == cz["K"] and pre is not None:
+                res["prefill_T8192_K6144"] = prefill_stages(layers[0], K, I)
             for h in layers:
                 h.free()
             torch.cuda.empty_cache()
         out[f"tp{G}_I{2048 // G}"] = res
     out["workload"] = ("one rank's share under tensor parallelism over I: moe_w2 decode K=4096 E=256 top-8 uniform "
-                       "routing at T=1,8,32 and the Zipf(1.1) T=64 batch at K=6144, I = 2048/G")
+                       "routing at T=1,8,32 and the Zipf(1.1) T=64 batch at K=6144, I = 2048/G; with the prefill "
+                       "leg, the T=8192 Zipf(1.1) batch at K=6144 on the same shard planes (GEMM stages)")
     return out
 
 
